@@ -1,0 +1,403 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against one of: a brute-force dense merge in numpy
+fp64 (W = s * At^T B formed first, then y + x W), exact small-integer
+arithmetic, closed forms of the scale, the skip / padding / linearity /
+permutation invariants, textbook special cases (rank 1, At = I), torch's own
+bf16 rounding, and the example adapter_config printed on the pages.  Together
+they fail on a dropped term, a flipped sign, a swapped index or operand, a scale
+taken from the padded rank, or a wrong rounding.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lora_adapter_application_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def _brute_dense_merge(x, y, idx, adapters):
+    """y + x @ W_k with W_k = s_k * At_k^T @ B_k formed first (fp64), per token."""
+    x = np.asarray(x, np.float64)
+    out = np.asarray(y, np.float64).copy()
+    for t in range(x.shape[0]):
+        k = int(idx[t])
+        if k < 0 or k >= len(adapters) or adapters[k] is None:
+            continue
+        a = adapters[k]
+        s = a["lora_alpha"] / (math.sqrt(a["r"]) if a.get("use_rslora") else a["r"])
+        W = s * (np.asarray(a["At"], np.float64).T @ np.asarray(a["B"], np.float64))
+        out[t] = out[t] + x[t] @ W
+    return out
+
+
+def _rand_adapters(rng, n, d_in, d_out, ranks, rslora=False, scale=0.3):
+    ads = []
+    for k in range(n):
+        r = ranks[k]
+        if r == 0:
+            ads.append(None)
+            continue
+        ads.append({"r": r, "lora_alpha": 2.0 * r + 1.0, "use_rslora": rslora,
+                    "At": _f32(rng.standard_normal((r, d_in)) * scale),
+                    "B": _f32(rng.standard_normal((r, d_out)) * scale)})
+    return ads
+
+
+# ---------------------------------------------------------------------------
+# brute force
+
+@pytest.mark.parametrize("rslora", [False, True])
+def test_brute_force_dense_merge_fp32(rslora):
+    rng = np.random.default_rng(7)
+    T, d_in, d_out = 24, 40, 56                     # d_in != d_out != r: a transposed operand fails
+    ads = _rand_adapters(rng, 5, d_in, d_out, [1, 3, 8, 0, 5], rslora=rslora)
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = rng.integers(-1, 6, size=T).astype(np.int32)    # includes -1, empty slot 3, and 5 >= n
+    got = oracle.apply(oracle.FP32, x, y, idx, ads)
+    ref = _brute_dense_merge(x, y, idx, ads)
+    np.testing.assert_allclose(got.astype(np.float64), ref, rtol=1e-6, atol=1e-6)
+    # the oracle rounds once: at most one fp32 ulp from the fp64 brute force rounded once
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - ref.astype(np.float32).astype(np.float64)) <= ulp)
+
+
+def test_brute_force_with_base_weight():
+    """x W + delta == x (W + s At^T B): the merged-weight form of the update."""
+    rng = np.random.default_rng(11)
+    T, d_in, d_out = 12, 32, 20
+    ads = _rand_adapters(rng, 2, d_in, d_out, [4, 6])
+    x = _f32(rng.standard_normal((T, d_in)))
+    W0 = rng.standard_normal((d_in, d_out)) * 0.2
+    idx = np.array([0, 1] * (T // 2), dtype=np.int32)
+    y_base = _f32(x.astype(np.float64) @ W0)
+    got = oracle.apply(oracle.FP32, x, y_base, idx, ads).astype(np.float64)
+    merged = np.empty((T, d_out))
+    for t in range(T):
+        a = ads[idx[t]]
+        W = W0 + (a["lora_alpha"] / a["r"]) * (a["At"].astype(np.float64).T @ a["B"].astype(np.float64))
+        merged[t] = x[t].astype(np.float64) @ W
+    np.testing.assert_allclose(got, merged, rtol=2e-6, atol=2e-6)
+
+
+def test_bf16_matches_brute_force_within_one_rounding():
+    rng = np.random.default_rng(3)
+    T, d_in, d_out = 16, 64, 48
+    ads32 = _rand_adapters(rng, 3, d_in, d_out, [2, 4, 8])
+    ads = []
+    for a in ads32:
+        ads.append({**a, "At": synth.to_bf16_bits(a["At"]), "B": synth.to_bf16_bits(a["B"])})
+    x = synth.to_bf16_bits(rng.standard_normal((T, d_in)).astype(np.float32))
+    y = synth.to_bf16_bits(rng.standard_normal((T, d_out)).astype(np.float32))
+    idx = rng.integers(-1, 3, size=T).astype(np.int32)
+    got = synth.bf16_bits_to_f32(oracle.apply(oracle.BF16, x, y, idx, ads)).astype(np.float64)
+    ads_f = [{**a, "At": synth.bf16_bits_to_f32(a["At"]), "B": synth.bf16_bits_to_f32(a["B"])}
+             for a in ads]
+    ref = _brute_dense_merge(synth.bf16_bits_to_f32(x), synth.bf16_bits_to_f32(y), idx, ads_f)
+    # one bf16 rounding of the exact value: within half a bf16 ulp (2^-8 relative), plus fp64 noise
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 * 1.0001 + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# exact small-integer arithmetic
+
+@pytest.mark.parametrize("dtype", [oracle.FP32, oracle.BF16])
+def test_exact_integers_bit_identical(dtype):
+    rng = np.random.default_rng(5)
+    if dtype == oracle.FP32:
+        T, d_in, d_out, ranks, lim = 32, 64, 48, [8, 4, 1, 8], 2
+    else:
+        T, d_in, d_out, ranks, lim = 32, 8, 24, [2, 1, 2, 2], 1   # final |y| <= 256: exact in bf16
+    ads, ads_int = [], []
+    for r in ranks:
+        At = rng.integers(-lim, lim + 1, (r, d_in))
+        B = rng.integers(-lim, lim + 1, (r, d_out))
+        ads_int.append((r, At, B))
+        cast = (lambda a: synth.to_bf16_bits(a.astype(np.float32))) if dtype == oracle.BF16 else _f32
+        ads.append({"r": r, "lora_alpha": 2.0 * r, "use_rslora": False, "At": cast(At), "B": cast(B)})
+    x_int = rng.integers(-lim, lim + 1, (T, d_in))
+    y_int = rng.integers(-lim, lim + 1, (T, d_out))
+    idx = rng.integers(-1, len(ranks), size=T).astype(np.int32)
+    if dtype == oracle.BF16:
+        x, y = synth.to_bf16_bits(x_int.astype(np.float32)), synth.to_bf16_bits(y_int.astype(np.float32))
+    else:
+        x, y = _f32(x_int), _f32(y_int)
+    got = oracle.apply(dtype, x, y, idx, ads)
+    expect = y_int.copy()
+    for t in range(T):
+        k = idx[t]
+        if k < 0:
+            continue
+        r, At, B = ads_int[k]
+        expect[t] += 2 * ((x_int[t] @ At.T) @ B)                  # s = alpha / r = 2, integer math
+    assert np.abs(expect).max() < (2 ** 24 if dtype == oracle.FP32 else 256)
+    exp_bits = synth.to_bf16_bits(expect.astype(np.float32)) if dtype == oracle.BF16 else _f32(expect)
+    assert np.array_equal(got.view(np.uint8), exp_bits.view(np.uint8))
+
+
+@pytest.mark.parametrize("r", [4, 16, 64])
+def test_rslora_scale_exact_integer(r):
+    """alpha = c * sqrt(r) with sqrt(r) an integer gives s = c exactly under rsLoRA."""
+    c = 3.0
+    alpha = c * math.isqrt(r)
+    assert oracle.scale(alpha, r, True) == c
+    rng = np.random.default_rng(r)
+    d_in, d_out, T = 16, 16, 8
+    At = rng.integers(-1, 2, (r, d_in)).astype(np.float32)
+    B = rng.integers(-1, 2, (r, d_out)).astype(np.float32)
+    x = rng.integers(-2, 3, (T, d_in)).astype(np.float32)
+    y = np.zeros((T, d_out), np.float32)
+    got = oracle.apply(oracle.FP32, x, y, np.zeros(T, np.int32),
+                       [{"r": r, "lora_alpha": alpha, "use_rslora": True, "At": At, "B": B}])
+    expect = c * ((x.astype(np.int64) @ At.T.astype(np.int64)) @ B.astype(np.int64))
+    assert np.array_equal(got, expect.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# closed forms of the scale, including the pages' example adapter config
+
+def test_scale_from_page_example_config():
+    cfg = json.load(open(os.path.join(GOLDEN, "adapter_config_example.json")))
+    assert cfg["peft_type"] == "LORA" and cfg["use_rslora"] is False
+    r, alpha = cfg["r"], cfg["lora_alpha"]
+    assert (r, alpha) == (16, 32)
+    assert oracle.scale(alpha, r, cfg["use_rslora"]) == 2.0        # 32 / 16
+    assert oracle.scale(alpha, r, True) == 8.0                     # 32 / sqrt(16)
+
+
+def test_scale_closed_form_qwen_rslora():
+    # alpha 64, rank 32, rsLoRA: 64 / sqrt(32) = 8 * sqrt(2)
+    s = oracle.scale(64.0, 32, True)
+    assert abs(s - 8.0 * math.sqrt(2.0)) <= 2 * np.spacing(s)
+    assert np.float32(s) == np.float32(11.313708498984761)
+
+
+def test_scale_through_identity_adapter():
+    """d_in = r = d_out, At = I, B = I: the update is exactly s * x."""
+    r = 16
+    I = np.eye(r, dtype=np.float32)
+    x = _f32(np.random.default_rng(2).integers(-8, 9, (5, r)))
+    y = np.zeros((5, r), np.float32)
+    for rs, s in ((False, 2.0), (True, 8.0)):
+        got = oracle.apply(oracle.FP32, x, y, np.zeros(5, np.int32),
+                           [{"r": r, "lora_alpha": 32.0, "use_rslora": rs, "At": I, "B": I}])
+        assert np.array_equal(got, s * x)
+
+
+# ---------------------------------------------------------------------------
+# skip semantics and invariants
+
+def test_skip_leaves_rows_bit_identical():
+    rng = np.random.default_rng(9)
+    T, d_in, d_out = 40, 32, 24
+    ads = _rand_adapters(rng, 4, d_in, d_out, [4, 0, 2, 3])        # slot 1 empty
+    ads[3] = None                                                  # "module not targeted"
+    x = _f32(rng.standard_normal((T, d_in)))
+    # y rows with arbitrary finite bit patterns, including -0.0 and subnormals
+    y = rng.integers(0, 2 ** 32, size=(T, d_out), dtype=np.uint64).astype(np.uint32)
+    y[(y & 0x7F800000) == 0x7F800000] &= 0xBFFFFFFF                 # no inf / nan
+    y = y.view(np.float32)
+    idx = np.array([-1, -7, 1, 3, 4, 99, 0, 2] * 5, dtype=np.int32)
+    got = oracle.apply(oracle.FP32, x, y, idx, ads)
+    skipped = np.isin(idx, [0, 2], invert=True)
+    assert np.array_equal(got[skipped].view(np.uint32), y[skipped].view(np.uint32))
+    assert not np.array_equal(got[~skipped].view(np.uint32), y[~skipped].view(np.uint32))
+
+
+def test_zero_padding_is_bit_identical():
+    rng = np.random.default_rng(13)
+    T, d_in, d_out, R = 20, 48, 40, 64
+    for dtype in (oracle.FP32, oracle.BF16):
+        cast = _f32 if dtype == oracle.FP32 else (lambda a: synth.to_bf16_bits(_f32(a)))
+        ads, padded = [], []
+        for r in (3, 8, 16):
+            At = cast(rng.standard_normal((r, d_in)))
+            B = cast(rng.standard_normal((r, d_out)))
+            ads.append({"r": r, "lora_alpha": 2.0 * r, "use_rslora": False, "At": At, "B": B})
+            Atp = np.zeros((R, d_in), At.dtype); Atp[:r] = At
+            Bp = np.zeros((R, d_out), B.dtype); Bp[:r] = B
+            # the padded copy keeps the adapter's own r in the scale (alpha scaled to match)
+            padded.append({"r": R, "lora_alpha": 2.0 * r * R / r, "use_rslora": False,
+                           "At": Atp, "B": Bp})
+        x = cast(rng.standard_normal((T, d_in)))
+        y = cast(rng.standard_normal((T, d_out)))
+        idx = rng.integers(0, 3, size=T).astype(np.int32)
+        a = oracle.apply(dtype, x, y, idx, ads)
+        b = oracle.apply(dtype, x, y, idx, padded)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_scale_uses_adapter_rank_not_padding():
+    """Same weights under rank r and zero-padded rank R with the same alpha differ by r/R."""
+    rng = np.random.default_rng(17)
+    r, R = 4, 16
+    At = _f32(rng.integers(-2, 3, (r, 8)))
+    B = _f32(rng.integers(-2, 3, (r, 8)))
+    Atp = np.zeros((R, 8), np.float32); Atp[:r] = At
+    Bp = np.zeros((R, 8), np.float32); Bp[:r] = B
+    x = _f32(rng.integers(-2, 3, (3, 8)))
+    y = np.zeros((3, 8), np.float32)
+    a = oracle.apply(oracle.FP32, x, y, np.zeros(3, np.int32),
+                     [{"r": r, "lora_alpha": 8.0, "use_rslora": False, "At": At, "B": B}])
+    b = oracle.apply(oracle.FP32, x, y, np.zeros(3, np.int32),
+                     [{"r": R, "lora_alpha": 8.0, "use_rslora": False, "At": Atp, "B": Bp}])
+    assert np.array_equal(a, b * (R / r))
+
+
+def test_linearity_in_x_exact():
+    rng = np.random.default_rng(19)
+    T, d_in, d_out = 16, 32, 24
+    ads = []
+    for r in (4, 8):
+        ads.append({"r": r, "lora_alpha": 2.0 * r, "use_rslora": False,
+                    "At": _f32(rng.integers(-2, 3, (r, d_in))),
+                    "B": _f32(rng.integers(-2, 3, (r, d_out)))})
+    x1 = _f32(rng.integers(-2, 3, (T, d_in)))
+    x2 = _f32(rng.integers(-2, 3, (T, d_in)))
+    y0 = np.zeros((T, d_out), np.float32)
+    idx = rng.integers(0, 2, size=T).astype(np.int32)
+    d = lambda x: oracle.apply(oracle.FP32, x, y0, idx, ads)
+    assert np.array_equal(d(2.0 * x1 - 0.5 * x2), 2.0 * d(x1) - 0.5 * d(x2))
+    # and within fp32 rounding for random real data
+    ads_r = _rand_adapters(rng, 2, d_in, d_out, [4, 8])
+    xa, xb = _f32(rng.standard_normal((T, d_in))), _f32(rng.standard_normal((T, d_in)))
+    dr = lambda x: oracle.apply(oracle.FP32, x, y0, idx, ads_r).astype(np.float64)
+    np.testing.assert_allclose(dr(_f32(3 * xa + xb)), 3 * dr(xa) + dr(xb), rtol=1e-5, atol=1e-5)
+
+
+def test_rank_one_is_a_scaled_outer_product():
+    rng = np.random.default_rng(23)
+    a = rng.integers(-3, 4, 12).astype(np.float32)
+    b = rng.integers(-3, 4, 10).astype(np.float32)
+    x = rng.integers(-3, 4, (6, 12)).astype(np.float32)
+    y = np.zeros((6, 10), np.float32)
+    got = oracle.apply(oracle.FP32, x, y, np.zeros(6, np.int32),
+                       [{"r": 1, "lora_alpha": 5.0, "use_rslora": False,
+                         "At": a[None, :], "B": b[None, :]}])
+    assert np.array_equal(got, 5.0 * np.outer(x @ a, b))
+
+
+def test_identity_down_projection_reduces_to_matmul():
+    """d_in = r and At = I make h = x, so the update is y + s * x B (numpy.matmul, fp64)."""
+    rng = np.random.default_rng(29)
+    r, d_out, T = 8, 24, 10
+    B = _f32(rng.standard_normal((r, d_out)))
+    x = _f32(rng.standard_normal((T, r)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    got = oracle.apply(oracle.FP32, x, y, np.zeros(T, np.int32),
+                       [{"r": r, "lora_alpha": 3.0 * r, "use_rslora": False,
+                         "At": np.eye(r, dtype=np.float32), "B": B}])
+    ref = y.astype(np.float64) + 3.0 * np.matmul(x.astype(np.float64), B.astype(np.float64))
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_permutation_equivariance_bit_identical():
+    rng = np.random.default_rng(31)
+    T, d_in, d_out = 30, 32, 16
+    ads = _rand_adapters(rng, 3, d_in, d_out, [2, 5, 7])
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = rng.integers(-1, 3, size=T).astype(np.int32)
+    p = rng.permutation(T)
+    a = oracle.apply(oracle.FP32, x, y, idx, ads)
+    b = oracle.apply(oracle.FP32, x[p], y[p], idx[p], ads)
+    assert np.array_equal(a[p].view(np.uint32), b.view(np.uint32))
+
+
+def test_empty_batch():
+    y = np.ones((0, 8), np.float32)
+    got = oracle.apply(oracle.FP32, np.ones((0, 4), np.float32), y, np.zeros(0, np.int32),
+                       [{"r": 1, "lora_alpha": 1.0, "use_rslora": False,
+                         "At": np.ones((1, 4), np.float32), "B": np.ones((1, 8), np.float32)}])
+    assert got.shape == (0, 8)
+
+
+def test_threads_do_not_change_bits():
+    rng = np.random.default_rng(37)
+    ads = _rand_adapters(rng, 4, 64, 32, [3, 4, 5, 6])
+    x = _f32(rng.standard_normal((50, 64)))
+    y = _f32(rng.standard_normal((50, 32)))
+    idx = rng.integers(-1, 4, size=50).astype(np.int32)
+    a = oracle.apply(oracle.FP32, x, y, idx, ads, n_threads=1)
+    b = oracle.apply(oracle.FP32, x, y, idx, ads, n_threads=4)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# rounding into bf16, against torch's conversion and textbook ties
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(41)
+    bits = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0x00000000, 0x80000000, 0x00000001, 0x007FFFFF, 0x00800000,
+                         0x3F808000, 0x3F818000, 0x3F80FFFF, 0x7F7FFFFF, 0x7F7F8000,
+                         0x7F7F7FFF, 0xFF7FFFFF, 0x7F800000, 0xFF800000, 0x00008000,
+                         0x00018000, 0x80008000], dtype=np.uint32)
+    vals = np.concatenate([bits, specials]).view(np.float32)
+    vals = vals[~np.isnan(vals)]
+    ref = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.round_bf16(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    assert oracle.round_bf16(float("nan")) == 0x7FC0
+
+
+def test_round_bf16_is_a_single_rounding_from_double():
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1.0
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 0x3F80
+    # 1 + 3 * 2^-8 is halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    # just above the tie: must round up; going through fp32 first would land on the tie
+    assert oracle.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -40)) == 0xBF81
+    # overflow: at and above the midpoint between the largest bf16 and 2^128 -> inf
+    assert oracle.round_bf16(2.0 ** 128 - 2.0 ** 119) == 0x7F80
+    assert oracle.round_bf16(2.0 ** 128 - 2.0 ** 119 - 2.0 ** 100) == 0x7F7F
+    # subnormal quantum 2^-133
+    assert oracle.round_bf16(2.0 ** -133) == 0x0001
+    assert oracle.round_bf16(2.0 ** -134) == 0x0000                # tie to even (zero)
+    assert oracle.round_bf16(-2.0 ** -140) == 0x8000
+
+
+def test_bf16_output_rounding_through_apply():
+    """At = I, B = I, s = 1: the bf16 result is the rounding of y + x (an exact fp32 sum)."""
+    r = 32
+    rng = np.random.default_rng(43)
+    xf = _f32(rng.uniform(0.5, 4.0, (64, r)) * rng.choice([-1, 1], (64, r)))
+    yf = _f32(rng.uniform(0.5, 4.0, (64, r)) * rng.choice([-1, 1], (64, r)))
+    x, y = synth.to_bf16_bits(xf), synth.to_bf16_bits(yf)
+    s32 = synth.bf16_bits_to_f32(x) + synth.bf16_bits_to_f32(y)
+    assert np.array_equal(s32.astype(np.float64),
+                          synth.bf16_bits_to_f32(x).astype(np.float64)
+                          + synth.bf16_bits_to_f32(y).astype(np.float64))   # exact in fp32
+    I = synth.to_bf16_bits(np.eye(r, dtype=np.float32))
+    got = oracle.apply(oracle.BF16, x, y, np.zeros(64, np.int32),
+                       [{"r": r, "lora_alpha": float(r), "use_rslora": False, "At": I, "B": I}])
+    ref = torch.from_numpy(s32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# the adapter size estimate on the pages
+
+def test_adapter_bytes_formula():
+    man = json.load(open(os.path.join(GOLDEN, "adapter_manifest_example.json")))
+    shapes = [(m.d_in, m.d_out) for m in synth.QWEN32B_ATTN]
+    assert [m.name for m in synth.QWEN32B_ATTN] == man["target_modules"]
+    per_layer = oracle.adapter_bytes(shapes, [True] * 4, man["rank"], 2)
+    # (5120+8192) + (5120+1024) * 2 + (8192+5120) = 38912 elements per rank
+    assert per_layer == 38912 * 32 * 2 == 2_490_368
+    assert oracle.adapter_bytes(shapes, [True, False, True, False], 32, 2) == (13312 + 6144) * 64
+    # the manifest's estimated_bytes is not a whole number of such layers, so it
+    # cannot be reproduced from the page's own formula and is not used as a pin
+    assert man["estimated_bytes"] % per_layer != 0
