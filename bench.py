@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-adapter LoRA apply path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_decode]
+
+One step is one pass of the whole hot path over one batch: the device plan
+(lora_plan_prepare) and, for every module of the workload's layer, lora_shrink
+then lora_expand.  Steps rotate over L "layer sets" (each with its own adapter
+weights, x and y, like the layers of a model) so that the bytes the kernels read
+come from HBM rather than from the 256 MB Infinity Cache.  Inputs are resident
+in HBM before timing starts.  Prints one JSON line.
+
+value      tokens of the batch (skipped tokens included) x K / wall time of K steps
+roofline   the kernel with the largest share of the step: algorithmic bytes per
+           launch / its average duration, timed with HIP events on the launch stream
+cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
+           same workload (rank 0, one GPU only)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFS = 2500.0     # dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default="llama7b_decode",
+                   choices=["llama7b_decode", "qwen32b_decode", "llama7b_prefill"])
+    p.add_argument("--layer-bytes", type=float, default=1.2e9,
+                   help="minimum footprint of the rotated layer sets (bytes)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="time the steps without per-kernel events (roofline then null)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run only a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def workload(name):
+    from lora_adapter_application_amd import synth
+    return {"llama7b_decode": synth.llama7b_decode, "qwen32b_decode": synth.qwen32b_decode,
+            "llama7b_prefill": synth.llama7b_prefill}[name]()
+
+
+def calib_copy(steps):
+    import torch
+    n = 1 << 30                                   # 1 GiB read + 1 GiB written per copy
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                      "ms_per_copy": dt * 1e3, "GBps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def kernel_source_sha():
+    p = os.path.join(ROOT, "lora_adapter_application_amd", "csrc", "lora_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def traffic_from_profiles(kernel, wl_name):
+    """HBM bytes per launch from the committed counter summary, if the kernel
+    source is still the one the counters were taken on; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wl_name}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
+              "by replicating slot pools per GPU with no exchange, which this build does not "
+              "measure.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calib_copy:
+        calib_copy(args.steps)
+        return
+
+    from lora_adapter_application_amd import binding, synth
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    wl = workload(args.workload)
+    T = wl.n_tokens
+    S, R = wl.max_loras, wl.max_rank
+    mods = wl.modules
+    b = 2                                                   # bf16
+    # rotation depth
+    per_set = sum(S * R * (m.d_in + m.d_out) * b + T * (m.d_in + 2 * m.d_out) * b for m in mods)
+    L = max(1, math.ceil(args.layer_bytes / per_set))
+    log(f"workload {wl.name}: T={T} S={S} R={R} modules={[(m.name, m.d_in, m.d_out) for m in mods]}"
+        f" layer sets={L} ({L * per_set / 1e9:.2f} GB)")
+
+    def dev_bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    shapes = [(m.d_in, m.d_out) for _ in range(L) for m in mods]
+    slots = binding.Slots(S, R, shapes, "bf16", max_tokens=T)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260101)
+    for k, ad in enumerate(wl.adapters):
+        A_t, B = [], []
+        for l in range(L):
+            for m in mods:
+                if l == 0:
+                    A_t.append(dev_bits(ad.At[m.name]))
+                    B.append(dev_bits(ad.B[m.name]))
+                else:
+                    bound = 1.0 / math.sqrt(m.d_in)
+                    A_t.append(((torch.rand(ad.r, m.d_in, generator=gen, device=dev) * 2 - 1)
+                                * bound).to(torch.bfloat16))
+                    B.append((torch.randn(ad.r, m.d_out, generator=gen, device=dev) * 0.01)
+                             .to(torch.bfloat16))
+        slots.load(k, A_t, B, ad.r, ad.lora_alpha, ad.use_rslora)
+        slots.sync_loads()
+        del A_t, B
+    idx = torch.from_numpy(wl.idx).to(dev)
+    xs, ys = [], []
+    for l in range(L):
+        for m in mods:
+            if l == 0:
+                xs.append(dev_bits(wl.x[m.name]))
+                ys.append(dev_bits(wl.y[m.name]))
+            else:
+                xs.append(torch.randn(T, m.d_in, generator=gen, device=dev).to(torch.bfloat16))
+                ys.append(torch.randn(T, m.d_out, generator=gen, device=dev).to(torch.bfloat16))
+    torch.cuda.synchronize()
+
+    # parity of layer set 0 against the oracle on a sample of rows, before timing
+    parity = None
+    try:
+        import oracle
+        rows = np.arange(min(T, 64))
+        y0 = {m.name: ys[i].clone() for i, m in enumerate(mods)}
+        slots.prepare(idx)
+        for i, m in enumerate(mods):
+            slots.shrink(xs[i], i)
+            slots.expand(y0[m.name], i)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for m in mods:
+            ref = oracle.apply(oracle.BF16, wl.x[m.name][rows], wl.y[m.name][rows], wl.idx[rows],
+                               synth.oracle_adapters(wl, m.name))
+            got = y0[m.name][rows].cpu().view(torch.int16).numpy().view(np.uint16)
+            g = synth.bf16_bits_to_f32(got).astype(np.float64)
+            r = synth.bf16_bits_to_f32(ref).astype(np.float64)
+            worst = max(worst, float((np.abs(g - r) / (2e-2 * (1 + np.abs(r)))).max()))
+        parity = {"rows": int(len(rows)), "worst_err_over_bound": worst, "ok": worst <= 1.0}
+        del y0
+    except Exception as e:                                   # reported, never hidden
+        parity = {"error": repr(e)}
+    log("parity:", parity)
+
+    nm = len(mods)
+    stream = torch.cuda.current_stream()
+    use_events = not args.no_kernel_events
+
+    def step(i, ev=None):
+        l = i % L
+        if ev is not None:
+            ev[0].record(stream)
+        slots.prepare(idx)
+        if ev is not None:
+            ev[1].record(stream)
+        for j in range(nm):
+            mi = l * nm + j
+            slots.shrink(xs[mi], mi)
+            if ev is not None:
+                ev[2 + 2 * j].record(stream)
+            slots.expand(ys[mi], mi)
+            if ev is not None:
+                ev[3 + 2 * j].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    n_ev = 2 + 2 * nm
+    events = ([[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+              if use_events else None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, events[i] if use_events else None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / K * 1e3
+    value = T * K / elapsed
+
+    # per-kernel durations from the events
+    act = (wl.idx >= 0) & (wl.idx < S)
+    T_act = int(act.sum())
+    used = np.unique(wl.idx[act])
+    sum_r = int(sum(wl.adapters[k].r for k in used))
+    roofline, kernels = None, None
+    if use_events:
+        plan_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+        shrink_ms = np.zeros((K, nm))
+        expand_ms = np.zeros((K, nm))
+        for i, e in enumerate(events):
+            prev = e[1]
+            for j in range(nm):
+                shrink_ms[i, j] = prev.elapsed_time(e[2 + 2 * j])
+                expand_ms[i, j] = e[2 + 2 * j].elapsed_time(e[3 + 2 * j])
+                prev = e[3 + 2 * j]
+        shrink_bytes = [b * m.d_in * (T_act + sum_r) for m in mods]
+        expand_bytes = [b * m.d_out * (2 * T_act + sum_r) for m in mods]
+        flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
+                 for m in mods]
+        kernels = {
+            "plan": {"avg_us": float(plan_ms.mean() * 1e3)},
+            "lora_shrink": {"avg_us": float(shrink_ms.mean() * 1e3),
+                            "alg_bytes_per_launch": float(np.mean(shrink_bytes)),
+                            "GBps": float(sum(shrink_bytes) / shrink_ms.mean(0).sum() / 1e6)},
+            "lora_expand": {"avg_us": float(expand_ms.mean() * 1e3),
+                            "alg_bytes_per_launch": float(np.mean(expand_bytes)),
+                            "GBps": float(sum(expand_bytes) / expand_ms.mean(0).sum() / 1e6)},
+            "step_alg_bytes": float(sum(shrink_bytes) + sum(expand_bytes)),
+            "step_alg_flops": float(sum(flops)),
+            "h_bytes_per_module_note": "h partials are a two-kernel artefact, not counted",
+        }
+        dom = "lora_expand" if expand_ms.sum() >= shrink_ms.sum() else "lora_shrink"
+        dom_ms = expand_ms if dom == "lora_expand" else shrink_ms
+        dom_bytes = expand_bytes if dom == "lora_expand" else shrink_bytes
+        achieved = sum(dom_bytes) / (dom_ms.mean(0).sum() * 1e-3) / 1e9      # GB/s
+        traffic = traffic_from_profiles(dom, wl.name)
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "alg_bytes_per_launch": float(np.mean(dom_bytes)),
+                    "avg_launch_us": float(dom_ms.mean() * 1e3)}
+        log("kernels:", json.dumps(kernels))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {
+        "metric": "multi-LoRA tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "active_tokens": T_act,
+                   "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
+                   "max_loras": S, "max_rank": R, "ranks": sorted({a.r for a in wl.adapters if a}),
+                   "layer_sets_rotated": L, "kernel_events_in_timed_region": use_events,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+    slots.close()
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle on the host over whole layers of the workload until ~`seconds` pass."""
+    import oracle
+    from lora_adapter_application_amd import synth
+    threads = oracle.max_threads()
+    ads = {m.name: synth.oracle_adapters(wl, m.name) for m in wl.modules}
+    T = wl.n_tokens
+    rows = np.arange(T)
+    if wl.name == "llama7b_prefill":                     # a bounded sample of the batch
+        rows = np.random.default_rng(0).choice(T, size=min(T, 2048), replace=False)
+        rows.sort()
+    layers = 0
+    t0 = time.perf_counter()
+    while True:
+        for m in wl.modules:
+            oracle.apply(oracle.BF16, wl.x[m.name][rows], wl.y[m.name][rows], wl.idx[rows],
+                         ads[m.name])
+        layers += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": round(layers * len(rows) / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{layers} layer passes of {len(rows)} tokens of {wl.name} "
+                      f"({len(wl.modules)} modules each), fp64 scalar C, OpenMP over tokens, "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

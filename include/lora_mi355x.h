@@ -1,0 +1,188 @@
+/*
+ * lora_mi355x.h -- C ABI of the MI355X (gfx950) multi-adapter LoRA library.
+ *
+ * The library applies, for every token t of a mixed batch and one linear
+ * module m,
+ *
+ *     y[t,:] += s_k * (x[t,:] . A_k) . B_k          with k = token_slot_idx[t]
+ *
+ * where slot k holds an adapter of rank r_k <= max_rank and
+ * s_k = lora_alpha / r_k, or lora_alpha / sqrt(r_k) with rsLoRA.  Those adapter
+ * fields (r, lora_alpha, use_rslora, target_modules) are the ones of the
+ * example PEFT adapter_config.json in "vLLM LoRA Resolver plugins explained"
+ * (blog.gitcode.com), section 3.2 "directory structure requirements".  The
+ * slot count and the padded rank are vLLM's max_loras and max_lora_rank of the
+ * parameter table in "Multi-LoRA adapter cache in production" (oh-bug.com),
+ * section "GPU, CPU and disk form the adapter storage hierarchy"; max_loras
+ * bounds the adapters one batch may use, not the adapters a server knows.
+ *
+ * Conventions shared by every call:
+ *  - Every call returns an int status (LORA_OK or a negative LORA_ERR_*).  No
+ *    call aborts or throws across the ABI.  All argument checks run on the
+ *    host before anything is enqueued, so an error has no partial effect.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *  - x, y and token_slot_idx are device pointers owned by the caller, who
+ *    keeps them alive until the stream has passed the call.
+ *  - A lora_ctx is used from one host thread at a time.  Calls that launch
+ *    kernels for one ctx (lora_plan_prepare, lora_shrink, lora_expand,
+ *    lora_apply) share the ctx's plan and intermediate buffers, so they must be
+ *    issued on one stream, or ordered by the caller.
+ *  - Element type of x, y, A and B is the ctx dtype: bf16 (raw 16-bit
+ *    patterns) or fp32.  Accumulation is always fp32; a bf16 y is rounded once,
+ *    to nearest even.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lora_ctx lora_ctx;
+
+typedef enum { LORA_BF16 = 0, LORA_FP32 = 1 } lora_dtype;
+
+typedef struct {
+    int32_t d_in;   /* input features of the linear (x row length), multiple of 8 */
+    int32_t d_out;  /* output features (y row length), multiple of 8 */
+} lora_module_shape;
+
+enum {
+    LORA_OK = 0,
+    LORA_ERR_INVALID_ARGUMENT = -1,
+    LORA_ERR_RANK_EXCEEDS_MAX = -2,   /* r > max_rank ("LoRA rank exceeds maximum",
+                                         "vLLM LoRA Resolver plugins explained", 6.1) */
+    LORA_ERR_SLOT_OUT_OF_RANGE = -3,
+    LORA_ERR_BAD_MODULE = -4,
+    LORA_ERR_TOO_MANY_TOKENS = -5,
+    LORA_ERR_HOST_NOT_PINNED = -6,
+    LORA_ERR_OUT_OF_MEMORY = -7,
+    LORA_ERR_HIP = -8,
+    LORA_ERR_NO_PLAN = -9
+};
+
+/* Library limits. */
+#define LORA_MAX_SLOTS 256   /* max_loras */
+#define LORA_MAX_RANK 128    /* max_rank */
+
+/* Sticky device-side flags, read with lora_get_device_flags. */
+#define LORA_FLAG_SLOT_INDEX_TOO_LARGE 0x1u  /* a token carried idx >= max_loras (skipped) */
+
+typedef struct {
+    int64_t loads;          /* lora_slot_load calls that succeeded */
+    int64_t clears;         /* lora_slot_clear calls that succeeded */
+    int64_t bytes_loaded;   /* sum over loads of sum_m (d_in + d_out) * r * bytes_per_elem */
+    int64_t plans;          /* plan kernels launched */
+    int64_t shrinks;        /* lora_shrink launches (including those inside lora_apply) */
+    int64_t expands;        /* lora_expand launches (including those inside lora_apply) */
+    int64_t tokens;         /* sum of n_tokens over planned batches */
+} lora_stats;
+
+/*
+ * Create a slot pool on `device`.
+ *   max_loras   slots, 1..LORA_MAX_SLOTS
+ *   max_rank    padded rank of every slot, 1..LORA_MAX_RANK
+ *   modules     n_modules shapes; a module index in later calls refers to this array
+ *   dtype       element type of x, y and the adapter weights
+ *   max_tokens  largest n_tokens of a batch, >= 1
+ * Allocates and zeroes, per module, A^T storage [max_loras][R][d_in] and B
+ * storage for [max_loras][R][d_out] (R = max_rank rounded up to 16), an fp32
+ * intermediate, plan buffers, and a side stream for loads.  Every slot starts
+ * empty.  On success *out owns all of it until lora_slots_destroy.
+ */
+int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
+                      const lora_module_shape *modules, int32_t n_modules,
+                      lora_dtype dtype, int32_t max_tokens, int32_t device);
+
+/* Wait for all work the ctx enqueued, then free it.  NULL is accepted. */
+int lora_slots_destroy(lora_ctx *ctx);
+
+/*
+ * Load one adapter into `slot` (the CPU-to-GPU upload of a "CPU hit",
+ * "Multi-LoRA adapter cache in production", section on cold-load tiers).
+ *   A_t[m]   r x d_in_m, row-major (A transposed: row j is rank j), or NULL when
+ *            module m is not in the adapter's target_modules
+ *   B[m]     r x d_out_m, row-major, NULL exactly when A_t[m] is NULL
+ *            Both must be pinned host memory or device memory, and must stay
+ *            unmodified until lora_sync_loads returns (or a later call on a
+ *            stream that waited for the load has completed).
+ *   r        adapter rank, 1..max_rank (r > max_rank -> LORA_ERR_RANK_EXCEEDS_MAX)
+ *   lora_alpha, use_rslora   give s = lora_alpha / r or lora_alpha / sqrt(r),
+ *            computed in double and rounded to fp32 once
+ * Asynchronous: copies run on the ctx's side stream.  Before overwriting the
+ * slot the side stream waits for every kernel already enqueued by this ctx, so
+ * an adapter in use by an in-flight batch is never overwritten ("an adapter in
+ * use must not be evicted", same page, data-plane section).  Later
+ * lora_plan_prepare / lora_shrink / lora_expand / lora_apply calls make their
+ * stream wait for the load.  Rows r..R-1 are zeroed, so padding changes nothing.
+ * The bytes moved are sum_m (d_in_m + d_out_m) * r * bytes_per_elem over the
+ * targeted modules, the page's adapter size estimate.
+ */
+int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
+                   int32_t r, double lora_alpha, int32_t use_rslora);
+
+/* Mark `slot` empty for every module (ordered like lora_slot_load). */
+int lora_slot_clear(lora_ctx *ctx, int32_t slot);
+
+/* Host waits until every load and clear issued so far has completed. */
+int lora_sync_loads(lora_ctx *ctx);
+
+/*
+ * Group the batch's tokens by slot on the device (no host synchronisation):
+ * a stable counting sort of token_slot_idx (int32[n_tokens], device) into a
+ * permutation, per-slot segments and tiles of up to 64 tokens.  Tokens with
+ * idx < 0 are not listed; idx >= max_loras are not listed and set
+ * LORA_FLAG_SLOT_INDEX_TOO_LARGE.  The plan stays valid for lora_shrink,
+ * lora_expand and lora_apply calls with the same (token_slot_idx, n_tokens)
+ * until the next lora_plan_prepare; the caller must not change the contents of
+ * token_slot_idx meanwhile.  n_tokens == 0 is allowed.
+ */
+int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_tokens,
+                      void *stream);
+
+/*
+ * lora_shrink: h = x . A_k for every planned token (fp32 intermediate of rank
+ * R, held in the ctx).  x is [n_tokens][d_in] of the prepared plan.
+ * Requires a prepared plan (else LORA_ERR_NO_PLAN).
+ */
+int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream);
+
+/*
+ * lora_expand: y[t,:] = round(y[t,:] + s_k * h[t,:] . B_k) for every planned
+ * token whose slot holds an adapter targeting `module`; every other row of y
+ * is left bit-identical.  Must follow lora_shrink of the same module on the
+ * same plan (else LORA_ERR_INVALID_ARGUMENT).  y is [n_tokens][d_out].
+ */
+int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream);
+
+/*
+ * One module's update in one call: plan (unless lora_plan_prepare was called
+ * for the same token_slot_idx and n_tokens), shrink, expand.  Tokens with
+ * idx == -1 (base model only), any other negative idx, idx >= max_loras, an
+ * empty slot, or a slot whose adapter does not target `module` leave their row
+ * of y bit-identical.  n_tokens == 0 is a no-op; n_tokens > max_tokens returns
+ * LORA_ERR_TOO_MANY_TOKENS.
+ */
+int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
+               int32_t n_tokens, int32_t module, void *stream);
+
+/* Synchronise the device, return the sticky LORA_FLAG_* bits and clear them. */
+int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags);
+
+/* Counters since creation. */
+int lora_get_stats(lora_ctx *ctx, lora_stats *out);
+
+/* Static text for a status code. */
+const char *lora_status_string(int status);
+
+/* Detail of the last error on ctx (or of the last failed lora_slots_create
+ * when ctx is NULL); empty string if none.  Valid until the next call. */
+const char *lora_last_error(lora_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

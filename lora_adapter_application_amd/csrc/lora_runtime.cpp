@@ -1,0 +1,643 @@
+// lora_runtime.cpp -- the C ABI declared in include/lora_mi355x.h: slot pool,
+// asynchronous slot loads on a side stream, device-side plan, and the
+// shrink / expand launches of the multi-adapter LoRA update.
+//
+// Slot pool ("GPU active slots" of the cache hierarchy in "Multi-LoRA adapter
+// cache in production", section "GPU, CPU and disk form the adapter storage
+// hierarchy"): per module m, A^T as [S][R_pad][d_in] (rank-major, rank j of a
+// slot is one contiguous row) and B as [S][R_pad/8][d_out][8] (groups of eight
+// ranks interleaved per output column, the order the expand MFMA consumes).
+// Rows r..R_pad-1 of a slot are kept zero.  Per (module, slot) the device holds
+// the rank (0 = nothing to apply) and per slot the fp32 scale.
+//
+// Ordering without host synchronisation:
+//  - a load or clear records an event on the side stream; a later kernel
+//    launch on a compute stream waits for it once (read after write);
+//  - before a load or clear overwrites a slot, the side stream waits for the
+//    current tail of every compute stream this ctx has launched on since the
+//    previous load, so weights an in-flight batch reads are never overwritten
+//    ("an adapter in use must not be evicted", same page, data-plane section).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/lora_mi355x.h"
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct StreamState {
+    hipStream_t stream;
+    uint64_t waited_gen;    // load generation this stream has waited for
+    bool used_since_load;   // launched on since the last load / clear
+    hipEvent_t tail;        // recorded at load time to fence the stream's tail
+};
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess)
+            prev = -1;
+        if (prev != dev)
+            ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0)
+            (void)hipSetDevice(prev);
+    }
+};
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct lora_ctx {
+    int device = 0;
+    lora_dtype dtype = LORA_BF16;
+    int S = 0, R = 0, R_pad = 0, n_modules = 0, max_tokens = 0, elem = 2;
+    std::vector<lora_module_shape> shapes;
+    std::vector<void *> A, Bi;
+    std::vector<int64_t> strideA, strideB;   // per-slot element strides
+    int32_t *rank_dev = nullptr;             // [n_modules][S]
+    float *scale_dev = nullptr;              // [S]
+    std::vector<int32_t> rank_host;          // mirror of rank_dev
+    std::vector<float> scale_host;
+    void *stage = nullptr;                   // B staging, R_pad * max d_out elements
+    float *hpart = nullptr;
+    int hbuf_rows = 0;
+    PlanBuffers plan{};
+    int max_tiles = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t load_done = nullptr;
+    uint64_t load_gen = 0;
+    std::vector<StreamState> streams;
+    // plan state
+    bool plan_valid = false, plan_prepared = false;
+    const int32_t *plan_idx = nullptr;
+    int32_t plan_T = 0;
+    // last shrink, consumed by expand
+    int last_shrink_module = -1;
+    int last_splits = 1, last_kchunk = 0;
+    lora_stats stats{};
+    std::string last_error;
+    std::vector<void *> allocations;
+};
+
+namespace {
+
+int fail(lora_ctx *c, int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c)
+        c->last_error = buf;
+    else
+        g_create_error = buf;
+    return status;
+}
+
+int hip_fail(lora_ctx *c, hipError_t e, const char *what)
+{
+    return fail(c, LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(ctx, expr)                                   \
+    do {                                                     \
+        hipError_t e_ = (expr);                              \
+        if (e_ != hipSuccess)                                \
+            return hip_fail((ctx), e_, #expr);               \
+    } while (0)
+
+StreamState *stream_state(lora_ctx *c, hipStream_t s)
+{
+    for (auto &st : c->streams)
+        if (st.stream == s)
+            return &st;
+    StreamState st{s, 0, false, nullptr};
+    if (hipEventCreateWithFlags(&st.tail, hipEventDisableTiming) != hipSuccess)
+        return nullptr;
+    c->streams.push_back(st);
+    return &c->streams.back();
+}
+
+// Make stream s wait for all loads issued so far, and mark it as in use.
+int before_launch(lora_ctx *c, hipStream_t s)
+{
+    StreamState *st = stream_state(c, s);
+    if (!st)
+        return fail(c, LORA_ERR_HIP, "hipEventCreateWithFlags failed");
+    if (st->waited_gen < c->load_gen) {
+        HIP_TRY(c, hipStreamWaitEvent(s, c->load_done, 0));
+        st->waited_gen = c->load_gen;
+    }
+    st->used_since_load = true;
+    return LORA_OK;
+}
+
+// Side stream waits for the current tail of every stream used since the last load.
+int fence_compute_streams(lora_ctx *c)
+{
+    for (auto &st : c->streams) {
+        if (!st.used_since_load)
+            continue;
+        HIP_TRY(c, hipEventRecord(st.tail, st.stream));
+        HIP_TRY(c, hipStreamWaitEvent(c->side, st.tail, 0));
+        st.used_since_load = false;
+    }
+    return LORA_OK;
+}
+
+int check_source(const void *p)
+{
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return LORA_ERR_HOST_NOT_PINNED;
+    }
+    if (attr.type == hipMemoryTypeHost || attr.type == hipMemoryTypeDevice ||
+        attr.type == hipMemoryTypeManaged)
+        return LORA_OK;
+    return LORA_ERR_HOST_NOT_PINNED;
+}
+
+void free_all(lora_ctx *c)
+{
+    for (void *p : c->allocations)
+        (void)hipFree(p);
+    c->allocations.clear();
+    for (auto &st : c->streams)
+        if (st.tail)
+            (void)hipEventDestroy(st.tail);
+    c->streams.clear();
+    if (c->load_done)
+        (void)hipEventDestroy(c->load_done);
+    if (c->side)
+        (void)hipStreamDestroy(c->side);
+    c->load_done = nullptr;
+    c->side = nullptr;
+}
+
+template <typename T>
+hipError_t dalloc(lora_ctx *c, T **p, size_t bytes)
+{
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+    if (e != hipSuccess)
+        return e;
+    c->allocations.push_back(q);
+    e = hipMemset(q, 0, bytes ? bytes : 16);
+    *p = (T *)q;
+    return e;
+}
+
+// K-split of the shrink for a batch of T tokens: enough workgroups to cover
+// the chip when the batch is small, none when it is large.
+void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
+{
+    const int tiles = max_tiles_for(T, c->S);
+    int want = ceil_div(1024, std::max(tiles, 1));
+    int cap = std::min(kMaxSplits, std::max(1, d_in / 256));
+    cap = std::min(cap, std::max(1, c->hbuf_rows / std::max(T, 1)));
+    int sp = std::max(1, std::min(want, cap));
+    int kc = round_up(ceil_div(d_in, sp), kShrinkKBlock);
+    *kchunk = kc;
+    *splits = ceil_div(d_in, kc);
+}
+
+int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
+
+int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
+{
+    if (T > 0) {
+        int rc = before_launch(c, s);
+        if (rc)
+            return rc;
+        HIP_TRY(c, launch_plan(idx, T, c->S, c->plan, s));
+        c->stats.plans += 1;
+    }
+    c->stats.tokens += T;
+    c->plan_valid = true;
+    c->plan_idx = idx;
+    c->plan_T = T;
+    c->last_shrink_module = -1;
+    return LORA_OK;
+}
+
+int run_shrink(lora_ctx *c, const void *x, int module, hipStream_t s)
+{
+    const int T = c->plan_T;
+    if (T > 0) {
+        int rc = before_launch(c, s);
+        if (rc)
+            return rc;
+        const lora_module_shape sh = c->shapes[module];
+        int splits = 1, kchunk = 0;
+        choose_splits(c, T, sh.d_in, &splits, &kchunk);
+        ShrinkArgs a;
+        a.x = x;
+        a.A = c->A[module];
+        a.slot_stride_A = c->strideA[module];
+        a.rank = c->rank_dev + (int64_t)module * c->S;
+        a.perm = c->plan.perm;
+        a.tiles = c->plan.tiles;
+        a.n_tiles = c->plan.n_tiles;
+        a.hpart = c->hpart;
+        a.split_stride = (int64_t)T * c->R_pad;
+        a.d_in = sh.d_in;
+        a.R_pad = c->R_pad;
+        a.k_chunk = kchunk;
+        a.splits = splits;
+        a.grid_tiles = max_tiles_for(T, c->S);
+        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, s));
+        c->last_splits = splits;
+        c->last_kchunk = kchunk;
+        c->stats.shrinks += 1;
+    }
+    c->last_shrink_module = module;
+    return LORA_OK;
+}
+
+int run_expand(lora_ctx *c, void *y, int module, hipStream_t s)
+{
+    const int T = c->plan_T;
+    if (T > 0) {
+        int rc = before_launch(c, s);
+        if (rc)
+            return rc;
+        const lora_module_shape sh = c->shapes[module];
+        ExpandArgs a;
+        a.y = y;
+        a.Bi = c->Bi[module];
+        a.slot_stride_B = c->strideB[module];
+        a.rank = c->rank_dev + (int64_t)module * c->S;
+        a.scale = c->scale_dev;
+        a.perm = c->plan.perm;
+        a.tiles = c->plan.tiles;
+        a.n_tiles = c->plan.n_tiles;
+        a.hpart = c->hpart;
+        a.split_stride = (int64_t)T * c->R_pad;
+        a.d_out = sh.d_out;
+        a.R_pad = c->R_pad;
+        a.splits = c->last_splits;
+        a.grid_tiles = max_tiles_for(T, c->S);
+        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, s));
+        c->stats.expands += 1;
+    }
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_status_string(int status)
+{
+    switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LORA_ERR_RANK_EXCEEDS_MAX: return "LoRA rank exceeds maximum (r > max_rank)";
+    case LORA_ERR_SLOT_OUT_OF_RANGE: return "slot out of range";
+    case LORA_ERR_BAD_MODULE: return "module index out of range";
+    case LORA_ERR_TOO_MANY_TOKENS: return "n_tokens exceeds max_tokens";
+    case LORA_ERR_HOST_NOT_PINNED: return "adapter weights are not in pinned host or device memory";
+    case LORA_ERR_OUT_OF_MEMORY: return "device out of memory";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    case LORA_ERR_NO_PLAN: return "no prepared plan (call lora_plan_prepare first)";
+    default: return "unknown status";
+    }
+}
+
+const char *lora_last_error(lora_ctx *ctx)
+{
+    return ctx ? ctx->last_error.c_str() : g_create_error.c_str();
+}
+
+int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
+                      const lora_module_shape *modules, int32_t n_modules, lora_dtype dtype,
+                      int32_t max_tokens, int32_t device)
+{
+    g_create_error.clear();
+    if (!out)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    if (max_loras < 1 || max_loras > LORA_MAX_SLOTS)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "max_loras %d not in 1..%d", max_loras,
+                    LORA_MAX_SLOTS);
+    if (max_rank < 1)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "max_rank %d < 1", max_rank);
+    if (max_rank > LORA_MAX_RANK)
+        return fail(nullptr, LORA_ERR_RANK_EXCEEDS_MAX, "max_rank %d > %d", max_rank,
+                    LORA_MAX_RANK);
+    if (!modules || n_modules < 1)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "no modules");
+    if (dtype != LORA_BF16 && dtype != LORA_FP32)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (max_tokens < 1)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "max_tokens %d < 1", max_tokens);
+    for (int m = 0; m < n_modules; ++m) {
+        const auto &sh = modules[m];
+        if (sh.d_in < 8 || sh.d_out < 8 || sh.d_in % 8 || sh.d_out % 8)
+            return fail(nullptr, LORA_ERR_INVALID_ARGUMENT,
+                        "module %d: d_in %d / d_out %d must be positive multiples of 8", m,
+                        sh.d_in, sh.d_out);
+    }
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+        (void)hipGetLastError();
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "device %d not available (%d devices)",
+                    device, ndev);
+    }
+    DeviceGuard guard(device);
+    if (!guard.ok)
+        return fail(nullptr, LORA_ERR_HIP, "hipSetDevice(%d) failed", device);
+
+    lora_ctx *c = new lora_ctx();
+    c->device = device;
+    c->dtype = dtype;
+    c->S = max_loras;
+    c->R = max_rank;
+    c->R_pad = round_up(max_rank, 16);
+    c->n_modules = n_modules;
+    c->max_tokens = max_tokens;
+    c->elem = dtype == LORA_BF16 ? 2 : 4;
+    c->shapes.assign(modules, modules + n_modules);
+    c->rank_host.assign((size_t)n_modules * max_loras, 0);
+    c->scale_host.assign(max_loras, 0.f);
+
+    hipError_t e = hipSuccess;
+    int max_out = 0;
+    for (int m = 0; m < n_modules && e == hipSuccess; ++m) {
+        const auto &sh = modules[m];
+        const int64_t sa = (int64_t)c->R_pad * sh.d_in, sb = (int64_t)c->R_pad * sh.d_out;
+        void *a = nullptr, *b = nullptr;
+        e = dalloc(c, &a, (size_t)(sa * max_loras * c->elem));
+        if (e == hipSuccess)
+            e = dalloc(c, &b, (size_t)(sb * max_loras * c->elem));
+        c->A.push_back(a);
+        c->Bi.push_back(b);
+        c->strideA.push_back(sa);
+        c->strideB.push_back(sb);
+        max_out = std::max(max_out, sh.d_out);
+    }
+    c->hbuf_rows = std::max(max_tokens, 16384);
+    c->max_tiles = max_tiles_for(max_tokens, max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->rank_dev, sizeof(int32_t) * (size_t)n_modules * max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->scale_dev, sizeof(float) * (size_t)max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
+    if (e == hipSuccess) e = dalloc(c, &c->hpart, sizeof(float) * (size_t)c->hbuf_rows * c->R_pad);
+    if (e == hipSuccess) e = dalloc(c, &c->plan.counts, sizeof(int32_t) * (size_t)max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->plan.seg_start, sizeof(int32_t) * (size_t)max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->plan.perm, sizeof(int32_t) * (size_t)max_tokens);
+    if (e == hipSuccess) e = dalloc(c, &c->plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
+    if (e == hipSuccess) e = dalloc(c, &c->plan.n_tiles, sizeof(int32_t));
+    if (e == hipSuccess) e = dalloc(c, &c->plan.n_active, sizeof(int32_t));
+    if (e == hipSuccess) e = dalloc(c, &c->plan.flags, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->load_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        int status = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+                         ? LORA_ERR_OUT_OF_MEMORY : LORA_ERR_HIP;
+        fail(nullptr, status, "slot pool allocation: %s", hipGetErrorString(e));
+        (void)hipGetLastError();
+        free_all(c);
+        delete c;
+        return status;
+    }
+    *out = c;
+    return LORA_OK;
+}
+
+int lora_slots_destroy(lora_ctx *ctx)
+{
+    if (!ctx)
+        return LORA_OK;
+    DeviceGuard guard(ctx->device);
+    (void)hipDeviceSynchronize();
+    free_all(ctx);
+    delete ctx;
+    return LORA_OK;
+}
+
+int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
+                   int32_t r, double lora_alpha, int32_t use_rslora)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (slot < 0 || slot >= ctx->S)
+        return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "slot %d not in 0..%d", slot, ctx->S - 1);
+    if (r > ctx->R)
+        return fail(ctx, LORA_ERR_RANK_EXCEEDS_MAX, "rank %d exceeds max_rank %d", r, ctx->R);
+    if (r < 1)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "rank %d < 1", r);
+    if (!A_t || !B)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "A_t / B arrays are NULL");
+    const double sd = use_rslora ? lora_alpha / std::sqrt((double)r) : lora_alpha / (double)r;
+    const float s = (float)sd;
+    if (!std::isfinite(s))
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "scale is not finite (lora_alpha %g)",
+                    lora_alpha);
+    {
+        DeviceGuard guard(ctx->device);
+        for (int m = 0; m < ctx->n_modules; ++m) {
+            if ((A_t[m] == nullptr) != (B[m] == nullptr))
+                return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                            "module %d: A_t and B must both be given or both be NULL", m);
+            if (A_t[m] && (check_source(A_t[m]) || check_source(B[m])))
+                return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
+                            "module %d: weights must be pinned host or device memory", m);
+        }
+    }
+    DeviceGuard guard(ctx->device);
+    int rc = fence_compute_streams(ctx);
+    if (rc)
+        return rc;
+    HIP_TRY(ctx, launch_slot_reset(ctx->rank_dev, ctx->n_modules, ctx->S, slot, ctx->side));
+    int64_t bytes = 0;
+    const bool bf16 = ctx->dtype == LORA_BF16;
+    for (int m = 0; m < ctx->n_modules; ++m) {
+        if (!A_t[m])
+            continue;
+        const auto sh = ctx->shapes[m];
+        char *Aslot = (char *)ctx->A[m] + (size_t)slot * ctx->strideA[m] * ctx->elem;
+        char *Bslot = (char *)ctx->Bi[m] + (size_t)slot * ctx->strideB[m] * ctx->elem;
+        const size_t abytes = (size_t)r * sh.d_in * ctx->elem;
+        const size_t bbytes = (size_t)r * sh.d_out * ctx->elem;
+        HIP_TRY(ctx, hipMemcpyAsync(Aslot, A_t[m], abytes, hipMemcpyDefault, ctx->side));
+        HIP_TRY(ctx, hipMemcpyAsync(ctx->stage, B[m], bbytes, hipMemcpyDefault, ctx->side));
+        HIP_TRY(ctx, launch_slot_finalize(bf16, Aslot, sh.d_in, Bslot, ctx->stage, sh.d_out, r,
+                                          ctx->R_pad, ctx->rank_dev + (int64_t)m * ctx->S + slot,
+                                          ctx->scale_dev + slot, s, ctx->side));
+        bytes += (int64_t)abytes + (int64_t)bbytes;
+    }
+    HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
+    ctx->load_gen += 1;
+    for (int m = 0; m < ctx->n_modules; ++m)
+        ctx->rank_host[(size_t)m * ctx->S + slot] = A_t[m] ? r : 0;
+    ctx->scale_host[slot] = s;
+    ctx->stats.loads += 1;
+    ctx->stats.bytes_loaded += bytes;
+    return LORA_OK;
+}
+
+int lora_slot_clear(lora_ctx *ctx, int32_t slot)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (slot < 0 || slot >= ctx->S)
+        return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "slot %d not in 0..%d", slot, ctx->S - 1);
+    DeviceGuard guard(ctx->device);
+    int rc = fence_compute_streams(ctx);
+    if (rc)
+        return rc;
+    HIP_TRY(ctx, launch_slot_reset(ctx->rank_dev, ctx->n_modules, ctx->S, slot, ctx->side));
+    HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
+    ctx->load_gen += 1;
+    for (int m = 0; m < ctx->n_modules; ++m)
+        ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
+    ctx->stats.clears += 1;
+    return LORA_OK;
+}
+
+int lora_sync_loads(lora_ctx *ctx)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(ctx->device);
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->side));
+    return LORA_OK;
+}
+
+int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_tokens,
+                      void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (n_tokens < 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "n_tokens %d < 0", n_tokens);
+    if (n_tokens > ctx->max_tokens)
+        return fail(ctx, LORA_ERR_TOO_MANY_TOKENS, "n_tokens %d > max_tokens %d", n_tokens,
+                    ctx->max_tokens);
+    if (n_tokens > 0 && !token_slot_idx)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "token_slot_idx is NULL");
+    DeviceGuard guard(ctx->device);
+    int rc = run_plan(ctx, token_slot_idx, n_tokens, (hipStream_t)stream);
+    if (rc) {
+        ctx->plan_valid = ctx->plan_prepared = false;
+        return rc;
+    }
+    ctx->plan_prepared = true;
+    return LORA_OK;
+}
+
+int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (module < 0 || module >= ctx->n_modules)
+        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    if (!ctx->plan_valid)
+        return fail(ctx, LORA_ERR_NO_PLAN, "lora_shrink needs a prepared plan");
+    if (ctx->plan_T > 0 && !x)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "x is NULL");
+    DeviceGuard guard(ctx->device);
+    return run_shrink(ctx, x, module, (hipStream_t)stream);
+}
+
+int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (module < 0 || module >= ctx->n_modules)
+        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    if (!ctx->plan_valid)
+        return fail(ctx, LORA_ERR_NO_PLAN, "lora_expand needs a prepared plan");
+    if (ctx->last_shrink_module != module)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                    "lora_expand(module %d) must follow lora_shrink of the same module", module);
+    if (ctx->plan_T > 0 && !y)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "y is NULL");
+    DeviceGuard guard(ctx->device);
+    return run_expand(ctx, y, module, (hipStream_t)stream);
+}
+
+int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
+               int32_t n_tokens, int32_t module, void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (module < 0 || module >= ctx->n_modules)
+        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    if (n_tokens < 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "n_tokens %d < 0", n_tokens);
+    if (n_tokens > ctx->max_tokens)
+        return fail(ctx, LORA_ERR_TOO_MANY_TOKENS, "n_tokens %d > max_tokens %d", n_tokens,
+                    ctx->max_tokens);
+    if (n_tokens == 0)
+        return LORA_OK;
+    if (!x || !y || !token_slot_idx)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "x, y and token_slot_idx must be non-NULL");
+    DeviceGuard guard(ctx->device);
+    hipStream_t s = (hipStream_t)stream;
+    int rc;
+    if (!(ctx->plan_valid && ctx->plan_prepared && ctx->plan_idx == token_slot_idx &&
+          ctx->plan_T == n_tokens)) {
+        ctx->plan_prepared = false;
+        rc = run_plan(ctx, token_slot_idx, n_tokens, s);
+        if (rc) {
+            ctx->plan_valid = false;
+            return rc;
+        }
+    }
+    rc = run_shrink(ctx, x, module, s);
+    if (rc)
+        return rc;
+    return run_expand(ctx, y, module, s);
+}
+
+int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)
+{
+    if (check_ctx(ctx) || !flags)
+        return LORA_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(ctx->device);
+    HIP_TRY(ctx, hipDeviceSynchronize());
+    HIP_TRY(ctx, hipMemcpy(flags, ctx->plan.flags, sizeof(uint32_t), hipMemcpyDeviceToHost));
+    HIP_TRY(ctx, hipMemset(ctx->plan.flags, 0, sizeof(uint32_t)));
+    HIP_TRY(ctx, hipDeviceSynchronize());
+    return LORA_OK;
+}
+
+int lora_get_stats(lora_ctx *ctx, lora_stats *out)
+{
+    if (check_ctx(ctx) || !out)
+        return LORA_ERR_INVALID_ARGUMENT;
+    *out = ctx->stats;
+    return LORA_OK;
+}
+
+}  // extern "C"

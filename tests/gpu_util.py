@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU tests: move synthetic workloads to the device, run
+the HIP path through the C ABI, run the oracle on the same bits, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from lora_adapter_application_amd import binding, synth
+
+# Tolerances of the parity bar: max |gpu - ref| <= tol * (1 + |ref|).
+TOL = {synth.FP32: 1e-5, synth.BF16: 2e-2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == synth.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda()
+
+
+def to_pinned(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == synth.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.pin_memory()
+
+
+def from_dev(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu()
+    if dtype == synth.BF16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == synth.BF16:
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None) -> binding.Slots:
+    """Create a ctx for the workload's modules and load every slot's adapter."""
+    S = binding.Slots(wl.max_loras, max_rank or wl.max_rank,
+                      [(m.d_in, m.d_out) for m in wl.modules], wl.dtype,
+                      max_tokens or max(wl.n_tokens, 1))
+    pinned = [] if keep is None else keep
+    for k, ad in enumerate(wl.adapters):
+        if ad is None:
+            continue
+        A_t, B = [], []
+        for m in wl.modules:
+            if m.name in ad.At:
+                a = to_pinned(ad.At[m.name], wl.dtype)
+                b = to_pinned(ad.B[m.name], wl.dtype)
+                pinned += [a, b]
+                A_t.append(a)
+                B.append(b)
+            else:
+                A_t.append(None)
+                B.append(None)
+        S.load(k, A_t, B, ad.r, ad.lora_alpha, ad.use_rslora)
+    S.sync_loads()
+    return S
+
+
+def run_gpu(wl: synth.Workload, S: binding.Slots, prepare=True):
+    """Apply every module once; returns {module name: y after (numpy bits)}."""
+    idx = torch.from_numpy(wl.idx).cuda()
+    out = {}
+    if prepare:
+        S.prepare(idx)
+    for mi, m in enumerate(wl.modules):
+        x = to_dev(wl.x[m.name], wl.dtype)
+        y = to_dev(wl.y[m.name], wl.dtype)
+        S.apply(x, y, idx, mi)
+        out[m.name] = y
+    torch.cuda.synchronize()
+    return {k: from_dev(v, wl.dtype) for k, v in out.items()}
+
+
+def run_oracle(wl: synth.Workload, module: str, rows=None, n_threads=0):
+    x, y, idx = wl.x[module], wl.y[module], wl.idx
+    if rows is not None:
+        x, y, idx = x[rows], y[rows], idx[rows]
+    odt = oracle.BF16 if wl.dtype == synth.BF16 else oracle.FP32
+    return oracle.apply(odt, x, y, idx, synth.oracle_adapters(wl, module), n_threads=n_threads)
+
+
+def check_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    g, r = as_f64(gpu, dtype), as_f64(ref, dtype)
+    tol = TOL[dtype]
+    err = np.abs(g - r)
+    bound = tol * (1.0 + np.abs(r))
+    worst = float((err / bound).max()) if err.size else 0.0
+    assert np.all(err <= bound), (
+        f"{what}: max |gpu-ref| = {err.max():.3e}, worst err/bound = {worst:.3f}")
+    return worst
+
+
+def rel_l2(gpu_delta: np.ndarray, ref_delta: np.ndarray) -> float:
+    n = np.linalg.norm(ref_delta)
+    return float(np.linalg.norm(gpu_delta - ref_delta) / n) if n > 0 else 0.0

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: max |gpu - oracle| <= 1e-5 * (1 + |oracle|) for fp32 data and
+<= 2e-2 * (1 + |oracle|) for bf16 data with fp32 accumulation; bit-identical
+rows wherever the update must not touch y; bit-identical results for exact
+small-integer fp32 data.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (as_f64, check_close, from_dev, log, make_slots, rel_l2, run_gpu,
+                      run_oracle, to_dev, to_pinned)
+from lora_adapter_application_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+
+def test_tiny_fp32_full():
+    wl = synth.tiny_fp32()
+    log("case tiny_fp32", wl.n_tokens)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    ref = run_oracle(wl, "linear")
+    check_close(got["linear"], ref, wl.dtype, "tiny_fp32")
+    skipped = wl.idx < 0
+    assert np.array_equal(got["linear"][skipped].view(np.uint32), wl.y["linear"][skipped].view(np.uint32))
+    S.close()
+
+
+def test_llama7b_decode_full():
+    wl = synth.llama7b_decode()
+    log("case llama7b_decode", wl.n_tokens)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    for m in wl.modules:
+        ref = run_oracle(wl, m.name)
+        check_close(got[m.name], ref, wl.dtype, "llama7b_decode " + m.name)
+        skipped = wl.idx < 0
+        assert np.array_equal(got[m.name][skipped], wl.y[m.name][skipped])
+    S.close()
+
+
+def test_llama7b_decode_weak_signal_diagnostic():
+    """With y = 0 the output is the update itself: relative L2 error of the delta."""
+    wl = synth.llama7b_decode(y_zero=True)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    for m in wl.modules:
+        ref = run_oracle(wl, m.name)
+        e = rel_l2(as_f64(got[m.name], wl.dtype), as_f64(ref, wl.dtype))
+        log(f"llama7b_decode y=0 {m.name}: rel L2 {e:.2e}")
+        assert e < 1e-2
+    S.close()
+
+
+def test_qwen32b_decode_full():
+    wl = synth.qwen32b_decode()
+    log("case qwen32b_decode", wl.n_tokens)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    for m in wl.modules:
+        ref = run_oracle(wl, m.name)
+        check_close(got[m.name], ref, wl.dtype, "qwen32b_decode " + m.name)
+        skipped = wl.idx < 0
+        assert np.array_equal(got[m.name][skipped], wl.y[m.name][skipped])
+    S.close()
+
+
+def test_llama7b_prefill_full_size_sampled():
+    wl = synth.llama7b_prefill()
+    T = wl.n_tokens
+    log("case llama7b_prefill", T)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    rng = np.random.default_rng(0)
+    # segment boundaries plus a random sample
+    edges = np.flatnonzero(np.diff(wl.idx)) if T > 1 else np.array([], int)
+    rows = np.unique(np.concatenate([[0, T - 1], edges, edges + 1, rng.integers(0, T, 256)]))
+    for m in wl.modules:
+        ref = run_oracle(wl, m.name, rows=rows)
+        check_close(got[m.name][rows], ref, wl.dtype, "llama7b_prefill " + m.name)
+        assert np.all(np.isfinite(synth.bf16_bits_to_f32(got[m.name])))
+    S.close()
+
+
+# ---------------------------------------------------------------------------
+# sweeps: ragged tiles and tails, mixed ranks, several tiles per slot
+
+SWEEP = [
+    # dtype, (d_in, d_out) list, max_loras, R, ranks, T, p_base_only
+    (synth.BF16, [(136, 264)], 8, 64, [1, 3, 16, 17, 33, 64, 8, 2], 300, 0.1),
+    (synth.BF16, [(4096, 1024), (1024, 4096)], 16, 32, [32] * 16, 1000, 0.05),
+    (synth.BF16, [(256, 512)], 4, 128, [128, 100, 65, 7], 200, 0.0),
+    (synth.BF16, [(512, 256)], 3, 16, [16, 5, 9], 1, 0.0),
+    (synth.BF16, [(128, 128)], 256, 8, [(k % 8) + 1 for k in range(256)], 5000, 0.2),
+    (synth.BF16, [(384, 392)], 5, 48, [48, 40, 30, 20, 10], 3077, 0.1),
+    (synth.FP32, [(72, 40)], 6, 8, [8, 1, 2, 3, 5, 8], 130, 0.1),
+    (synth.FP32, [(264, 136), (96, 200)], 4, 24, [24, 17, 1, 9], 700, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_sweep(case):
+    dtype, shapes, S_, R, ranks, T, pb = SWEEP[case]
+    mods = [synth.Module(f"m{i}", a, b) for i, (a, b) in enumerate(shapes)]
+    wl = synth.random_case(100 + case, dtype, mods, T, S_, R, ranks, p_base_only=pb)
+    log(f"case sweep {case}: {dtype} {shapes} S={S_} R={R} T={T}")
+    Sl = make_slots(wl)
+    got = run_gpu(wl, Sl)
+    for m in mods:
+        check_close(got[m.name], run_oracle(wl, m.name), dtype, f"sweep {case} {m.name}")
+    Sl.close()
+
+
+def test_exact_integers_fp32_bit_identical():
+    mods = [synth.Module("a", 200, 136), synth.Module("b", 64, 520)]
+    wl = synth.random_case(7, synth.FP32, mods, 333, 4, 16, [16, 9, 4, 1], integer=True)
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    for m in mods:
+        ref = run_oracle(wl, m.name)
+        assert np.array_equal(got[m.name].view(np.uint32), ref.view(np.uint32)), m.name
+    S.close()
+
+
+def test_exact_integers_bf16_bit_identical():
+    # final |y| stays <= 256 so every value is exact in bf16
+    mods = [synth.Module("a", 8, 24)]
+    wl = synth.random_case(8, synth.BF16, mods, 100, 3, 16, [2, 1, 2], integer=True)
+    for ad in wl.adapters:
+        for k in ad.At:
+            ad.At[k] = synth.to_bf16_bits(np.clip(synth.bf16_bits_to_f32(ad.At[k]), -1, 1))
+            ad.B[k] = synth.to_bf16_bits(np.clip(synth.bf16_bits_to_f32(ad.B[k]), -1, 1))
+    wl.x["a"] = synth.to_bf16_bits(np.clip(synth.bf16_bits_to_f32(wl.x["a"]), -1, 1))
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    ref = run_oracle(wl, "a")
+    assert np.array_equal(got["a"], ref)
+    S.close()
+
+
+# ---------------------------------------------------------------------------
+# skip semantics, padding, determinism
+
+def test_skip_rows_bit_identical_and_flag():
+    mods = [synth.Module("q", 256, 256), synth.Module("v", 256, 256)]
+    wl = synth.random_case(9, synth.BF16, mods, 64, 4, 16, [16, 8, 4, 2],
+                           targeted=[[True, True], [True, False], [False, True], [True, True]],
+                           empty_slots=[3], p_base_only=0.0)
+    wl.idx = np.array([-1, -5, 0, 1, 2, 3, 4, 1000] * 8, dtype=np.int32)
+    S = make_slots(wl)
+    assert S.flags() == 0
+    got = run_gpu(wl, S)
+    assert S.flags() & binding.LORA_FLAG_SLOT_INDEX_TOO_LARGE
+    assert S.flags() == 0                                   # read clears
+    for mi, m in enumerate(mods):
+        active = np.isin(wl.idx, [0, 1] if m.name == "q" else [0, 2])
+        assert np.array_equal(got[m.name][~active], wl.y[m.name][~active]), m.name
+        assert not np.array_equal(got[m.name][active], wl.y[m.name][active])
+        check_close(got[m.name], run_oracle(wl, m.name), wl.dtype, m.name)
+    S.close()
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32])
+def test_padding_to_max_rank_changes_nothing(dtype):
+    mods = [synth.Module("a", 512, 768)]
+    wl = synth.random_case(10, dtype, mods, 400, 4, 16, [16, 13, 8, 1], p_base_only=0.1)
+    S16 = make_slots(wl, max_rank=16)
+    S64 = make_slots(wl, max_rank=64)
+    a = run_gpu(wl, S16)["a"]
+    b = run_gpu(wl, S64)["a"]
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    check_close(a, run_oracle(wl, "a"), dtype, "padding")
+    S16.close()
+    S64.close()
+
+
+def test_deterministic_and_prepared_plan_matches_unprepared():
+    wl = synth.random_case(11, synth.BF16, [synth.Module("a", 1024, 2048)], 700, 8, 32,
+                           [32, 16, 8, 4, 32, 16, 8, 4])
+    S = make_slots(wl)
+    a = run_gpu(wl, S, prepare=True)["a"]
+    b = run_gpu(wl, S, prepare=False)["a"]
+    assert np.array_equal(a, b)
+    # shrink and expand as separate entry points on a prepared plan
+    idx = torch.from_numpy(wl.idx).cuda()
+    x = to_dev(wl.x["a"], wl.dtype)
+    y = to_dev(wl.y["a"], wl.dtype)
+    S.prepare(idx)
+    S.shrink(x, 0)
+    S.expand(y, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(y, wl.dtype), a)
+    S.close()
+
+
+def test_empty_batch_is_a_noop():
+    wl = synth.random_case(12, synth.BF16, [synth.Module("a", 128, 128)], 4, 2, 16, [16, 8])
+    S = make_slots(wl)
+    y = to_dev(wl.y["a"], wl.dtype)
+    before = from_dev(y, wl.dtype)
+    empty = torch.zeros(0, dtype=torch.int32, device="cuda")
+    S.apply(to_dev(wl.x["a"], wl.dtype), y, empty, 0)
+    S.prepare(empty)
+    S.shrink(None, 0)
+    S.expand(None, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(y, wl.dtype), before)
+    S.close()
+
+
+# ---------------------------------------------------------------------------
+# loads: byte count, ordering against in-flight work, errors
+
+def test_bytes_loaded_follow_the_page_formula():
+    wl = synth.qwen32b_decode(n_tokens=8)
+    S = make_slots(wl)
+    st = S.stats()
+    shapes = [(m.d_in, m.d_out) for m in wl.modules]
+    per = oracle.adapter_bytes(shapes, [True] * 4, 32, 2)
+    assert st["loads"] == 16 and st["bytes_loaded"] == 16 * per
+    S.close()
+
+
+def _reload(S, wl, slot, A_list, B_list, r, alpha, keep):
+    A_t, B = [], []
+    for a, b in zip(A_list, B_list):
+        ta, tb = to_pinned(a, wl.dtype), to_pinned(b, wl.dtype)
+        keep += [ta, tb]
+        A_t.append(ta)
+        B.append(tb)
+    S.load(slot, A_t, B, r, alpha)
+
+
+def test_load_waits_for_in_flight_applies_and_applies_wait_for_loads():
+    """WAR: a load issued while applies are in flight must not change their result.
+    RAW: an apply issued right after a load must see the new weights."""
+    T = 8192
+    mods = [synth.Module("a", 4096, 4096)]
+    wl = synth.random_case(13, synth.BF16, mods, T, 2, 16, [16, 16], p_base_only=0.0,
+                           zipf_s=0.01)
+    S = make_slots(wl, max_tokens=T)
+    idx = torch.from_numpy(wl.idx).cuda()
+    x = to_dev(wl.x["a"], wl.dtype)
+    ys = [to_dev(wl.y["a"], wl.dtype) for _ in range(12)]
+    new = synth.random_case(14, synth.BF16, mods, 1, 2, 16, [16, 16])
+    keep = []
+    S.prepare(idx)
+    for y in ys:                                   # ~a dozen large applies in flight
+        S.apply(x, y, idx, 0)
+    _reload(S, wl, 0, [new.adapters[0].At["a"]], [new.adapters[0].B["a"]], 16, 32.0, keep)
+    y_after = to_dev(wl.y["a"], wl.dtype)
+    S.apply(x, y_after, idx, 0)                    # must see the new slot 0
+    torch.cuda.synchronize()
+    old_ref = run_oracle(wl, "a")
+    for y in ys:
+        check_close(from_dev(y, wl.dtype), old_ref, wl.dtype, "in-flight apply")
+    wl.adapters[0] = new.adapters[0]
+    check_close(from_dev(y_after, wl.dtype), run_oracle(wl, "a"), wl.dtype, "apply after load")
+    S.close()
+
+
+def test_clear_makes_slot_a_noop():
+    wl = synth.random_case(15, synth.BF16, [synth.Module("a", 256, 256)], 128, 3, 16, [16, 8, 4],
+                           p_base_only=0.0)
+    S = make_slots(wl)
+    S.clear(1)
+    got = run_gpu(wl, S)["a"]
+    on1 = wl.idx == 1
+    assert np.array_equal(got[on1], wl.y["a"][on1])
+    wl.adapters[1] = None
+    check_close(got, run_oracle(wl, "a"), wl.dtype, "after clear")
+    S.close()
+
+
+def test_error_codes():
+    S = binding.Slots(4, 16, [(128, 256), (256, 128)], "bf16", max_tokens=32)
+    a = torch.zeros(16, 128, dtype=torch.bfloat16).pin_memory()
+    b = torch.zeros(16, 256, dtype=torch.bfloat16).pin_memory()
+    unpinned = torch.zeros(16, 128, dtype=torch.bfloat16)
+
+    def status(fn):
+        with pytest.raises(binding.LoraError) as e:
+            fn()
+        return e.value.status
+
+    assert status(lambda: S.load(4, [a, None], [b, None], 16, 32.0)) == binding.LORA_ERR_SLOT_OUT_OF_RANGE
+    assert status(lambda: S.load(-1, [a, None], [b, None], 16, 32.0)) == binding.LORA_ERR_SLOT_OUT_OF_RANGE
+    assert status(lambda: S.load(0, [a, None], [b, None], 17, 32.0)) == binding.LORA_ERR_RANK_EXCEEDS_MAX
+    assert status(lambda: S.load(0, [a, None], [b, None], 0, 32.0)) == binding.LORA_ERR_INVALID_ARGUMENT
+    assert status(lambda: S.load(0, [a, None], [None, None], 16, 32.0)) == binding.LORA_ERR_INVALID_ARGUMENT
+    assert status(lambda: S.load(0, [unpinned, None], [b, None], 16, 32.0)) == binding.LORA_ERR_HOST_NOT_PINNED
+    assert status(lambda: S.clear(9)) == binding.LORA_ERR_SLOT_OUT_OF_RANGE
+    x = torch.zeros(64, 128, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(64, 256, dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(64, dtype=torch.int32, device="cuda")
+    assert status(lambda: S.apply(x, y, idx, 0)) == binding.LORA_ERR_TOO_MANY_TOKENS
+    assert status(lambda: S.apply(x[:8], y[:8], idx[:8], 2)) == binding.LORA_ERR_BAD_MODULE
+    assert status(lambda: S.shrink(x, 0)) == binding.LORA_ERR_NO_PLAN
+    S.prepare(idx[:8])
+    assert status(lambda: S.expand(y, 1)) == binding.LORA_ERR_INVALID_ARGUMENT
+    assert "max_rank" in binding.lora_status_string(binding.LORA_ERR_RANK_EXCEEDS_MAX)
+    with pytest.raises(binding.LoraError) as e:
+        binding.Slots(4, 200, [(128, 128)], "bf16")
+    assert e.value.status == binding.LORA_ERR_RANK_EXCEEDS_MAX
+    with pytest.raises(binding.LoraError):
+        binding.Slots(4, 16, [(100, 128)], "bf16")          # d_in not a multiple of 8
+    # nothing was loaded by the failed calls
+    assert S.stats()["loads"] == 0
+    S.close()
