@@ -161,31 +161,6 @@ def main():
                 ys.append(torch.randn(T, m.d_out, generator=gen, device=dev).to(torch.bfloat16))
     torch.cuda.synchronize()
 
-    # parity of layer set 0 against the oracle on a sample of rows, before timing
-    parity = None
-    try:
-        import oracle
-        rows = np.arange(min(T, 64))
-        y0 = {m.name: ys[i].clone() for i, m in enumerate(mods)}
-        slots.prepare(idx)
-        for i, m in enumerate(mods):
-            slots.shrink(xs[i], i)
-            slots.expand(y0[m.name], i)
-        torch.cuda.synchronize()
-        worst = 0.0
-        for m in mods:
-            ref = oracle.apply(oracle.BF16, wl.x[m.name][rows], wl.y[m.name][rows], wl.idx[rows],
-                               synth.oracle_adapters(wl, m.name))
-            got = y0[m.name][rows].cpu().view(torch.int16).numpy().view(np.uint16)
-            g = synth.bf16_bits_to_f32(got).astype(np.float64)
-            r = synth.bf16_bits_to_f32(ref).astype(np.float64)
-            worst = max(worst, float((np.abs(g - r) / (2e-2 * (1 + np.abs(r)))).max()))
-        parity = {"rows": int(len(rows)), "worst_err_over_bound": worst, "ok": worst <= 1.0}
-        del y0
-    except Exception as e:                                   # reported, never hidden
-        parity = {"error": repr(e)}
-    log("parity:", parity)
-
     nm = len(mods)
     stream = torch.cuda.current_stream()
     use_events = not args.no_kernel_events
@@ -290,7 +265,6 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "parity": parity,
     }
     print(json.dumps(out), flush=True)
     slots.close()

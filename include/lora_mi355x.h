@@ -123,10 +123,12 @@ int lora_slots_destroy(lora_ctx *ctx);
 int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
                    int32_t r, double lora_alpha, int32_t use_rslora);
 
-/* Mark `slot` empty for every module (ordered like lora_slot_load). */
+/* Mark `slot` empty for every module.  Batches enqueued after this call skip
+ * the slot; batches already enqueued still apply the adapter it held.  Host-only:
+ * no device work is enqueued. */
 int lora_slot_clear(lora_ctx *ctx, int32_t slot);
 
-/* Host waits until every load and clear issued so far has completed. */
+/* Host waits until every load issued so far has completed. */
 int lora_sync_loads(lora_ctx *ctx);
 
 /*

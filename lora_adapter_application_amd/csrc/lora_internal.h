@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lora_mi355x.h"
+
 namespace lora {
 
 // Tokens per tile: a tile is a run of at most kTileTokens tokens of one slot.
@@ -13,8 +15,8 @@ constexpr int kTileTokens = 64;
 constexpr int kExpandCols = 256;
 // K elements one shrink wave consumes per step (4 MFMA steps of 32).
 constexpr int kShrinkKBlock = 128;
-// Upper bound of shrink K-splits.
-constexpr int kMaxSplits = 32;
+// Upper bound of shrink K-splits (the expand sums at most this many partials).
+constexpr int kMaxSplits = 16;
 // Largest padded rank (LORA_MAX_RANK rounded up to 16).
 #define LORA_MAX_RANK_PAD 128
 
@@ -28,17 +30,23 @@ struct alignas(16) Tile {
 struct PlanBuffers {
     int32_t *counts;     // [S] tokens per slot
     int32_t *seg_start;  // [S] first position of each slot's run
-    int32_t *perm;       // [max_tokens] token index per position
     Tile *tiles;         // [max_tiles]
+    int32_t *tile_tok;   // [max_tiles][kTileTokens]: token index of each tile row
     int32_t *n_tiles;    // scalar
     int32_t *n_active;   // scalar
     uint32_t *flags;     // scalar, sticky
+    int32_t *chunk_counts;  // [ceil(max_tokens/1024)][S], batches above 1024 tokens
+};
+
+// Per-launch slot metadata, passed by value: rank of each slot for the module
+// being applied (0 = empty slot or module not targeted) and the slot's scale.
+struct SlotMeta {
+    float scale[LORA_MAX_SLOTS];
+    uint8_t rank[LORA_MAX_SLOTS];
 };
 
 inline int max_tiles_for(int T, int S) { return (T + kTileTokens - 1) / kTileTokens + (S < T ? S : T); }
 
-// LDS bytes the plan kernel needs for S slots.
-inline size_t plan_lds_bytes(int S) { return sizeof(int32_t) * (size_t)S * (2 + 2 * 16); }
 
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
                        hipStream_t st);
@@ -48,8 +56,7 @@ struct ShrinkArgs {
     const void *x;          // [T][d_in]
     const void *A;          // module base: [S][R_pad][d_in]
     int64_t slot_stride_A;  // elements
-    const int32_t *rank;    // [S] rank of each slot for this module (0 = skip)
-    const int32_t *perm;
+    const int32_t *tile_tok;
     const Tile *tiles;
     const int32_t *n_tiles;
     float *hpart;           // [splits][T][R_pad]
@@ -59,15 +66,14 @@ struct ShrinkArgs {
     int32_t k_chunk;
     int32_t splits;
     int32_t grid_tiles;
+    int32_t mixed;          // batch above 1024 tokens: long tiles take the segment path
 };
 
 struct ExpandArgs {
     void *y;                // [T][d_out]
     const void *Bi;         // module base: [S][R_pad/8][d_out][8]
     int64_t slot_stride_B;  // elements
-    const int32_t *rank;
-    const float *scale;     // [S]
-    const int32_t *perm;
+    const int32_t *tile_tok;
     const Tile *tiles;
     const int32_t *n_tiles;
     const float *hpart;
@@ -78,14 +84,12 @@ struct ExpandArgs {
     int32_t grid_tiles;
 };
 
-hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, hipStream_t st);
-hipError_t launch_expand(bool bf16, const ExpandArgs &a, hipStream_t st);
+hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st);
+hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st);
 
 // Slot maintenance, on the side stream.
-hipError_t launch_slot_reset(int32_t *rank_all, int32_t n_modules, int32_t S, int32_t slot,
-                             hipStream_t st);
 hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_slot,
                                 const void *B_stage, int32_t d_out, int32_t r, int32_t R_pad,
-                                int32_t *rank_entry, float *scale_entry, float s, hipStream_t st);
+                                hipStream_t st);
 
 }  // namespace lora

@@ -1,8 +1,9 @@
 // lora_kernels.hip -- gfx950 kernels of the multi-adapter LoRA update
 //
 //   plan     stable counting sort of the per-token slot index into runs of one
-//            slot, cut into tiles of up to 64 tokens (device only, no host sync)
-//   shrink   h[p, :] = x[perm[p], :] . A_k^T over a K range (fp32 partials)
+//            slot, cut into tiles of up to 64 tokens; each tile record lists its
+//            token indices (device only, no host sync)
+//   shrink   h[p, :] = x[tok(p), :] . A_k^T over a K range (fp32 partials)
 //   expand   y[t, :] = round(y[t, :] + s_k * h[p, :] . B_k)
 //
 // The update itself, its scale and the adapter fields it reads are those of the
@@ -45,77 +46,101 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 // ----------------------------------------------------------------------------
 // plan
 
-// Exclusive scan of one int per thread over a 1024-thread block.
-__device__ int block_excl_scan_1024(int v, int *wsum /*[17]*/, int *total)
+// Exclusive scan of two ints per thread over a 1024-thread block.
+__device__ void block_excl_scan2_1024(int &a, int &b, int2 *wsum /*[17]*/, int &total_a, int &total_b)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int s = v;
+    int sa = a, sb = b;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(s, d, 64);
-        if (lane >= d)
-            s += o;
+        const int oa = __shfl_up(sa, d, 64), ob = __shfl_up(sb, d, 64);
+        if (lane >= d) {
+            sa += oa;
+            sb += ob;
+        }
     }
     if (lane == 63)
-        wsum[wave] = s;
+        wsum[wave] = make_int2(sa, sb);
     __syncthreads();
     if (wave == 0) {
-        int ws = lane < 16 ? wsum[lane] : 0;
-        int t = ws;
+        const int2 w = lane < 16 ? wsum[lane] : make_int2(0, 0);
+        int ta = w.x, tb = w.y;
 #pragma unroll
         for (int d = 1; d < 16; d <<= 1) {
-            int o = __shfl_up(t, d, 64);
-            if (lane >= d)
-                t += o;
+            const int oa = __shfl_up(ta, d, 64), ob = __shfl_up(tb, d, 64);
+            if (lane >= d) {
+                ta += oa;
+                tb += ob;
+            }
         }
         if (lane < 16)
-            wsum[lane] = t - ws;
+            wsum[lane] = make_int2(ta - w.x, tb - w.y);
         if (lane == 15)
-            wsum[16] = t;
+            wsum[16] = make_int2(ta, tb);
     }
     __syncthreads();
-    int excl = s - v + wsum[wave];
-    *total = wsum[16];
-    __syncthreads();
-    return excl;
+    const int2 base = wsum[wave], tot = wsum[16];
+    a = sa - a + base.x;
+    b = sb - b + base.y;
+    total_a = tot.x;
+    total_b = tot.y;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ idx, int32_t T,
-                                                    int32_t S, PlanBuffers pb)
+// Rank of this thread's token among the earlier tokens of its wave with the
+// same slot (one ballot per distinct slot in the wave); the first lane of each
+// slot writes the wave's count of that slot to wcnt[wave][slot].
+__device__ __forceinline__ int wave_stable_rank(int v, bool valid, int32_t *wcnt, int S)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t act = __ballot(valid);
+    int my_rank = 0;
+    while (act) {
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const int lv = __shfl(v, leader, 64);
+        const bool mine = valid && v == lv;
+        const uint64_t m = __ballot(mine);
+        if (mine)
+            my_rank = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == leader)
+            wcnt[wave * S + lv] = __popcll(m);
+        act &= ~m;
+    }
+    return my_rank;
+}
+
+// Batches of at most 1024 tokens: one token per thread, one ballot pass gives
+// both the per-slot counts and each token's rank among equal slots.
+__global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restrict__ idx,
+                                                          int32_t T, int32_t S, PlanBuffers pb)
 {
     extern __shared__ int32_t sm[];
-    int32_t *cnt = sm;             // [S]
-    int32_t *base = sm + S;        // [S]
-    int32_t *wcnt = sm + 2 * S;    // [16][S] tokens of slot s in wave w of the chunk
-    int32_t *woff = sm + 18 * S;   // [16][S] first position for them
-    __shared__ int32_t wsum[17];
-    __shared__ int32_t bad;
+    int32_t *wcnt = sm;             // [16][S]: count, then offset within the slot's run
+    int32_t *tbase = sm + 16 * S;   // [S]: first tile of slot s
+    __shared__ int2 wsum[17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int i = tid; i < S; i += 1024)
-        cnt[i] = 0;
+    const int v = tid < T ? idx[tid] : -1;
     for (int i = tid; i < 16 * S; i += 1024)
         wcnt[i] = 0;
-    if (tid == 0)
-        bad = 0;
+    const bool valid = v >= 0 && v < S;
+    const uint64_t too_large = __ballot(v >= S);
+    if (too_large && lane == 0)
+        atomicOr(pb.flags, 1u);
     __syncthreads();
-    for (int i = tid; i < T; i += 1024) {
-        int v = idx[i];
-        if (v >= S)
-            bad = 1;
-        else if (v >= 0)
-            atomicAdd(&cnt[v], 1);
-    }
+    const int my_rank = wave_stable_rank(v, valid, wcnt, S);
     __syncthreads();
-
-    // Runs and tiles, one slot per thread (S <= 1024).
-    const int c = tid < S ? cnt[tid] : 0;
-    int n_active, n_tiles;
-    const int start = block_excl_scan_1024(c, wsum, &n_active);
-    const int nt = (c + kTileTokens - 1) / kTileTokens;
-    const int tstart = block_excl_scan_1024(nt, wsum, &n_tiles);
+    int c = 0;
     if (tid < S) {
-        base[tid] = start;
+        for (int w = 0; w < 16; ++w) {
+            const int k = wcnt[w * S + tid];
+            wcnt[w * S + tid] = c;
+            c += k;
+        }
+    }
+    int start = c, tstart = (c + kTileTokens - 1) / kTileTokens, n_active, n_tiles;
+    const int nt = tstart;
+    block_excl_scan2_1024(start, tstart, wsum, n_active, n_tiles);
+    if (tid < S) {
+        tbase[tid] = tstart;
         pb.counts[tid] = c;
         pb.seg_start[tid] = start;
         for (int j = 0; j < nt; ++j) {
@@ -130,52 +155,125 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
     if (tid == 0) {
         *pb.n_tiles = n_tiles;
         *pb.n_active = n_active;
-        if (bad)
-            atomicOr(pb.flags, 1u);
     }
     __syncthreads();
+    if (valid) {
+        const int rel = wcnt[wave * S + v] + my_rank;          // position within the slot's run
+        pb.tile_tok[(int64_t)(tbase[v] + rel / kTileTokens) * kTileTokens + rel % kTileTokens] = tid;
+    }
+}
 
-    // Stable scatter, 1024 tokens per pass in index order.  Within a wave, a
-    // token's rank among equal slots comes from ballots, one per distinct slot.
-    for (int c0 = 0; c0 < T; c0 += 1024) {
-        const int i = c0 + tid;
-        const int v = i < T ? idx[i] : -1;
-        const bool valid = v >= 0 && v < S;
-        uint64_t act = __ballot(valid);
-        int my_rank = 0;
-        while (act) {
-            const int leader = __ffsll((unsigned long long)act) - 1;
-            const int lv = __shfl(v, leader, 64);
-            const bool mine = valid && v == lv;
-            const uint64_t m = __ballot(mine);
-            if (mine)
-                my_rank = __popcll(m & ((1ull << lane) - 1ull));
-            if (lane == leader)
-                wcnt[wave * S + lv] = __popcll(m);
-            act &= ~m;
-        }
-        __syncthreads();
-        for (int s = tid; s < S; s += 1024) {
-            int run = base[s];
-            for (int w = 0; w < 16; ++w) {
-                const int k = wcnt[w * S + s];
-                wcnt[w * S + s] = 0;
-                woff[w * S + s] = run;
-                run += k;
+// Batches above 1024 tokens run in two launches over chunks of 1024 tokens:
+// count (per chunk and slot), then scatter, where every workgroup derives its
+// chunk's offsets and the slot runs from all chunk counts (workgroup 0 also
+// writes the tile list).
+__global__ __launch_bounds__(1024) void plan_count_kernel(const int32_t *__restrict__ idx,
+                                                          int32_t T, int32_t S, PlanBuffers pb)
+{
+    extern __shared__ int32_t wcnt[];   // [16][S]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int i = blockIdx.x * 1024 + tid;
+    const int v = i < T ? idx[i] : -1;
+    for (int k = tid; k < 16 * S; k += 1024)
+        wcnt[k] = 0;
+    const bool valid = v >= 0 && v < S;
+    if (__ballot(v >= S) && lane == 0)
+        atomicOr(pb.flags, 1u);
+    __syncthreads();
+    (void)wave_stable_rank(v, valid, wcnt, S);
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += 1024) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w)
+            c += wcnt[w * S + sl];
+        pb.chunk_counts[(int64_t)blockIdx.x * S + sl] = c;
+    }
+}
+
+__global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__restrict__ idx,
+                                                            int32_t T, int32_t S, int32_t n_chunks,
+                                                            PlanBuffers pb)
+{
+    extern __shared__ int32_t sm[];
+    int32_t *wcnt = sm;              // [16][S]
+    int32_t *seg = sm + 16 * S;      // [S] first position of slot s
+    int32_t *tbase = sm + 17 * S;    // [S] first tile of slot s
+    __shared__ int2 wsum[17];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int chunk = blockIdx.x;
+    const int i = chunk * 1024 + tid;
+    const int v = i < T ? idx[i] : -1;
+    for (int k = tid; k < 16 * S; k += 1024)
+        wcnt[k] = 0;
+    const bool valid = v >= 0 && v < S;
+    // this slot's tokens in earlier chunks, and in all chunks
+    int pre = 0, tot = 0;
+    if (tid < S) {
+        for (int ch0 = 0; ch0 < n_chunks; ch0 += 16) {
+            int k[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                k[u] = ch0 + u < n_chunks ? pb.chunk_counts[(int64_t)(ch0 + u) * S + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                pre += ch0 + u < chunk ? k[u] : 0;
+                tot += k[u];
             }
-            base[s] = run;
         }
-        __syncthreads();
-        if (valid)
-            pb.perm[woff[wave * S + v] + my_rank] = i;
-        __syncthreads();
+    }
+    __syncthreads();
+    const int my_rank = wave_stable_rank(v, valid, wcnt, S);
+    int start = tot, tstart = (tot + kTileTokens - 1) / kTileTokens, n_active, n_tiles;
+    const int nt = tstart;
+    block_excl_scan2_1024(start, tstart, wsum, n_active, n_tiles);
+    if (tid < S) {
+        seg[tid] = start;
+        tbase[tid] = tstart;
+        int run = start + pre;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int k = wcnt[w * S + tid];
+            wcnt[w * S + tid] = run;
+            run += k;
+        }
+        if (chunk == 0) {
+            pb.counts[tid] = tot;
+            pb.seg_start[tid] = start;
+            for (int j = 0; j < nt; ++j) {
+                Tile t;
+                t.slot = tid;
+                t.start = start + j * kTileTokens;
+                t.len = min(kTileTokens, tot - j * kTileTokens);
+                t.pad = 0;
+                pb.tiles[tstart + j] = t;
+            }
+        }
+    }
+    if (chunk == 0 && tid == 0) {
+        *pb.n_tiles = n_tiles;
+        *pb.n_active = n_active;
+    }
+    __syncthreads();
+    if (valid) {
+        const int rel = wcnt[wave * S + v] + my_rank - seg[v];
+        pb.tile_tok[(int64_t)(tbase[v] + rel / kTileTokens) * kTileTokens + rel % kTileTokens] = i;
     }
 }
 
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
                        hipStream_t st)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), plan_lds_bytes(S), st, idx, T, S, pb);
+    if (T <= 1024) {
+        hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(1024),
+                           sizeof(int32_t) * (size_t)S * 17, st, idx, T, S, pb);
+    } else {
+        const int n_chunks = (T + 1023) / 1024;
+        hipLaunchKernelGGL(plan_count_kernel, dim3(n_chunks), dim3(1024),
+                           sizeof(int32_t) * (size_t)S * 16, st, idx, T, S, pb);
+        hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_chunks), dim3(1024),
+                           sizeof(int32_t) * (size_t)S * 18, st, idx, T, S, n_chunks, pb);
+    }
     return hipGetLastError();
 }
 
@@ -187,27 +285,187 @@ hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffe
 // (subtile, K part) so short tiles still keep all 4 waves loading.  Per step a
 // lane loads 64 contiguous bytes of its token's x row and of its rank's A^T row
 // and feeds them to 4 MFMAs; both operands use the same K order, so the sum is
-// the plain dot product over that K block.  Output: h as [rank][token] blocks,
-// lane l holding ranks 4g..4g+3 of token (l & 15) -> one 16-byte store.
+// the plain dot product over that K block.  The next K block is loaded before
+// the MFMAs of the current one (register double buffering) when the rank fits.
+// Output: h as [rank][token] blocks, lane l holding ranks 4g..4g+3 of token
+// (l & 15) -> one 16-byte store.
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
 template <int NB>
-__global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a)
+struct KBlock {
+    uint4 x[4];
+    uint4 a[NB][4];
+};
+
+template <int NB>
+__device__ __forceinline__ void load_kblock(KBlock<NB> &blk, const uint16_t *xrow,
+                                            const uint16_t *arow0, int64_t d_in, int kk, int k1,
+                                            int nb, bool tok_ok)
 {
-    if ((int)blockIdx.x >= *a.n_tiles)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ke = kk + q * 8;
+        blk.x[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ke = kk + q * 8;
+            blk.a[b][q] = (b < nb && ke < k1) ? ld16(arow0 + b * 16 * d_in + ke)
+                                               : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void mfma_kblock(f32x4_t (&acc)[NB], const KBlock<NB> &blk, int nb)
+{
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if (b < nb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, blk.a[b][q]),
+                    __builtin_bit_cast(bf16x8_t, blk.x[q]), acc[b], 0, 0, 0);
+        }
+    }
+}
+
+// Segment path (SGMV) for tiles of 33..64 tokens: wave w owns subtile w over
+// the whole K range.  Each K block of A^T (nb*16 ranks x 128) is loaded once per
+// workgroup into LDS (double buffered) and shared by the 4 waves; x is
+// prefetched two K blocks ahead in registers.
+constexpr int kLdsRow = kShrinkKBlock + 8;   // bf16 elements per staged A row (padded)
+
+template <int NB>
+__device__ __forceinline__ void shrink_sgmv(const ShrinkArgs &a, const Tile &tile, int nb, int k0,
+                                            int k1, int split, uint16_t *lds)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, g = lane >> 4;
+    const int t_in = wave * 16 + row;
+    const bool tok_ok = t_in < tile.len;
+    const int p = tile.start + t_in;
+    const uint16_t *xrow = (const uint16_t *)a.x + (int64_t)(tok_ok ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t_in] : 0) * a.d_in;
+    const uint16_t *Aslot = (const uint16_t *)a.A + (int64_t)tile.slot * a.slot_stride_A;
+    const int nkb = (k1 - k0 + kShrinkKBlock - 1) / kShrinkKBlock;
+    constexpr int buf_elems = NB * 16 * kLdsRow;
+
+    uint4 ra[NB];
+    auto load_a = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = tid + 256 * i;
+            const int r = c >> 4, col = (c & 15) * 8;
+            ra[i] = (i < nb && kb + col < k1) ? ld16(Aslot + (int64_t)r * a.d_in + kb + col)
+                                              : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i < nb) {
+                const int c = tid + 256 * i;
+                const int r = c >> 4, col = (c & 15) * 8;
+                *(uint4 *)(lds + buf * buf_elems + r * kLdsRow + col) = ra[i];
+            }
+        }
+    };
+    auto load_x = [&](uint4 (&xv)[4], int kb) {
+        const int kk = kb + g * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ke = kk + q * 8;
+            xv[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 x0[4], x1[4], x2[4];
+    load_a(k0);
+    load_x(x0, k0);
+    if (nkb > 1)
+        load_x(x1, k0 + kShrinkKBlock);
+    store_a(0);
+    if (nkb > 1)
+        load_a(k0 + kShrinkKBlock);
+    __syncthreads();
+    for (int i = 0; i < nkb; ++i) {
+        const int kb = k0 + i * kShrinkKBlock;
+        if (i + 2 < nkb)
+            load_x(x2, kb + 2 * kShrinkKBlock);
+        const uint16_t *L = lds + (i & 1) * buf_elems;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b < nb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 av = *(const uint4 *)(L + (b * 16 + row) * kLdsRow + g * 32 + q * 8);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, x0[q]),
+                        acc[b], 0, 0, 0);
+                }
+            }
+        }
+        if (i + 1 < nkb) {
+            store_a((i + 1) & 1);
+            if (i + 2 < nkb)
+                load_a(kb + 2 * kShrinkKBlock);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x0[q] = x1[q];
+            x1[q] = x2[q];
+        }
+    }
+    if (tok_ok) {
+        float *hrow = a.hpart + (int64_t)split * a.split_stride + (int64_t)p * a.R_pad;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (b < nb)
+                *(f32x4_t *)(hrow + b * 16 + g * 4) = acc[b];
+    }
+}
+
+// MIXED: batches above 1024 tokens (tiles of any length; long ones take the
+// segment path, the rest the gather path single-buffered).  Otherwise every
+// tile takes the gather path, double-buffered when the rank allows.
+template <int NB, bool MIXED>
+__global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
+{
+    const int n_tiles = *a.n_tiles;
+    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
+    if ((int)blockIdx.x >= n_tiles)
         return;
-    const Tile tile = a.tiles[blockIdx.x];
-    const int rank = a.rank[tile.slot];
-    if (rank <= 0)
+    const int rank = meta.rank[tile.slot];
+    if (rank == 0)
         return;
     const int nb = (rank + 15) >> 4;
     const int split = blockIdx.y;
     const int k0 = split * a.k_chunk;
     const int k1 = min(a.d_in, k0 + a.k_chunk);
+    const int nsub = (tile.len + 15) >> 4;
+
+    constexpr int kRedBytes = 4 * NB * 64 * 16;
+    constexpr int kSgmvBytes = MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0;
+    constexpr int kSmemBytes = kRedBytes > kSgmvBytes ? kRedBytes : kSgmvBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+
+    if (MIXED && nsub >= 3) {
+        shrink_sgmv<NB>(a, tile, nb, k0, k1, split, (uint16_t *)smem);
+        return;
+    }
+
+    // Gather path (BGMV): waves split the tile's subtiles and the K range.
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = lane & 15, g = lane >> 4;
-    const int nsub = (tile.len + 15) >> 4;
     const int nsub_pad = nsub == 3 ? 4 : nsub;
     const int kparts = 4 / nsub_pad;
     const int sub = wave % nsub_pad, kp = wave / nsub_pad;
@@ -216,8 +474,9 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a)
     const bool tok_ok = wave_on && tok_in_tile < tile.len;
     const int p = tile.start + tok_in_tile;
 
-    const uint16_t *xrow = (const uint16_t *)a.x + (int64_t)(tok_ok ? a.perm[p] : 0) * a.d_in;
-    const uint16_t *Aslot = (const uint16_t *)a.A + (int64_t)tile.slot * a.slot_stride_A;
+    const uint16_t *xrow = (const uint16_t *)a.x + (int64_t)(tok_ok ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + tok_in_tile] : 0) * a.d_in;
+    const uint16_t *arow0 = (const uint16_t *)a.A + (int64_t)tile.slot * a.slot_stride_A +
+                            (int64_t)row * a.d_in;
 
     f32x4_t acc[NB];
 #pragma unroll
@@ -225,35 +484,29 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a)
         acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if (wave_on) {
-        for (int kb = k0 + kp * kShrinkKBlock; kb < k1; kb += kparts * kShrinkKBlock) {
-            const int kk = kb + g * 32;
-            uint4 xv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ke = kk + q * 8;
-                xv[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
+        const int kstep = kparts * kShrinkKBlock;
+        int kb = k0 + kp * kShrinkKBlock;
+        if (!MIXED && NB <= 4) {
+            KBlock<NB> cur, nxt;
+            if (kb < k1)
+                load_kblock<NB>(cur, xrow, arow0, a.d_in, kb + g * 32, k1, nb, tok_ok);
+            for (; kb < k1; kb += kstep) {
+                const int kn = kb + kstep;
+                if (kn < k1)
+                    load_kblock<NB>(nxt, xrow, arow0, a.d_in, kn + g * 32, k1, nb, tok_ok);
+                mfma_kblock<NB>(acc, cur, nb);
+                cur = nxt;
             }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (b < nb) {
-                    const uint16_t *arow = Aslot + (int64_t)(b * 16 + row) * a.d_in;
-                    uint4 av[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int ke = kk + q * 8;
-                        av[q] = ke < k1 ? ld16(arow + ke) : make_uint4(0, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, av[q]), __builtin_bit_cast(bf16x8_t, xv[q]),
-                            acc[b], 0, 0, 0);
-                }
+        } else {
+            for (; kb < k1; kb += kstep) {
+                KBlock<NB> cur;
+                load_kblock<NB>(cur, xrow, arow0, a.d_in, kb + g * 32, k1, nb, tok_ok);
+                mfma_kblock<NB>(acc, cur, nb);
             }
         }
     }
 
-    __shared__ f32x4_t red[4][NB][64];
+    f32x4_t (*red)[NB][64] = (f32x4_t (*)[NB][64])smem;
     if (kparts > 1) {
         if (wave_on && kp > 0) {
 #pragma unroll
@@ -281,64 +534,115 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a)
 // ----------------------------------------------------------------------------
 // expand, bf16 on MFMA
 //
-// One workgroup = one tile x 256 columns of y.  The product is formed
-// transposed, out[n][t] = sum_j B[j][n] h[t][j], so the result of one lane is
-// four columns of one token.  B is stored in groups of 8 ranks,
-// Bi[j/8][n][j%8], so the rank slice an MFMA lane needs is contiguous.  Rows
-// of the 16x16 output blocks are mapped to columns so that lane group g of a
-// wave owns 16 adjacent columns: y is read and written 32 bytes per lane.
+// One workgroup = one tile (<= 64 tokens of one slot) x 256 columns of y; wave
+// w owns the 64 columns 64w..64w+63 for every subtile of the tile.  The
+// product is formed transposed, out[n][t] = sum_j B[j][n] h[t][j].  B is
+// stored in groups of 8 ranks, Bi[j/8][n][j%8], so the rank slice an MFMA lane
+// needs is contiguous; rows of the 16x16 output blocks are mapped to columns
+// so that lane group g of a wave owns 16 adjacent columns of one token, and y
+// is read and written 32 bytes per lane.  Every global load of the wave (token
+// ids, B, y) is issued before any arithmetic; the K-split partials of h are summed
+// once per workgroup into LDS, then split into a bf16 high and low half.
 
 template <int NB>
-__global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a)
+__global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
-    if ((int)blockIdx.x >= *a.n_tiles)
-        return;
+    const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    const int rank = a.rank[tile.slot];
-    if (rank <= 0)
+    if ((int)blockIdx.x >= n_tiles)
+        return;
+    const int rank = meta.rank[tile.slot];
+    if (rank == 0)
         return;
     const int nb = (rank + 15) >> 4;
-    const float s = a.scale[tile.slot];
-    const int c0 = blockIdx.y * kExpandCols;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float s = meta.scale[tile.slot];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row = lane & 15, g = lane >> 4;
+    const int cb = blockIdx.y * kExpandCols + wave * 64;
+    const bool cols_ok = cb < a.d_out;
     const int nsub = (tile.len + 15) >> 4;
-    const int nsub_pad = nsub == 3 ? 4 : nsub;
-    const int cparts = 4 / nsub_pad;
-    const int sub = wave % nsub_pad, cp = wave / nsub_pad;
-    if (sub >= nsub)
-        return;
-    const int tok_in_tile = sub * 16 + row;
-    const bool tok_ok = tok_in_tile < tile.len;
-    const int p = tile.start + tok_in_tile;
 
-    // h for this lane's token, ranks kst*16 + 4g .. +3, summed over K splits,
-    // split into bf16 high and low halves.
-    s16x4_t hhi[NB], hlo[NB];
+    // tokens of this lane in each subtile
+    int tok[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int t = st * 16 + row;
+        tok_ok[st] = cols_ok && t < tile.len;
+        tok[st] = tok_ok[st] ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t] : 0;
+    }
+    // B operands: lane row -> column cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 4g..+3
+    const uint16_t *Bslot = (const uint16_t *)a.Bi + (int64_t)tile.slot * a.slot_stride_B;
+    uint2 bop[NB][4];
 #pragma unroll
     for (int kst = 0; kst < NB; ++kst) {
-        f32x4_t hs = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kst < nb && tok_ok) {
-            const float *hp = a.hpart + (int64_t)p * a.R_pad + kst * 16 + g * 4;
-            for (int sp = 0; sp < a.splits; ++sp)
-                hs += *(const f32x4_t *)(hp + (int64_t)sp * a.split_stride);
-        }
+        const int G = kst * 2 + (g >> 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t hi = f32_to_bf16_bits(hs[e]);
-            const uint32_t lo = f32_to_bf16_bits(hs[e] - bf16_bits_to_f32(hi));
-            hhi[kst][e] = (short)hi;
-            hlo[kst][e] = (short)lo;
+        for (int b = 0; b < 4; ++b) {
+            const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
+            bop[kst][b] = (kst < nb && cols_ok && n < a.d_out)
+                              ? *(const uint2 *)(Bslot + ((int64_t)G * a.d_out + n) * 8 + (g & 1) * 4)
+                              : make_uint2(0, 0);
+        }
+    }
+    // y: 16 adjacent columns of one token per lane and subtile
+    uint4 yv[4][2];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+            const int col = cb + g * 16 + piece * 8;
+            yv[st][piece] = (tok_ok[st] && col < a.d_out)
+                                ? *(const uint4 *)((const uint16_t *)a.y + (int64_t)tok[st] * a.d_out + col)
+                                : make_uint4(0, 0, 0, 0);
         }
     }
 
-    const int tok = tok_ok ? a.perm[p] : 0;
-    uint16_t *yrow = (uint16_t *)a.y + (int64_t)tok * a.d_out;
-    const uint16_t *Bslot = (const uint16_t *)a.Bi + (int64_t)tile.slot * a.slot_stride_B;
+    // h of the tile, summed over K splits, into LDS (fp32).  Thread tid owns
+    // the float4 quads e = tid + 256 i (i < NB) of the tile's len x nb*16 block;
+    // all partial loads are issued before any sum.
+    __shared__ float hs[kTileTokens][NB * 16 + 4];
+    const int quads = nb * 4;
+    const int n_el = tile.len * quads;
+    if (a.splits == 1) {
+        f32x4_t hv[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            const int t = e / quads, q = e - t * quads;
+            hv[i] = e < n_el ? *(const f32x4_t *)(a.hpart + (int64_t)(tile.start + t) * a.R_pad + q * 4)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            const int t = e / quads, q = e - t * quads;
+            if (e < n_el)
+                *(f32x4_t *)&hs[t][q * 4] = hv[i];
+        }
+    } else {
+        for (int e = tid; e < n_el; e += 256) {
+            const int t = e / quads, q = e - t * quads;
+            const float *hp = a.hpart + (int64_t)(tile.start + t) * a.R_pad + q * 4;
+            f32x4_t v[kMaxSplits];
+#pragma unroll
+            for (int u = 0; u < kMaxSplits; ++u)
+                v[u] = u < a.splits ? *(const f32x4_t *)(hp + (int64_t)u * a.split_stride)
+                                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            f32x4_t sum = v[0];
+#pragma unroll
+            for (int u = 1; u < kMaxSplits; ++u)
+                sum += v[u];
+            *(f32x4_t *)&hs[t][q * 4] = sum;
+        }
+    }
+    __syncthreads();
+    if (!cols_ok)
+        return;
 
-    for (int cg = cp; cg < 4; cg += cparts) {
-        const int cb = c0 + cg * 64;
-        if (cb >= a.d_out)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (st >= nsub)
             break;
         f32x4_t acc[4];
 #pragma unroll
@@ -347,26 +651,31 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a)
 #pragma unroll
         for (int kst = 0; kst < NB; ++kst) {
             if (kst < nb) {
-                const int G = kst * 2 + (g >> 1);
+                // rows beyond the tile read stale LDS; their results are never stored
+                const f32x4_t h = *(const f32x4_t *)&hs[st * 16 + row][kst * 16 + g * 4];
+                s16x4_t hhi, hlo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t hi = f32_to_bf16_bits(h[e]);
+                    hhi[e] = (short)hi;
+                    hlo[e] = (short)f32_to_bf16_bits(h[e] - bf16_bits_to_f32(hi));
+                }
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
-                    uint2 bv = make_uint2(0, 0);
-                    if (n < a.d_out)
-                        bv = *(const uint2 *)(Bslot + ((int64_t)G * a.d_out + n) * 8 + (g & 1) * 4);
-                    const s16x4_t bop = __builtin_bit_cast(s16x4_t, bv);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bop, hhi[kst], acc[b], 0, 0, 0);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bop, hlo[kst], acc[b], 0, 0, 0);
+                    const s16x4_t bo = __builtin_bit_cast(s16x4_t, bop[kst][b]);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hhi, acc[b], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hlo, acc[b], 0, 0, 0);
                 }
             }
         }
-        if (tok_ok) {
+        if (tok_ok[st]) {
+            uint16_t *yrow = (uint16_t *)a.y + (int64_t)tok[st] * a.d_out;
 #pragma unroll
             for (int piece = 0; piece < 2; ++piece) {
                 const int col = cb + g * 16 + piece * 8;
                 if (col < a.d_out) {
-                    uint4 yv = *(const uint4 *)(yrow + col);
-                    uint32_t w[4] = {yv.x, yv.y, yv.z, yv.w};
+                    const uint4 yw = yv[st][piece];
+                    uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
 #pragma unroll
                     for (int h2 = 0; h2 < 4; ++h2) {
                         const int e0 = piece * 8 + h2 * 2, e1 = e0 + 1;
@@ -384,13 +693,14 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a)
 // ----------------------------------------------------------------------------
 // fp32 on VALU
 
-__global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a)
+__global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta meta)
 {
-    if ((int)blockIdx.x >= *a.n_tiles)
-        return;
+    const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    const int rank = a.rank[tile.slot];
-    if (rank <= 0)
+    if ((int)blockIdx.x >= n_tiles)
+        return;
+    const int rank = meta.rank[tile.slot];
+    if (rank == 0)
         return;
     const int split = blockIdx.y;
     const int k0 = split * a.k_chunk;
@@ -402,7 +712,7 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a)
     __shared__ float as[LORA_MAX_RANK_PAD][33];
     __shared__ int toks[kTileTokens];
     if (tid < kTileTokens)
-        toks[tid] = tid < tile.len ? a.perm[tile.start + tid] : 0;
+        toks[tid] = tid < tile.len ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + tid] : 0;
     const int npairs = tile.len * rank;   // <= 64 * 128 = 32 per thread
     float acc[32];
 #pragma unroll
@@ -443,15 +753,16 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a)
     }
 }
 
-__global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a)
+__global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta meta)
 {
-    if ((int)blockIdx.x >= *a.n_tiles)
-        return;
+    const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    const int rank = a.rank[tile.slot];
-    if (rank <= 0)
+    if ((int)blockIdx.x >= n_tiles)
         return;
-    const float s = a.scale[tile.slot];
+    const int rank = meta.rank[tile.slot];
+    if (rank == 0)
+        return;
+    const float s = meta.scale[tile.slot];
     const int tid = threadIdx.x;
     __shared__ float hs[kTileTokens][LORA_MAX_RANK_PAD + 1];
     for (int e = tid; e < tile.len * rank; e += 256) {
@@ -482,7 +793,7 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a)
 #pragma unroll
     for (int t = 0; t < kTileTokens; ++t) {
         if (t < tile.len) {
-            const int64_t o = (int64_t)a.perm[tile.start + t] * a.d_out + n;
+            const int64_t o = (int64_t)a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t] * a.d_out + n;
             y[o] = y[o] + s * acc[t];
         }
     }
@@ -491,40 +802,47 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a)
 // ----------------------------------------------------------------------------
 // launches
 
-hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, hipStream_t st)
+template <bool MIXED>
+static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st)
+{
+    const int nbmax = a.R_pad / 16;
+    if (nbmax <= 1)
+        hipLaunchKernelGGL((shrink_bf16_kernel<1, MIXED>), grid, dim3(256), 0, st, a, m);
+    else if (nbmax <= 2)
+        hipLaunchKernelGGL((shrink_bf16_kernel<2, MIXED>), grid, dim3(256), 0, st, a, m);
+    else if (nbmax <= 4)
+        hipLaunchKernelGGL((shrink_bf16_kernel<4, MIXED>), grid, dim3(256), 0, st, a, m);
+    else
+        hipLaunchKernelGGL((shrink_bf16_kernel<8, MIXED>), grid, dim3(256), 0, st, a, m);
+}
+
+hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st)
 {
     const dim3 grid(a.grid_tiles, a.splits), block(256);
-    if (!bf16) {
-        hipLaunchKernelGGL(shrink_f32_kernel, grid, block, 0, st, a);
-    } else {
-        const int nbmax = a.R_pad / 16;
-        if (nbmax <= 1)
-            hipLaunchKernelGGL(shrink_bf16_kernel<1>, grid, block, 0, st, a);
-        else if (nbmax <= 2)
-            hipLaunchKernelGGL(shrink_bf16_kernel<2>, grid, block, 0, st, a);
-        else if (nbmax <= 4)
-            hipLaunchKernelGGL(shrink_bf16_kernel<4>, grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL(shrink_bf16_kernel<8>, grid, block, 0, st, a);
-    }
+    if (!bf16)
+        hipLaunchKernelGGL(shrink_f32_kernel, grid, block, 0, st, a, m);
+    else if (a.mixed)
+        launch_shrink_bf16<true>(a, m, grid, st);
+    else
+        launch_shrink_bf16<false>(a, m, grid, st);
     return hipGetLastError();
 }
 
-hipError_t launch_expand(bool bf16, const ExpandArgs &a, hipStream_t st)
+hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st)
 {
     const dim3 grid(a.grid_tiles, (a.d_out + kExpandCols - 1) / kExpandCols), block(256);
     if (!bf16) {
-        hipLaunchKernelGGL(expand_f32_kernel, grid, block, 0, st, a);
+        hipLaunchKernelGGL(expand_f32_kernel, grid, block, 0, st, a, m);
     } else {
         const int nbmax = a.R_pad / 16;
         if (nbmax <= 1)
-            hipLaunchKernelGGL(expand_bf16_kernel<1>, grid, block, 0, st, a);
+            hipLaunchKernelGGL(expand_bf16_kernel<1>, grid, block, 0, st, a, m);
         else if (nbmax <= 2)
-            hipLaunchKernelGGL(expand_bf16_kernel<2>, grid, block, 0, st, a);
+            hipLaunchKernelGGL(expand_bf16_kernel<2>, grid, block, 0, st, a, m);
         else if (nbmax <= 4)
-            hipLaunchKernelGGL(expand_bf16_kernel<4>, grid, block, 0, st, a);
+            hipLaunchKernelGGL(expand_bf16_kernel<4>, grid, block, 0, st, a, m);
         else
-            hipLaunchKernelGGL(expand_bf16_kernel<8>, grid, block, 0, st, a);
+            hipLaunchKernelGGL(expand_bf16_kernel<8>, grid, block, 0, st, a, m);
     }
     return hipGetLastError();
 }
@@ -532,28 +850,11 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, hipStream_t st)
 // ----------------------------------------------------------------------------
 // slot maintenance
 
-__global__ void slot_reset_kernel(int32_t *rank_all, int32_t n_modules, int32_t S, int32_t slot)
-{
-    for (int m = blockIdx.x * blockDim.x + threadIdx.x; m < n_modules; m += gridDim.x * blockDim.x)
-        rank_all[(int64_t)m * S + slot] = 0;
-}
-
-hipError_t launch_slot_reset(int32_t *rank_all, int32_t n_modules, int32_t S, int32_t slot,
-                             hipStream_t st)
-{
-    const int blocks = (n_modules + 255) / 256;
-    hipLaunchKernelGGL(slot_reset_kernel, dim3(blocks), dim3(256), 0, st, rank_all, n_modules, S,
-                       slot);
-    return hipGetLastError();
-}
-
 // Repack B (r x d_out, row-major, staged on the device) into groups of 8 ranks,
-// Bi[j/8][n][j%8], zero ranks r..R_pad-1 of both A^T and B, then publish the
-// rank and scale of the slot for this module.
+// Bi[j/8][n][j%8], and zero ranks r..R_pad-1 of both A^T and B.
 template <typename E>
 __global__ void slot_finalize_kernel(E *A_slot, int32_t d_in, E *Bi_slot, const E *B_stage,
-                                     int32_t d_out, int32_t r, int32_t R_pad, int32_t *rank_entry,
-                                     float *scale_entry, float s)
+                                     int32_t d_out, int32_t r, int32_t R_pad)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -569,15 +870,11 @@ __global__ void slot_finalize_kernel(E *A_slot, int32_t d_in, E *Bi_slot, const 
     const int64_t nA = (int64_t)(R_pad - r) * d_in;
     for (int64_t o = first; o < nA; o += stride)
         A_slot[(int64_t)r * d_in + o] = E(0);
-    if (first == 0) {
-        *rank_entry = r;
-        *scale_entry = s;
-    }
 }
 
 hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_slot,
                                 const void *B_stage, int32_t d_out, int32_t r, int32_t R_pad,
-                                int32_t *rank_entry, float *scale_entry, float s, hipStream_t st)
+                                hipStream_t st)
 {
     const int64_t work = (int64_t)R_pad * (d_out > d_in ? d_out : d_in);
     int blocks = (int)((work + 255) / 256);
@@ -586,11 +883,11 @@ hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_
     if (bf16)
         hipLaunchKernelGGL(slot_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
                            (uint16_t *)A_slot, d_in, (uint16_t *)Bi_slot,
-                           (const uint16_t *)B_stage, d_out, r, R_pad, rank_entry, scale_entry, s);
+                           (const uint16_t *)B_stage, d_out, r, R_pad);
     else
         hipLaunchKernelGGL(slot_finalize_kernel<float>, dim3(blocks), dim3(256), 0, st,
                            (float *)A_slot, d_in, (float *)Bi_slot, (const float *)B_stage, d_out,
-                           r, R_pad, rank_entry, scale_entry, s);
+                           r, R_pad);
     return hipGetLastError();
 }
 

@@ -7,13 +7,15 @@
 // hierarchy"): per module m, A^T as [S][R_pad][d_in] (rank-major, rank j of a
 // slot is one contiguous row) and B as [S][R_pad/8][d_out][8] (groups of eight
 // ranks interleaved per output column, the order the expand MFMA consumes).
-// Rows r..R_pad-1 of a slot are kept zero.  Per (module, slot) the device holds
-// the rank (0 = nothing to apply) and per slot the fp32 scale.
+// Rows r..R_pad-1 of a slot are kept zero.  The host keeps, per (module, slot),
+// the rank (0 = nothing to apply) and per slot the fp32 scale; every launch gets
+// the module's table by value, so a kernel sees exactly the slots that were
+// loaded before it was enqueued.
 //
 // Ordering without host synchronisation:
-//  - a load or clear records an event on the side stream; a later kernel
-//    launch on a compute stream waits for it once (read after write);
-//  - before a load or clear overwrites a slot, the side stream waits for the
+//  - a load records an event on the side stream; a later kernel launch on a
+//    compute stream waits for it once (read after write);
+//  - before a load overwrites a slot, the side stream waits for the
 //    current tail of every compute stream this ctx has launched on since the
 //    previous load, so weights an in-flight batch reads are never overwritten
 //    ("an adapter in use must not be evicted", same page, data-plane section).
@@ -23,6 +25,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -39,7 +42,7 @@ thread_local std::string g_create_error;
 struct StreamState {
     hipStream_t stream;
     uint64_t waited_gen;    // load generation this stream has waited for
-    bool used_since_load;   // launched on since the last load / clear
+    bool used_since_load;   // launched on since the last load
     hipEvent_t tail;        // recorded at load time to fence the stream's tail
 };
 
@@ -72,13 +75,12 @@ struct lora_ctx {
     std::vector<lora_module_shape> shapes;
     std::vector<void *> A, Bi;
     std::vector<int64_t> strideA, strideB;   // per-slot element strides
-    int32_t *rank_dev = nullptr;             // [n_modules][S]
-    float *scale_dev = nullptr;              // [S]
-    std::vector<int32_t> rank_host;          // mirror of rank_dev
+    std::vector<int32_t> rank_host;          // [n_modules][S]
     std::vector<float> scale_host;
     void *stage = nullptr;                   // B staging, R_pad * max d_out elements
     float *hpart = nullptr;
     int hbuf_rows = 0;
+    int max_splits = 16;                     // K-split cap of the shrink (tuning)
     PlanBuffers plan{};
     int max_tiles = 0;
     hipStream_t side = nullptr;
@@ -215,7 +217,7 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 {
     const int tiles = max_tiles_for(T, c->S);
     int want = ceil_div(1024, std::max(tiles, 1));
-    int cap = std::min(kMaxSplits, std::max(1, d_in / 256));
+    int cap = std::min(c->max_splits, std::max(1, d_in / 256));
     cap = std::min(cap, std::max(1, c->hbuf_rows / std::max(T, 1)));
     int sp = std::max(1, std::min(want, cap));
     int kc = round_up(ceil_div(d_in, sp), kShrinkKBlock);
@@ -224,6 +226,18 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 }
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
+
+SlotMeta slot_meta(const lora_ctx *c, int module)
+{
+    SlotMeta m;
+    std::memset(&m, 0, sizeof m);
+    const int32_t *r = c->rank_host.data() + (size_t)module * c->S;
+    for (int k = 0; k < c->S; ++k) {
+        m.rank[k] = (uint8_t)r[k];
+        m.scale[k] = c->scale_host[k];
+    }
+    return m;
+}
 
 int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
 {
@@ -256,8 +270,7 @@ int run_shrink(lora_ctx *c, const void *x, int module, hipStream_t s)
         a.x = x;
         a.A = c->A[module];
         a.slot_stride_A = c->strideA[module];
-        a.rank = c->rank_dev + (int64_t)module * c->S;
-        a.perm = c->plan.perm;
+        a.tile_tok = c->plan.tile_tok;
         a.tiles = c->plan.tiles;
         a.n_tiles = c->plan.n_tiles;
         a.hpart = c->hpart;
@@ -267,7 +280,8 @@ int run_shrink(lora_ctx *c, const void *x, int module, hipStream_t s)
         a.k_chunk = kchunk;
         a.splits = splits;
         a.grid_tiles = max_tiles_for(T, c->S);
-        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, s));
+        a.mixed = T > 1024;
+        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, slot_meta(c, module), s));
         c->last_splits = splits;
         c->last_kchunk = kchunk;
         c->stats.shrinks += 1;
@@ -288,9 +302,7 @@ int run_expand(lora_ctx *c, void *y, int module, hipStream_t s)
         a.y = y;
         a.Bi = c->Bi[module];
         a.slot_stride_B = c->strideB[module];
-        a.rank = c->rank_dev + (int64_t)module * c->S;
-        a.scale = c->scale_dev;
-        a.perm = c->plan.perm;
+        a.tile_tok = c->plan.tile_tok;
         a.tiles = c->plan.tiles;
         a.n_tiles = c->plan.n_tiles;
         a.hpart = c->hpart;
@@ -299,7 +311,7 @@ int run_expand(lora_ctx *c, void *y, int module, hipStream_t s)
         a.R_pad = c->R_pad;
         a.splits = c->last_splits;
         a.grid_tiles = max_tiles_for(T, c->S);
-        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, s));
+        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, slot_meta(c, module), s));
         c->stats.expands += 1;
     }
     return LORA_OK;
@@ -399,18 +411,25 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         max_out = std::max(max_out, sh.d_out);
     }
     c->hbuf_rows = std::max(max_tokens, 16384);
+    if (const char *env = std::getenv("LORA_MI355X_MAX_SPLITS")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v <= kMaxSplits)
+            c->max_splits = v;
+    }
     c->max_tiles = max_tiles_for(max_tokens, max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->rank_dev, sizeof(int32_t) * (size_t)n_modules * max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->scale_dev, sizeof(float) * (size_t)max_loras);
     if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
     if (e == hipSuccess) e = dalloc(c, &c->hpart, sizeof(float) * (size_t)c->hbuf_rows * c->R_pad);
     if (e == hipSuccess) e = dalloc(c, &c->plan.counts, sizeof(int32_t) * (size_t)max_loras);
     if (e == hipSuccess) e = dalloc(c, &c->plan.seg_start, sizeof(int32_t) * (size_t)max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->plan.perm, sizeof(int32_t) * (size_t)max_tokens);
     if (e == hipSuccess) e = dalloc(c, &c->plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
+    if (e == hipSuccess)
+        e = dalloc(c, &c->plan.tile_tok, sizeof(int32_t) * (size_t)c->max_tiles * kTileTokens);
     if (e == hipSuccess) e = dalloc(c, &c->plan.n_tiles, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->plan.n_active, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->plan.flags, sizeof(uint32_t));
+    if (e == hipSuccess)
+        e = dalloc(c, &c->plan.chunk_counts,
+                   sizeof(int32_t) * (size_t)ceil_div(max_tokens, 1024) * max_loras);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->load_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -472,7 +491,6 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
     int rc = fence_compute_streams(ctx);
     if (rc)
         return rc;
-    HIP_TRY(ctx, launch_slot_reset(ctx->rank_dev, ctx->n_modules, ctx->S, slot, ctx->side));
     int64_t bytes = 0;
     const bool bf16 = ctx->dtype == LORA_BF16;
     for (int m = 0; m < ctx->n_modules; ++m) {
@@ -486,8 +504,7 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
         HIP_TRY(ctx, hipMemcpyAsync(Aslot, A_t[m], abytes, hipMemcpyDefault, ctx->side));
         HIP_TRY(ctx, hipMemcpyAsync(ctx->stage, B[m], bbytes, hipMemcpyDefault, ctx->side));
         HIP_TRY(ctx, launch_slot_finalize(bf16, Aslot, sh.d_in, Bslot, ctx->stage, sh.d_out, r,
-                                          ctx->R_pad, ctx->rank_dev + (int64_t)m * ctx->S + slot,
-                                          ctx->scale_dev + slot, s, ctx->side));
+                                          ctx->R_pad, ctx->side));
         bytes += (int64_t)abytes + (int64_t)bbytes;
     }
     HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
@@ -507,13 +524,8 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot)
     ctx->last_error.clear();
     if (slot < 0 || slot >= ctx->S)
         return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "slot %d not in 0..%d", slot, ctx->S - 1);
-    DeviceGuard guard(ctx->device);
-    int rc = fence_compute_streams(ctx);
-    if (rc)
-        return rc;
-    HIP_TRY(ctx, launch_slot_reset(ctx->rank_dev, ctx->n_modules, ctx->S, slot, ctx->side));
-    HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
-    ctx->load_gen += 1;
+    // Launches capture the rank table by value, so clearing needs no device work:
+    // batches already enqueued keep the adapter, later ones skip the slot.
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
     ctx->stats.clears += 1;

@@ -106,6 +106,9 @@ SWEEP = [
     (synth.BF16, [(512, 256)], 3, 16, [16, 5, 9], 1, 0.0),
     (synth.BF16, [(128, 128)], 256, 8, [(k % 8) + 1 for k in range(256)], 5000, 0.2),
     (synth.BF16, [(384, 392)], 5, 48, [48, 40, 30, 20, 10], 3077, 0.1),
+    (synth.BF16, [(200, 328)], 3, 64, [64, 33, 5], 2500, 0.05),
+    (synth.BF16, [(4096, 1024)], 3, 32, [32, 16, 8], 1100, 0.0),
+    (synth.BF16, [(1024, 512)], 8, 128, [128, 120, 64, 17, 1, 96, 32, 8], 4000, 0.1),
     (synth.FP32, [(72, 40)], 6, 8, [8, 1, 2, 3, 5, 8], 130, 0.1),
     (synth.FP32, [(264, 136), (96, 200)], 4, 24, [24, 17, 1, 9], 700, 0.1),
 ]
