@@ -66,6 +66,7 @@ enum {
 /* Library limits. */
 #define LORA_MAX_SLOTS 256   /* max_loras */
 #define LORA_MAX_RANK 128    /* max_rank */
+#define LORA_MAX_GROUP 8     /* modules of one grouped shrink / expand / apply call */
 
 /* Sticky device-side flags, read with lora_get_device_flags. */
 #define LORA_FLAG_SLOT_INDEX_TOO_LARGE 0x1u  /* a token carried idx >= max_loras (skipped) */
@@ -169,6 +170,24 @@ int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream);
  */
 int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
                int32_t n_tokens, int32_t module, void *stream);
+
+/*
+ * Grouped forms: the same operations for n (1..LORA_MAX_GROUP) modules of one
+ * batch in one kernel launch per phase, e.g. the q, k and v projections of a
+ * layer.  modules[i] is a module index, x[i] / y[i] that module's
+ * [n_tokens][d_in] input and [n_tokens][d_out] output.  A module may appear more
+ * than once (with its own x and y); the y buffers must not overlap (identical
+ * pointers are rejected with LORA_ERR_INVALID_ARGUMENT).  lora_expand_group must
+ * follow lora_shrink_group with the same module list.  Results equal n
+ * single-module calls.
+ */
+int lora_shrink_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                      void *stream);
+int lora_expand_group(lora_ctx *ctx, int32_t n, const int32_t *modules, void *const *y,
+                      void *stream);
+int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                     void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
+                     void *stream);
 
 /* Synchronise the device, return the sticky LORA_FLAG_* bits and clear them. */
 int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags);

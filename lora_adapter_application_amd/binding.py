@@ -37,7 +37,10 @@ LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
 # Every symbol the header declares, for the export check.
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_clear",
            "lora_sync_loads", "lora_plan_prepare", "lora_shrink", "lora_expand", "lora_apply",
+           "lora_shrink_group", "lora_expand_group", "lora_apply_group",
            "lora_get_device_flags", "lora_get_stats", "lora_status_string", "lora_last_error")
+
+LORA_MAX_GROUP = 8
 
 
 class LoraError(RuntimeError):
@@ -80,6 +83,10 @@ def load_library(path: str = LIB_PATH):
         "lora_shrink": ([P, P, I32, P], ctypes.c_int),
         "lora_expand": ([P, P, I32, P], ctypes.c_int),
         "lora_apply": ([P, P, P, P, I32, I32, P], ctypes.c_int),
+        "lora_shrink_group": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P), P], ctypes.c_int),
+        "lora_expand_group": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P), P], ctypes.c_int),
+        "lora_apply_group": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(P),
+                              P, I32, P], ctypes.c_int),
         "lora_get_device_flags": ([P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
         "lora_get_stats": ([P, ctypes.POINTER(_Stats)], ctypes.c_int),
         "lora_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -215,6 +222,41 @@ def lora_apply(ctx, x, y, token_slot_idx, module: int, n_tokens: Optional[int] =
                                      int(module), _stream(stream)), ctx)
 
 
+def _group(modules, tensors, name):
+    n = len(modules)
+    if len(tensors) != n:
+        raise ValueError(f"{name}: one tensor per module")
+    for t in tensors:
+        if t is not None:
+            _require_cuda(t, name)
+    mods = (ctypes.c_int32 * max(n, 1))(*[int(m) for m in modules])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
+    return n, mods, ptrs
+
+
+def lora_shrink_group(ctx, modules: Sequence[int], x: Sequence, stream=None) -> None:
+    n, mods, xp = _group(modules, x, "x")
+    _check(load_library().lora_shrink_group(ctx, n, mods, xp, _stream(stream)), ctx)
+
+
+def lora_expand_group(ctx, modules: Sequence[int], y: Sequence, stream=None) -> None:
+    n, mods, yp = _group(modules, y, "y")
+    _check(load_library().lora_expand_group(ctx, n, mods, yp, _stream(stream)), ctx)
+
+
+def lora_apply_group(ctx, modules: Sequence[int], x: Sequence, y: Sequence, token_slot_idx,
+                     n_tokens: Optional[int] = None, stream=None) -> None:
+    import torch
+    if n_tokens is None:
+        n_tokens = token_slot_idx.numel() if token_slot_idx is not None else 0
+    if n_tokens:
+        _require_cuda(token_slot_idx, "token_slot_idx", torch.int32, n_tokens)
+    n, mods, xp = _group(modules, x, "x")
+    _, _, yp = _group(modules, y, "y")
+    _check(load_library().lora_apply_group(ctx, n, mods, xp, yp, _ptr(token_slot_idx),
+                                           int(n_tokens), _stream(stream)), ctx)
+
+
 def lora_get_device_flags(ctx) -> int:
     v = ctypes.c_uint32(0)
     _check(load_library().lora_get_device_flags(ctx, ctypes.byref(v)), ctx)
@@ -262,6 +304,15 @@ class Slots:
 
     def apply(self, x, y, idx, module, n_tokens=None, stream=None):
         lora_apply(self.ctx, x, y, idx, module, n_tokens, stream)
+
+    def shrink_group(self, modules, x, stream=None):
+        lora_shrink_group(self.ctx, modules, x, stream)
+
+    def expand_group(self, modules, y, stream=None):
+        lora_expand_group(self.ctx, modules, y, stream)
+
+    def apply_group(self, modules, x, y, idx, n_tokens=None, stream=None):
+        lora_apply_group(self.ctx, modules, x, y, idx, n_tokens, stream)
 
     def flags(self):
         return lora_get_device_flags(self.ctx)

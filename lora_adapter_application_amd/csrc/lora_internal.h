@@ -17,6 +17,12 @@ constexpr int kExpandCols = 256;
 constexpr int kShrinkKBlock = 128;
 // Upper bound of shrink K-splits (the expand sums at most this many partials).
 constexpr int kMaxSplits = 16;
+// Rank blocks of 16 a kernel instance is compiled for: the padded rank's block
+// count rounded up to 1, 2, 4 or 8.
+constexpr int nb_template(int R_pad) { return R_pad <= 16 ? 1 : R_pad <= 32 ? 2 : R_pad <= 64 ? 4 : 8; }
+// K-splits the expand can sum for a kernel instance of NB rank blocks (keeps
+// the partials of one thread at kMaxSplits float4 registers).
+constexpr int splits_cap(int NB) { return kMaxSplits / NB > 0 ? kMaxSplits / NB : 1; }
 // Largest padded rank (LORA_MAX_RANK rounded up to 16).
 #define LORA_MAX_RANK_PAD 128
 
@@ -38,50 +44,61 @@ struct PlanBuffers {
     int32_t *chunk_counts;  // [ceil(max_tokens/1024)][S], batches above 1024 tokens
 };
 
-// Per-launch slot metadata, passed by value: rank of each slot for the module
-// being applied (0 = empty slot or module not targeted) and the slot's scale.
+// Modules one grouped shrink / expand launch covers (blockIdx.z = member).
+constexpr int kMaxGroup = 8;
+
+// Slot metadata of one launch, passed by value: per slot its adapter's rank
+// (0 = empty) and scale, and per group member one bit per slot telling whether
+// that adapter targets the member's module.  Launches capture it when they are
+// enqueued, so a kernel sees exactly the slots loaded before it.
 struct SlotMeta {
     float scale[LORA_MAX_SLOTS];
     uint8_t rank[LORA_MAX_SLOTS];
+    uint32_t target[kMaxGroup][LORA_MAX_SLOTS / 32];
 };
 
 inline int max_tiles_for(int T, int S) { return (T + kTileTokens - 1) / kTileTokens + (S < T ? S : T); }
 
-
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
                        hipStream_t st);
 
-// bf16 (elem = uint16_t bit patterns) and fp32 (elem = float) entry points.
+// Element type: bf16 (uint16_t bit patterns) or fp32.
 struct ShrinkArgs {
-    const void *x;          // [T][d_in]
-    const void *A;          // module base: [S][R_pad][d_in]
-    int64_t slot_stride_A;  // elements
-    const int32_t *tile_tok;
+    int32_t n;                          // group members
+    const void *x[kMaxGroup];           // [T][d_in]
+    const void *A[kMaxGroup];           // module base: [S][R_pad][d_in]
+    int64_t slot_stride_A[kMaxGroup];   // elements
+    int32_t d_in[kMaxGroup];
+    int32_t k_chunk[kMaxGroup];
+    int32_t splits[kMaxGroup];
     const Tile *tiles;
+    const int32_t *tile_tok;
     const int32_t *n_tiles;
-    float *hpart;           // [splits][T][R_pad]
-    int64_t split_stride;   // elements
-    int32_t d_in;
+    float *hpart;                       // [member][split][T][R_pad]
+    int64_t member_stride;              // elements
+    int64_t split_stride;               // T * R_pad
     int32_t R_pad;
-    int32_t k_chunk;
-    int32_t splits;
     int32_t grid_tiles;
-    int32_t mixed;          // batch above 1024 tokens: long tiles take the segment path
+    int32_t grid_splits;                // max splits over the members
+    int32_t mixed;                      // batch above 1024 tokens: long tiles take the segment path
 };
 
 struct ExpandArgs {
-    void *y;                // [T][d_out]
-    const void *Bi;         // module base: [S][R_pad/8][d_out][8]
-    int64_t slot_stride_B;  // elements
-    const int32_t *tile_tok;
+    int32_t n;
+    void *y[kMaxGroup];                 // [T][d_out]
+    const void *Bi[kMaxGroup];          // module base: [S][R_pad/8][d_out][8]
+    int64_t slot_stride_B[kMaxGroup];
+    int32_t d_out[kMaxGroup];
+    int32_t splits[kMaxGroup];
     const Tile *tiles;
+    const int32_t *tile_tok;
     const int32_t *n_tiles;
     const float *hpart;
+    int64_t member_stride;
     int64_t split_stride;
-    int32_t d_out;
     int32_t R_pad;
-    int32_t splits;
     int32_t grid_tiles;
+    int32_t grid_cols;                  // max column chunks over the members
 };
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st);

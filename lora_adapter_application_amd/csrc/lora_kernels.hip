@@ -14,7 +14,9 @@
 // bf16 data runs on the matrix cores: v_mfma_f32_16x16x32_bf16 for shrink
 // (K = d_in) and v_mfma_f32_16x16x16_bf16 for expand (K = rank), with the fp32
 // intermediate split into a bf16 high and low part so the expand keeps ~16
-// bits of h.  fp32 data runs on plain VALU loops.
+// bits of h; results are rounded to bf16 by v_cvt_pk_bf16_f32 (round to
+// nearest even).  fp32 data runs on plain VALU loops.  One shrink or expand
+// launch covers a group of up to kMaxGroup modules (blockIdx.z).
 //
 // Operand layout of a 16x16xK MFMA on a 64-wide wave, as used below: lane l
 // supplies row (l & 15) of A and column (l & 15) of B, each with the K slice of
@@ -32,16 +34,6 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
 
 // ----------------------------------------------------------------------------
 // plan
@@ -280,18 +272,41 @@ hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffe
 // ----------------------------------------------------------------------------
 // shrink, bf16 on MFMA
 //
-// One workgroup (4 waves) = one tile (<= 64 tokens of one slot) x one K split.
-// A tile has nsub = ceil(len/16) subtiles of 16 tokens; waves split the work as
-// (subtile, K part) so short tiles still keep all 4 waves loading.  Per step a
-// lane loads 64 contiguous bytes of its token's x row and of its rank's A^T row
-// and feeds them to 4 MFMAs; both operands use the same K order, so the sum is
-// the plain dot product over that K block.  The next K block is loaded before
-// the MFMAs of the current one (register double buffering) when the rank fits.
-// Output: h as [rank][token] blocks, lane l holding ranks 4g..4g+3 of token
-// (l & 15) -> one 16-byte store.
+// One workgroup (4 waves) = one tile (<= 64 tokens of one slot) x one K split x
+// one group member (blockIdx.z).  Output: the member's h partial of the split
+// as [rank][token] blocks, lane l holding ranks 4g..4g+3 of token (l & 15),
+// stored as one 16-byte write.
+
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two fp32 values to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
+__device__ __forceinline__ int member_rank(const SlotMeta &meta, int m, int slot)
+{
+    return ((meta.target[m][slot >> 5] >> (slot & 31)) & 1u) ? (int)meta.rank[slot] : 0;
+}
+
+// One member's view of a shrink launch.
+struct ShrinkView {
+    const uint16_t *x;
+    const uint16_t *A;      // slot's A^T block
+    int64_t d_in;
+    int k0, k1;             // K range of this split
+    float *h;               // this member's split partial: [T][R_pad]
+    int R_pad;
+};
+
+// Gather path (BGMV): waves split the tile's subtiles and the K range.  Per
+// step a lane loads 64 contiguous bytes of its token's x row and of its rank's
+// A^T row and feeds them to 4 MFMAs; both operands use the same K order, so the
+// sum is the plain dot product over that K block.
 template <int NB>
 struct KBlock {
     uint4 x[4];
@@ -304,11 +319,6 @@ __device__ __forceinline__ void load_kblock(KBlock<NB> &blk, const uint16_t *xro
                                             int nb, bool tok_ok)
 {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ke = kk + q * 8;
-        blk.x[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -316,6 +326,11 @@ __device__ __forceinline__ void load_kblock(KBlock<NB> &blk, const uint16_t *xro
             blk.a[b][q] = (b < nb && ke < k1) ? ld16(arow0 + b * 16 * d_in + ke)
                                                : make_uint4(0, 0, 0, 0);
         }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ke = kk + q * 8;
+        blk.x[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -334,6 +349,73 @@ __device__ __forceinline__ void mfma_kblock(f32x4_t (&acc)[NB], const KBlock<NB>
     }
 }
 
+template <int NB, bool DOUBLE_BUFFER>
+__device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &tile,
+                                            const int32_t *tok_row, int nb, unsigned char *smem)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = lane & 15, g = lane >> 4;
+    const int nsub = (tile.len + 15) >> 4;
+    const int nsub_pad = nsub == 3 ? 4 : nsub;
+    const int kparts = 4 / nsub_pad;
+    const int sub = wave % nsub_pad, kp = wave / nsub_pad;
+    const bool wave_on = sub < nsub;
+    const int t_in = sub * 16 + row;
+    const bool tok_ok = wave_on && t_in < tile.len;
+    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok_row[t_in] : 0) * v.d_in;
+    const uint16_t *arow0 = v.A + (int64_t)row * v.d_in;
+
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (wave_on) {
+        const int kstep = kparts * kShrinkKBlock;
+        int kb = v.k0 + kp * kShrinkKBlock;
+        if (DOUBLE_BUFFER) {
+            KBlock<NB> cur, nxt;
+            if (kb < v.k1)
+                load_kblock<NB>(cur, xrow, arow0, v.d_in, kb + g * 32, v.k1, nb, tok_ok);
+            for (; kb < v.k1; kb += kstep) {
+                const int kn = kb + kstep;
+                if (kn < v.k1)
+                    load_kblock<NB>(nxt, xrow, arow0, v.d_in, kn + g * 32, v.k1, nb, tok_ok);
+                mfma_kblock<NB>(acc, cur, nb);
+                cur = nxt;
+            }
+        } else {
+            for (; kb < v.k1; kb += kstep) {
+                KBlock<NB> cur;
+                load_kblock<NB>(cur, xrow, arow0, v.d_in, kb + g * 32, v.k1, nb, tok_ok);
+                mfma_kblock<NB>(acc, cur, nb);
+            }
+        }
+    }
+    f32x4_t (*red)[NB][64] = (f32x4_t (*)[NB][64])smem;
+    if (kparts > 1) {
+        if (wave_on && kp > 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                red[wave][b][lane] = acc[b];
+        }
+        __syncthreads();
+        if (wave_on && kp == 0) {
+            for (int k = 1; k < kparts; ++k) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] += red[sub + k * nsub_pad][b][lane];
+            }
+        }
+    }
+    if (kp == 0 && tok_ok) {
+        float *hrow = v.h + (int64_t)(tile.start + t_in) * v.R_pad;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (b < nb)
+                *(f32x4_t *)(hrow + b * 16 + g * 4) = acc[b];
+    }
+}
+
 // Segment path (SGMV) for tiles of 33..64 tokens: wave w owns subtile w over
 // the whole K range.  Each K block of A^T (nb*16 ranks x 128) is loaded once per
 // workgroup into LDS (double buffered) and shared by the 4 waves; x is
@@ -341,16 +423,15 @@ __device__ __forceinline__ void mfma_kblock(f32x4_t (&acc)[NB], const KBlock<NB>
 constexpr int kLdsRow = kShrinkKBlock + 8;   // bf16 elements per staged A row (padded)
 
 template <int NB>
-__device__ __forceinline__ void shrink_sgmv(const ShrinkArgs &a, const Tile &tile, int nb, int k0,
-                                            int k1, int split, uint16_t *lds)
+__device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &tile,
+                                            const int32_t *tok_row, int nb, uint16_t *lds)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row = lane & 15, g = lane >> 4;
     const int t_in = wave * 16 + row;
     const bool tok_ok = t_in < tile.len;
-    const int p = tile.start + t_in;
-    const uint16_t *xrow = (const uint16_t *)a.x + (int64_t)(tok_ok ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t_in] : 0) * a.d_in;
-    const uint16_t *Aslot = (const uint16_t *)a.A + (int64_t)tile.slot * a.slot_stride_A;
+    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok_row[t_in] : 0) * v.d_in;
+    const int k0 = v.k0, k1 = v.k1;
     const int nkb = (k1 - k0 + kShrinkKBlock - 1) / kShrinkKBlock;
     constexpr int buf_elems = NB * 16 * kLdsRow;
 
@@ -360,7 +441,7 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkArgs &a, const Tile &til
         for (int i = 0; i < NB; ++i) {
             const int c = tid + 256 * i;
             const int r = c >> 4, col = (c & 15) * 8;
-            ra[i] = (i < nb && kb + col < k1) ? ld16(Aslot + (int64_t)r * a.d_in + kb + col)
+            ra[i] = (i < nb && kb + col < k1) ? ld16(v.A + (int64_t)r * v.d_in + kb + col)
                                               : make_uint4(0, 0, 0, 0);
         }
     };
@@ -426,7 +507,7 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkArgs &a, const Tile &til
         }
     }
     if (tok_ok) {
-        float *hrow = a.hpart + (int64_t)split * a.split_stride + (int64_t)p * a.R_pad;
+        float *hrow = v.h + (int64_t)(tile.start + t_in) * v.R_pad;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if (b < nb)
@@ -434,133 +515,77 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkArgs &a, const Tile &til
     }
 }
 
-// MIXED: batches above 1024 tokens (tiles of any length; long ones take the
-// segment path, the rest the gather path single-buffered).  Otherwise every
-// tile takes the gather path, double-buffered when the rank allows.
+// MIXED: batches above 1024 tokens; tiles of 33..64 tokens take the segment
+// path, shorter ones the gather path single-buffered.  Otherwise every tile
+// takes the gather path, double-buffered when the rank allows.
 template <int NB, bool MIXED>
 __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
 {
     const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
-    if ((int)blockIdx.x >= n_tiles)
+    const int m = blockIdx.z;
+    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y >= a.splits[m])
         return;
-    const int rank = meta.rank[tile.slot];
+    const int rank = member_rank(meta, m, tile.slot);
     if (rank == 0)
         return;
     const int nb = (rank + 15) >> 4;
-    const int split = blockIdx.y;
-    const int k0 = split * a.k_chunk;
-    const int k1 = min(a.d_in, k0 + a.k_chunk);
-    const int nsub = (tile.len + 15) >> 4;
+    ShrinkView v;
+    v.d_in = a.d_in[m];
+    v.x = (const uint16_t *)a.x[m];
+    v.A = (const uint16_t *)a.A[m] + (int64_t)tile.slot * a.slot_stride_A[m];
+    v.k0 = blockIdx.y * a.k_chunk[m];
+    v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
+    v.h = a.hpart + m * a.member_stride + (int64_t)blockIdx.y * a.split_stride;
+    v.R_pad = a.R_pad;
+    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
 
     constexpr int kRedBytes = 4 * NB * 64 * 16;
     constexpr int kSgmvBytes = MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0;
     constexpr int kSmemBytes = kRedBytes > kSgmvBytes ? kRedBytes : kSgmvBytes;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
-    if (MIXED && nsub >= 3) {
-        shrink_sgmv<NB>(a, tile, nb, k0, k1, split, (uint16_t *)smem);
-        return;
-    }
-
-    // Gather path (BGMV): waves split the tile's subtiles and the K range.
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = lane & 15, g = lane >> 4;
-    const int nsub_pad = nsub == 3 ? 4 : nsub;
-    const int kparts = 4 / nsub_pad;
-    const int sub = wave % nsub_pad, kp = wave / nsub_pad;
-    const bool wave_on = sub < nsub;
-    const int tok_in_tile = sub * 16 + row;
-    const bool tok_ok = wave_on && tok_in_tile < tile.len;
-    const int p = tile.start + tok_in_tile;
-
-    const uint16_t *xrow = (const uint16_t *)a.x + (int64_t)(tok_ok ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + tok_in_tile] : 0) * a.d_in;
-    const uint16_t *arow0 = (const uint16_t *)a.A + (int64_t)tile.slot * a.slot_stride_A +
-                            (int64_t)row * a.d_in;
-
-    f32x4_t acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if (wave_on) {
-        const int kstep = kparts * kShrinkKBlock;
-        int kb = k0 + kp * kShrinkKBlock;
-        if (!MIXED && NB <= 4) {
-            KBlock<NB> cur, nxt;
-            if (kb < k1)
-                load_kblock<NB>(cur, xrow, arow0, a.d_in, kb + g * 32, k1, nb, tok_ok);
-            for (; kb < k1; kb += kstep) {
-                const int kn = kb + kstep;
-                if (kn < k1)
-                    load_kblock<NB>(nxt, xrow, arow0, a.d_in, kn + g * 32, k1, nb, tok_ok);
-                mfma_kblock<NB>(acc, cur, nb);
-                cur = nxt;
-            }
-        } else {
-            for (; kb < k1; kb += kstep) {
-                KBlock<NB> cur;
-                load_kblock<NB>(cur, xrow, arow0, a.d_in, kb + g * 32, k1, nb, tok_ok);
-                mfma_kblock<NB>(acc, cur, nb);
-            }
-        }
-    }
-
-    f32x4_t (*red)[NB][64] = (f32x4_t (*)[NB][64])smem;
-    if (kparts > 1) {
-        if (wave_on && kp > 0) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                red[wave][b][lane] = acc[b];
-        }
-        __syncthreads();
-        if (wave_on && kp == 0) {
-            for (int k = 1; k < kparts; ++k) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] += red[sub + k * nsub_pad][b][lane];
-            }
-        }
-    }
-    if (kp == 0 && tok_ok) {
-        float *hrow = a.hpart + (int64_t)split * a.split_stride + (int64_t)p * a.R_pad;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (b < nb)
-                *(f32x4_t *)(hrow + b * 16 + g * 4) = acc[b];
-    }
+    if (MIXED && tile.len > 32)
+        shrink_sgmv<NB>(v, tile, tok_row, nb, (uint16_t *)smem);
+    else
+        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tok_row, nb, smem);
 }
 
 // ----------------------------------------------------------------------------
 // expand, bf16 on MFMA
 //
-// One workgroup = one tile (<= 64 tokens of one slot) x 256 columns of y; wave
-// w owns the 64 columns 64w..64w+63 for every subtile of the tile.  The
-// product is formed transposed, out[n][t] = sum_j B[j][n] h[t][j].  B is
-// stored in groups of 8 ranks, Bi[j/8][n][j%8], so the rank slice an MFMA lane
-// needs is contiguous; rows of the 16x16 output blocks are mapped to columns
-// so that lane group g of a wave owns 16 adjacent columns of one token, and y
-// is read and written 32 bytes per lane.  Every global load of the wave (token
-// ids, B, y) is issued before any arithmetic; the K-split partials of h are summed
-// once per workgroup into LDS, then split into a bf16 high and low half.
+// One workgroup = one tile (<= 64 tokens of one slot) x 256 columns of y x one
+// group member; wave w owns the 64 columns 64w..64w+63 for every subtile of the
+// tile.  The product is formed transposed, out[n][t] = sum_j B[j][n] h[t][j].
+// B is stored in groups of 8 ranks, Bi[j/8][n][j%8], so the rank slice an MFMA
+// lane needs is contiguous; rows of the 16x16 output blocks are mapped to
+// columns so that lane group g of a wave owns 16 adjacent columns of one token,
+// and y is read and written 32 bytes per lane.  Every global load of the wave
+// (token ids, B, y, h partials) is issued before any arithmetic.  The K-split
+// partials of h are summed once per workgroup and split into a bf16 high part
+// and a bf16 low part (h - high) in LDS; two MFMAs per step keep ~16 bits of h.
 
 template <int NB>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
     const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    if ((int)blockIdx.x >= n_tiles)
+    const int m = blockIdx.z;
+    const int d_out = a.d_out[m];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int cb = blockIdx.y * kExpandCols + wave * 64;
+    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= d_out)
         return;
-    const int rank = meta.rank[tile.slot];
+    const int rank = member_rank(meta, m, tile.slot);
     if (rank == 0)
         return;
     const int nb = (rank + 15) >> 4;
     const float s = meta.scale[tile.slot];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row = lane & 15, g = lane >> 4;
-    const int cb = blockIdx.y * kExpandCols + wave * 64;
-    const bool cols_ok = cb < a.d_out;
+    const bool cols_ok = cb < d_out;
     const int nsub = (tile.len + 15) >> 4;
+    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
+    uint16_t *ybase = (uint16_t *)a.y[m];
 
     // tokens of this lane in each subtile
     int tok[4];
@@ -569,10 +594,45 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
     for (int st = 0; st < 4; ++st) {
         const int t = st * 16 + row;
         tok_ok[st] = cols_ok && t < tile.len;
-        tok[st] = tok_ok[st] ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t] : 0;
+        tok[st] = tok_ok[st] ? tok_row[t] : 0;
+    }
+    // h partials of the tile: thread tid owns quads e = tid + 256 i (i < NB) of
+    // the len x nb*16 block
+    const int quads = nb * 4;
+    const int n_el = tile.len * quads;
+    const int splits = a.splits[m];
+    const float *hbase = a.hpart + m * a.member_stride;
+    f32x4_t hsum[NB];
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            const int t = e / quads, q = e - t * quads;
+            hsum[i] = e < n_el ? *(const f32x4_t *)(hbase + (int64_t)(tile.start + t) * a.R_pad + q * 4)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    } else {
+        // at most splits_cap(NB) partials per quad (the host caps the K-split so)
+        constexpr int MS = splits_cap(NB);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            const int t = e / quads, q = e - t * quads;
+            f32x4_t pv[MS];
+            const float *hp = hbase + (int64_t)(tile.start + t) * a.R_pad + q * 4;
+#pragma unroll
+            for (int u = 0; u < MS; ++u)
+                pv[u] = (e < n_el && u < splits) ? *(const f32x4_t *)(hp + (int64_t)u * a.split_stride)
+                                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            f32x4_t sum = pv[0];
+#pragma unroll
+            for (int u = 1; u < MS; ++u)
+                sum += pv[u];
+            hsum[i] = sum;
+        }
     }
     // B operands: lane row -> column cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 4g..+3
-    const uint16_t *Bslot = (const uint16_t *)a.Bi + (int64_t)tile.slot * a.slot_stride_B;
+    const uint16_t *Bslot = (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m];
     uint2 bop[NB][4];
 #pragma unroll
     for (int kst = 0; kst < NB; ++kst) {
@@ -580,8 +640,8 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
-            bop[kst][b] = (kst < nb && cols_ok && n < a.d_out)
-                              ? *(const uint2 *)(Bslot + ((int64_t)G * a.d_out + n) * 8 + (g & 1) * 4)
+            bop[kst][b] = (kst < nb && cols_ok && n < d_out)
+                              ? *(const uint2 *)(Bslot + ((int64_t)G * d_out + n) * 8 + (g & 1) * 4)
                               : make_uint2(0, 0);
         }
     }
@@ -592,48 +652,28 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 #pragma unroll
         for (int piece = 0; piece < 2; ++piece) {
             const int col = cb + g * 16 + piece * 8;
-            yv[st][piece] = (tok_ok[st] && col < a.d_out)
-                                ? *(const uint4 *)((const uint16_t *)a.y + (int64_t)tok[st] * a.d_out + col)
+            yv[st][piece] = (tok_ok[st] && col < d_out)
+                                ? *(const uint4 *)(ybase + (int64_t)tok[st] * d_out + col)
                                 : make_uint4(0, 0, 0, 0);
         }
     }
-
-    // h of the tile, summed over K splits, into LDS (fp32).  Thread tid owns
-    // the float4 quads e = tid + 256 i (i < NB) of the tile's len x nb*16 block;
-    // all partial loads are issued before any sum.
-    __shared__ float hs[kTileTokens][NB * 16 + 4];
-    const int quads = nb * 4;
-    const int n_el = tile.len * quads;
-    if (a.splits == 1) {
-        f32x4_t hv[NB];
+    // h -> bf16 high and low halves in LDS
+    constexpr int HS = NB * 16 + 8;             // row stride (bf16 elements, 16-byte multiple)
+    __shared__ __attribute__((aligned(16))) uint16_t hs_hi[kTileTokens][HS];
+    __shared__ __attribute__((aligned(16))) uint16_t hs_lo[kTileTokens][HS];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int e = tid + 256 * i;
+    for (int i = 0; i < NB; ++i) {
+        const int e = tid + 256 * i;
+        if (e < n_el) {
             const int t = e / quads, q = e - t * quads;
-            hv[i] = e < n_el ? *(const f32x4_t *)(a.hpart + (int64_t)(tile.start + t) * a.R_pad + q * 4)
-                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int e = tid + 256 * i;
-            const int t = e / quads, q = e - t * quads;
-            if (e < n_el)
-                *(f32x4_t *)&hs[t][q * 4] = hv[i];
-        }
-    } else {
-        for (int e = tid; e < n_el; e += 256) {
-            const int t = e / quads, q = e - t * quads;
-            const float *hp = a.hpart + (int64_t)(tile.start + t) * a.R_pad + q * 4;
-            f32x4_t v[kMaxSplits];
-#pragma unroll
-            for (int u = 0; u < kMaxSplits; ++u)
-                v[u] = u < a.splits ? *(const f32x4_t *)(hp + (int64_t)u * a.split_stride)
-                                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            f32x4_t sum = v[0];
-#pragma unroll
-            for (int u = 1; u < kMaxSplits; ++u)
-                sum += v[u];
-            *(f32x4_t *)&hs[t][q * 4] = sum;
+            const f32x4_t h = hsum[i];
+            const uint32_t hi01 = pack_bf16x2(h[0], h[1]), hi23 = pack_bf16x2(h[2], h[3]);
+            const uint32_t lo01 = pack_bf16x2(h[0] - bf16_bits_to_f32(hi01 & 0xffffu),
+                                              h[1] - bf16_bits_to_f32(hi01 >> 16));
+            const uint32_t lo23 = pack_bf16x2(h[2] - bf16_bits_to_f32(hi23 & 0xffffu),
+                                              h[3] - bf16_bits_to_f32(hi23 >> 16));
+            *(uint2 *)&hs_hi[t][q * 4] = make_uint2(hi01, hi23);
+            *(uint2 *)&hs_lo[t][q * 4] = make_uint2(lo01, lo23);
         }
     }
     __syncthreads();
@@ -652,14 +692,8 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
         for (int kst = 0; kst < NB; ++kst) {
             if (kst < nb) {
                 // rows beyond the tile read stale LDS; their results are never stored
-                const f32x4_t h = *(const f32x4_t *)&hs[st * 16 + row][kst * 16 + g * 4];
-                s16x4_t hhi, hlo;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t hi = f32_to_bf16_bits(h[e]);
-                    hhi[e] = (short)hi;
-                    hlo[e] = (short)f32_to_bf16_bits(h[e] - bf16_bits_to_f32(hi));
-                }
+                const s16x4_t hhi = __builtin_bit_cast(s16x4_t, *(const uint2 *)&hs_hi[st * 16 + row][kst * 16 + g * 4]);
+                const s16x4_t hlo = __builtin_bit_cast(s16x4_t, *(const uint2 *)&hs_lo[st * 16 + row][kst * 16 + g * 4]);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const s16x4_t bo = __builtin_bit_cast(s16x4_t, bop[kst][b]);
@@ -669,11 +703,11 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
             }
         }
         if (tok_ok[st]) {
-            uint16_t *yrow = (uint16_t *)a.y + (int64_t)tok[st] * a.d_out;
+            uint16_t *yrow = ybase + (int64_t)tok[st] * d_out;
 #pragma unroll
             for (int piece = 0; piece < 2; ++piece) {
                 const int col = cb + g * 16 + piece * 8;
-                if (col < a.d_out) {
+                if (col < d_out) {
                     const uint4 yw = yv[st][piece];
                     uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
 #pragma unroll
@@ -681,7 +715,7 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
                         const int e0 = piece * 8 + h2 * 2, e1 = e0 + 1;
                         const float v0 = bf16_bits_to_f32(w[h2] & 0xffffu) + s * acc[e0 >> 2][e0 & 3];
                         const float v1 = bf16_bits_to_f32(w[h2] >> 16) + s * acc[e1 >> 2][e1 & 3];
-                        w[h2] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+                        w[h2] = pack_bf16x2(v0, v1);
                     }
                     *(uint4 *)(yrow + col) = make_uint4(w[0], w[1], w[2], w[3]);
                 }
@@ -691,28 +725,30 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 }
 
 // ----------------------------------------------------------------------------
-// fp32 on VALU
+// fp32 on VALU (same grids and h layout as the bf16 kernels)
 
 __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta meta)
 {
     const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    if ((int)blockIdx.x >= n_tiles)
+    const int m = blockIdx.z;
+    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y >= a.splits[m])
         return;
-    const int rank = meta.rank[tile.slot];
+    const int rank = member_rank(meta, m, tile.slot);
     if (rank == 0)
         return;
-    const int split = blockIdx.y;
-    const int k0 = split * a.k_chunk;
-    const int k1 = min(a.d_in, k0 + a.k_chunk);
+    const int d_in = a.d_in[m];
+    const int k0 = blockIdx.y * a.k_chunk[m];
+    const int k1 = min(d_in, k0 + a.k_chunk[m]);
     const int tid = threadIdx.x;
-    const float *x = (const float *)a.x;
-    const float *Aslot = (const float *)a.A + (int64_t)tile.slot * a.slot_stride_A;
+    const float *x = (const float *)a.x[m];
+    const float *Aslot = (const float *)a.A[m] + (int64_t)tile.slot * a.slot_stride_A[m];
+    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
     __shared__ float xs[kTileTokens][33];
     __shared__ float as[LORA_MAX_RANK_PAD][33];
     __shared__ int toks[kTileTokens];
     if (tid < kTileTokens)
-        toks[tid] = tid < tile.len ? a.tile_tok[(int64_t)blockIdx.x * kTileTokens + tid] : 0;
+        toks[tid] = tid < tile.len ? tok_row[tid] : 0;
     const int npairs = tile.len * rank;   // <= 64 * 128 = 32 per thread
     float acc[32];
 #pragma unroll
@@ -722,11 +758,11 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
     for (int kc = k0; kc < k1; kc += 32) {
         for (int e = tid; e < kTileTokens * 32; e += 256) {
             const int t = e >> 5, kk = e & 31;
-            xs[t][kk] = (t < tile.len && kc + kk < k1) ? x[(int64_t)toks[t] * a.d_in + kc + kk] : 0.f;
+            xs[t][kk] = (t < tile.len && kc + kk < k1) ? x[(int64_t)toks[t] * d_in + kc + kk] : 0.f;
         }
         for (int e = tid; e < rank * 32; e += 256) {
             const int j = e >> 5, kk = e & 31;
-            as[j][kk] = kc + kk < k1 ? Aslot[(int64_t)j * a.d_in + kc + kk] : 0.f;
+            as[j][kk] = kc + kk < k1 ? Aslot[(int64_t)j * d_in + kc + kk] : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -742,7 +778,7 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
         }
         __syncthreads();
     }
-    float *hp = a.hpart + (int64_t)split * a.split_stride;
+    float *hp = a.hpart + m * a.member_stride + (int64_t)blockIdx.y * a.split_stride;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
         const int e = tid + q * 256;
@@ -757,43 +793,47 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta 
 {
     const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];
-    if ((int)blockIdx.x >= n_tiles)
+    const int m = blockIdx.z;
+    const int d_out = a.d_out[m];
+    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= d_out)
         return;
-    const int rank = meta.rank[tile.slot];
+    const int rank = member_rank(meta, m, tile.slot);
     if (rank == 0)
         return;
     const float s = meta.scale[tile.slot];
     const int tid = threadIdx.x;
+    const float *hbase = a.hpart + m * a.member_stride;
     __shared__ float hs[kTileTokens][LORA_MAX_RANK_PAD + 1];
     for (int e = tid; e < tile.len * rank; e += 256) {
         const int t = e / rank, j = e % rank;
-        const float *hp = a.hpart + (int64_t)(tile.start + t) * a.R_pad + j;
+        const float *hp = hbase + (int64_t)(tile.start + t) * a.R_pad + j;
         float v = 0.f;
-        for (int sp = 0; sp < a.splits; ++sp)
+        for (int sp = 0; sp < a.splits[m]; ++sp)
             v += hp[(int64_t)sp * a.split_stride];
         hs[t][j] = v;
     }
     __syncthreads();
     const int n = blockIdx.y * kExpandCols + tid;
-    if (n >= a.d_out)
+    if (n >= d_out)
         return;
-    const float *Bslot = (const float *)a.Bi + (int64_t)tile.slot * a.slot_stride_B;
+    const float *Bslot = (const float *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m];
+    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
     float acc[kTileTokens];
 #pragma unroll
     for (int t = 0; t < kTileTokens; ++t)
         acc[t] = 0.f;
     for (int j = 0; j < rank; ++j) {
-        const float bj = Bslot[((int64_t)(j >> 3) * a.d_out + n) * 8 + (j & 7)];
+        const float bj = Bslot[((int64_t)(j >> 3) * d_out + n) * 8 + (j & 7)];
 #pragma unroll
         for (int t = 0; t < kTileTokens; ++t)
             if (t < tile.len)
                 acc[t] += hs[t][j] * bj;
     }
-    float *y = (float *)a.y;
+    float *y = (float *)a.y[m];
 #pragma unroll
     for (int t = 0; t < kTileTokens; ++t) {
         if (t < tile.len) {
-            const int64_t o = (int64_t)a.tile_tok[(int64_t)blockIdx.x * kTileTokens + t] * a.d_out + n;
+            const int64_t o = (int64_t)tok_row[t] * d_out + n;
             y[o] = y[o] + s * acc[t];
         }
     }
@@ -818,7 +858,7 @@ static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st)
 {
-    const dim3 grid(a.grid_tiles, a.splits), block(256);
+    const dim3 grid(a.grid_tiles, a.grid_splits, a.n), block(256);
     if (!bf16)
         hipLaunchKernelGGL(shrink_f32_kernel, grid, block, 0, st, a, m);
     else if (a.mixed)
@@ -830,7 +870,7 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
 
 hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st)
 {
-    const dim3 grid(a.grid_tiles, (a.d_out + kExpandCols - 1) / kExpandCols), block(256);
+    const dim3 grid(a.grid_tiles, a.grid_cols, a.n), block(256);
     if (!bf16) {
         hipLaunchKernelGGL(expand_f32_kernel, grid, block, 0, st, a, m);
     } else {

@@ -75,7 +75,8 @@ struct lora_ctx {
     std::vector<lora_module_shape> shapes;
     std::vector<void *> A, Bi;
     std::vector<int64_t> strideA, strideB;   // per-slot element strides
-    std::vector<int32_t> rank_host;          // [n_modules][S]
+    std::vector<int32_t> rank_host;          // [n_modules][S]: r if the slot's adapter targets m
+    std::vector<int32_t> slot_rank;          // [S]: rank of the adapter in the slot (0 = empty)
     std::vector<float> scale_host;
     void *stage = nullptr;                   // B staging, R_pad * max d_out elements
     float *hpart = nullptr;
@@ -91,9 +92,10 @@ struct lora_ctx {
     bool plan_valid = false, plan_prepared = false;
     const int32_t *plan_idx = nullptr;
     int32_t plan_T = 0;
-    // last shrink, consumed by expand
-    int last_shrink_module = -1;
-    int last_splits = 1, last_kchunk = 0;
+    // last shrink group, consumed by expand
+    int last_n = 0;
+    int last_modules[kMaxGroup] = {};
+    int last_splits[kMaxGroup] = {};
     lora_stats stats{};
     std::string last_error;
     std::vector<void *> allocations;
@@ -218,6 +220,7 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
     const int tiles = max_tiles_for(T, c->S);
     int want = ceil_div(1024, std::max(tiles, 1));
     int cap = std::min(c->max_splits, std::max(1, d_in / 256));
+    cap = std::min(cap, splits_cap(nb_template(c->R_pad)));
     cap = std::min(cap, std::max(1, c->hbuf_rows / std::max(T, 1)));
     int sp = std::max(1, std::min(want, cap));
     int kc = round_up(ceil_div(d_in, sp), kShrinkKBlock);
@@ -227,14 +230,19 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
-SlotMeta slot_meta(const lora_ctx *c, int module)
+SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
 {
     SlotMeta m;
     std::memset(&m, 0, sizeof m);
-    const int32_t *r = c->rank_host.data() + (size_t)module * c->S;
     for (int k = 0; k < c->S; ++k) {
-        m.rank[k] = (uint8_t)r[k];
         m.scale[k] = c->scale_host[k];
+        m.rank[k] = (uint8_t)c->slot_rank[k];
+    }
+    for (int i = 0; i < n; ++i) {
+        const int32_t *r = c->rank_host.data() + (size_t)modules[i] * c->S;
+        for (int k = 0; k < c->S; ++k)
+            if (r[k] > 0)
+                m.target[i][k >> 5] |= 1u << (k & 31);
     }
     return m;
 }
@@ -252,67 +260,111 @@ int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
     c->plan_valid = true;
     c->plan_idx = idx;
     c->plan_T = T;
-    c->last_shrink_module = -1;
+    c->last_n = 0;
     return LORA_OK;
 }
 
-int run_shrink(lora_ctx *c, const void *x, int module, hipStream_t s)
+int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x, hipStream_t s)
 {
     const int T = c->plan_T;
     if (T > 0) {
         int rc = before_launch(c, s);
         if (rc)
             return rc;
-        const lora_module_shape sh = c->shapes[module];
-        int splits = 1, kchunk = 0;
-        choose_splits(c, T, sh.d_in, &splits, &kchunk);
         ShrinkArgs a;
-        a.x = x;
-        a.A = c->A[module];
-        a.slot_stride_A = c->strideA[module];
-        a.tile_tok = c->plan.tile_tok;
+        std::memset(&a, 0, sizeof a);
+        a.n = n;
+        a.grid_splits = 1;
+        for (int i = 0; i < n; ++i) {
+            const int mod = modules[i];
+            const lora_module_shape sh = c->shapes[mod];
+            int splits = 1, kchunk = 0;
+            choose_splits(c, T, sh.d_in, &splits, &kchunk);
+            a.x[i] = x[i];
+            a.A[i] = c->A[mod];
+            a.slot_stride_A[i] = c->strideA[mod];
+            a.d_in[i] = sh.d_in;
+            a.k_chunk[i] = kchunk;
+            a.splits[i] = splits;
+            a.grid_splits = std::max(a.grid_splits, splits);
+            c->last_splits[i] = splits;
+        }
         a.tiles = c->plan.tiles;
+        a.tile_tok = c->plan.tile_tok;
         a.n_tiles = c->plan.n_tiles;
         a.hpart = c->hpart;
+        a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
         a.split_stride = (int64_t)T * c->R_pad;
-        a.d_in = sh.d_in;
         a.R_pad = c->R_pad;
-        a.k_chunk = kchunk;
-        a.splits = splits;
         a.grid_tiles = max_tiles_for(T, c->S);
         a.mixed = T > 1024;
-        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, slot_meta(c, module), s));
-        c->last_splits = splits;
-        c->last_kchunk = kchunk;
-        c->stats.shrinks += 1;
+        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s));
+        c->stats.shrinks += n;
     }
-    c->last_shrink_module = module;
+    c->last_n = n;
+    for (int i = 0; i < n; ++i)
+        c->last_modules[i] = modules[i];
     return LORA_OK;
 }
 
-int run_expand(lora_ctx *c, void *y, int module, hipStream_t s)
+int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipStream_t s)
 {
     const int T = c->plan_T;
     if (T > 0) {
         int rc = before_launch(c, s);
         if (rc)
             return rc;
-        const lora_module_shape sh = c->shapes[module];
         ExpandArgs a;
-        a.y = y;
-        a.Bi = c->Bi[module];
-        a.slot_stride_B = c->strideB[module];
-        a.tile_tok = c->plan.tile_tok;
+        std::memset(&a, 0, sizeof a);
+        a.n = n;
+        a.grid_cols = 1;
+        for (int i = 0; i < n; ++i) {
+            const int mod = modules[i];
+            const lora_module_shape sh = c->shapes[mod];
+            a.y[i] = y[i];
+            a.Bi[i] = c->Bi[mod];
+            a.slot_stride_B[i] = c->strideB[mod];
+            a.d_out[i] = sh.d_out;
+            a.splits[i] = c->last_splits[i];
+            a.grid_cols = std::max(a.grid_cols, ceil_div(sh.d_out, kExpandCols));
+        }
         a.tiles = c->plan.tiles;
+        a.tile_tok = c->plan.tile_tok;
         a.n_tiles = c->plan.n_tiles;
         a.hpart = c->hpart;
+        a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
         a.split_stride = (int64_t)T * c->R_pad;
-        a.d_out = sh.d_out;
         a.R_pad = c->R_pad;
-        a.splits = c->last_splits;
         a.grid_tiles = max_tiles_for(T, c->S);
-        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, slot_meta(c, module), s));
-        c->stats.expands += 1;
+        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s));
+        c->stats.expands += n;
+    }
+    return LORA_OK;
+}
+
+int check_group(lora_ctx *c, int32_t n, const int32_t *modules)
+{
+    if (n < 1 || n > LORA_MAX_GROUP || !modules)
+        return fail(c, LORA_ERR_INVALID_ARGUMENT, "group size %d not in 1..%d", n, LORA_MAX_GROUP);
+    for (int i = 0; i < n; ++i)
+        if (modules[i] < 0 || modules[i] >= c->n_modules)
+            return fail(c, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", modules[i],
+                        c->n_modules - 1);
+    return LORA_OK;
+}
+
+int check_ptrs(lora_ctx *c, int32_t n, const void *const *p, const char *what, bool distinct)
+{
+    if (!p)
+        return fail(c, LORA_ERR_INVALID_ARGUMENT, "%s array is NULL", what);
+    for (int i = 0; i < n; ++i) {
+        if (!p[i])
+            return fail(c, LORA_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", what, i);
+        if (distinct)
+            for (int j = 0; j < i; ++j)
+                if (p[j] == p[i])
+                    return fail(c, LORA_ERR_INVALID_ARGUMENT, "%s[%d] and %s[%d] are the same buffer",
+                                what, j, what, i);
     }
     return LORA_OK;
 }
@@ -411,6 +463,7 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         max_out = std::max(max_out, sh.d_out);
     }
     c->hbuf_rows = std::max(max_tokens, 16384);
+    c->slot_rank.assign(max_loras, 0);
     if (const char *env = std::getenv("LORA_MI355X_MAX_SPLITS")) {
         const int v = std::atoi(env);
         if (v >= 1 && v <= kMaxSplits)
@@ -418,7 +471,8 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     }
     c->max_tiles = max_tiles_for(max_tokens, max_loras);
     if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
-    if (e == hipSuccess) e = dalloc(c, &c->hpart, sizeof(float) * (size_t)c->hbuf_rows * c->R_pad);
+    if (e == hipSuccess)
+        e = dalloc(c, &c->hpart, sizeof(float) * (size_t)kMaxGroup * c->hbuf_rows * c->R_pad);
     if (e == hipSuccess) e = dalloc(c, &c->plan.counts, sizeof(int32_t) * (size_t)max_loras);
     if (e == hipSuccess) e = dalloc(c, &c->plan.seg_start, sizeof(int32_t) * (size_t)max_loras);
     if (e == hipSuccess) e = dalloc(c, &c->plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
@@ -511,6 +565,7 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
     ctx->load_gen += 1;
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = A_t[m] ? r : 0;
+    ctx->slot_rank[slot] = r;
     ctx->scale_host[slot] = s;
     ctx->stats.loads += 1;
     ctx->stats.bytes_loaded += bytes;
@@ -528,6 +583,7 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot)
     // batches already enqueued keep the adapter, later ones skip the slot.
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
+    ctx->slot_rank[slot] = 0;
     ctx->stats.clears += 1;
     return LORA_OK;
 }
@@ -564,47 +620,66 @@ int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_to
     return LORA_OK;
 }
 
-int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream)
+int lora_shrink_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                      void *stream)
 {
     if (check_ctx(ctx))
         return LORA_ERR_INVALID_ARGUMENT;
     ctx->last_error.clear();
-    if (module < 0 || module >= ctx->n_modules)
-        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    int rc = check_group(ctx, n, modules);
+    if (rc)
+        return rc;
     if (!ctx->plan_valid)
         return fail(ctx, LORA_ERR_NO_PLAN, "lora_shrink needs a prepared plan");
-    if (ctx->plan_T > 0 && !x)
-        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "x is NULL");
+    if (ctx->plan_T > 0 && (rc = check_ptrs(ctx, n, x, "x", false)))
+        return rc;
     DeviceGuard guard(ctx->device);
-    return run_shrink(ctx, x, module, (hipStream_t)stream);
+    return run_shrink(ctx, n, modules, x, (hipStream_t)stream);
+}
+
+int lora_expand_group(lora_ctx *ctx, int32_t n, const int32_t *modules, void *const *y,
+                      void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    int rc = check_group(ctx, n, modules);
+    if (rc)
+        return rc;
+    if (!ctx->plan_valid)
+        return fail(ctx, LORA_ERR_NO_PLAN, "lora_expand needs a prepared plan");
+    bool same = ctx->last_n == n;
+    for (int i = 0; same && i < n; ++i)
+        same = ctx->last_modules[i] == modules[i];
+    if (!same)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                    "lora_expand must follow lora_shrink of the same module list");
+    if (ctx->plan_T > 0 && (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
+        return rc;
+    DeviceGuard guard(ctx->device);
+    return run_expand(ctx, n, modules, y, (hipStream_t)stream);
+}
+
+int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream)
+{
+    return lora_shrink_group(ctx, 1, &module, &x, stream);
 }
 
 int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream)
 {
-    if (check_ctx(ctx))
-        return LORA_ERR_INVALID_ARGUMENT;
-    ctx->last_error.clear();
-    if (module < 0 || module >= ctx->n_modules)
-        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
-    if (!ctx->plan_valid)
-        return fail(ctx, LORA_ERR_NO_PLAN, "lora_expand needs a prepared plan");
-    if (ctx->last_shrink_module != module)
-        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
-                    "lora_expand(module %d) must follow lora_shrink of the same module", module);
-    if (ctx->plan_T > 0 && !y)
-        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "y is NULL");
-    DeviceGuard guard(ctx->device);
-    return run_expand(ctx, y, module, (hipStream_t)stream);
+    return lora_expand_group(ctx, 1, &module, &y, stream);
 }
 
-int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
-               int32_t n_tokens, int32_t module, void *stream)
+int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                     void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
+                     void *stream)
 {
     if (check_ctx(ctx))
         return LORA_ERR_INVALID_ARGUMENT;
     ctx->last_error.clear();
-    if (module < 0 || module >= ctx->n_modules)
-        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    int rc = check_group(ctx, n, modules);
+    if (rc)
+        return rc;
     if (n_tokens < 0)
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "n_tokens %d < 0", n_tokens);
     if (n_tokens > ctx->max_tokens)
@@ -612,11 +687,13 @@ int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_
                     ctx->max_tokens);
     if (n_tokens == 0)
         return LORA_OK;
-    if (!x || !y || !token_slot_idx)
-        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "x, y and token_slot_idx must be non-NULL");
+    if (!token_slot_idx)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "token_slot_idx is NULL");
+    if ((rc = check_ptrs(ctx, n, x, "x", false)) ||
+        (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
+        return rc;
     DeviceGuard guard(ctx->device);
     hipStream_t s = (hipStream_t)stream;
-    int rc;
     if (!(ctx->plan_valid && ctx->plan_prepared && ctx->plan_idx == token_slot_idx &&
           ctx->plan_T == n_tokens)) {
         ctx->plan_prepared = false;
@@ -626,10 +703,16 @@ int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_
             return rc;
         }
     }
-    rc = run_shrink(ctx, x, module, s);
+    rc = run_shrink(ctx, n, modules, x, s);
     if (rc)
         return rc;
-    return run_expand(ctx, y, module, s);
+    return run_expand(ctx, n, modules, y, s);
+}
+
+int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
+               int32_t n_tokens, int32_t module, void *stream)
+{
+    return lora_apply_group(ctx, 1, &module, &x, &y, token_slot_idx, n_tokens, stream);
 }
 
 int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)

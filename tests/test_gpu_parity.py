@@ -323,3 +323,66 @@ def test_error_codes():
     # nothing was loaded by the failed calls
     assert S.stats()["loads"] == 0
     S.close()
+
+
+# ---------------------------------------------------------------------------
+# grouped calls: one launch per phase for several modules
+
+def test_group_calls_equal_single_module_calls():
+    mods = [synth.Module("q", 512, 1024), synth.Module("k", 512, 256),
+            synth.Module("v", 1024, 512), synth.Module("o", 1024, 1024)]
+    wl = synth.random_case(16, synth.BF16, mods, 300, 6, 32, [32, 16, 8, 32, 1, 24],
+                           targeted=[[True, True, True, True], [True, False, True, False],
+                                     [False, True, True, True], [True, True, True, True],
+                                     [True, True, False, False], [False, False, False, True]],
+                           p_base_only=0.1)
+    S = make_slots(wl)
+    single = run_gpu(wl, S)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+    S.apply_group([0, 1, 2, 3], xs, ys, idx)
+    torch.cuda.synchronize()
+    for i, m in enumerate(mods):
+        assert np.array_equal(from_dev(ys[i], wl.dtype), single[m.name]), m.name
+        check_close(single[m.name], run_oracle(wl, m.name), wl.dtype, m.name)
+    # separate phases, a module listed twice with its own x and y, prepared plan
+    y2 = [to_dev(wl.y[m.name], wl.dtype) for m in (mods[2], mods[0], mods[2])]
+    x2 = [xs[2], xs[0], xs[2]]
+    S.prepare(idx)
+    S.shrink_group([2, 0, 2], x2)
+    S.expand_group([2, 0, 2], y2)
+    torch.cuda.synchronize()
+    for yy, name in zip(y2, ("v", "q", "v")):
+        assert np.array_equal(from_dev(yy, wl.dtype), single[name]), name
+    # errors
+    with pytest.raises(binding.LoraError) as e:
+        S.expand_group([0, 2, 2], y2)                       # not the shrunk list
+    assert e.value.status == binding.LORA_ERR_INVALID_ARGUMENT
+    with pytest.raises(binding.LoraError) as e:
+        S.apply_group([0, 0], [xs[0], xs[0]], [ys[0], ys[0]], idx)   # same y twice
+    assert e.value.status == binding.LORA_ERR_INVALID_ARGUMENT
+    with pytest.raises(binding.LoraError) as e:
+        S.apply_group([0] * 9, [xs[0]] * 9, [to_dev(wl.y["q"], wl.dtype) for _ in range(9)], idx)
+    assert e.value.status == binding.LORA_ERR_INVALID_ARGUMENT
+    with pytest.raises(binding.LoraError) as e:
+        S.apply_group([0, 7], [xs[0], xs[1]], [ys[0], ys[1]], idx)
+    assert e.value.status == binding.LORA_ERR_BAD_MODULE
+    S.close()
+
+
+@pytest.mark.parametrize("T", [700, 3000])
+def test_group_of_eight_modules(T):
+    shapes = [(256, 512), (512, 256), (256, 256), (384, 640), (640, 384), (128, 1024),
+              (1024, 128), (256, 768)]
+    mods = [synth.Module(f"m{i}", a, b) for i, (a, b) in enumerate(shapes)]
+    wl = synth.random_case(17 + T, synth.BF16, mods, T, 4, 64, [64, 16, 40, 8], p_base_only=0.05)
+    S = make_slots(wl, max_tokens=T)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+    S.apply_group(list(range(8)), xs, ys, idx)
+    torch.cuda.synchronize()
+    for i, m in enumerate(mods):
+        check_close(from_dev(ys[i], wl.dtype), run_oracle(wl, m.name), wl.dtype, m.name)
+    S.close()
