@@ -11,8 +11,10 @@ come from HBM rather than from the 256 MB Infinity Cache.  Inputs are resident
 in HBM before timing starts.  Prints one JSON line.
 
 value      tokens of the batch (skipped tokens included) x K / wall time of K steps
-roofline   the kernel with the largest share of the step: algorithmic bytes per
-           launch / its average duration, timed with HIP events on the launch stream
+roofline   the kernel with the largest share of the step: its algorithmic bytes /
+           its kernel time, from start / stop events the library attaches to each of
+           its dispatches (hipExtLaunchKernelGGL) during a second pass of the same K
+           steps right after the timed one
 cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
            same workload (rank 0, one GPU only)
 """
@@ -50,8 +52,8 @@ def parse():
                    help="minimum footprint of the rotated layer sets (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--no-kernel-events", action="store_true",
-                   help="time the steps without per-kernel events (roofline then null)")
+    p.add_argument("--no-kernel-timing", action="store_true",
+                   help="time the steps without per-dispatch kernel events (roofline then null)")
     p.add_argument("--calib-copy", action="store_true",
                    help="run only a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -172,84 +174,77 @@ def main():
     names = [m.name for m in mods]
     groups = [[names.index(n) for n in g] for g in GROUPS[wl.name]]
     ng = len(groups)
-    stream = torch.cuda.current_stream()
-    use_events = not args.no_kernel_events
+    use_timing = not args.no_kernel_timing
 
-    def step(i, ev=None):
+    def step(i):
         l = i % L
-        if ev is not None:
-            ev[0].record(stream)
         slots.prepare(idx)
-        if ev is not None:
-            ev[1].record(stream)
-        for gi, g in enumerate(groups):
+        for g in groups:
             mis = [l * nm + j for j in g]
             slots.shrink_group(mis, [xs[mi] for mi in mis])
-            if ev is not None:
-                ev[2 + 2 * gi].record(stream)
             slots.expand_group(mis, [ys[mi] for mi in mis])
-            if ev is not None:
-                ev[3 + 2 * gi].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    n_ev = 2 + 2 * ng
-    events = ([[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
-              if use_events else None)
-    torch.cuda.synchronize()
+    # timed region: K steps, nothing but the library calls
     t0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, events[i] if use_events else None)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / K * 1e3
     value = T * K / elapsed
+    if use_timing:
+        # the same K steps again with per-dispatch kernel events (their host cost
+        # would distort the step time above, so they get a pass of their own);
+        # the events are created before this pass starts
+        slots.profile_begin(K * (2 * ng + 2))
+        torch.cuda.synchronize()
+        for i in range(K):
+            step(args.warmup + K + i)
+        torch.cuda.synchronize()
 
-    # per-launch durations from the events (one shrink and one expand launch per group)
     act = (wl.idx >= 0) & (wl.idx < S)
     T_act = int(act.sum())
     used = np.unique(wl.idx[act])
     sum_r = int(sum(wl.adapters[k].r for k in used))
     roofline, kernels = None, None
-    if use_events:
-        plan_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-        shrink_ms = np.zeros((K, ng))
-        expand_ms = np.zeros((K, ng))
-        for i, e in enumerate(events):
-            prev = e[1]
-            for gi in range(ng):
-                shrink_ms[i, gi] = prev.elapsed_time(e[2 + 2 * gi])
-                expand_ms[i, gi] = e[2 + 2 * gi].elapsed_time(e[3 + 2 * gi])
-                prev = e[3 + 2 * gi]
+    if use_timing:
+        prof = slots.profile_end()
+        n = prof["launches"]
+        tot = prof["total_ms"]
         # algorithmic bytes of one launch of each group
         shrink_bytes = [sum(b * mods[j].d_in * (T_act + sum_r) for j in g) for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
         flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
                  for m in mods]
+        def avg_us(kind):
+            return tot[kind] / n[kind] * 1e3 if n[kind] else None
         kernels = {
             "groups": [[names[j] for j in g] for g in groups],
-            "plan": {"avg_us": float(plan_ms.mean() * 1e3)},
-            "lora_shrink": {"avg_us_per_launch": [float(v) for v in shrink_ms.mean(0) * 1e3],
-                            "alg_bytes_per_launch": [float(v) for v in shrink_bytes],
-                            "GBps": float(sum(shrink_bytes) / shrink_ms.mean(0).sum() / 1e6)},
-            "lora_expand": {"avg_us_per_launch": [float(v) for v in expand_ms.mean(0) * 1e3],
-                            "alg_bytes_per_launch": [float(v) for v in expand_bytes],
-                            "GBps": float(sum(expand_bytes) / expand_ms.mean(0).sum() / 1e6)},
+            "timed_dispatches": n, "untimed_dispatches": prof["untimed"],
+            "plan": {"avg_us": avg_us("plan"), "per_step_us": tot["plan"] / K * 1e3},
+            "lora_shrink": {"avg_us": avg_us("shrink"), "per_step_us": tot["shrink"] / K * 1e3,
+                            "alg_bytes_per_step": float(sum(shrink_bytes)),
+                            "GBps": float(sum(shrink_bytes) * K / (tot["shrink"] * 1e-3) / 1e9)},
+            "lora_expand": {"avg_us": avg_us("expand"), "per_step_us": tot["expand"] / K * 1e3,
+                            "alg_bytes_per_step": float(sum(expand_bytes)),
+                            "GBps": float(sum(expand_bytes) * K / (tot["expand"] * 1e-3) / 1e9)},
             "step_alg_bytes": float(sum(shrink_bytes) + sum(expand_bytes)),
             "step_alg_flops": float(sum(flops)),
         }
-        dom = "lora_expand" if expand_ms.sum() >= shrink_ms.sum() else "lora_shrink"
-        dom_ms = expand_ms if dom == "lora_expand" else shrink_ms
-        dom_bytes = expand_bytes if dom == "lora_expand" else shrink_bytes
-        achieved = sum(dom_bytes) / (dom_ms.mean(0).sum() * 1e-3) / 1e9      # GB/s
-        traffic = traffic_from_profiles(dom, wl.name)
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        dom = "expand" if tot["expand"] >= tot["shrink"] else "shrink"
+        dom_bytes = expand_bytes if dom == "expand" else shrink_bytes
+        achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
+        kname = "lora_" + dom
+        traffic = traffic_from_profiles(kname, wl.name)
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic,
                     "alg_bytes_per_launch": float(np.mean(dom_bytes)),
-                    "avg_launch_us": float(dom_ms.mean() * 1e3)}
+                    "avg_launch_us": avg_us(dom)}
         log("kernels:", json.dumps(kernels))
 
     cpu = None
@@ -272,7 +267,8 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "active_tokens": T_act,
                    "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
                    "max_loras": S, "max_rank": R, "ranks": sorted({a.r for a in wl.adapters if a}),
-                   "layer_sets_rotated": L, "kernel_events_in_timed_region": use_events,
+                   "layer_sets_rotated": L, "groups": [[names[j] for j in g] for g in groups],
+                   "kernel_timing": "per-dispatch events" if use_timing else "none",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,

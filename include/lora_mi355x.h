@@ -137,7 +137,9 @@ int lora_sync_loads(lora_ctx *ctx);
  * a stable counting sort of token_slot_idx (int32[n_tokens], device) into a
  * permutation, per-slot segments and tiles of up to 64 tokens.  Tokens with
  * idx < 0 are not listed; idx >= max_loras are not listed and set
- * LORA_FLAG_SLOT_INDEX_TOO_LARGE.  The plan stays valid for lora_shrink,
+ * LORA_FLAG_SLOT_INDEX_TOO_LARGE.  For bf16 batches of at most 1024 tokens the
+ * grouping runs inside each lora_shrink launch instead of a launch of its own.
+ * The plan stays valid for lora_shrink,
  * lora_expand and lora_apply calls with the same (token_slot_idx, n_tokens)
  * until the next lora_plan_prepare; the caller must not change the contents of
  * token_slot_idx meanwhile.  n_tokens == 0 is allowed.
@@ -156,7 +158,8 @@ int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream);
  * lora_expand: y[t,:] = round(y[t,:] + s_k * h[t,:] . B_k) for every planned
  * token whose slot holds an adapter targeting `module`; every other row of y
  * is left bit-identical.  Must follow lora_shrink of the same module on the
- * same plan (else LORA_ERR_INVALID_ARGUMENT).  y is [n_tokens][d_out].
+ * same plan, with no lora_slot_load or lora_slot_clear in between (else
+ * LORA_ERR_INVALID_ARGUMENT).  y is [n_tokens][d_out].
  */
 int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream);
 
@@ -194,6 +197,23 @@ int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags);
 
 /* Counters since creation. */
 int lora_get_stats(lora_ctx *ctx, lora_stats *out);
+
+/*
+ * Kernel timing.  Between lora_profile_begin and lora_profile_end, each of the
+ * ctx's dispatches (up to max_launches of them) carries a start and a stop
+ * event recorded with the dispatch itself, so the elapsed time is that
+ * kernel's execution.  lora_profile_end waits for the timed dispatches and
+ * returns, per kind, how many were timed and their summed duration.  Events
+ * are created by lora_profile_begin, outside any timed region.
+ */
+typedef struct {
+    int64_t launches[3];   /* [0] plan, [1] shrink, [2] expand dispatches timed */
+    double total_ms[3];    /* their summed kernel time, milliseconds */
+    int64_t untimed;       /* dispatches past max_launches (not timed) */
+} lora_profile;
+
+int lora_profile_begin(lora_ctx *ctx, int32_t max_launches);
+int lora_profile_end(lora_ctx *ctx, lora_profile *out);
 
 /* Static text for a status code. */
 const char *lora_status_string(int status);

@@ -16,7 +16,8 @@ import os
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liblora_mi355x.so")
+# LORA_MI355X_LIB selects another build of the library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(PKG, "liblora_mi355x.so")
 
 LORA_BF16 = 0
 LORA_FP32 = 1
@@ -38,7 +39,8 @@ LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_clear",
            "lora_sync_loads", "lora_plan_prepare", "lora_shrink", "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
-           "lora_get_device_flags", "lora_get_stats", "lora_status_string", "lora_last_error")
+           "lora_get_device_flags", "lora_get_stats", "lora_profile_begin", "lora_profile_end",
+           "lora_status_string", "lora_last_error")
 
 LORA_MAX_GROUP = 8
 
@@ -51,6 +53,11 @@ class LoraError(RuntimeError):
 
 class _ModuleShape(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
+
+
+class _Profile(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * 3), ("total_ms", ctypes.c_double * 3),
+                ("untimed", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
@@ -89,6 +96,8 @@ def load_library(path: str = LIB_PATH):
                               P, I32, P], ctypes.c_int),
         "lora_get_device_flags": ([P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
         "lora_get_stats": ([P, ctypes.POINTER(_Stats)], ctypes.c_int),
+        "lora_profile_begin": ([P, I32], ctypes.c_int),
+        "lora_profile_end": ([P, ctypes.POINTER(_Profile)], ctypes.c_int),
         "lora_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "lora_last_error": ([P], ctypes.c_char_p),
     }
@@ -269,6 +278,19 @@ def lora_get_stats(ctx) -> dict:
     return {name: int(getattr(s, name)) for name, _ in _Stats._fields_}
 
 
+def lora_profile_begin(ctx, max_launches: int) -> None:
+    _check(load_library().lora_profile_begin(ctx, int(max_launches)), ctx)
+
+
+def lora_profile_end(ctx) -> dict:
+    p = _Profile()
+    _check(load_library().lora_profile_end(ctx, ctypes.byref(p)), ctx)
+    kinds = ("plan", "shrink", "expand")
+    return {"launches": {k: int(p.launches[i]) for i, k in enumerate(kinds)},
+            "total_ms": {k: float(p.total_ms[i]) for i, k in enumerate(kinds)},
+            "untimed": int(p.untimed)}
+
+
 # ---------------------------------------------------------------------------
 # convenience owner of a ctx
 
@@ -313,6 +335,12 @@ class Slots:
 
     def apply_group(self, modules, x, y, idx, n_tokens=None, stream=None):
         lora_apply_group(self.ctx, modules, x, y, idx, n_tokens, stream)
+
+    def profile_begin(self, max_launches):
+        lora_profile_begin(self.ctx, max_launches)
+
+    def profile_end(self):
+        return lora_profile_end(self.ctx)
 
     def flags(self):
         return lora_get_device_flags(self.ctx)

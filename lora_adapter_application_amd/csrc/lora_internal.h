@@ -28,9 +28,11 @@ constexpr int splits_cap(int NB) { return kMaxSplits / NB > 0 ? kMaxSplits / NB 
 
 struct alignas(16) Tile {
     int32_t slot;
-    int32_t start;  // first position in the permutation
+    int32_t start;  // first position in the slot-sorted order
     int32_t len;    // 1..kTileTokens
-    int32_t pad;
+    int32_t rank;   // rank of the slot's adapter, written by the shrink for the expand
+    float scale;    // the slot's scale, written with rank
+    int32_t pad[3];
 };
 
 struct PlanBuffers {
@@ -44,6 +46,8 @@ struct PlanBuffers {
     int32_t *chunk_counts;  // [ceil(max_tokens/1024)][S], batches above 1024 tokens
 };
 
+// Batches up to this many tokens are planned inside the bf16 shrink kernel.
+constexpr int kInlinePlanTokens = 1024;
 // Modules one grouped shrink / expand launch covers (blockIdx.z = member).
 constexpr int kMaxGroup = 8;
 
@@ -57,10 +61,18 @@ struct SlotMeta {
     uint32_t target[kMaxGroup][LORA_MAX_SLOTS / 32];
 };
 
+// Optional events around one dispatch (both null: untimed), recorded with the
+// dispatch itself so they bracket exactly the kernel's execution.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 inline int max_tiles_for(int T, int S) { return (T + kTileTokens - 1) / kTileTokens + (S < T ? S : T); }
 
+// A plan of more than 1024 tokens takes two launches; t[0] and t[1] time them.
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
-                       hipStream_t st);
+                       hipStream_t st, const LaunchTiming *t /* [2] or null */);
 
 // Element type: bf16 (uint16_t bit patterns) or fp32.
 struct ShrinkArgs {
@@ -71,9 +83,11 @@ struct ShrinkArgs {
     int32_t d_in[kMaxGroup];
     int32_t k_chunk[kMaxGroup];
     int32_t splits[kMaxGroup];
-    const Tile *tiles;
-    const int32_t *tile_tok;
-    const int32_t *n_tiles;
+    PlanBuffers plan;                   // read, or written by an inline plan
+    const int32_t *idx;                 // token slot index (inline plan)
+    int32_t T;
+    int32_t S;
+    int32_t inline_plan;                // batch of <= kInlinePlanTokens: plan computed in the shrink
     float *hpart;                       // [member][split][T][R_pad]
     int64_t member_stride;              // elements
     int64_t split_stride;               // T * R_pad
@@ -101,8 +115,10 @@ struct ExpandArgs {
     int32_t grid_cols;                  // max column chunks over the members
 };
 
-hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st);
-hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st);
+hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
+                         const LaunchTiming &t);
+hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,
+                         const LaunchTiming &t);
 
 // Slot maintenance, on the side stream.
 hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_slot,

@@ -22,6 +22,7 @@
 // supplies row (l & 15) of A and column (l & 15) of B, each with the K slice of
 // lane group g = l >> 4 (8 values for K=32, 4 for K=16); the 16x16 fp32 result
 // leaves rows 4g..4g+3 of column (l & 15) in lane l.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,11 +36,23 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Launch, with the dispatch bracketed by t's events when it has them.
+template <typename K, typename... Args>
+static void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                   const LaunchTiming &t, Args... args)
+{
+    if (t.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, t.start, t.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
+
 // ----------------------------------------------------------------------------
 // plan
 
-// Exclusive scan of two ints per thread over a 1024-thread block.
-__device__ void block_excl_scan2_1024(int &a, int &b, int2 *wsum /*[17]*/, int &total_a, int &total_b)
+// Exclusive scan of two ints per thread over a block of NW waves.
+template <int NW>
+__device__ void block_excl_scan2(int &a, int &b, int2 *wsum /*[NW + 1]*/, int &total_a, int &total_b)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int sa = a, sb = b;
@@ -55,35 +68,40 @@ __device__ void block_excl_scan2_1024(int &a, int &b, int2 *wsum /*[17]*/, int &
         wsum[wave] = make_int2(sa, sb);
     __syncthreads();
     if (wave == 0) {
-        const int2 w = lane < 16 ? wsum[lane] : make_int2(0, 0);
+        const int2 w = lane < NW ? wsum[lane] : make_int2(0, 0);
         int ta = w.x, tb = w.y;
 #pragma unroll
-        for (int d = 1; d < 16; d <<= 1) {
+        for (int d = 1; d < NW; d <<= 1) {
             const int oa = __shfl_up(ta, d, 64), ob = __shfl_up(tb, d, 64);
             if (lane >= d) {
                 ta += oa;
                 tb += ob;
             }
         }
-        if (lane < 16)
+        if (lane < NW)
             wsum[lane] = make_int2(ta - w.x, tb - w.y);
-        if (lane == 15)
-            wsum[16] = make_int2(ta, tb);
+        if (lane == NW - 1)
+            wsum[NW] = make_int2(ta, tb);
     }
     __syncthreads();
-    const int2 base = wsum[wave], tot = wsum[16];
+    const int2 base = wsum[wave], tot = wsum[NW];
     a = sa - a + base.x;
     b = sb - b + base.y;
     total_a = tot.x;
     total_b = tot.y;
 }
 
+__device__ __forceinline__ void block_excl_scan2_1024(int &a, int &b, int2 *wsum, int &ta, int &tb)
+{
+    block_excl_scan2<16>(a, b, wsum, ta, tb);
+}
+
 // Rank of this thread's token among the earlier tokens of its wave with the
 // same slot (one ballot per distinct slot in the wave); the first lane of each
-// slot writes the wave's count of that slot to wcnt[wave][slot].
-__device__ __forceinline__ int wave_stable_rank(int v, bool valid, int32_t *wcnt, int S)
+// slot writes the wave's count of that slot to row[slot].
+__device__ __forceinline__ int wave_stable_rank_row(int v, bool valid, int32_t *row)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     uint64_t act = __ballot(valid);
     int my_rank = 0;
     while (act) {
@@ -94,10 +112,15 @@ __device__ __forceinline__ int wave_stable_rank(int v, bool valid, int32_t *wcnt
         if (mine)
             my_rank = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == leader)
-            wcnt[wave * S + lv] = __popcll(m);
+            row[lv] = __popcll(m);
         act &= ~m;
     }
     return my_rank;
+}
+
+__device__ __forceinline__ int wave_stable_rank(int v, bool valid, int32_t *wcnt, int S)
+{
+    return wave_stable_rank_row(v, valid, wcnt + (threadIdx.x >> 6) * S);
 }
 
 // Batches of at most 1024 tokens: one token per thread, one ballot pass gives
@@ -140,7 +163,9 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restr
             t.slot = tid;
             t.start = start + j * kTileTokens;
             t.len = min(kTileTokens, c - j * kTileTokens);
-            t.pad = 0;
+            t.rank = 0;
+            t.scale = 0.f;
+            t.pad[0] = t.pad[1] = t.pad[2] = 0;
             pb.tiles[tstart + j] = t;
         }
     }
@@ -237,7 +262,9 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
                 t.slot = tid;
                 t.start = start + j * kTileTokens;
                 t.len = min(kTileTokens, tot - j * kTileTokens);
-                t.pad = 0;
+                t.rank = 0;
+            t.scale = 0.f;
+            t.pad[0] = t.pad[1] = t.pad[2] = 0;
                 pb.tiles[tstart + j] = t;
             }
         }
@@ -254,17 +281,18 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
 }
 
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
-                       hipStream_t st)
+                       hipStream_t st, const LaunchTiming *t)
 {
+    const LaunchTiming none;
     if (T <= 1024) {
-        hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(1024),
-                           sizeof(int32_t) * (size_t)S * 17, st, idx, T, S, pb);
+        launch(plan_small_kernel, dim3(1), dim3(1024), sizeof(int32_t) * (size_t)S * 17, st,
+               t ? t[0] : none, idx, T, S, pb);
     } else {
         const int n_chunks = (T + 1023) / 1024;
-        hipLaunchKernelGGL(plan_count_kernel, dim3(n_chunks), dim3(1024),
-                           sizeof(int32_t) * (size_t)S * 16, st, idx, T, S, pb);
-        hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_chunks), dim3(1024),
-                           sizeof(int32_t) * (size_t)S * 18, st, idx, T, S, n_chunks, pb);
+        launch(plan_count_kernel, dim3(n_chunks), dim3(1024), sizeof(int32_t) * (size_t)S * 16, st,
+               t ? t[0] : none, idx, T, S, pb);
+        launch(plan_scatter_kernel, dim3(n_chunks), dim3(1024), sizeof(int32_t) * (size_t)S * 18,
+               st, t ? t[1] : none, idx, T, S, n_chunks, pb);
     }
     return hipGetLastError();
 }
@@ -293,6 +321,33 @@ __device__ __forceinline__ int member_rank(const SlotMeta &meta, int m, int slot
     return ((meta.target[m][slot >> 5] >> (slot & 31)) & 1u) ? (int)meta.rank[slot] : 0;
 }
 
+// Slot metadata fetched at kernel start, independent of the tile: every lane
+// holds 4 slot ranks (rk) and, in lanes 0..7, one 32-slot word of the member's
+// target mask (tw); a lookup by slot is then a cross-lane shuffle.
+struct MetaRegs {
+    uint32_t rk;
+    uint32_t tw;
+};
+
+__device__ __forceinline__ MetaRegs load_meta_regs(const SlotMeta &meta, int m)
+{
+    const int lane = threadIdx.x & 63;
+    MetaRegs r;
+    r.rk = ((const uint32_t *)meta.rank)[lane];
+    r.tw = lane < LORA_MAX_SLOTS / 32 ? meta.target[m][lane] : 0u;
+    return r;
+}
+
+__device__ __forceinline__ int meta_rank(const MetaRegs &r, int slot)
+{
+    return (__shfl(r.rk, slot >> 2, 64) >> ((slot & 3) * 8)) & 0xff;
+}
+
+__device__ __forceinline__ bool meta_targets(const MetaRegs &r, int slot)
+{
+    return (__shfl(r.tw, slot >> 5, 64) >> (slot & 31)) & 1u;
+}
+
 // One member's view of a shrink launch.
 struct ShrinkView {
     const uint16_t *x;
@@ -306,7 +361,8 @@ struct ShrinkView {
 // Gather path (BGMV): waves split the tile's subtiles and the K range.  Per
 // step a lane loads 64 contiguous bytes of its token's x row and of its rank's
 // A^T row and feeds them to 4 MFMAs; both operands use the same K order, so the
-// sum is the plain dot product over that K block.
+// sum is the plain dot product over that K block.  tokv: lane l of every wave
+// holds the token of tile row l.
 template <int NB>
 struct KBlock {
     uint4 x[4];
@@ -350,8 +406,8 @@ __device__ __forceinline__ void mfma_kblock(f32x4_t (&acc)[NB], const KBlock<NB>
 }
 
 template <int NB, bool DOUBLE_BUFFER>
-__device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &tile,
-                                            const int32_t *tok_row, int nb, unsigned char *smem)
+__device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
+                                            unsigned char *smem)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = lane & 15, g = lane >> 4;
@@ -362,7 +418,8 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
     const bool wave_on = sub < nsub;
     const int t_in = sub * 16 + row;
     const bool tok_ok = wave_on && t_in < tile.len;
-    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok_row[t_in] : 0) * v.d_in;
+    const int tok = __shfl(tokv, t_in & 63, 64);
+    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok : 0) * v.d_in;
     const uint16_t *arow0 = v.A + (int64_t)row * v.d_in;
 
     f32x4_t acc[NB];
@@ -423,14 +480,15 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
 constexpr int kLdsRow = kShrinkKBlock + 8;   // bf16 elements per staged A row (padded)
 
 template <int NB>
-__device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &tile,
-                                            const int32_t *tok_row, int nb, uint16_t *lds)
+__device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
+                                            uint16_t *lds)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row = lane & 15, g = lane >> 4;
     const int t_in = wave * 16 + row;
     const bool tok_ok = t_in < tile.len;
-    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok_row[t_in] : 0) * v.d_in;
+    const int tok = __shfl(tokv, t_in, 64);
+    const uint16_t *xrow = v.x + (int64_t)(tok_ok ? tok : 0) * v.d_in;
     const int k0 = v.k0, k1 = v.k1;
     const int nkb = (k1 - k0 + kShrinkKBlock - 1) / kShrinkKBlock;
     constexpr int buf_elems = NB * 16 * kLdsRow;
@@ -515,21 +573,134 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &til
     }
 }
 
+// Inline plan (batches of at most kInlinePlanTokens): every workgroup of the
+// shrink groups the batch's tokens by slot in LDS, the same stable counting sort
+// the plan kernels run, and picks its own tile; workgroups with blockIdx.y == 0
+// and blockIdx.z == 0 publish their tile (and workgroup 0 the totals) for the
+// expand.  Returns false for workgroups past the last tile.
+struct InlinePlanLds {
+    int32_t wcnt[16][LORA_MAX_SLOTS];   // per (256-token chunk, wave): count, then offset
+    int32_t base[LORA_MAX_SLOTS];       // first position of slot s
+    int32_t tbase[LORA_MAX_SLOTS];      // first tile of slot s
+    int32_t cnt[LORA_MAX_SLOTS];
+    int32_t perm[kInlinePlanTokens];    // token at each slot-sorted position
+    int2 wsum[5];
+    int32_t my_slot;
+};
+
+__device__ bool inline_plan(const ShrinkArgs &a, const SlotMeta &meta, InlinePlanLds &L,
+                            Tile &tile, int &tokv)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int T = a.T, S = a.S;
+    int v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int i = c * 256 + tid;
+        v[c] = i < T ? a.idx[i] : -1;
+    }
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+        for (int sl = tid; sl < S; sl += 256)
+            L.wcnt[w][sl] = 0;
+    __syncthreads();
+    int myr[4];
+    bool too_large = false;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        too_large |= v[c] >= S;
+        myr[c] = wave_stable_rank_row(v[c], v[c] >= 0 && v[c] < S, L.wcnt[c * 4 + wave]);
+    }
+    __syncthreads();
+    int c_s = 0;
+    if (tid < S) {
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int k = L.wcnt[w][tid];
+            L.wcnt[w][tid] = c_s;
+            c_s += k;
+        }
+    }
+    int start = c_s, tst = (c_s + kTileTokens - 1) / kTileTokens, n_active, n_tiles;
+    const int nt = tst;
+    block_excl_scan2<4>(start, tst, L.wsum, n_active, n_tiles);
+    const int b = blockIdx.x;
+    if (tid < S) {
+        L.base[tid] = start;
+        L.tbase[tid] = tst;
+        L.cnt[tid] = c_s;
+        if (b >= tst && b < tst + nt)
+            L.my_slot = tid;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (v[c] >= 0 && v[c] < S)
+            L.perm[L.base[v[c]] + L.wcnt[c * 4 + wave][v[c]] + myr[c]] = c * 256 + tid;
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+    if (first) {
+        if (tid < S) {
+            a.plan.counts[tid] = c_s;
+            a.plan.seg_start[tid] = start;
+        }
+        if (tid == 0) {
+            *a.plan.n_tiles = n_tiles;
+            *a.plan.n_active = n_active;
+        }
+        if (too_large)
+            atomicOr(a.plan.flags, 1u);
+    }
+    __syncthreads();
+    if (b >= n_tiles)
+        return false;
+    const int sl = L.my_slot;
+    const int j = b - L.tbase[sl];
+    tile.slot = sl;
+    tile.start = L.base[sl] + j * kTileTokens;
+    tile.len = min(kTileTokens, L.cnt[sl] - j * kTileTokens);
+    tile.rank = meta.rank[sl];
+    tile.scale = meta.scale[sl];
+    tokv = lane < tile.len ? L.perm[tile.start + lane] : 0;
+    if (blockIdx.y == 0 && blockIdx.z == 0) {
+        if (tid == 0)
+            a.plan.tiles[b] = tile;
+        if (tid < tile.len)
+            a.plan.tile_tok[(int64_t)b * kTileTokens + tid] = L.perm[tile.start + tid];
+    }
+    return true;
+}
+
 // MIXED: batches above 1024 tokens; tiles of 33..64 tokens take the segment
 // path, shorter ones the gather path single-buffered.  Otherwise every tile
-// takes the gather path, double-buffered when the rank allows.
-template <int NB, bool MIXED>
+// takes the gather path, double-buffered when the rank allows.  INLINE: the
+// batch is planned in the kernel (see inline_plan).
+template <int NB, bool MIXED, bool INLINE>
 __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
 {
-    const int n_tiles = *a.n_tiles;
-    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
     const int m = blockIdx.z;
-    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y >= a.splits[m])
+    const int lane = threadIdx.x & 63;
+    const MetaRegs mr = load_meta_regs(meta, m);
+    Tile tile;
+    int tokv;
+    if (INLINE) {
+        __shared__ InlinePlanLds L;
+        if (!inline_plan(a, meta, L, tile, tokv))
+            return;
+    } else {
+        const int n_tiles = *a.plan.n_tiles;
+        tile = a.plan.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
+        tokv = a.plan.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
+        if ((int)blockIdx.x >= n_tiles)
+            return;
+        tile.rank = meta_rank(mr, tile.slot);
+        if (blockIdx.y == 0 && m == 0 && threadIdx.x == 0) {
+            a.plan.tiles[blockIdx.x].rank = tile.rank;
+            a.plan.tiles[blockIdx.x].scale = meta.scale[tile.slot];
+        }
+    }
+    if ((int)blockIdx.y >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, tile.slot))
         return;
-    const int rank = member_rank(meta, m, tile.slot);
-    if (rank == 0)
-        return;
-    const int nb = (rank + 15) >> 4;
+    const int nb = (tile.rank + 15) >> 4;
     ShrinkView v;
     v.d_in = a.d_in[m];
     v.x = (const uint16_t *)a.x[m];
@@ -538,7 +709,6 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
     v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
     v.h = a.hpart + m * a.member_stride + (int64_t)blockIdx.y * a.split_stride;
     v.R_pad = a.R_pad;
-    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
 
     constexpr int kRedBytes = 4 * NB * 64 * 16;
     constexpr int kSgmvBytes = MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0;
@@ -546,9 +716,9 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
     if (MIXED && tile.len > 32)
-        shrink_sgmv<NB>(v, tile, tok_row, nb, (uint16_t *)smem);
+        shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
     else
-        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tok_row, nb, smem);
+        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
 }
 
 // ----------------------------------------------------------------------------
@@ -568,23 +738,25 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
 template <int NB>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
-    const int n_tiles = *a.n_tiles;
-    const Tile tile = a.tiles[blockIdx.x];
     const int m = blockIdx.z;
-    const int d_out = a.d_out[m];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const MetaRegs mr = load_meta_regs(meta, m);
+    const int n_tiles = *a.n_tiles;
+    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
+    const int tokv = a.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
+    const int d_out = a.d_out[m];
     const int cb = blockIdx.y * kExpandCols + wave * 64;
     if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= d_out)
         return;
-    const int rank = member_rank(meta, m, tile.slot);
-    if (rank == 0)
+    // rank and scale of the slot as the shrink of this batch saw them
+    const int rank = tile.rank;
+    if (rank == 0 || !meta_targets(mr, tile.slot))
         return;
     const int nb = (rank + 15) >> 4;
-    const float s = meta.scale[tile.slot];
+    const float s = tile.scale;
     const int row = lane & 15, g = lane >> 4;
     const bool cols_ok = cb < d_out;
     const int nsub = (tile.len + 15) >> 4;
-    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
     uint16_t *ybase = (uint16_t *)a.y[m];
 
     // tokens of this lane in each subtile
@@ -594,7 +766,8 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
     for (int st = 0; st < 4; ++st) {
         const int t = st * 16 + row;
         tok_ok[st] = cols_ok && t < tile.len;
-        tok[st] = tok_ok[st] ? tok_row[t] : 0;
+        const int tv = __shfl(tokv, t, 64);
+        tok[st] = tok_ok[st] ? tv : 0;
     }
     // h partials of the tile: thread tid owns quads e = tid + 256 i (i < NB) of
     // the len x nb*16 block
@@ -729,8 +902,8 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 
 __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta meta)
 {
-    const int n_tiles = *a.n_tiles;
-    const Tile tile = a.tiles[blockIdx.x];
+    const int n_tiles = *a.plan.n_tiles;
+    const Tile tile = a.plan.tiles[blockIdx.x];
     const int m = blockIdx.z;
     if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y >= a.splits[m])
         return;
@@ -743,7 +916,7 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
     const int tid = threadIdx.x;
     const float *x = (const float *)a.x[m];
     const float *Aslot = (const float *)a.A[m] + (int64_t)tile.slot * a.slot_stride_A[m];
-    const int32_t *tok_row = a.tile_tok + (int64_t)blockIdx.x * kTileTokens;
+    const int32_t *tok_row = a.plan.tile_tok + (int64_t)blockIdx.x * kTileTokens;
     __shared__ float xs[kTileTokens][33];
     __shared__ float as[LORA_MAX_RANK_PAD][33];
     __shared__ int toks[kTileTokens];
@@ -842,47 +1015,52 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta 
 // ----------------------------------------------------------------------------
 // launches
 
-template <bool MIXED>
-static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st)
+template <bool MIXED, bool INLINE>
+static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st,
+                               const LaunchTiming &t)
 {
     const int nbmax = a.R_pad / 16;
     if (nbmax <= 1)
-        hipLaunchKernelGGL((shrink_bf16_kernel<1, MIXED>), grid, dim3(256), 0, st, a, m);
+        launch(shrink_bf16_kernel<1, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 2)
-        hipLaunchKernelGGL((shrink_bf16_kernel<2, MIXED>), grid, dim3(256), 0, st, a, m);
+        launch(shrink_bf16_kernel<2, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 4)
-        hipLaunchKernelGGL((shrink_bf16_kernel<4, MIXED>), grid, dim3(256), 0, st, a, m);
+        launch(shrink_bf16_kernel<4, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
     else
-        hipLaunchKernelGGL((shrink_bf16_kernel<8, MIXED>), grid, dim3(256), 0, st, a, m);
+        launch(shrink_bf16_kernel<8, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
 }
 
-hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st)
+hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
+                         const LaunchTiming &t)
 {
     const dim3 grid(a.grid_tiles, a.grid_splits, a.n), block(256);
     if (!bf16)
-        hipLaunchKernelGGL(shrink_f32_kernel, grid, block, 0, st, a, m);
+        launch(shrink_f32_kernel, grid, block, 0, st, t, a, m);
+    else if (a.inline_plan)
+        launch_shrink_bf16<false, true>(a, m, grid, st, t);
     else if (a.mixed)
-        launch_shrink_bf16<true>(a, m, grid, st);
+        launch_shrink_bf16<true, false>(a, m, grid, st, t);
     else
-        launch_shrink_bf16<false>(a, m, grid, st);
+        launch_shrink_bf16<false, false>(a, m, grid, st, t);
     return hipGetLastError();
 }
 
-hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st)
+hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,
+                         const LaunchTiming &t)
 {
     const dim3 grid(a.grid_tiles, a.grid_cols, a.n), block(256);
     if (!bf16) {
-        hipLaunchKernelGGL(expand_f32_kernel, grid, block, 0, st, a, m);
+        launch(expand_f32_kernel, grid, block, 0, st, t, a, m);
     } else {
         const int nbmax = a.R_pad / 16;
         if (nbmax <= 1)
-            hipLaunchKernelGGL(expand_bf16_kernel<1>, grid, block, 0, st, a, m);
+            launch(expand_bf16_kernel<1>, grid, block, 0, st, t, a, m);
         else if (nbmax <= 2)
-            hipLaunchKernelGGL(expand_bf16_kernel<2>, grid, block, 0, st, a, m);
+            launch(expand_bf16_kernel<2>, grid, block, 0, st, t, a, m);
         else if (nbmax <= 4)
-            hipLaunchKernelGGL(expand_bf16_kernel<4>, grid, block, 0, st, a, m);
+            launch(expand_bf16_kernel<4>, grid, block, 0, st, t, a, m);
         else
-            hipLaunchKernelGGL(expand_bf16_kernel<8>, grid, block, 0, st, a, m);
+            launch(expand_bf16_kernel<8>, grid, block, 0, st, t, a, m);
     }
     return hipGetLastError();
 }

@@ -88,8 +88,10 @@ struct lora_ctx {
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
     std::vector<StreamState> streams;
-    // plan state
+    // plan state; an inline plan is computed by every shrink launch itself
     bool plan_valid = false, plan_prepared = false;
+    bool plan_inline = false;   // the next shrink computes the plan in-kernel and publishes it
+    uint64_t slot_epoch = 0, shrink_epoch = 0;   // loads + clears, and their count at the last shrink
     const int32_t *plan_idx = nullptr;
     int32_t plan_T = 0;
     // last shrink group, consumed by expand
@@ -97,6 +99,12 @@ struct lora_ctx {
     int last_modules[kMaxGroup] = {};
     int last_splits[kMaxGroup] = {};
     lora_stats stats{};
+    // kernel timing (lora_profile_begin / lora_profile_end)
+    bool profiling = false;
+    std::vector<LaunchTiming> prof_events;
+    std::vector<int> prof_kind;
+    size_t prof_used = 0, prof_cap = 0;
+    int64_t prof_untimed = 0;
     std::string last_error;
     std::vector<void *> allocations;
 };
@@ -185,6 +193,11 @@ int check_source(const void *p)
 
 void free_all(lora_ctx *c)
 {
+    for (auto &t : c->prof_events) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    c->prof_events.clear();
     for (void *p : c->allocations)
         (void)hipFree(p);
     c->allocations.clear();
@@ -230,6 +243,21 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
+enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2 };
+
+// Events for the next dispatch while profiling (none once the reserve is used up).
+LaunchTiming next_timing(lora_ctx *c, int kind)
+{
+    if (!c->profiling)
+        return LaunchTiming{};
+    if (c->prof_used >= c->prof_cap) {
+        c->prof_untimed += 1;
+        return LaunchTiming{};
+    }
+    c->prof_kind[c->prof_used] = kind;
+    return c->prof_events[c->prof_used++];
+}
+
 SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
 {
     SlotMeta m;
@@ -249,13 +277,19 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
 
 int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
 {
-    if (T > 0) {
+    c->plan_inline = c->dtype == LORA_BF16 && T <= kInlinePlanTokens;
+    if (T > 0 && !c->plan_inline) {
         int rc = before_launch(c, s);
         if (rc)
             return rc;
-        HIP_TRY(c, launch_plan(idx, T, c->S, c->plan, s));
-        c->stats.plans += 1;
+        LaunchTiming t[2];
+        t[0] = next_timing(c, PROF_PLAN);
+        if (T > 1024)
+            t[1] = next_timing(c, PROF_PLAN);
+        HIP_TRY(c, launch_plan(idx, T, c->S, c->plan, s, t));
     }
+    if (T > 0)
+        c->stats.plans += 1;
     c->stats.tokens += T;
     c->plan_valid = true;
     c->plan_idx = idx;
@@ -289,19 +323,24 @@ int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x,
             a.grid_splits = std::max(a.grid_splits, splits);
             c->last_splits[i] = splits;
         }
-        a.tiles = c->plan.tiles;
-        a.tile_tok = c->plan.tile_tok;
-        a.n_tiles = c->plan.n_tiles;
+        a.plan = c->plan;
+        a.idx = c->plan_idx;
+        a.T = T;
+        a.S = c->S;
+        a.inline_plan = c->plan_inline ? 1 : 0;
         a.hpart = c->hpart;
         a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
         a.split_stride = (int64_t)T * c->R_pad;
         a.R_pad = c->R_pad;
         a.grid_tiles = max_tiles_for(T, c->S);
         a.mixed = T > 1024;
-        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s));
+        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
+                                 next_timing(c, PROF_SHRINK)));
+        c->plan_inline = false;   // later shrinks read the plan this launch published
         c->stats.shrinks += n;
     }
     c->last_n = n;
+    c->shrink_epoch = c->slot_epoch;
     for (int i = 0; i < n; ++i)
         c->last_modules[i] = modules[i];
     return LORA_OK;
@@ -336,7 +375,8 @@ int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipSt
         a.split_stride = (int64_t)T * c->R_pad;
         a.R_pad = c->R_pad;
         a.grid_tiles = max_tiles_for(T, c->S);
-        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s));
+        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
+                                 next_timing(c, PROF_EXPAND)));
         c->stats.expands += n;
     }
     return LORA_OK;
@@ -567,6 +607,7 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
         ctx->rank_host[(size_t)m * ctx->S + slot] = A_t[m] ? r : 0;
     ctx->slot_rank[slot] = r;
     ctx->scale_host[slot] = s;
+    ctx->slot_epoch += 1;
     ctx->stats.loads += 1;
     ctx->stats.bytes_loaded += bytes;
     return LORA_OK;
@@ -584,6 +625,7 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot)
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
     ctx->slot_rank[slot] = 0;
+    ctx->slot_epoch += 1;
     ctx->stats.clears += 1;
     return LORA_OK;
 }
@@ -654,6 +696,9 @@ int lora_expand_group(lora_ctx *ctx, int32_t n, const int32_t *modules, void *co
     if (!same)
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
                     "lora_expand must follow lora_shrink of the same module list");
+    if (ctx->shrink_epoch != ctx->slot_epoch)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                    "a slot was loaded or cleared between lora_shrink and lora_expand");
     if (ctx->plan_T > 0 && (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
         return rc;
     DeviceGuard guard(ctx->device);
@@ -724,6 +769,52 @@ int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)
     HIP_TRY(ctx, hipMemcpy(flags, ctx->plan.flags, sizeof(uint32_t), hipMemcpyDeviceToHost));
     HIP_TRY(ctx, hipMemset(ctx->plan.flags, 0, sizeof(uint32_t)));
     HIP_TRY(ctx, hipDeviceSynchronize());
+    return LORA_OK;
+}
+
+int lora_profile_begin(lora_ctx *ctx, int32_t max_launches)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (max_launches < 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "max_launches %d < 0", max_launches);
+    DeviceGuard guard(ctx->device);
+    while ((int32_t)ctx->prof_events.size() < max_launches) {
+        LaunchTiming t;
+        HIP_TRY(ctx, hipEventCreate(&t.start));
+        if (hipEventCreate(&t.stop) != hipSuccess) {
+            (void)hipEventDestroy(t.start);
+            return fail(ctx, LORA_ERR_HIP, "hipEventCreate failed");
+        }
+        ctx->prof_events.push_back(t);
+    }
+    ctx->prof_kind.assign(ctx->prof_events.size(), 0);
+    ctx->prof_cap = (size_t)max_launches;
+    ctx->prof_used = 0;
+    ctx->prof_untimed = 0;
+    ctx->profiling = true;
+    return LORA_OK;
+}
+
+int lora_profile_end(lora_ctx *ctx, lora_profile *out)
+{
+    if (check_ctx(ctx) || !out)
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    std::memset(out, 0, sizeof *out);
+    DeviceGuard guard(ctx->device);
+    ctx->profiling = false;
+    for (size_t i = 0; i < ctx->prof_used; ++i) {
+        const LaunchTiming &t = ctx->prof_events[i];
+        HIP_TRY(ctx, hipEventSynchronize(t.stop));
+        float ms = 0.f;
+        HIP_TRY(ctx, hipEventElapsedTime(&ms, t.start, t.stop));
+        out->launches[ctx->prof_kind[i]] += 1;
+        out->total_ms[ctx->prof_kind[i]] += ms;
+    }
+    out->untimed = ctx->prof_untimed;
+    ctx->prof_used = 0;
     return LORA_OK;
 }
 

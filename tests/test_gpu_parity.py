@@ -386,3 +386,27 @@ def test_group_of_eight_modules(T):
     for i, m in enumerate(mods):
         check_close(from_dev(ys[i], wl.dtype), run_oracle(wl, m.name), wl.dtype, m.name)
     S.close()
+
+
+def test_profile_times_every_dispatch():
+    wl = synth.random_case(18, synth.BF16, [synth.Module("a", 512, 512), synth.Module("b", 512, 256)],
+                           200, 4, 16, [16, 8, 4, 16])
+    S = make_slots(wl)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in wl.modules]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in wl.modules]
+    S.profile_begin(16)
+    for _ in range(3):
+        S.prepare(idx)
+        S.shrink_group([0, 1], xs)
+        S.expand_group([0, 1], ys)
+    p = S.profile_end()
+    assert p["launches"]["shrink"] == 3 and p["launches"]["expand"] == 3
+    assert p["launches"]["plan"] == 0                     # planned inside the shrink
+    assert p["total_ms"]["shrink"] > 0 and p["total_ms"]["expand"] > 0 and p["untimed"] == 0
+    S.profile_begin(2)
+    S.apply(xs[0], ys[0], idx, 0)
+    S.apply(xs[0], ys[0], idx, 0)
+    p = S.profile_end()
+    assert p["launches"]["shrink"] + p["launches"]["expand"] == 2 and p["untimed"] == 2
+    S.close()
