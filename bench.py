@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="llama7b_decode",
-                   choices=["llama7b_decode", "qwen32b_decode", "llama7b_prefill"])
+                   choices=["llama7b_decode", "qwen32b_decode", "llama7b_prefill", "churn"])
+    p.add_argument("--churn-steps", type=int, default=50)
     p.add_argument("--layer-bytes", type=float, default=1.2e9,
                    help="minimum footprint of the rotated layer sets (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,6 +124,9 @@ def main():
 
     from lora_adapter_application_amd import binding, synth
     binding.load_library()
+    if args.workload == "churn":
+        churn(args)
+        return
     dev = torch.device("cuda:0")
     wl = workload(args.workload)
     T = wl.n_tokens
@@ -273,6 +277,83 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    slots.close()
+
+
+def churn(args):
+    """Mixed batches with slot churn: 128 slots, a 200-adapter pinned host pool,
+    host LRU residency, misses loaded with lora_slot_load before each step (the
+    "CPU hit = H2D upload" tier), then the five modules applied in three groups.
+    Cold start: step 0 loads 128 adapters."""
+    import torch
+    from lora_adapter_application_amd import binding, synth
+    from lora_adapter_application_amd.lru import SlotLRU
+    mods = synth.CHURN_MODULES
+    names = [m.name for m in mods]
+    groups = [["q_proj", "v_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+    pool = synth.churn_pool_device()
+    slots = binding.Slots(128, 64, [(m.d_in, m.d_out) for m in mods], "bf16", max_tokens=8192)
+    lru = SlotLRU(128)
+    t_load = t_apply = 0.0
+    t_load_warm = t_apply_warm = 0.0
+    tokens = tokens_warm = 0
+    redraws = 0
+    per_miss = []
+    for step in range(args.churn_steps):
+        ids, rd, x, y = synth.churn_step_device(step)
+        redraws += rd
+        slot_idx, loads = lru.plan_step(ids)
+        idx = torch.from_numpy(slot_idx).cuda()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for slot, a in loads:
+            slots.load(slot, [pool.At[n][a] for n in names], [pool.B[n][a] for n in names], 64, 128.0)
+        slots.sync_loads()
+        t1 = time.perf_counter()
+        slots.prepare(idx)
+        for g in groups:
+            mi = [names.index(n) for n in g]
+            slots.shrink_group(mi, [x[n] for n in g])
+            slots.expand_group(mi, [y[n] for n in g])
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        t_load += t1 - t0
+        t_apply += t2 - t1
+        tokens += ids.shape[0]
+        if loads:
+            per_miss.append((t1 - t0) / len(loads))
+        if step > 0:
+            t_load_warm += t1 - t0
+            t_apply_warm += t2 - t1
+            tokens_warm += ids.shape[0]
+        del x, y
+    st = lru.stats
+    bytes_loaded = slots.stats()["bytes_loaded"]
+    out = {
+        "metric": "multi-LoRA tokens/s",
+        "value": round(tokens / (t_load + t_apply), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.churn_steps, "warmup": 0,
+        "ms_per_step": round((t_load + t_apply) / args.churn_steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "churn", "tokens_per_step": 8192,
+                   "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
+                   "groups": groups, "max_loras": 128, "max_rank": 64, "pool_adapters": 200,
+                   "zipf": 0.9, "cold_start": True, "parallelism": "none (1 GPU)"},
+        "apply_only_tokens_per_s": round(tokens / t_apply, 1),
+        "steady_state": {"steps": args.churn_steps - 1,
+                         "load_plus_apply_tokens_per_s": round(tokens_warm / (t_load_warm + t_apply_warm), 1),
+                         "apply_only_tokens_per_s": round(tokens_warm / t_apply_warm, 1),
+                         "ms_per_step": round((t_load_warm + t_apply_warm) / (args.churn_steps - 1) * 1e3, 4)},
+        "h2d": {"bytes": bytes_loaded, "seconds": round(t_load, 6),
+                "GBps": round(bytes_loaded / t_load / 1e9, 2) if t_load else None,
+                "adapter_h2d_seconds_mean": round(float(np.mean(per_miss)), 7) if per_miss else None,
+                "bytes_per_adapter": bytes_loaded // max(st.misses, 1)},
+        "lru": {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
+                "reloads_after_eviction": st.reloads_after_eviction,
+                "thrash_ratio": round(st.thrash_ratio, 4), "capped_redraws": redraws},
     }
     print(json.dumps(out), flush=True)
     slots.close()

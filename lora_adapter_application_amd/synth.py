@@ -218,23 +218,6 @@ def qwen32b_decode(seed: Optional[int] = None, n_tokens: int = 512, y_zero: bool
 # ----------------------------------------------------------------------------
 # churn workload: a pool of adapters in host memory and a stream of steps
 
-@dataclass
-class ChurnStep:
-    adapter_ids: np.ndarray        # int32 [T]: pool adapter id per token
-    x: Dict[str, np.ndarray]
-    y: Dict[str, np.ndarray]
-    redraws: int                   # decode draws redrawn to respect the per-step cap
-
-
-def churn_pool(n_adapters: int = 200, rank: int = 64, modules=None, seed: Optional[int] = None
-               ) -> List[Adapter]:
-    mods = list(modules) if modules is not None else list(CHURN_MODULES)
-    base = SEEDS["churn"] if seed is None else seed
-    r_a, r_b = _children(base * 7919 + 1, 2)
-    return _make_adapters(r_a, r_b, mods, [rank] * n_adapters, [2.0 * rank] * n_adapters,
-                          False, "uniform", 0.01, BF16)
-
-
 def churn_adapter_ids(rng: np.random.Generator, n_adapters: int = 200, s: float = 0.9,
                       n_prefill: int = 8, prefill_len: int = 128, n_decode: int = 7168,
                       cap: int = 128):
@@ -254,18 +237,6 @@ def churn_adapter_ids(rng: np.random.Generator, n_adapters: int = 200, s: float 
         dec[i] = a
     ids = np.concatenate([np.repeat(pre, prefill_len), dec]).astype(np.int32)
     return ids, redraws
-
-
-def churn_step(step: int, modules=None, seed: Optional[int] = None, n_adapters: int = 200,
-               n_prefill: int = 8, prefill_len: int = 128, n_decode: int = 7168,
-               cap: int = 128) -> ChurnStep:
-    mods = list(modules) if modules is not None else list(CHURN_MODULES)
-    base = SEEDS["churn"] if seed is None else seed
-    r_i, r_x, r_y = [np.random.default_rng(c) for c in
-                     np.random.SeedSequence([base, step]).spawn(3)]
-    ids, redraws = churn_adapter_ids(r_i, n_adapters, 0.9, n_prefill, prefill_len, n_decode, cap)
-    x, y = _activations(r_x, r_y, mods, int(ids.shape[0]), BF16)
-    return ChurnStep(ids, x, y, redraws)
 
 
 # ----------------------------------------------------------------------------
@@ -322,3 +293,67 @@ def oracle_adapters(wl: Workload, module: str, adapters=None):
             out.append({"r": ad.r, "lora_alpha": ad.lora_alpha, "use_rslora": ad.use_rslora,
                         "At": ad.At[module], "B": ad.B[module]})
     return out
+
+
+# ----------------------------------------------------------------------------
+# churn workload drawn on the device (the pool is 1.6 GB; numpy would take minutes)
+
+@dataclass
+class DevicePool:
+    """Adapter pool in pinned host memory: At[name] is [n][r][d_in], B[name] [n][r][d_out] (bf16)."""
+    r: int
+    lora_alpha: float
+    At: Dict[str, "object"]
+    B: Dict[str, "object"]
+
+    def adapter(self, module: str, a: int) -> dict:
+        """The oracle's record for adapter a on one module (views of the pinned pool)."""
+        import torch
+        At = self.At[module][a].view(torch.int16).numpy().view(np.uint16)
+        B = self.B[module][a].view(torch.int16).numpy().view(np.uint16)
+        return {"r": self.r, "lora_alpha": self.lora_alpha, "use_rslora": False, "At": At, "B": B}
+
+
+def _dev_gen(seed: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) % (2 ** 63))
+    return g
+
+
+def churn_pool_device(n_adapters: int = 200, rank: int = 64, modules=None, seed: Optional[int] = None,
+                      device="cuda") -> DevicePool:
+    """A^T ~ U(+-1/sqrt(d_in)) and B ~ N(0, 0.01), drawn with a seeded torch generator on
+    the device, rounded to bf16 (torch), copied to pinned host memory."""
+    import torch
+    mods = list(modules) if modules is not None else list(CHURN_MODULES)
+    base = SEEDS["churn"] if seed is None else seed
+    g = _dev_gen(base * 7919 + 11, device)
+    At, B = {}, {}
+    for m in mods:
+        a = torch.empty((n_adapters, rank, m.d_in), dtype=torch.bfloat16, pin_memory=True)
+        b = torch.empty((n_adapters, rank, m.d_out), dtype=torch.bfloat16, pin_memory=True)
+        bound = 1.0 / np.sqrt(m.d_in)
+        a.copy_(((torch.rand((n_adapters, rank, m.d_in), generator=g, device=device) * 2 - 1)
+                 * bound).to(torch.bfloat16))
+        b.copy_((torch.randn((n_adapters, rank, m.d_out), generator=g, device=device) * 0.01)
+                .to(torch.bfloat16))
+        At[m.name], B[m.name] = a, b
+    return DevicePool(rank, 2.0 * rank, At, B)
+
+
+def churn_step_device(step: int, modules=None, seed: Optional[int] = None, n_adapters: int = 200,
+                      n_prefill: int = 8, prefill_len: int = 128, n_decode: int = 7168,
+                      cap: int = 128, device="cuda"):
+    """One churn step: adapter id per token (numpy), redraw count, and x, y per module
+    as device bf16 tensors drawn with a seeded torch generator (N(0, 1))."""
+    import torch
+    mods = list(modules) if modules is not None else list(CHURN_MODULES)
+    base = SEEDS["churn"] if seed is None else seed
+    r_i = np.random.default_rng(np.random.SeedSequence([base, step]))
+    ids, redraws = churn_adapter_ids(r_i, n_adapters, 0.9, n_prefill, prefill_len, n_decode, cap)
+    g = _dev_gen(base * 1000003 + step, device)
+    T = int(ids.shape[0])
+    x = {m.name: torch.randn((T, m.d_in), generator=g, device=device).to(torch.bfloat16) for m in mods}
+    y = {m.name: torch.randn((T, m.d_out), generator=g, device=device).to(torch.bfloat16) for m in mods}
+    return ids, redraws, x, y

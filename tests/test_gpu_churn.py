@@ -1,0 +1,76 @@
+"""The churn workload on the GPU: 128 slots, a 200-adapter pinned pool, LRU
+residency, loads before every step, and parity on every step.
+
+The oracle takes each sampled token's *adapter id* and reads the host pool
+directly, so a wrong slot mapping, a stale slot or a load that landed in the
+wrong place fails the comparison."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import as_f64, log
+from lora_adapter_application_amd import binding, synth
+from lora_adapter_application_amd.lru import SlotLRU
+
+pytestmark = pytest.mark.gpu
+
+GROUPS = [["q_proj", "v_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+N_STEPS = 50
+
+
+def bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def pool():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+    return synth.churn_pool_device()
+
+
+def test_churn_all_steps_match_oracle(pool):
+    mods = synth.CHURN_MODULES
+    names = [m.name for m in mods]
+    S = binding.Slots(128, 64, [(m.d_in, m.d_out) for m in mods], "bf16", max_tokens=8192)
+    lru = SlotLRU(128)
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for step in range(N_STEPS):
+        ids, redraws, x, y = synth.churn_step_device(step)
+        slots, loads = lru.plan_step(ids)
+        assert len(np.unique(ids)) <= 128
+        for slot, a in loads:
+            S.load(slot, [pool.At[n][a] for n in names], [pool.B[n][a] for n in names], 64, 128.0)
+        T = ids.shape[0]
+        rows = np.unique(np.concatenate([[0, 1023, 1024, T - 1], rng.integers(0, T, 20)]))
+        rows_t = torch.from_numpy(rows).cuda()
+        y0 = {n: bits(y[n][rows_t]) for n in names}
+        idx = torch.from_numpy(slots).cuda()
+        S.prepare(idx)
+        for g in GROUPS:
+            mi = [names.index(n) for n in g]
+            S.shrink_group(mi, [x[n] for n in g])
+            S.expand_group(mi, [y[n] for n in g])
+        torch.cuda.synchronize()
+        for n in names:
+            adapters = [None] * 200
+            for a in np.unique(ids[rows]):
+                adapters[int(a)] = pool.adapter(n, int(a))
+            ref = oracle.apply(oracle.BF16, bits(x[n][rows_t]), y0[n], ids[rows], adapters)
+            got = bits(y[n][rows_t])
+            g64, r64 = as_f64(got, synth.BF16), as_f64(ref, synth.BF16)
+            w = float((np.abs(g64 - r64) / (2e-2 * (1 + np.abs(r64)))).max())
+            worst = max(worst, w)
+            assert w <= 1.0, f"step {step} {n}: err/bound {w:.3f}"
+        if step % 10 == 0:
+            log(f"churn step {step}: {len(loads)} loads, redraws {redraws}, worst {worst:.3f}")
+    st = lru.stats
+    log(f"churn: hits {st.hits} misses {st.misses} evictions {st.evictions} "
+        f"thrash {st.thrash_ratio:.3f} worst err/bound {worst:.3f}")
+    assert S.stats()["loads"] == st.misses
+    assert S.stats()["bytes_loaded"] == st.misses * oracle.adapter_bytes(
+        [(m.d_in, m.d_out) for m in mods], [True] * 5, 64, 2)
+    S.close()

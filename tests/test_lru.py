@@ -1,0 +1,65 @@
+"""The host-side slot residency driver, against hand-worked sequences."""
+import numpy as np
+import pytest
+
+from lora_adapter_application_amd import synth
+from lora_adapter_application_amd.lru import SlotLRU
+
+
+def test_cold_start_fills_slots_in_first_appearance_order():
+    lru = SlotLRU(4)
+    slots, loads = lru.plan_step(np.array([7, 3, 7, -1, 9]))
+    assert loads == [(0, 7), (1, 3), (2, 9)]
+    assert list(slots) == [0, 1, 0, -1, 2]
+    assert (lru.stats.hits, lru.stats.misses, lru.stats.evictions) == (0, 3, 0)
+
+
+def test_hit_touches_and_lru_victim_excludes_the_steps_own_adapters():
+    lru = SlotLRU(3)
+    lru.plan_step(np.array([1, 2, 3]))          # slots 0,1,2 <- 1,2,3 ; use order 1,2,3
+    lru.plan_step(np.array([1]))                # hit 1: now 2 is least recently used
+    slots, loads = lru.plan_step(np.array([4, 2]))
+    # 2 is a hit in this step, so it is protected although it is the LRU entry;
+    # the victim is 3 (slot 2), the least recently used slot the step does not use
+    assert loads == [(2, 4)]
+    assert list(slots) == [2, 1]
+    assert lru.resident() == {1: 0, 2: 1, 4: 2}
+    assert lru.stats.evictions == 1 and lru.stats.hits == 2
+
+
+def test_misses_in_one_step_never_evict_each_other():
+    lru = SlotLRU(2)
+    lru.plan_step(np.array([1, 2]))
+    slots, loads = lru.plan_step(np.array([3, 4]))
+    assert sorted(s for s, _ in loads) == [0, 1]
+    assert set(lru.resident()) == {3, 4}
+    assert lru.stats.evictions == 2
+
+
+def test_too_many_adapters_for_the_slots_is_refused():
+    lru = SlotLRU(2)
+    with pytest.raises(ValueError):
+        lru.plan_step(np.array([1, 2, 3]))
+
+
+def test_thrash_ratio_counts_quick_reloads():
+    lru = SlotLRU(1, thrash_window=2)
+    for a in (1, 2, 1, 2):
+        lru.plan_step(np.array([a]))
+    # evictions: 1 (step1), 2 (step2), 1 (step3); reloads within 2 steps: 1 at step2, 2 at step3
+    assert lru.stats.evictions == 3
+    assert lru.stats.reloads_after_eviction == 2
+    assert abs(lru.stats.thrash_ratio - 2 / 3) < 1e-12
+
+
+def test_churn_steps_respect_cap_and_mapping():
+    rng = np.random.default_rng(3)
+    lru = SlotLRU(128)
+    for _ in range(6):
+        ids, _ = synth.churn_adapter_ids(rng)
+        slots, loads = lru.plan_step(ids)
+        # every token maps to the slot that holds its adapter
+        res = lru.resident()
+        assert np.array_equal(slots, np.array([res[int(a)] for a in ids], dtype=np.int32))
+        assert len(set(res.values())) == len(res) <= 128
+    assert lru.stats.misses >= 128 and lru.stats.hits > 0
