@@ -4,10 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_decode]
 
 One step is one pass of the whole hot path over one batch: the device plan
-(lora_plan_prepare) and, for every module of the workload's layer, lora_shrink
-then lora_expand.  Steps rotate over L "layer sets" (each with its own adapter
-weights, x and y, like the layers of a model) so that the bytes the kernels read
-come from HBM rather than from the 256 MB Infinity Cache.  Inputs are resident
+(lora_plan_prepare) and, for every group of modules of the workload's layer,
+lora_apply_group, which runs the group's shrink and expand in one launch.
+Steps rotate over L "layer sets" (each with its own adapter weights, x and y,
+like the layers of a model) so that the bytes the kernels read come from HBM
+rather than from the 256 MB Infinity Cache.  Inputs are resident
 in HBM before timing starts.  Prints one JSON line.
 
 value      tokens of the batch (skipped tokens included) x K / wall time of K steps
@@ -185,8 +186,7 @@ def main():
         slots.prepare(idx)
         for g in groups:
             mis = [l * nm + j for j in g]
-            slots.shrink_group(mis, [xs[mi] for mi in mis])
-            slots.expand_group(mis, [ys[mi] for mi in mis])
+            slots.apply_group(mis, [xs[mi] for mi in mis], [ys[mi] for mi in mis], idx)
 
     for i in range(args.warmup):
         step(i)
@@ -222,25 +222,29 @@ def main():
         # algorithmic bytes of one launch of each group
         shrink_bytes = [sum(b * mods[j].d_in * (T_act + sum_r) for j in g) for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
+        group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes,
+                       "apply": [s_ + e_ for s_, e_ in zip(shrink_bytes, expand_bytes)]}
         flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
                  for m in mods]
+
         def avg_us(kind):
             return tot[kind] / n[kind] * 1e3 if n[kind] else None
         kernels = {
             "groups": [[names[j] for j in g] for g in groups],
             "timed_dispatches": n, "untimed_dispatches": prof["untimed"],
             "plan": {"avg_us": avg_us("plan"), "per_step_us": tot["plan"] / K * 1e3},
-            "lora_shrink": {"avg_us": avg_us("shrink"), "per_step_us": tot["shrink"] / K * 1e3,
-                            "alg_bytes_per_step": float(sum(shrink_bytes)),
-                            "GBps": float(sum(shrink_bytes) * K / (tot["shrink"] * 1e-3) / 1e9)},
-            "lora_expand": {"avg_us": avg_us("expand"), "per_step_us": tot["expand"] / K * 1e3,
-                            "alg_bytes_per_step": float(sum(expand_bytes)),
-                            "GBps": float(sum(expand_bytes) * K / (tot["expand"] * 1e-3) / 1e9)},
             "step_alg_bytes": float(sum(shrink_bytes) + sum(expand_bytes)),
             "step_alg_flops": float(sum(flops)),
         }
-        dom = "expand" if tot["expand"] >= tot["shrink"] else "shrink"
-        dom_bytes = expand_bytes if dom == "expand" else shrink_bytes
+        for kind in ("shrink", "expand", "apply"):
+            if n[kind]:
+                step_bytes = float(sum(group_bytes[kind]))
+                kernels["lora_" + kind] = {
+                    "avg_us": avg_us(kind), "per_step_us": tot[kind] / K * 1e3,
+                    "alg_bytes_per_step": step_bytes,
+                    "GBps": float(step_bytes * K / (tot[kind] * 1e-3) / 1e9)}
+        dom = max(("shrink", "expand", "apply"), key=lambda k: tot[k])
+        dom_bytes = group_bytes[dom]
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
         kname = "lora_" + dom
         traffic = traffic_from_profiles(kname, wl.name)

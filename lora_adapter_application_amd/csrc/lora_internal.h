@@ -46,8 +46,12 @@ struct PlanBuffers {
     int32_t *chunk_counts;  // [ceil(max_tokens/1024)][S], batches above 1024 tokens
 };
 
-// Batches up to this many tokens are planned inside the bf16 shrink kernel.
+// Batches up to this many tokens are planned inside the bf16 kernels.
 constexpr int kInlinePlanTokens = 1024;
+// How a bf16 launch finds its tiles: kPlanTiles reads the tiles a plan kernel
+// or an earlier launch published; kPlanInline derives each workgroup's tile in
+// the kernel (batches of at most kInlinePlanTokens) and publishes it.
+enum PlanMode { kPlanTiles = 0, kPlanInline = 1 };
 // Modules one grouped shrink / expand launch covers (blockIdx.z = member).
 constexpr int kMaxGroup = 8;
 
@@ -87,7 +91,7 @@ struct ShrinkArgs {
     const int32_t *idx;                 // token slot index (inline plan)
     int32_t T;
     int32_t S;
-    int32_t inline_plan;                // batch of <= kInlinePlanTokens: plan computed in the shrink
+    int32_t plan_mode;                  // PlanMode
     float *hpart;                       // [member][split][T][R_pad]
     int64_t member_stride;              // elements
     int64_t split_stride;               // T * R_pad
@@ -114,6 +118,23 @@ struct ExpandArgs {
     int32_t grid_tiles;
     int32_t grid_cols;                  // max column chunks over the members
 };
+
+// Shrink and expand of a bf16 batch in one launch (apply_bf16_kernel):
+// workgroups take tickets in the order they start, the first n_shrink do shrink
+// parts, the rest expand parts, which wait on per (member, tile) arrival counts.
+struct ChainArgs {
+    uint32_t *sync;         // [2][sync_words]: per parity, the ticket counter, then
+                            // arrivals [kMaxGroup][tiles_stride]
+    int32_t sync_words;     // 1 + kMaxGroup * tiles_stride
+    int32_t tiles_stride;   // tiles of the largest batch (max_tiles)
+    int32_t parity;         // counter set of this launch; the launch zeroes the other
+    int32_t n_shrink;       // grid_tiles * grid_splits * n
+    int32_t spin_limit;     // polls before an expand part gives up
+    uint32_t *flags;
+};
+
+hipError_t launch_apply(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
+                        const SlotMeta &m, hipStream_t st, const LaunchTiming &t);
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);

@@ -358,11 +358,13 @@ struct ShrinkView {
     int R_pad;
 };
 
-// Gather path (BGMV): waves split the tile's subtiles and the K range.  Per
-// step a lane loads 64 contiguous bytes of its token's x row and of its rank's
-// A^T row and feeds them to 4 MFMAs; both operands use the same K order, so the
-// sum is the plain dot product over that K block.  tokv: lane l of every wave
-// holds the token of tile row l.
+// Gather path (BGMV): waves split the tile's subtiles and the K range.  A K
+// block is 128 elements; MFMA step q of a block takes elements 32q .. 32q+31,
+// lane group g holding 8g .. 8g+7 of them, so the four lanes of a row read 64
+// contiguous bytes per instruction, of the token's x row and of the rank's A^T
+// row alike.  A K chunk past the split's end is zero; a row beyond the tile
+// reads token 0's row (it only reaches h rows that are not stored).  tokv:
+// lane l of every wave holds the token of tile row l.
 template <int NB>
 struct KBlock {
     uint4 x[4];
@@ -371,22 +373,20 @@ struct KBlock {
 
 template <int NB>
 __device__ __forceinline__ void load_kblock(KBlock<NB> &blk, const uint16_t *xrow,
-                                            const uint16_t *arow0, int64_t d_in, int kk, int k1,
-                                            int nb, bool tok_ok)
+                                            const uint16_t *arow0, int64_t d_in, int kb, int k1, int nb)
 {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ke = kk + q * 8;
-            blk.a[b][q] = (b < nb && ke < k1) ? ld16(arow0 + b * 16 * d_in + ke)
-                                               : make_uint4(0, 0, 0, 0);
-        }
-    }
+    const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int ke = kk + q * 8;
-        blk.x[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
+#ifdef LORA_KORDER_PER_LANE
+        const int ke = kb + g * 32 + q * 8;
+#else
+        const int ke = kb + q * 32 + g * 8;
+#endif
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            blk.a[b][q] = (b < nb && ke < k1) ? ld16(arow0 + b * 16 * d_in + ke) : make_uint4(0, 0, 0, 0);
+        blk.x[q] = ke < k1 ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -409,7 +409,8 @@ template <int NB, bool DOUBLE_BUFFER>
 __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
                                             unsigned char *smem)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane & 15, g = lane >> 4;
     const int nsub = (tile.len + 15) >> 4;
     const int nsub_pad = nsub == 3 ? 4 : nsub;
@@ -427,23 +428,25 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
     for (int b = 0; b < NB; ++b)
         acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (wave_on) {
+        // this wave's K blocks: k0 + kp*128, then every kparts*128
         const int kstep = kparts * kShrinkKBlock;
-        int kb = v.k0 + kp * kShrinkKBlock;
+        const int kb0 = v.k0 + kp * kShrinkKBlock;
+        const int nblk = kb0 < v.k1 ? (v.k1 - kb0 + kstep - 1) / kstep : 0;
         if (DOUBLE_BUFFER) {
-            KBlock<NB> cur, nxt;
-            if (kb < v.k1)
-                load_kblock<NB>(cur, xrow, arow0, v.d_in, kb + g * 32, v.k1, nb, tok_ok);
-            for (; kb < v.k1; kb += kstep) {
-                const int kn = kb + kstep;
-                if (kn < v.k1)
-                    load_kblock<NB>(nxt, xrow, arow0, v.d_in, kn + g * 32, v.k1, nb, tok_ok);
-                mfma_kblock<NB>(acc, cur, nb);
-                cur = nxt;
+            // two K blocks in flight per round
+            for (int i = 0; i < nblk; i += 2) {
+                KBlock<NB> b0, b1;
+                load_kblock<NB>(b0, xrow, arow0, v.d_in, kb0 + i * kstep, v.k1, nb);
+                if (i + 1 < nblk)
+                    load_kblock<NB>(b1, xrow, arow0, v.d_in, kb0 + (i + 1) * kstep, v.k1, nb);
+                mfma_kblock<NB>(acc, b0, nb);
+                if (i + 1 < nblk)
+                    mfma_kblock<NB>(acc, b1, nb);
             }
         } else {
-            for (; kb < v.k1; kb += kstep) {
+            for (int i = 0; i < nblk; ++i) {
                 KBlock<NB> cur;
-                load_kblock<NB>(cur, xrow, arow0, v.d_in, kb + g * 32, v.k1, nb, tok_ok);
+                load_kblock<NB>(cur, xrow, arow0, v.d_in, kb0 + i * kstep, v.k1, nb);
                 mfma_kblock<NB>(acc, cur, nb);
             }
         }
@@ -573,118 +576,210 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &til
     }
 }
 
-// Inline plan (batches of at most kInlinePlanTokens): every workgroup of the
-// shrink groups the batch's tokens by slot in LDS, the same stable counting sort
-// the plan kernels run, and picks its own tile; workgroups with blockIdx.y == 0
-// and blockIdx.z == 0 publish their tile (and workgroup 0 the totals) for the
-// expand.  Returns false for workgroups past the last tile.
-struct InlinePlanLds {
-    int32_t wcnt[16][LORA_MAX_SLOTS];   // per (256-token chunk, wave): count, then offset
-    int32_t base[LORA_MAX_SLOTS];       // first position of slot s
-    int32_t tbase[LORA_MAX_SLOTS];      // first tile of slot s
-    int32_t cnt[LORA_MAX_SLOTS];
-    int32_t perm[kInlinePlanTokens];    // token at each slot-sorted position
-    int2 wsum[5];
-    int32_t my_slot;
+// Inline plan (batches of at most kInlinePlanTokens tokens): every workgroup
+// derives its own tile of the stable slot-sorted plan the plan kernels make,
+// without sorting the batch: per-slot token counts (an LDS histogram), per-slot
+// tile and position offsets (one wave scans them), then the sorted positions of
+// its own slot's tokens (one ballot per 64 tokens, in token order).  One
+// workgroup per tile publishes it, and one workgroup the totals, so that later
+// launches on the same plan can read them.
+struct TilePlanLds {
+    int32_t cnt[LORA_MAX_SLOTS];                 // tokens per slot
+    int32_t wc[kInlinePlanTokens / 64];          // tokens of the tile's slot per 64 tokens
+    int32_t list[kTileTokens];                   // token ids of the tile
+    int32_t slot, j, start, count, n_tiles, ticket;
 };
 
-__device__ bool inline_plan(const ShrinkArgs &a, const SlotMeta &meta, InlinePlanLds &L,
-                            Tile &tile, int &tokv)
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Tile index of a workgroup of a grid with one workgroup per tile along x.
+struct BlockTile {
+    __device__ int operator()(const TilePlanLds &) const { return (int)blockIdx.x; }
+};
+
+// b_of(L) gives the tile index; it is called once, after the first barrier, so
+// a caller can derive it from a value one lane stored in L.ticket
+// (ticket_val >= 0: lane 0 stores it before that barrier).  publish: write the
+// tile and its token ids to the plan buffers; first: write the totals and the
+// flag.  Returns false past the last tile.
+template <typename TileIndex>
+__device__ bool plan_tile(const int32_t *idx, int T, int S, const SlotMeta &meta,
+                          const PlanBuffers &pb, TilePlanLds &L, TileIndex b_of, int ticket_val,
+                          bool publish, bool first, Tile &tile, int &tokv)
 {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int T = a.T, S = a.S;
-    int v[4];
+    constexpr int NC = kInlinePlanTokens / 256;   // tokens per thread
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int v[NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int i = c * 256 + tid;
-        v[c] = i < T ? a.idx[i] : -1;
+        v[c] = i < T ? idx[i] : -1;
     }
-#pragma unroll
-    for (int w = 0; w < 16; ++w)
-        for (int sl = tid; sl < S; sl += 256)
-            L.wcnt[w][sl] = 0;
+    if (tid < S)
+        L.cnt[tid] = 0;
+    if (ticket_val >= 0 && tid == 0)
+        L.ticket = ticket_val;
     __syncthreads();
-    int myr[4];
-    bool too_large = false;
+    const int b = __builtin_amdgcn_readfirstlane(b_of(L));
+    bool big = false;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        too_large |= v[c] >= S;
-        myr[c] = wave_stable_rank_row(v[c], v[c] >= 0 && v[c] < S, L.wcnt[c * 4 + wave]);
-    }
-    __syncthreads();
-    int c_s = 0;
-    if (tid < S) {
-#pragma unroll
-        for (int w = 0; w < 16; ++w) {
-            const int k = L.wcnt[w][tid];
-            L.wcnt[w][tid] = c_s;
-            c_s += k;
-        }
-    }
-    int start = c_s, tst = (c_s + kTileTokens - 1) / kTileTokens, n_active, n_tiles;
-    const int nt = tst;
-    block_excl_scan2<4>(start, tst, L.wsum, n_active, n_tiles);
-    const int b = blockIdx.x;
-    if (tid < S) {
-        L.base[tid] = start;
-        L.tbase[tid] = tst;
-        L.cnt[tid] = c_s;
-        if (b >= tst && b < tst + nt)
-            L.my_slot = tid;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NC; ++c) {
         if (v[c] >= 0 && v[c] < S)
-            L.perm[L.base[v[c]] + L.wcnt[c * 4 + wave][v[c]] + myr[c]] = c * 256 + tid;
-    const bool first = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+            atomicAdd(&L.cnt[v[c]], 1);
+        big |= v[c] >= S;
+    }
     if (first) {
-        if (tid < S) {
-            a.plan.counts[tid] = c_s;
-            a.plan.seg_start[tid] = start;
-        }
-        if (tid == 0) {
-            *a.plan.n_tiles = n_tiles;
-            *a.plan.n_active = n_active;
-        }
-        if (too_large)
-            atomicOr(a.plan.flags, 1u);
+        const uint64_t bigm = __ballot(big);
+        if (bigm && lane == 0)
+            atomicOr(pb.flags, LORA_FLAG_SLOT_INDEX_TOO_LARGE);
     }
     __syncthreads();
-    if (b >= n_tiles)
+    if (wave == 0) {
+        // lane l takes slots 4l .. 4l+3: counts, tiles, and exclusive prefixes
+        int c4[4], n4[4], sc = 0, sn = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int sl = 4 * lane + k;
+            c4[k] = sl < S ? L.cnt[sl] : 0;
+            n4[k] = (c4[k] + kTileTokens - 1) / kTileTokens;
+            sc += c4[k];
+            sn += n4[k];
+        }
+        int ic = sc, in = sn;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int oc = __shfl_up(ic, d, 64), on = __shfl_up(in, d, 64);
+            if (lane >= d) {
+                ic += oc;
+                in += on;
+            }
+        }
+        int pc = ic - sc, pn = in - sn;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int sl = 4 * lane + k;
+            if (sl < S) {
+                if (b >= pn && b < pn + n4[k]) {
+                    L.slot = sl;
+                    L.j = b - pn;
+                    L.start = pc;
+                    L.count = c4[k];
+                }
+                if (first) {
+                    pb.counts[sl] = c4[k];
+                    pb.seg_start[sl] = pc;
+                }
+            }
+            pc += c4[k];
+            pn += n4[k];
+        }
+        if (lane == 63) {
+            L.n_tiles = in;
+            if (first) {
+                *pb.n_tiles = in;
+                *pb.n_active = ic;
+            }
+        }
+    }
+    __syncthreads();
+    if (b >= L.n_tiles)
         return false;
-    const int sl = L.my_slot;
-    const int j = b - L.tbase[sl];
+    const int sl = L.slot, j = L.j;
+    uint64_t mk[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        mk[c] = __ballot(v[c] == sl);
+        if (lane == 0)
+            L.wc[c * 4 + wave] = __popcll(mk[c]);
+    }
+    __syncthreads();
+    // window c*4 + wave holds tokens c*256 + 64*wave .. +63, so windows in index
+    // order are tokens in order
+    int pre[NC], before = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        pre[c] = 0;
+#pragma unroll
+    for (int w = 0; w < kInlinePlanTokens / 64; ++w) {
+        const int k = L.wc[w];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (w == c * 4 + wave)
+                pre[c] = before;
+        before += k;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (v[c] == sl) {
+            const int r = pre[c] - j * kTileTokens +
+                          (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk[c] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mk[c], 0u));
+            if (r >= 0 && r < kTileTokens)
+                L.list[r] = c * 256 + tid;
+        }
+    }
+    __syncthreads();
     tile.slot = sl;
-    tile.start = L.base[sl] + j * kTileTokens;
-    tile.len = min(kTileTokens, L.cnt[sl] - j * kTileTokens);
+    tile.start = L.start + j * kTileTokens;
+    tile.len = min(kTileTokens, L.count - j * kTileTokens);
     tile.rank = meta.rank[sl];
     tile.scale = meta.scale[sl];
-    tokv = lane < tile.len ? L.perm[tile.start + lane] : 0;
-    if (blockIdx.y == 0 && blockIdx.z == 0) {
+    tokv = lane < tile.len ? L.list[lane] : 0;
+    if (publish) {
         if (tid == 0)
-            a.plan.tiles[b] = tile;
+            pb.tiles[b] = tile;
         if (tid < tile.len)
-            a.plan.tile_tok[(int64_t)b * kTileTokens + tid] = L.perm[tile.start + tid];
+            pb.tile_tok[(int64_t)b * kTileTokens + tid] = L.list[tid];
     }
     return true;
 }
 
+// LDS of a shrink workgroup: K-split reduction, or the segment path's A stage.
+constexpr int shrink_smem_bytes(int NB, bool MIXED)
+{
+    return cmax(4 * NB * 64 * 16, MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0);
+}
+
+// The shrink of one tile for K split `split` of member m: writes the member's h
+// partial of that split for the tile's rows.  Requires 0 < tile.rank.
+template <int NB, bool MIXED>
+__device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int split, const Tile &tile,
+                                            int tokv, unsigned char *smem)
+{
+    const int nb = (tile.rank + 15) >> 4;
+    ShrinkView v;
+    v.d_in = a.d_in[m];
+    v.x = (const uint16_t *)a.x[m];
+    v.A = (const uint16_t *)a.A[m] + (int64_t)tile.slot * a.slot_stride_A[m];
+    v.k0 = split * a.k_chunk[m];
+    v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
+    v.h = a.hpart + m * a.member_stride + (int64_t)split * a.split_stride;
+    v.R_pad = a.R_pad;
+    if (MIXED && tile.len > 32)
+        shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
+    else
+        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
+}
+
 // MIXED: batches above 1024 tokens; tiles of 33..64 tokens take the segment
 // path, shorter ones the gather path single-buffered.  Otherwise every tile
-// takes the gather path, double-buffered when the rank allows.  INLINE: the
-// batch is planned in the kernel (see inline_plan).
-template <int NB, bool MIXED, bool INLINE>
+// takes the gather path, double-buffered when the rank allows.  PLAN: how the
+// workgroup finds its tile (PlanMode).
+template <int NB, bool MIXED, int PLAN>
 __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
 {
     const int m = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta, m);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[shrink_smem_bytes(NB, MIXED)];
     Tile tile;
     int tokv;
-    if (INLINE) {
-        __shared__ InlinePlanLds L;
-        if (!inline_plan(a, meta, L, tile, tokv))
+    if constexpr (PLAN == kPlanInline) {
+        __shared__ TilePlanLds P;
+        const bool y0z0 = blockIdx.y == 0 && blockIdx.z == 0;
+        if (!plan_tile(a.idx, a.T, a.S, meta, a.plan, P, BlockTile{}, -1, y0z0,
+                       y0z0 && blockIdx.x == 0, tile, tokv))
             return;
     } else {
         const int n_tiles = *a.plan.n_tiles;
@@ -700,25 +795,7 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
     }
     if ((int)blockIdx.y >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, tile.slot))
         return;
-    const int nb = (tile.rank + 15) >> 4;
-    ShrinkView v;
-    v.d_in = a.d_in[m];
-    v.x = (const uint16_t *)a.x[m];
-    v.A = (const uint16_t *)a.A[m] + (int64_t)tile.slot * a.slot_stride_A[m];
-    v.k0 = blockIdx.y * a.k_chunk[m];
-    v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
-    v.h = a.hpart + m * a.member_stride + (int64_t)blockIdx.y * a.split_stride;
-    v.R_pad = a.R_pad;
-
-    constexpr int kRedBytes = 4 * NB * 64 * 16;
-    constexpr int kSgmvBytes = MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0;
-    constexpr int kSmemBytes = kRedBytes > kSgmvBytes ? kRedBytes : kSgmvBytes;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
-
-    if (MIXED && tile.len > 32)
-        shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
-    else
-        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
+    shrink_tile<NB, MIXED>(a, m, blockIdx.y, tile, tokv, lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -735,47 +812,165 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
 // partials of h are summed once per workgroup and split into a bf16 high part
 // and a bf16 low part (h - high) in LDS; two MFMAs per step keep ~16 bits of h.
 
-template <int NB>
-__global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
-{
-    const int m = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const MetaRegs mr = load_meta_regs(meta, m);
-    const int n_tiles = *a.n_tiles;
-    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
-    const int tokv = a.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
-    const int d_out = a.d_out[m];
-    const int cb = blockIdx.y * kExpandCols + wave * 64;
-    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= d_out)
-        return;
-    // rank and scale of the slot as the shrink of this batch saw them
-    const int rank = tile.rank;
-    if (rank == 0 || !meta_targets(mr, tile.slot))
-        return;
-    const int nb = (rank + 15) >> 4;
-    const float s = tile.scale;
-    const int row = lane & 15, g = lane >> 4;
-    const bool cols_ok = cb < d_out;
-    const int nsub = (tile.len + 15) >> 4;
-    uint16_t *ybase = (uint16_t *)a.y[m];
+// Operand loads of the expand are unconditional: a lane whose element lies
+// outside the data reads the first element instead, and that value only reaches
+// outputs that are never stored (rank blocks >= nb are skipped, columns >= d_out
+// and rows beyond the tile are not written).  With no branch around a load the
+// compiler can count outstanding loads exactly and wait only for the ones an
+// instruction needs.
 
-    // tokens of this lane in each subtile
-    int tok[4];
-    bool tok_ok[4];
+// B operands of one wave's 64 columns cb..cb+63: lane row -> column
+// cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 4g..4g+3.
+template <int NB>
+__device__ __forceinline__ void load_b_ops(uint2 (&bop)[NB][4], const uint16_t *Bslot, int d_out,
+                                           int cb, int nb, bool cols_ok)
+{
+    const int lane = threadIdx.x & 63, row = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int t = st * 16 + row;
-        tok_ok[st] = cols_ok && t < tile.len;
-        const int tv = __shfl(tokv, t, 64);
-        tok[st] = tok_ok[st] ? tv : 0;
+    for (int kst = 0; kst < NB; ++kst) {
+        const int G = kst * 2 + (g >> 1);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
+            const bool ok = kst < nb && cols_ok && n < d_out;
+            bop[kst][b] = *(const uint2 *)(Bslot + (ok ? ((int64_t)G * d_out + n) * 8 + (g & 1) * 4 : 0));
+        }
     }
-    // h partials of the tile: thread tid owns quads e = tid + 256 i (i < NB) of
-    // the len x nb*16 block
+}
+
+// y of one wave: 16 adjacent columns cb + 16g.. of one token per lane and subtile.
+template <int NSUB>
+__device__ __forceinline__ void load_y(uint4 (&yv)[NSUB][2], const uint16_t *ybase, int d_out,
+                                       int cb, const int (&tok)[NSUB], const bool (&tok_ok)[NSUB])
+{
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+            const int col = cb + g * 16 + piece * 8;
+            const bool ok = tok_ok[st] && col < d_out;
+            yv[st][piece] = *(const uint4 *)(ybase + (ok ? (int64_t)tok[st] * d_out + col : 0));
+        }
+    }
+}
+
+// Four h values to packed bf16 high halves and bf16 low halves (h - high).
+__device__ __forceinline__ void split_hi_lo(const f32x4_t h, uint2 &hi, uint2 &lo)
+{
+    const uint32_t hi01 = pack_bf16x2(h[0], h[1]), hi23 = pack_bf16x2(h[2], h[3]);
+    hi = make_uint2(hi01, hi23);
+    lo = make_uint2(pack_bf16x2(h[0] - bf16_bits_to_f32(hi01 & 0xffffu), h[1] - bf16_bits_to_f32(hi01 >> 16)),
+                    pack_bf16x2(h[2] - bf16_bits_to_f32(hi23 & 0xffffu), h[3] - bf16_bits_to_f32(hi23 >> 16)));
+}
+
+// out[n][t] = sum_j B[j][n] h[t][j] for the wave's 64 columns and the tile's
+// subtiles, then y = round(y + s * out) for the rows of the tile.  hs_hi / hs_lo:
+// the tile's h as bf16 high / low halves in LDS, row stride HS elements.  Rows
+// beyond the tile hold stale LDS; they only reach output columns of tokens that
+// are not stored.
+template <int NB, int NSUB, int HS>
+__device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16_t *hs_lo,
+                                             const uint2 (&bop)[NB][4], const uint4 (&yv)[NSUB][2],
+                                             const int (&tok)[NSUB], const bool (&tok_ok)[NSUB],
+                                             int nsub, int nb, float s, uint16_t *ybase, int d_out,
+                                             int cb)
+{
+    const int lane = threadIdx.x & 63, row = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+        if (st >= nsub)
+            break;
+        f32x4_t acc[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kst = 0; kst < NB; ++kst) {
+            if (kst < nb) {
+                const int o = (st * 16 + row) * HS + kst * 16 + g * 4;
+                const s16x4_t hhi = __builtin_bit_cast(s16x4_t, *(const uint2 *)(hs_hi + o));
+                const s16x4_t hlo = __builtin_bit_cast(s16x4_t, *(const uint2 *)(hs_lo + o));
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const s16x4_t bo = __builtin_bit_cast(s16x4_t, bop[kst][b]);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hhi, acc[b], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hlo, acc[b], 0, 0, 0);
+                }
+            }
+        }
+        if (tok_ok[st]) {
+            uint16_t *yrow = ybase + (int64_t)tok[st] * d_out;
+#pragma unroll
+            for (int piece = 0; piece < 2; ++piece) {
+                const int col = cb + g * 16 + piece * 8;
+                if (col < d_out) {
+                    const uint4 yw = yv[st][piece];
+                    uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
+#pragma unroll
+                    for (int h2 = 0; h2 < 4; ++h2) {
+                        const int e0 = piece * 8 + h2 * 2, e1 = e0 + 1;
+                        const float v0 = bf16_bits_to_f32(w[h2] & 0xffffu) + s * acc[e0 >> 2][e0 & 3];
+                        const float v1 = bf16_bits_to_f32(w[h2] >> 16) + s * acc[e1 >> 2][e1 & 3];
+                        w[h2] = pack_bf16x2(v0, v1);
+                    }
+                    *(uint4 *)(yrow + col) = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+        }
+    }
+}
+
+// Arrival counts of the shrink parts of one tile, for an expand running in the
+// same launch as the shrink (apply_bf16_kernel).
+struct TileWait {
+    const uint32_t *count;   // null: h is complete before the launch
+    uint32_t want;           // the member's K-split count
+    int32_t spin_limit;
+    uint32_t *flags;
+};
+
+// Wait until `want` shrink parts of the tile have arrived.  One lane polls; a
+// wait longer than spin_limit polls sets LORA_FLAG_SYNC_TIMEOUT and gives up.
+// Afterwards every wave takes an agent-scope acquire, so its loads see the h
+// partials that the arriving workgroups released.
+__device__ __forceinline__ void wait_arrivals(const TileWait &w)
+{
+    if (threadIdx.x == 0) {
+        int polls = 0;
+        while (__hip_atomic_load(w.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < w.want) {
+            if (++polls > w.spin_limit) {
+                atomicOr(w.flags, LORA_FLAG_SYNC_TIMEOUT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Publish one shrink part: every wave releases its h stores at agent scope,
+// then one lane counts the arrival.
+__device__ __forceinline__ void arrive(uint32_t *count)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// h partials of a tile for the expand, summed over the K splits in split
+// order: thread tid owns quads e = tid + 256 i (i < NB) of the len x nb*16 block.
+template <int NB>
+__device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArgs &a, int m,
+                                            const Tile &tile, int nb)
+{
+    const int tid = threadIdx.x;
     const int quads = nb * 4;
     const int n_el = tile.len * quads;
     const int splits = a.splits[m];
     const float *hbase = a.hpart + m * a.member_stride;
-    f32x4_t hsum[NB];
     if (splits == 1) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -804,96 +999,225 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
             hsum[i] = sum;
         }
     }
-    // B operands: lane row -> column cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 4g..+3
-    const uint16_t *Bslot = (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m];
-    uint2 bop[NB][4];
-#pragma unroll
-    for (int kst = 0; kst < NB; ++kst) {
-        const int G = kst * 2 + (g >> 1);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
-            bop[kst][b] = (kst < nb && cols_ok && n < d_out)
-                              ? *(const uint2 *)(Bslot + ((int64_t)G * d_out + n) * 8 + (g & 1) * 4)
-                              : make_uint2(0, 0);
-        }
-    }
-    // y: 16 adjacent columns of one token per lane and subtile
-    uint4 yv[4][2];
+}
+
+// The expand of one tile for the 256 columns of chunk `chunk` of member m.
+// Requires 0 < tile.rank and an adapter that targets the member.  With a wait
+// (w.count set), B and y are loaded first and h after the wait; otherwise h
+// first.
+template <int NB>
+__device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chunk, const Tile &tile,
+                                            int tokv, uint16_t *hs_hi, uint16_t *hs_lo,
+                                            const TileWait &w)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int d_out = a.d_out[m];
+    const int cb = chunk * kExpandCols + wave * 64;
+    const int nb = (tile.rank + 15) >> 4;
+    const int row = lane & 15;
+    const bool cols_ok = cb < d_out;
+    const int nsub = (tile.len + 15) >> 4;
+    uint16_t *ybase = (uint16_t *)a.y[m];
+
+    // tokens of this lane in each subtile
+    int tok[4];
+    bool tok_ok[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int piece = 0; piece < 2; ++piece) {
-            const int col = cb + g * 16 + piece * 8;
-            yv[st][piece] = (tok_ok[st] && col < d_out)
-                                ? *(const uint4 *)(ybase + (int64_t)tok[st] * d_out + col)
-                                : make_uint4(0, 0, 0, 0);
-        }
+        const int t = st * 16 + row;
+        tok_ok[st] = cols_ok && t < tile.len;
+        const int tv = __shfl(tokv, t, 64);
+        tok[st] = tok_ok[st] ? tv : 0;
+    }
+    f32x4_t hsum[NB];
+    if (!w.count)
+        load_h_sums<NB>(hsum, a, m, tile, nb);
+    uint2 bop[NB][4];
+    load_b_ops<NB>(bop, (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m], d_out,
+                   cb, nb, cols_ok);
+    uint4 yv[4][2];
+    load_y<4>(yv, ybase, d_out, cb, tok, tok_ok);
+    if (w.count) {
+        wait_arrivals(w);
+        load_h_sums<NB>(hsum, a, m, tile, nb);
     }
     // h -> bf16 high and low halves in LDS
     constexpr int HS = NB * 16 + 8;             // row stride (bf16 elements, 16-byte multiple)
-    __shared__ __attribute__((aligned(16))) uint16_t hs_hi[kTileTokens][HS];
-    __shared__ __attribute__((aligned(16))) uint16_t hs_lo[kTileTokens][HS];
+    const int quads = nb * 4;
+    const int n_el = tile.len * quads;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int e = tid + 256 * i;
         if (e < n_el) {
             const int t = e / quads, q = e - t * quads;
-            const f32x4_t h = hsum[i];
-            const uint32_t hi01 = pack_bf16x2(h[0], h[1]), hi23 = pack_bf16x2(h[2], h[3]);
-            const uint32_t lo01 = pack_bf16x2(h[0] - bf16_bits_to_f32(hi01 & 0xffffu),
-                                              h[1] - bf16_bits_to_f32(hi01 >> 16));
-            const uint32_t lo23 = pack_bf16x2(h[2] - bf16_bits_to_f32(hi23 & 0xffffu),
-                                              h[3] - bf16_bits_to_f32(hi23 >> 16));
-            *(uint2 *)&hs_hi[t][q * 4] = make_uint2(hi01, hi23);
-            *(uint2 *)&hs_lo[t][q * 4] = make_uint2(lo01, lo23);
+            split_hi_lo(hsum[i], *(uint2 *)&hs_hi[t * HS + q * 4], *(uint2 *)&hs_lo[t * HS + q * 4]);
         }
     }
     __syncthreads();
     if (!cols_ok)
         return;
+    expand_store<NB, 4, HS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase, d_out, cb);
+}
 
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        if (st >= nsub)
-            break;
-        f32x4_t acc[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kst = 0; kst < NB; ++kst) {
-            if (kst < nb) {
-                // rows beyond the tile read stale LDS; their results are never stored
-                const s16x4_t hhi = __builtin_bit_cast(s16x4_t, *(const uint2 *)&hs_hi[st * 16 + row][kst * 16 + g * 4]);
-                const s16x4_t hlo = __builtin_bit_cast(s16x4_t, *(const uint2 *)&hs_lo[st * 16 + row][kst * 16 + g * 4]);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const s16x4_t bo = __builtin_bit_cast(s16x4_t, bop[kst][b]);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hhi, acc[b], 0, 0, 0);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hlo, acc[b], 0, 0, 0);
-                }
-            }
+constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
+
+// Tiles as the shrink published them, with rank and scale of the slot as that
+// shrink saw them.
+template <int NB>
+__global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
+{
+    const int m = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const MetaRegs mr = load_meta_regs(meta, m);
+    const int n_tiles = *a.n_tiles;
+    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
+    const int tokv = a.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
+    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= a.d_out[m])
+        return;
+    if (tile.rank == 0 || !meta_targets(mr, tile.slot))
+        return;
+    __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB)];
+    __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB)];
+    expand_tile<NB>(a, m, blockIdx.y, tile, tokv, hs_hi, hs_lo, TileWait{});
+}
+
+// ----------------------------------------------------------------------------
+// shrink and expand in one launch, bf16
+//
+// Workgroups take tickets from a device counter in the order they start.  The
+// first n_shrink tickets are shrink parts (tile, K split, member), the rest
+// expand parts (tile, column chunk, member), both ordered by tile first.  A
+// shrink part never waits; after storing its h partial it counts its arrival on
+// the (member, tile) counter.  An expand part loads its B operands and y, then
+// waits for all K splits of its tile to arrive, then finishes as the expand
+// kernel does.  An expand part only starts after every shrink ticket has been
+// handed out, so every part it waits for is already running: the wait ends
+// without any assumption on how many workgroups fit on the chip or in which
+// order they are dispatched.  The arithmetic is that of the two kernels, so the
+// results are bit-identical to lora_shrink followed by lora_expand.
+//
+// The counters come in two sets; a launch uses set `parity` (zeroed by the
+// launch before it) and zeroes the other set for the launch after it.
+
+// Slot metadata of every group member in registers: lane l holds 4 slot ranks
+// and word l % 8 of member l / 8's target mask.
+struct MetaRegsAll {
+    uint32_t rk;
+    uint32_t tw;
+};
+
+__device__ __forceinline__ MetaRegsAll load_meta_regs_all(const SlotMeta &meta)
+{
+    const int lane = threadIdx.x & 63;
+    MetaRegsAll r;
+    r.rk = ((const uint32_t *)meta.rank)[lane];
+    r.tw = ((const uint32_t *)meta.target)[lane];
+    return r;
+}
+
+__device__ __forceinline__ bool meta_targets_m(const MetaRegsAll &r, int m, int slot)
+{
+    return (__shfl(r.tw, m * (LORA_MAX_SLOTS / 32) + (slot >> 5), 64) >> (slot & 31)) & 1u;
+}
+
+template <int NB, bool MIXED>
+struct ChainLds {
+    static constexpr int kBytes = cmax(shrink_smem_bytes(NB, MIXED), 2 * expand_hs_elems(NB) * 2);
+    unsigned char u[kBytes];
+    TilePlanLds plan;
+};
+
+// Role of a ticket: b, member, part (K split or column chunk).
+struct ChainRole {
+    int b, m, part;
+    bool shrink;
+};
+
+__device__ __forceinline__ ChainRole chain_role(int t, const ShrinkArgs &sa, const ExpandArgs &ea,
+                                                const ChainArgs &ca)
+{
+    ChainRole r;
+    r.shrink = t < ca.n_shrink;
+    if (r.shrink) {
+        const int per_tile = sa.n * sa.grid_splits;
+        r.b = t / per_tile;
+        r.m = (t - r.b * per_tile) / sa.grid_splits;
+        r.part = t - r.b * per_tile - r.m * sa.grid_splits;
+    } else {
+        const int te = t - ca.n_shrink, per_tile = ea.n * ea.grid_cols;
+        r.b = te / per_tile;
+        r.m = (te - r.b * per_tile) / ea.grid_cols;
+        r.part = te - r.b * per_tile - r.m * ea.grid_cols;
+    }
+    return r;
+}
+
+template <int NB, bool MIXED, int PLAN>
+__global__ __launch_bounds__(256) void apply_bf16_kernel(ShrinkArgs sa, ExpandArgs ea, ChainArgs ca,
+                                                         SlotMeta meta)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t *sync = ca.sync + (int64_t)ca.parity * ca.sync_words;
+    if (blockIdx.x == 0) {
+        uint32_t *next = ca.sync + (int64_t)(1 - ca.parity) * ca.sync_words;
+        for (int i = tid; i < ca.sync_words; i += 256)
+            next[i] = 0;
+    }
+    uint32_t tk = 0;
+    if (tid == 0)
+        tk = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const MetaRegsAll mr = load_meta_regs_all(meta);
+    __shared__ __attribute__((aligned(16))) ChainLds<NB, MIXED> L;
+    Tile tile;
+    int tokv;
+    ChainRole r;
+    if (PLAN == kPlanInline) {
+        // the ticket reaches LDS inside the plan, behind its first barrier
+        const auto role_b = [&](const TilePlanLds &P) {
+            r = chain_role(__builtin_amdgcn_readfirstlane(P.ticket), sa, ea, ca);
+            return r.b;
+        };
+        const bool ok = plan_tile(sa.idx, sa.T, sa.S, meta, sa.plan, L.plan, role_b, (int)tk,
+                                  false, blockIdx.x == 0, tile, tokv);
+        if (!r.shrink && r.part * kExpandCols >= ea.d_out[r.m])
+            return;
+        if (!ok)
+            return;
+        if (r.shrink && r.part == 0 && r.m == 0) {
+            if (tid == 0)
+                sa.plan.tiles[r.b] = tile;
+            if (tid < tile.len)
+                sa.plan.tile_tok[(int64_t)r.b * kTileTokens + tid] = L.plan.list[tid];
         }
-        if (tok_ok[st]) {
-            uint16_t *yrow = ybase + (int64_t)tok[st] * d_out;
-#pragma unroll
-            for (int piece = 0; piece < 2; ++piece) {
-                const int col = cb + g * 16 + piece * 8;
-                if (col < d_out) {
-                    const uint4 yw = yv[st][piece];
-                    uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
-#pragma unroll
-                    for (int h2 = 0; h2 < 4; ++h2) {
-                        const int e0 = piece * 8 + h2 * 2, e1 = e0 + 1;
-                        const float v0 = bf16_bits_to_f32(w[h2] & 0xffffu) + s * acc[e0 >> 2][e0 & 3];
-                        const float v1 = bf16_bits_to_f32(w[h2] >> 16) + s * acc[e1 >> 2][e1 & 3];
-                        w[h2] = pack_bf16x2(v0, v1);
-                    }
-                    *(uint4 *)(yrow + col) = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
-        }
+    } else {
+        if (tid == 0)
+            L.plan.ticket = (int)tk;
+        __syncthreads();
+        r = chain_role(__builtin_amdgcn_readfirstlane(L.plan.ticket), sa, ea, ca);
+        if (!r.shrink && r.part * kExpandCols >= ea.d_out[r.m])
+            return;
+        const int n_tiles = *sa.plan.n_tiles;
+        tile = sa.plan.tiles[r.b];            // in bounds: the tile buffer covers every ticket's tile
+        tokv = sa.plan.tile_tok[(int64_t)r.b * kTileTokens + lane];
+        if (r.b >= n_tiles)
+            return;
+        tile.rank = (__shfl(mr.rk, tile.slot >> 2, 64) >> ((tile.slot & 3) * 8)) & 0xff;
+        tile.scale = meta.scale[tile.slot];
+    }
+    const int b = r.b, m = r.m, part = r.part;
+    const bool is_shrink = r.shrink;
+    if (tile.rank == 0 || !meta_targets_m(mr, m, tile.slot))
+        return;
+    uint32_t *count = sync + 1 + (int64_t)m * ca.tiles_stride + b;
+    if (is_shrink) {
+        if (part >= sa.splits[m])
+            return;
+        shrink_tile<NB, MIXED>(sa, m, part, tile, tokv, L.u);
+        arrive(count);
+    } else {
+        uint16_t *hs = (uint16_t *)L.u;
+        expand_tile<NB>(ea, m, part, tile, tokv, hs, hs + expand_hs_elems(NB),
+                        TileWait{count, (uint32_t)ea.splits[m], ca.spin_limit, ca.flags});
     }
 }
 
@@ -1015,19 +1339,19 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta 
 // ----------------------------------------------------------------------------
 // launches
 
-template <bool MIXED, bool INLINE>
+template <bool MIXED, int PLAN>
 static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st,
                                const LaunchTiming &t)
 {
     const int nbmax = a.R_pad / 16;
     if (nbmax <= 1)
-        launch(shrink_bf16_kernel<1, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<1, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 2)
-        launch(shrink_bf16_kernel<2, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<2, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 4)
-        launch(shrink_bf16_kernel<4, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<4, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
     else
-        launch(shrink_bf16_kernel<8, MIXED, INLINE>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<8, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
 }
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
@@ -1036,12 +1360,41 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
     const dim3 grid(a.grid_tiles, a.grid_splits, a.n), block(256);
     if (!bf16)
         launch(shrink_f32_kernel, grid, block, 0, st, t, a, m);
-    else if (a.inline_plan)
-        launch_shrink_bf16<false, true>(a, m, grid, st, t);
+    else if (a.plan_mode == kPlanInline)
+        launch_shrink_bf16<false, kPlanInline>(a, m, grid, st, t);
     else if (a.mixed)
-        launch_shrink_bf16<true, false>(a, m, grid, st, t);
+        launch_shrink_bf16<true, kPlanTiles>(a, m, grid, st, t);
     else
-        launch_shrink_bf16<false, false>(a, m, grid, st, t);
+        launch_shrink_bf16<false, kPlanTiles>(a, m, grid, st, t);
+    return hipGetLastError();
+}
+
+template <bool MIXED, int PLAN>
+static void launch_apply_bf16(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
+                              const SlotMeta &m, dim3 grid, hipStream_t st, const LaunchTiming &t)
+{
+    const int nbmax = sa.R_pad / 16;
+    if (nbmax <= 1)
+        launch(apply_bf16_kernel<1, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
+    else if (nbmax <= 2)
+        launch(apply_bf16_kernel<2, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
+    else if (nbmax <= 4)
+        launch(apply_bf16_kernel<4, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
+    else
+        launch(apply_bf16_kernel<8, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
+}
+
+hipError_t launch_apply(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
+                        const SlotMeta &m, hipStream_t st, const LaunchTiming &t)
+{
+    const int64_t n_expand = (int64_t)ea.grid_tiles * ea.grid_cols * ea.n;
+    const dim3 grid((unsigned)(ca.n_shrink + n_expand));
+    if (sa.plan_mode == kPlanInline)
+        launch_apply_bf16<false, kPlanInline>(sa, ea, ca, m, grid, st, t);
+    else if (sa.mixed)
+        launch_apply_bf16<true, kPlanTiles>(sa, ea, ca, m, grid, st, t);
+    else
+        launch_apply_bf16<false, kPlanTiles>(sa, ea, ca, m, grid, st, t);
     return hipGetLastError();
 }
 

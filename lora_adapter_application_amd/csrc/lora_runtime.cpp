@@ -82,6 +82,11 @@ struct lora_ctx {
     float *hpart = nullptr;
     int hbuf_rows = 0;
     int max_splits = 16;                     // K-split cap of the shrink (tuning)
+    bool one_launch = false;                 // bf16 lora_apply runs shrink and expand in one launch
+    uint32_t *sync = nullptr;                // one-launch apply: [2][sync_words] ticket + arrival counters
+    int sync_words = 0;
+    uint32_t sync_generation = 0;            // one-launch applies so far (parity of the next one)
+    int spin_limit = 1 << 18;                // polls before a waiting expand part gives up
     PlanBuffers plan{};
     int max_tiles = 0;
     hipStream_t side = nullptr;
@@ -90,7 +95,7 @@ struct lora_ctx {
     std::vector<StreamState> streams;
     // plan state; an inline plan is computed by every shrink launch itself
     bool plan_valid = false, plan_prepared = false;
-    bool plan_inline = false;   // the next shrink computes the plan in-kernel and publishes it
+    int plan_mode = kPlanTiles;  // PlanMode of the next bf16 launch on this plan
     uint64_t slot_epoch = 0, shrink_epoch = 0;   // loads + clears, and their count at the last shrink
     const int32_t *plan_idx = nullptr;
     int32_t plan_T = 0;
@@ -243,7 +248,7 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
-enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2 };
+enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2, PROF_APPLY = 3 };
 
 // Events for the next dispatch while profiling (none once the reserve is used up).
 LaunchTiming next_timing(lora_ctx *c, int kind)
@@ -277,8 +282,8 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
 
 int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
 {
-    c->plan_inline = c->dtype == LORA_BF16 && T <= kInlinePlanTokens;
-    if (T > 0 && !c->plan_inline) {
+    c->plan_mode = c->dtype == LORA_BF16 && T <= kInlinePlanTokens ? kPlanInline : kPlanTiles;
+    if (T > 0 && c->plan_mode == kPlanTiles) {
         int rc = before_launch(c, s);
         if (rc)
             return rc;
@@ -298,6 +303,72 @@ int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
     return LORA_OK;
 }
 
+// Launch arguments of a shrink of the planned batch for a group of modules
+// (records the K-splits for the expand that follows).
+ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *const *x)
+{
+    const int T = c->plan_T;
+    ShrinkArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.n = n;
+    a.grid_splits = 1;
+    for (int i = 0; i < n; ++i) {
+        const int mod = modules[i];
+        const lora_module_shape sh = c->shapes[mod];
+        int splits = 1, kchunk = 0;
+        choose_splits(c, T, sh.d_in, &splits, &kchunk);
+        a.x[i] = x[i];
+        a.A[i] = c->A[mod];
+        a.slot_stride_A[i] = c->strideA[mod];
+        a.d_in[i] = sh.d_in;
+        a.k_chunk[i] = kchunk;
+        a.splits[i] = splits;
+        a.grid_splits = std::max(a.grid_splits, splits);
+        c->last_splits[i] = splits;
+    }
+    a.plan = c->plan;
+    a.idx = c->plan_idx;
+    a.T = T;
+    a.S = c->S;
+    a.plan_mode = c->plan_mode;
+    a.hpart = c->hpart;
+    a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
+    a.split_stride = (int64_t)T * c->R_pad;
+    a.R_pad = c->R_pad;
+    a.grid_tiles = max_tiles_for(T, c->S);
+    a.mixed = T > 1024;
+    return a;
+}
+
+// Launch arguments of the expand matching the last shrink_args.
+ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *y)
+{
+    const int T = c->plan_T;
+    ExpandArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.n = n;
+    a.grid_cols = 1;
+    for (int i = 0; i < n; ++i) {
+        const int mod = modules[i];
+        const lora_module_shape sh = c->shapes[mod];
+        a.y[i] = y[i];
+        a.Bi[i] = c->Bi[mod];
+        a.slot_stride_B[i] = c->strideB[mod];
+        a.d_out[i] = sh.d_out;
+        a.splits[i] = c->last_splits[i];
+        a.grid_cols = std::max(a.grid_cols, ceil_div(sh.d_out, kExpandCols));
+    }
+    a.tiles = c->plan.tiles;
+    a.tile_tok = c->plan.tile_tok;
+    a.n_tiles = c->plan.n_tiles;
+    a.hpart = c->hpart;
+    a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
+    a.split_stride = (int64_t)T * c->R_pad;
+    a.R_pad = c->R_pad;
+    a.grid_tiles = max_tiles_for(T, c->S);
+    return a;
+}
+
 int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x, hipStream_t s)
 {
     const int T = c->plan_T;
@@ -305,38 +376,11 @@ int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x,
         int rc = before_launch(c, s);
         if (rc)
             return rc;
-        ShrinkArgs a;
-        std::memset(&a, 0, sizeof a);
-        a.n = n;
-        a.grid_splits = 1;
-        for (int i = 0; i < n; ++i) {
-            const int mod = modules[i];
-            const lora_module_shape sh = c->shapes[mod];
-            int splits = 1, kchunk = 0;
-            choose_splits(c, T, sh.d_in, &splits, &kchunk);
-            a.x[i] = x[i];
-            a.A[i] = c->A[mod];
-            a.slot_stride_A[i] = c->strideA[mod];
-            a.d_in[i] = sh.d_in;
-            a.k_chunk[i] = kchunk;
-            a.splits[i] = splits;
-            a.grid_splits = std::max(a.grid_splits, splits);
-            c->last_splits[i] = splits;
-        }
-        a.plan = c->plan;
-        a.idx = c->plan_idx;
-        a.T = T;
-        a.S = c->S;
-        a.inline_plan = c->plan_inline ? 1 : 0;
-        a.hpart = c->hpart;
-        a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
-        a.split_stride = (int64_t)T * c->R_pad;
-        a.R_pad = c->R_pad;
-        a.grid_tiles = max_tiles_for(T, c->S);
-        a.mixed = T > 1024;
+        const ShrinkArgs a = shrink_args(c, n, modules, x);
         HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
                                  next_timing(c, PROF_SHRINK)));
-        c->plan_inline = false;   // later shrinks read the plan this launch published
+        if (c->plan_mode == kPlanInline)
+            c->plan_mode = kPlanTiles;   // later launches read the plan this one published
         c->stats.shrinks += n;
     }
     c->last_n = n;
@@ -353,32 +397,42 @@ int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipSt
         int rc = before_launch(c, s);
         if (rc)
             return rc;
-        ExpandArgs a;
-        std::memset(&a, 0, sizeof a);
-        a.n = n;
-        a.grid_cols = 1;
-        for (int i = 0; i < n; ++i) {
-            const int mod = modules[i];
-            const lora_module_shape sh = c->shapes[mod];
-            a.y[i] = y[i];
-            a.Bi[i] = c->Bi[mod];
-            a.slot_stride_B[i] = c->strideB[mod];
-            a.d_out[i] = sh.d_out;
-            a.splits[i] = c->last_splits[i];
-            a.grid_cols = std::max(a.grid_cols, ceil_div(sh.d_out, kExpandCols));
-        }
-        a.tiles = c->plan.tiles;
-        a.tile_tok = c->plan.tile_tok;
-        a.n_tiles = c->plan.n_tiles;
-        a.hpart = c->hpart;
-        a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
-        a.split_stride = (int64_t)T * c->R_pad;
-        a.R_pad = c->R_pad;
-        a.grid_tiles = max_tiles_for(T, c->S);
+        const ExpandArgs a = expand_args(c, n, modules, y);
         HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
                                  next_timing(c, PROF_EXPAND)));
         c->stats.expands += n;
     }
+    return LORA_OK;
+}
+
+// lora_apply of a planned bf16 batch: shrink and expand in one launch.
+int run_apply_one_launch(lora_ctx *c, int n, const int32_t *modules, const void *const *x,
+                         void *const *y, hipStream_t s)
+{
+    const int T = c->plan_T;
+    if (T > 0) {
+        int rc = before_launch(c, s);
+        if (rc)
+            return rc;
+        const ShrinkArgs sa = shrink_args(c, n, modules, x);
+        const ExpandArgs ea = expand_args(c, n, modules, y);
+        ChainArgs ca;
+        std::memset(&ca, 0, sizeof ca);
+        ca.sync = c->sync;
+        ca.sync_words = c->sync_words;
+        ca.tiles_stride = c->max_tiles;
+        ca.parity = (int)(c->sync_generation & 1u);
+        ca.n_shrink = sa.grid_tiles * sa.grid_splits * n;
+        ca.spin_limit = c->spin_limit;
+        ca.flags = c->plan.flags;
+        HIP_TRY(c, launch_apply(sa, ea, ca, group_meta(c, n, modules), s, next_timing(c, PROF_APPLY)));
+        c->sync_generation += 1;
+        if (c->plan_mode == kPlanInline)
+            c->plan_mode = kPlanTiles;   // later launches read the plan this one published
+        c->stats.applies_one_launch += n;
+    }
+    c->last_n = 0;                // the h of this launch is not kept for a lora_expand
+    c->shrink_epoch = c->slot_epoch;
     return LORA_OK;
 }
 
@@ -509,7 +563,17 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         if (v >= 1 && v <= kMaxSplits)
             c->max_splits = v;
     }
+    if (const char *env = std::getenv("LORA_MI355X_ONE_LAUNCH"))
+        c->one_launch = std::atoi(env) != 0;
+    if (const char *env = std::getenv("LORA_MI355X_SPIN_LIMIT")) {
+        const int v = std::atoi(env);
+        if (v >= 0)
+            c->spin_limit = v;
+    }
     c->max_tiles = max_tiles_for(max_tokens, max_loras);
+    c->sync_words = 1 + kMaxGroup * c->max_tiles;
+    if (e == hipSuccess)
+        e = dalloc(c, &c->sync, sizeof(uint32_t) * 2 * (size_t)c->sync_words);
     if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
     if (e == hipSuccess)
         e = dalloc(c, &c->hpart, sizeof(float) * (size_t)kMaxGroup * c->hbuf_rows * c->R_pad);
@@ -748,6 +812,8 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
             return rc;
         }
     }
+    if (ctx->one_launch && ctx->dtype == LORA_BF16)
+        return run_apply_one_launch(ctx, n, modules, x, y, s);
     rc = run_shrink(ctx, n, modules, x, s);
     if (rc)
         return rc;

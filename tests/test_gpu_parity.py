@@ -127,6 +127,76 @@ def test_sweep(case):
     Sl.close()
 
 
+# bf16 lora_apply runs shrink and expand in one launch (apply_bf16_kernel); the
+# split path (lora_shrink, lora_expand) runs the same arithmetic in two.  Cases:
+# K ranges that end in a partial K block, column counts that are not a multiple
+# of a wave's 64 columns, tiles of every length 1..64, 256 slots, one token, the
+# largest inline-planned batch, batches above it (plan kernels, segment path),
+# every padded-rank class.
+ONE_LAUNCH_SWEEP = [
+    # (d_in, d_out) list, max_loras, R, ranks, T, p_base_only, zipf_s
+    ([(136, 264)], 8, 32, [1, 3, 16, 17, 31, 32, 8, 2], 300, 0.1, 1.1),
+    ([(8, 8), (24, 1000)], 4, 16, [16, 1, 9, 4], 257, 0.05, 0.5),
+    ([(5120, 1024), (1024, 520)], 16, 32, [32] * 16, 1024, 0.05, 1.2),
+    ([(4096, 4096)], 8, 16, [16] * 8, 1, 0.0, 1.1),
+    ([(512, 1536)], 256, 16, [(k % 16) + 1 for k in range(256)], 1024, 0.02, 0.3),
+    ([(1160, 648)], 3, 32, [32, 20, 12], 1000, 0.0, 0.01),
+    ([(2048, 8192), (8192, 2048)], 16, 32, [32] * 16, 512, 0.05, 1.2),
+    ([(384, 392), (200, 328)], 5, 64, [64, 40, 30, 20, 10], 1025, 0.1, 1.1),
+    ([(1024, 512)], 8, 128, [128, 120, 64, 17, 1, 96, 32, 8], 2600, 0.1, 0.8),
+    ([(256, 256)], 64, 8, [(k % 8) + 1 for k in range(64)], 4000, 0.2, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ONE_LAUNCH_SWEEP)))
+def test_one_launch_apply_matches_split_path_and_oracle(case):
+    shapes, S_, R, ranks, T, pb, zs = ONE_LAUNCH_SWEEP[case]
+    mods = [synth.Module(f"m{i}", a, b) for i, (a, b) in enumerate(shapes)]
+    wl = synth.random_case(200 + case, synth.BF16, mods, T, S_, R, ranks, p_base_only=pb,
+                           zipf_s=zs)
+    log(f"case one-launch sweep {case}: {shapes} S={S_} R={R} T={T}")
+    Sl = make_slots(wl, one_launch=True)
+    one = run_gpu(wl, Sl)
+    assert Sl.stats()["applies_one_launch"] == len(mods)
+    split = run_gpu(wl, Sl, path="split")
+    assert Sl.flags() == 0
+    Sl.close()
+    Sl = make_slots(wl, one_launch=False)
+    two = run_gpu(wl, Sl)
+    assert Sl.stats()["applies_one_launch"] == 0
+    for m in mods:
+        assert np.array_equal(one[m.name], split[m.name]), m.name
+        assert np.array_equal(two[m.name], split[m.name]), m.name
+        check_close(one[m.name], run_oracle(wl, m.name), wl.dtype, f"one-launch sweep {case} {m.name}")
+        skipped = np.ones(T, bool)
+        for k, ad in enumerate(wl.adapters):
+            if ad is not None and m.name in ad.At:
+                skipped &= wl.idx != k
+        assert np.array_equal(one[m.name][skipped], wl.y[m.name][skipped])
+    Sl.close()
+
+
+def test_one_launch_counters_across_batch_sizes():
+    """Consecutive one-launch applies on one ctx with changing batch sizes (and so
+    changing grids) use alternating counter sets; each equals the split path."""
+    mods = [synth.Module("a", 640, 384)]
+    wl = synth.random_case(31, synth.BF16, mods, 3000, 6, 32, [32, 16, 8, 4, 32, 1], p_base_only=0.05)
+    S = make_slots(wl, max_tokens=3000, one_launch=True)
+    x = to_dev(wl.x["a"], wl.dtype)
+    for T in (3000, 100, 1, 1024, 1025, 3000, 64, 700):
+        idx = torch.from_numpy(wl.idx[:T]).cuda()
+        y1 = to_dev(wl.y["a"][:T], wl.dtype)
+        y2 = to_dev(wl.y["a"][:T], wl.dtype)
+        S.apply(x[:T], y1, idx, 0)
+        S.prepare(idx)
+        S.shrink(x[:T], 0)
+        S.expand(y2, 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(y1, wl.dtype), from_dev(y2, wl.dtype)), T
+    assert S.flags() == 0
+    S.close()
+
+
 def test_exact_integers_fp32_bit_identical():
     mods = [synth.Module("a", 200, 136), synth.Module("b", 64, 520)]
     wl = synth.random_case(7, synth.FP32, mods, 333, 4, 16, [16, 9, 4, 1], integer=True)
@@ -176,36 +246,50 @@ def test_skip_rows_bit_identical_and_flag():
     S.close()
 
 
-@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32])
-def test_padding_to_max_rank_changes_nothing(dtype):
+@pytest.mark.parametrize("dtype,path,wide", [(synth.BF16, "apply", 64), (synth.BF16, "split", 128),
+                                             (synth.FP32, "apply", 64)])
+def test_padding_to_max_rank_changes_nothing(dtype, path, wide):
+    """Zero ranks added up to max_rank leave the result bit-identical."""
     mods = [synth.Module("a", 512, 768)]
     wl = synth.random_case(10, dtype, mods, 400, 4, 16, [16, 13, 8, 1], p_base_only=0.1)
     S16 = make_slots(wl, max_rank=16)
-    S64 = make_slots(wl, max_rank=64)
-    a = run_gpu(wl, S16)["a"]
-    b = run_gpu(wl, S64)["a"]
+    Sw = make_slots(wl, max_rank=wide)
+    a = run_gpu(wl, S16, path=path)["a"]
+    b = run_gpu(wl, Sw, path=path)["a"]
     assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
     check_close(a, run_oracle(wl, "a"), dtype, "padding")
     S16.close()
-    S64.close()
+    Sw.close()
 
 
-def test_deterministic_and_prepared_plan_matches_unprepared():
-    wl = synth.random_case(11, synth.BF16, [synth.Module("a", 1024, 2048)], 700, 8, 32,
+@pytest.mark.parametrize("R", [32, 64])
+def test_deterministic_and_prepared_plan_matches_unprepared(R):
+    """Repeated runs are bit-identical, whether the plan is computed in the kernel
+    or read from an earlier launch, and the separate shrink / expand entry points
+    equal the one-launch apply."""
+    wl = synth.random_case(11, synth.BF16, [synth.Module("a", 1024, 2048)], 700, 8, R,
                            [32, 16, 8, 4, 32, 16, 8, 4])
     S = make_slots(wl)
     a = run_gpu(wl, S, prepare=True)["a"]
     b = run_gpu(wl, S, prepare=False)["a"]
     assert np.array_equal(a, b)
-    # shrink and expand as separate entry points on a prepared plan
+    # a second apply on the same prepared plan reads the plan the first one published
     idx = torch.from_numpy(wl.idx).cuda()
     x = to_dev(wl.x["a"], wl.dtype)
-    y = to_dev(wl.y["a"], wl.dtype)
+    ys = [to_dev(wl.y["a"], wl.dtype) for _ in range(2)]
     S.prepare(idx)
-    S.shrink(x, 0)
-    S.expand(y, 0)
+    for y in ys:
+        S.apply(x, y, idx, 0)
     torch.cuda.synchronize()
-    assert np.array_equal(from_dev(y, wl.dtype), a)
+    for y in ys:
+        assert np.array_equal(from_dev(y, wl.dtype), a)
+    # shrink and expand as separate entry points on a prepared plan
+    s1 = run_gpu(wl, S, path="split")["a"]
+    s2 = run_gpu(wl, S, path="split")["a"]
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(s1, a)
+    check_close(s1, run_oracle(wl, "a"), wl.dtype, "split")
+    check_close(a, run_oracle(wl, "a"), wl.dtype, "apply")
     S.close()
 
 
@@ -338,6 +422,7 @@ def test_group_calls_equal_single_module_calls():
                            p_base_only=0.1)
     S = make_slots(wl)
     single = run_gpu(wl, S)
+    single_split = run_gpu(wl, S, path="split")
     idx = torch.from_numpy(wl.idx).cuda()
     xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
     ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
@@ -345,6 +430,7 @@ def test_group_calls_equal_single_module_calls():
     torch.cuda.synchronize()
     for i, m in enumerate(mods):
         assert np.array_equal(from_dev(ys[i], wl.dtype), single[m.name]), m.name
+        assert np.array_equal(single_split[m.name], single[m.name]), m.name
         check_close(single[m.name], run_oracle(wl, m.name), wl.dtype, m.name)
     # separate phases, a module listed twice with its own x and y, prepared plan
     y2 = [to_dev(wl.y[m.name], wl.dtype) for m in (mods[2], mods[0], mods[2])]
@@ -354,7 +440,7 @@ def test_group_calls_equal_single_module_calls():
     S.expand_group([2, 0, 2], y2)
     torch.cuda.synchronize()
     for yy, name in zip(y2, ("v", "q", "v")):
-        assert np.array_equal(from_dev(yy, wl.dtype), single[name]), name
+        assert np.array_equal(from_dev(yy, wl.dtype), single_split[name]), name
     # errors
     with pytest.raises(binding.LoraError) as e:
         S.expand_group([0, 2, 2], y2)                       # not the shrunk list
@@ -404,9 +490,17 @@ def test_profile_times_every_dispatch():
     assert p["launches"]["shrink"] == 3 and p["launches"]["expand"] == 3
     assert p["launches"]["plan"] == 0                     # planned inside the shrink
     assert p["total_ms"]["shrink"] > 0 and p["total_ms"]["expand"] > 0 and p["untimed"] == 0
-    S.profile_begin(2)
-    S.apply(xs[0], ys[0], idx, 0)
+    S.profile_begin(1)
+    S.apply(xs[0], ys[0], idx, 0)                        # shrink and expand dispatches
     S.apply(xs[0], ys[0], idx, 0)
     p = S.profile_end()
-    assert p["launches"]["shrink"] + p["launches"]["expand"] == 2 and p["untimed"] == 2
+    assert p["launches"]["shrink"] == 1 and p["untimed"] == 3
+    S.close()
+    S = make_slots(wl, one_launch=True)
+    S.profile_begin(1)
+    S.apply(xs[0], ys[0], idx, 0)                        # one dispatch per apply
+    S.apply(xs[0], ys[0], idx, 0)
+    p = S.profile_end()
+    assert p["launches"]["apply"] == 1 and p["untimed"] == 1
+    assert p["launches"]["shrink"] + p["launches"]["expand"] == 0
     S.close()
