@@ -5,7 +5,7 @@
 
 One step is one pass of the whole hot path over one batch: the device plan
 (lora_plan_prepare) and, for every group of modules of the workload's layer,
-lora_apply_group, which runs the group's shrink and expand in one launch.
+lora_apply_group (a shrink launch and an expand launch).
 Steps rotate over L "layer sets" (each with its own adapter weights, x and y,
 like the layers of a model) so that the bytes the kernels read come from HBM
 rather than from the 256 MB Infinity Cache.  Inputs are resident
@@ -222,8 +222,7 @@ def main():
         # algorithmic bytes of one launch of each group
         shrink_bytes = [sum(b * mods[j].d_in * (T_act + sum_r) for j in g) for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
-        group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes,
-                       "apply": [s_ + e_ for s_, e_ in zip(shrink_bytes, expand_bytes)]}
+        group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes}
         flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
                  for m in mods]
 
@@ -236,14 +235,14 @@ def main():
             "step_alg_bytes": float(sum(shrink_bytes) + sum(expand_bytes)),
             "step_alg_flops": float(sum(flops)),
         }
-        for kind in ("shrink", "expand", "apply"):
+        for kind in ("shrink", "expand"):
             if n[kind]:
                 step_bytes = float(sum(group_bytes[kind]))
                 kernels["lora_" + kind] = {
                     "avg_us": avg_us(kind), "per_step_us": tot[kind] / K * 1e3,
                     "alg_bytes_per_step": step_bytes,
                     "GBps": float(step_bytes * K / (tot[kind] * 1e-3) / 1e9)}
-        dom = max(("shrink", "expand", "apply"), key=lambda k: tot[k])
+        dom = max(("shrink", "expand"), key=lambda k: tot[k])
         dom_bytes = group_bytes[dom]
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
         kname = "lora_" + dom

@@ -70,8 +70,6 @@ enum {
 
 /* Sticky device-side flags, read with lora_get_device_flags. */
 #define LORA_FLAG_SLOT_INDEX_TOO_LARGE 0x1u  /* a token carried idx >= max_loras (skipped) */
-#define LORA_FLAG_SYNC_TIMEOUT 0x2u          /* a one-launch lora_apply gave up waiting for its
-                                                shrink parts (results of that launch invalid) */
 
 typedef struct {
     int64_t loads;          /* lora_slot_load calls that succeeded */
@@ -81,7 +79,6 @@ typedef struct {
     int64_t shrinks;        /* lora_shrink launches (including those inside lora_apply) */
     int64_t expands;        /* lora_expand launches (including those inside lora_apply) */
     int64_t tokens;         /* sum of n_tokens over planned batches */
-    int64_t applies_one_launch;  /* lora_apply module updates done in one launch */
 } lora_stats;
 
 /*
@@ -210,8 +207,8 @@ int lora_get_stats(lora_ctx *ctx, lora_stats *out);
  * are created by lora_profile_begin, outside any timed region.
  */
 typedef struct {
-    int64_t launches[4];   /* [0] plan, [1] shrink, [2] expand, [3] one-launch apply dispatches */
-    double total_ms[4];    /* their summed kernel time, milliseconds */
+    int64_t launches[3];   /* [0] plan, [1] shrink, [2] expand dispatches timed */
+    double total_ms[3];    /* their summed kernel time, milliseconds */
     int64_t untimed;       /* dispatches past max_launches (not timed) */
 } lora_profile;
 

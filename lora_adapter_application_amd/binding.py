@@ -34,7 +34,6 @@ LORA_ERR_HIP = -8
 LORA_ERR_NO_PLAN = -9
 
 LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
-LORA_FLAG_SYNC_TIMEOUT = 0x2
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_clear",
@@ -57,14 +56,13 @@ class _ModuleShape(ctypes.Structure):
 
 
 class _Profile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 4), ("total_ms", ctypes.c_double * 4),
+    _fields_ = [("launches", ctypes.c_int64 * 3), ("total_ms", ctypes.c_double * 3),
                 ("untimed", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("loads", "clears", "bytes_loaded", "plans", "shrinks", "expands", "tokens",
-                 "applies_one_launch")]
+                ("loads", "clears", "bytes_loaded", "plans", "shrinks", "expands", "tokens")]
 
 
 _lib = None
@@ -287,7 +285,7 @@ def lora_profile_begin(ctx, max_launches: int) -> None:
 def lora_profile_end(ctx) -> dict:
     p = _Profile()
     _check(load_library().lora_profile_end(ctx, ctypes.byref(p)), ctx)
-    kinds = ("plan", "shrink", "expand", "apply")
+    kinds = ("plan", "shrink", "expand")
     return {"launches": {k: int(p.launches[i]) for i, k in enumerate(kinds)},
             "total_ms": {k: float(p.total_ms[i]) for i, k in enumerate(kinds)},
             "untimed": int(p.untimed)}

@@ -119,23 +119,6 @@ struct ExpandArgs {
     int32_t grid_cols;                  // max column chunks over the members
 };
 
-// Shrink and expand of a bf16 batch in one launch (apply_bf16_kernel):
-// workgroups take tickets in the order they start, the first n_shrink do shrink
-// parts, the rest expand parts, which wait on per (member, tile) arrival counts.
-struct ChainArgs {
-    uint32_t *sync;         // [2][sync_words]: per parity, the ticket counter, then
-                            // arrivals [kMaxGroup][tiles_stride]
-    int32_t sync_words;     // 1 + kMaxGroup * tiles_stride
-    int32_t tiles_stride;   // tiles of the largest batch (max_tiles)
-    int32_t parity;         // counter set of this launch; the launch zeroes the other
-    int32_t n_shrink;       // grid_tiles * grid_splits * n
-    int32_t spin_limit;     // polls before an expand part gives up
-    uint32_t *flags;
-};
-
-hipError_t launch_apply(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
-                        const SlotMeta &m, hipStream_t st, const LaunchTiming &t);
-
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);
 hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,

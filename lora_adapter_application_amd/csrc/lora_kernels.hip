@@ -321,31 +321,65 @@ __device__ __forceinline__ int member_rank(const SlotMeta &meta, int m, int slot
     return ((meta.target[m][slot >> 5] >> (slot & 31)) & 1u) ? (int)meta.rank[slot] : 0;
 }
 
-// Slot metadata fetched at kernel start, independent of the tile: every lane
-// holds 4 slot ranks (rk) and, in lanes 0..7, one 32-slot word of the member's
-// target mask (tw); a lookup by slot is then a cross-lane shuffle.
+// Slot metadata fetched at kernel start, independent of the tile: lane l holds
+// the ranks of slots 4l .. 4l+3 (rk), word l % 8 of group member l / 8's target
+// mask (tw) and the scales of slots l, l+64, l+128, l+192 (sc).  A lookup for a
+// wave-uniform slot reads one lane (v_readlane), with no memory access.
 struct MetaRegs {
     uint32_t rk;
     uint32_t tw;
+    float sc[LORA_MAX_SLOTS / 64];
 };
 
-__device__ __forceinline__ MetaRegs load_meta_regs(const SlotMeta &meta, int m)
+__device__ __forceinline__ MetaRegs load_meta_regs(const SlotMeta &meta)
 {
     const int lane = threadIdx.x & 63;
     MetaRegs r;
     r.rk = ((const uint32_t *)meta.rank)[lane];
-    r.tw = lane < LORA_MAX_SLOTS / 32 ? meta.target[m][lane] : 0u;
+    r.tw = ((const uint32_t *)meta.target)[lane];
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_SLOTS / 64; ++i)
+        r.sc[i] = meta.scale[lane + 64 * i];
     return r;
 }
 
 __device__ __forceinline__ int meta_rank(const MetaRegs &r, int slot)
 {
-    return (__shfl(r.rk, slot >> 2, 64) >> ((slot & 3) * 8)) & 0xff;
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    return (__builtin_amdgcn_readlane(r.rk, slot >> 2) >> ((slot & 3) * 8)) & 0xff;
 }
 
-__device__ __forceinline__ bool meta_targets(const MetaRegs &r, int slot)
+__device__ __forceinline__ bool meta_targets(const MetaRegs &r, int m, int slot)
 {
-    return (__shfl(r.tw, slot >> 5, 64) >> (slot & 31)) & 1u;
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    return (__builtin_amdgcn_readlane(r.tw, m * (LORA_MAX_SLOTS / 32) + (slot >> 5)) >> (slot & 31)) & 1u;
+}
+
+// The lookups read other lanes' registers: call them where every lane of the
+// wave is active, or the compiler may compute those registers in fewer lanes.
+__device__ __forceinline__ float meta_scale(const MetaRegs &r, int slot)
+{
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    int v[LORA_MAX_SLOTS / 64];
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_SLOTS / 64; ++i)
+        v[i] = __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.sc[i]), slot & 63);
+    const int i = slot >> 6;
+    return __builtin_bit_cast(float, i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3]);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then the totals of rows 0 and 2 into rows
+// 1 and 3 (row_bcast:15) and of rows 0-1 into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
 }
 
 // One member's view of a shrink launch.
@@ -592,36 +626,31 @@ struct TilePlanLds {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Tile index of a workgroup of a grid with one workgroup per tile along x.
-struct BlockTile {
-    __device__ int operator()(const TilePlanLds &) const { return (int)blockIdx.x; }
-};
+constexpr int kPlanPerThread = kInlinePlanTokens / 256;
 
-// b_of(L) gives the tile index; it is called once, after the first barrier, so
-// a caller can derive it from a value one lane stored in L.ticket
-// (ticket_val >= 0: lane 0 stores it before that barrier).  publish: write the
-// tile and its token ids to the plan buffers; first: write the totals and the
-// flag.  Returns false past the last tile.
-template <typename TileIndex>
-__device__ bool plan_tile(const int32_t *idx, int T, int S, const SlotMeta &meta,
-                          const PlanBuffers &pb, TilePlanLds &L, TileIndex b_of, int ticket_val,
-                          bool publish, bool first, Tile &tile, int &tokv)
+// The batch's slot indices, thread tid holding tokens c*256 + tid (-1 past T).
+__device__ __forceinline__ void plan_load_idx(const int32_t *idx, int T, int (&v)[kPlanPerThread])
 {
-    constexpr int NC = kInlinePlanTokens / 256;   // tokens per thread
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int v[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int i = c * 256 + tid;
+    for (int c = 0; c < kPlanPerThread; ++c) {
+        const int i = c * 256 + threadIdx.x;
         v[c] = i < T ? idx[i] : -1;
     }
+}
+
+// Tile b of the plan, from the slot indices v (plan_load_idx).  publish: write
+// the tile and its token ids to the plan buffers; first: write the totals and
+// the flag.  Returns false past the last tile.
+__device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs &mr,
+                          const PlanBuffers &pb, TilePlanLds &L, int b, bool publish, bool first,
+                          Tile &tile, int &tokv)
+{
+    constexpr int NC = kPlanPerThread;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < S)
         L.cnt[tid] = 0;
-    if (ticket_val >= 0 && tid == 0)
-        L.ticket = ticket_val;
     __syncthreads();
-    const int b = __builtin_amdgcn_readfirstlane(b_of(L));
     bool big = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -646,15 +675,7 @@ __device__ bool plan_tile(const int32_t *idx, int T, int S, const SlotMeta &meta
             sc += c4[k];
             sn += n4[k];
         }
-        int ic = sc, in = sn;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int oc = __shfl_up(ic, d, 64), on = __shfl_up(in, d, 64);
-            if (lane >= d) {
-                ic += oc;
-                in += on;
-            }
-        }
+        const int ic = wave_incl_scan(sc), in = wave_incl_scan(sn);
         int pc = ic - sc, pn = in - sn;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -723,8 +744,8 @@ __device__ bool plan_tile(const int32_t *idx, int T, int S, const SlotMeta &meta
     tile.slot = sl;
     tile.start = L.start + j * kTileTokens;
     tile.len = min(kTileTokens, L.count - j * kTileTokens);
-    tile.rank = meta.rank[sl];
-    tile.scale = meta.scale[sl];
+    tile.rank = meta_rank(mr, sl);
+    tile.scale = meta_scale(mr, sl);
     tokv = lane < tile.len ? L.list[lane] : 0;
     if (publish) {
         if (tid == 0)
@@ -771,15 +792,16 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
 {
     const int m = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const MetaRegs mr = load_meta_regs(meta, m);
+    const MetaRegs mr = load_meta_regs(meta);
     __shared__ __attribute__((aligned(16))) unsigned char lds[shrink_smem_bytes(NB, MIXED)];
     Tile tile;
     int tokv;
     if constexpr (PLAN == kPlanInline) {
         __shared__ TilePlanLds P;
         const bool y0z0 = blockIdx.y == 0 && blockIdx.z == 0;
-        if (!plan_tile(a.idx, a.T, a.S, meta, a.plan, P, BlockTile{}, -1, y0z0,
-                       y0z0 && blockIdx.x == 0, tile, tokv))
+        int v[kPlanPerThread];
+        plan_load_idx(a.idx, a.T, v);
+        if (!plan_tile(v, a.S, mr, a.plan, P, blockIdx.x, y0z0, y0z0 && blockIdx.x == 0, tile, tokv))
             return;
     } else {
         const int n_tiles = *a.plan.n_tiles;
@@ -787,13 +809,15 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
         tokv = a.plan.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
         if ((int)blockIdx.x >= n_tiles)
             return;
+        // lookups in code every lane runs (see meta_scale), stores by one lane
         tile.rank = meta_rank(mr, tile.slot);
+        tile.scale = meta_scale(mr, tile.slot);
         if (blockIdx.y == 0 && m == 0 && threadIdx.x == 0) {
             a.plan.tiles[blockIdx.x].rank = tile.rank;
-            a.plan.tiles[blockIdx.x].scale = meta.scale[tile.slot];
+            a.plan.tiles[blockIdx.x].scale = tile.scale;
         }
     }
-    if ((int)blockIdx.y >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, tile.slot))
+    if ((int)blockIdx.y >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
     shrink_tile<NB, MIXED>(a, m, blockIdx.y, tile, tokv, lds);
 }
@@ -921,45 +945,6 @@ __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16
     }
 }
 
-// Arrival counts of the shrink parts of one tile, for an expand running in the
-// same launch as the shrink (apply_bf16_kernel).
-struct TileWait {
-    const uint32_t *count;   // null: h is complete before the launch
-    uint32_t want;           // the member's K-split count
-    int32_t spin_limit;
-    uint32_t *flags;
-};
-
-// Wait until `want` shrink parts of the tile have arrived.  One lane polls; a
-// wait longer than spin_limit polls sets LORA_FLAG_SYNC_TIMEOUT and gives up.
-// Afterwards every wave takes an agent-scope acquire, so its loads see the h
-// partials that the arriving workgroups released.
-__device__ __forceinline__ void wait_arrivals(const TileWait &w)
-{
-    if (threadIdx.x == 0) {
-        int polls = 0;
-        while (__hip_atomic_load(w.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < w.want) {
-            if (++polls > w.spin_limit) {
-                atomicOr(w.flags, LORA_FLAG_SYNC_TIMEOUT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// Publish one shrink part: every wave releases its h stores at agent scope,
-// then one lane counts the arrival.
-__device__ __forceinline__ void arrive(uint32_t *count)
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // h partials of a tile for the expand, summed over the K splits in split
 // order: thread tid owns quads e = tid + 256 i (i < NB) of the len x nb*16 block.
 template <int NB>
@@ -1002,13 +987,11 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
 }
 
 // The expand of one tile for the 256 columns of chunk `chunk` of member m.
-// Requires 0 < tile.rank and an adapter that targets the member.  With a wait
-// (w.count set), B and y are loaded first and h after the wait; otherwise h
-// first.
+// Requires 0 < tile.rank and an adapter that targets the member.  Every global
+// load (h partials, B, y) is issued before any arithmetic.
 template <int NB>
 __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chunk, const Tile &tile,
-                                            int tokv, uint16_t *hs_hi, uint16_t *hs_lo,
-                                            const TileWait &w)
+                                            int tokv, uint16_t *hs_hi, uint16_t *hs_lo)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int d_out = a.d_out[m];
@@ -1030,17 +1013,12 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
         tok[st] = tok_ok[st] ? tv : 0;
     }
     f32x4_t hsum[NB];
-    if (!w.count)
-        load_h_sums<NB>(hsum, a, m, tile, nb);
+    load_h_sums<NB>(hsum, a, m, tile, nb);
     uint2 bop[NB][4];
     load_b_ops<NB>(bop, (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m], d_out,
                    cb, nb, cols_ok);
     uint4 yv[4][2];
     load_y<4>(yv, ybase, d_out, cb, tok, tok_ok);
-    if (w.count) {
-        wait_arrivals(w);
-        load_h_sums<NB>(hsum, a, m, tile, nb);
-    }
     // h -> bf16 high and low halves in LDS
     constexpr int HS = NB * 16 + 8;             // row stride (bf16 elements, 16-byte multiple)
     const int quads = nb * 4;
@@ -1068,157 +1046,17 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 {
     const int m = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const MetaRegs mr = load_meta_regs(meta, m);
+    const MetaRegs mr = load_meta_regs(meta);
     const int n_tiles = *a.n_tiles;
     const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
     const int tokv = a.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
     if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= a.d_out[m])
         return;
-    if (tile.rank == 0 || !meta_targets(mr, tile.slot))
+    if (tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
     __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB)];
     __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB)];
-    expand_tile<NB>(a, m, blockIdx.y, tile, tokv, hs_hi, hs_lo, TileWait{});
-}
-
-// ----------------------------------------------------------------------------
-// shrink and expand in one launch, bf16
-//
-// Workgroups take tickets from a device counter in the order they start.  The
-// first n_shrink tickets are shrink parts (tile, K split, member), the rest
-// expand parts (tile, column chunk, member), both ordered by tile first.  A
-// shrink part never waits; after storing its h partial it counts its arrival on
-// the (member, tile) counter.  An expand part loads its B operands and y, then
-// waits for all K splits of its tile to arrive, then finishes as the expand
-// kernel does.  An expand part only starts after every shrink ticket has been
-// handed out, so every part it waits for is already running: the wait ends
-// without any assumption on how many workgroups fit on the chip or in which
-// order they are dispatched.  The arithmetic is that of the two kernels, so the
-// results are bit-identical to lora_shrink followed by lora_expand.
-//
-// The counters come in two sets; a launch uses set `parity` (zeroed by the
-// launch before it) and zeroes the other set for the launch after it.
-
-// Slot metadata of every group member in registers: lane l holds 4 slot ranks
-// and word l % 8 of member l / 8's target mask.
-struct MetaRegsAll {
-    uint32_t rk;
-    uint32_t tw;
-};
-
-__device__ __forceinline__ MetaRegsAll load_meta_regs_all(const SlotMeta &meta)
-{
-    const int lane = threadIdx.x & 63;
-    MetaRegsAll r;
-    r.rk = ((const uint32_t *)meta.rank)[lane];
-    r.tw = ((const uint32_t *)meta.target)[lane];
-    return r;
-}
-
-__device__ __forceinline__ bool meta_targets_m(const MetaRegsAll &r, int m, int slot)
-{
-    return (__shfl(r.tw, m * (LORA_MAX_SLOTS / 32) + (slot >> 5), 64) >> (slot & 31)) & 1u;
-}
-
-template <int NB, bool MIXED>
-struct ChainLds {
-    static constexpr int kBytes = cmax(shrink_smem_bytes(NB, MIXED), 2 * expand_hs_elems(NB) * 2);
-    unsigned char u[kBytes];
-    TilePlanLds plan;
-};
-
-// Role of a ticket: b, member, part (K split or column chunk).
-struct ChainRole {
-    int b, m, part;
-    bool shrink;
-};
-
-__device__ __forceinline__ ChainRole chain_role(int t, const ShrinkArgs &sa, const ExpandArgs &ea,
-                                                const ChainArgs &ca)
-{
-    ChainRole r;
-    r.shrink = t < ca.n_shrink;
-    if (r.shrink) {
-        const int per_tile = sa.n * sa.grid_splits;
-        r.b = t / per_tile;
-        r.m = (t - r.b * per_tile) / sa.grid_splits;
-        r.part = t - r.b * per_tile - r.m * sa.grid_splits;
-    } else {
-        const int te = t - ca.n_shrink, per_tile = ea.n * ea.grid_cols;
-        r.b = te / per_tile;
-        r.m = (te - r.b * per_tile) / ea.grid_cols;
-        r.part = te - r.b * per_tile - r.m * ea.grid_cols;
-    }
-    return r;
-}
-
-template <int NB, bool MIXED, int PLAN>
-__global__ __launch_bounds__(256) void apply_bf16_kernel(ShrinkArgs sa, ExpandArgs ea, ChainArgs ca,
-                                                         SlotMeta meta)
-{
-    const int tid = threadIdx.x, lane = tid & 63;
-    uint32_t *sync = ca.sync + (int64_t)ca.parity * ca.sync_words;
-    if (blockIdx.x == 0) {
-        uint32_t *next = ca.sync + (int64_t)(1 - ca.parity) * ca.sync_words;
-        for (int i = tid; i < ca.sync_words; i += 256)
-            next[i] = 0;
-    }
-    uint32_t tk = 0;
-    if (tid == 0)
-        tk = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const MetaRegsAll mr = load_meta_regs_all(meta);
-    __shared__ __attribute__((aligned(16))) ChainLds<NB, MIXED> L;
-    Tile tile;
-    int tokv;
-    ChainRole r;
-    if (PLAN == kPlanInline) {
-        // the ticket reaches LDS inside the plan, behind its first barrier
-        const auto role_b = [&](const TilePlanLds &P) {
-            r = chain_role(__builtin_amdgcn_readfirstlane(P.ticket), sa, ea, ca);
-            return r.b;
-        };
-        const bool ok = plan_tile(sa.idx, sa.T, sa.S, meta, sa.plan, L.plan, role_b, (int)tk,
-                                  false, blockIdx.x == 0, tile, tokv);
-        if (!r.shrink && r.part * kExpandCols >= ea.d_out[r.m])
-            return;
-        if (!ok)
-            return;
-        if (r.shrink && r.part == 0 && r.m == 0) {
-            if (tid == 0)
-                sa.plan.tiles[r.b] = tile;
-            if (tid < tile.len)
-                sa.plan.tile_tok[(int64_t)r.b * kTileTokens + tid] = L.plan.list[tid];
-        }
-    } else {
-        if (tid == 0)
-            L.plan.ticket = (int)tk;
-        __syncthreads();
-        r = chain_role(__builtin_amdgcn_readfirstlane(L.plan.ticket), sa, ea, ca);
-        if (!r.shrink && r.part * kExpandCols >= ea.d_out[r.m])
-            return;
-        const int n_tiles = *sa.plan.n_tiles;
-        tile = sa.plan.tiles[r.b];            // in bounds: the tile buffer covers every ticket's tile
-        tokv = sa.plan.tile_tok[(int64_t)r.b * kTileTokens + lane];
-        if (r.b >= n_tiles)
-            return;
-        tile.rank = (__shfl(mr.rk, tile.slot >> 2, 64) >> ((tile.slot & 3) * 8)) & 0xff;
-        tile.scale = meta.scale[tile.slot];
-    }
-    const int b = r.b, m = r.m, part = r.part;
-    const bool is_shrink = r.shrink;
-    if (tile.rank == 0 || !meta_targets_m(mr, m, tile.slot))
-        return;
-    uint32_t *count = sync + 1 + (int64_t)m * ca.tiles_stride + b;
-    if (is_shrink) {
-        if (part >= sa.splits[m])
-            return;
-        shrink_tile<NB, MIXED>(sa, m, part, tile, tokv, L.u);
-        arrive(count);
-    } else {
-        uint16_t *hs = (uint16_t *)L.u;
-        expand_tile<NB>(ea, m, part, tile, tokv, hs, hs + expand_hs_elems(NB),
-                        TileWait{count, (uint32_t)ea.splits[m], ca.spin_limit, ca.flags});
-    }
+    expand_tile<NB>(a, m, blockIdx.y, tile, tokv, hs_hi, hs_lo);
 }
 
 // ----------------------------------------------------------------------------
@@ -1366,35 +1204,6 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
         launch_shrink_bf16<true, kPlanTiles>(a, m, grid, st, t);
     else
         launch_shrink_bf16<false, kPlanTiles>(a, m, grid, st, t);
-    return hipGetLastError();
-}
-
-template <bool MIXED, int PLAN>
-static void launch_apply_bf16(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
-                              const SlotMeta &m, dim3 grid, hipStream_t st, const LaunchTiming &t)
-{
-    const int nbmax = sa.R_pad / 16;
-    if (nbmax <= 1)
-        launch(apply_bf16_kernel<1, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
-    else if (nbmax <= 2)
-        launch(apply_bf16_kernel<2, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
-    else if (nbmax <= 4)
-        launch(apply_bf16_kernel<4, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
-    else
-        launch(apply_bf16_kernel<8, MIXED, PLAN>, grid, dim3(256), 0, st, t, sa, ea, ca, m);
-}
-
-hipError_t launch_apply(const ShrinkArgs &sa, const ExpandArgs &ea, const ChainArgs &ca,
-                        const SlotMeta &m, hipStream_t st, const LaunchTiming &t)
-{
-    const int64_t n_expand = (int64_t)ea.grid_tiles * ea.grid_cols * ea.n;
-    const dim3 grid((unsigned)(ca.n_shrink + n_expand));
-    if (sa.plan_mode == kPlanInline)
-        launch_apply_bf16<false, kPlanInline>(sa, ea, ca, m, grid, st, t);
-    else if (sa.mixed)
-        launch_apply_bf16<true, kPlanTiles>(sa, ea, ca, m, grid, st, t);
-    else
-        launch_apply_bf16<false, kPlanTiles>(sa, ea, ca, m, grid, st, t);
     return hipGetLastError();
 }
 

@@ -82,11 +82,6 @@ struct lora_ctx {
     float *hpart = nullptr;
     int hbuf_rows = 0;
     int max_splits = 16;                     // K-split cap of the shrink (tuning)
-    bool one_launch = false;                 // bf16 lora_apply runs shrink and expand in one launch
-    uint32_t *sync = nullptr;                // one-launch apply: [2][sync_words] ticket + arrival counters
-    int sync_words = 0;
-    uint32_t sync_generation = 0;            // one-launch applies so far (parity of the next one)
-    int spin_limit = 1 << 18;                // polls before a waiting expand part gives up
     PlanBuffers plan{};
     int max_tiles = 0;
     hipStream_t side = nullptr;
@@ -248,7 +243,7 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
-enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2, PROF_APPLY = 3 };
+enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2 };
 
 // Events for the next dispatch while profiling (none once the reserve is used up).
 LaunchTiming next_timing(lora_ctx *c, int kind)
@@ -405,37 +400,6 @@ int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipSt
     return LORA_OK;
 }
 
-// lora_apply of a planned bf16 batch: shrink and expand in one launch.
-int run_apply_one_launch(lora_ctx *c, int n, const int32_t *modules, const void *const *x,
-                         void *const *y, hipStream_t s)
-{
-    const int T = c->plan_T;
-    if (T > 0) {
-        int rc = before_launch(c, s);
-        if (rc)
-            return rc;
-        const ShrinkArgs sa = shrink_args(c, n, modules, x);
-        const ExpandArgs ea = expand_args(c, n, modules, y);
-        ChainArgs ca;
-        std::memset(&ca, 0, sizeof ca);
-        ca.sync = c->sync;
-        ca.sync_words = c->sync_words;
-        ca.tiles_stride = c->max_tiles;
-        ca.parity = (int)(c->sync_generation & 1u);
-        ca.n_shrink = sa.grid_tiles * sa.grid_splits * n;
-        ca.spin_limit = c->spin_limit;
-        ca.flags = c->plan.flags;
-        HIP_TRY(c, launch_apply(sa, ea, ca, group_meta(c, n, modules), s, next_timing(c, PROF_APPLY)));
-        c->sync_generation += 1;
-        if (c->plan_mode == kPlanInline)
-            c->plan_mode = kPlanTiles;   // later launches read the plan this one published
-        c->stats.applies_one_launch += n;
-    }
-    c->last_n = 0;                // the h of this launch is not kept for a lora_expand
-    c->shrink_epoch = c->slot_epoch;
-    return LORA_OK;
-}
-
 int check_group(lora_ctx *c, int32_t n, const int32_t *modules)
 {
     if (n < 1 || n > LORA_MAX_GROUP || !modules)
@@ -563,17 +527,7 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         if (v >= 1 && v <= kMaxSplits)
             c->max_splits = v;
     }
-    if (const char *env = std::getenv("LORA_MI355X_ONE_LAUNCH"))
-        c->one_launch = std::atoi(env) != 0;
-    if (const char *env = std::getenv("LORA_MI355X_SPIN_LIMIT")) {
-        const int v = std::atoi(env);
-        if (v >= 0)
-            c->spin_limit = v;
-    }
     c->max_tiles = max_tiles_for(max_tokens, max_loras);
-    c->sync_words = 1 + kMaxGroup * c->max_tiles;
-    if (e == hipSuccess)
-        e = dalloc(c, &c->sync, sizeof(uint32_t) * 2 * (size_t)c->sync_words);
     if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
     if (e == hipSuccess)
         e = dalloc(c, &c->hpart, sizeof(float) * (size_t)kMaxGroup * c->hbuf_rows * c->R_pad);
@@ -812,8 +766,6 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
             return rc;
         }
     }
-    if (ctx->one_launch && ctx->dtype == LORA_BF16)
-        return run_apply_one_launch(ctx, n, modules, x, y, s);
     rc = run_shrink(ctx, n, modules, x, s);
     if (rc)
         return rc;

@@ -2,7 +2,6 @@
 the HIP path through the C ABI, run the oracle on the same bits, compare."""
 from __future__ import annotations
 
-import os
 import sys
 
 import numpy as np
@@ -48,23 +47,11 @@ def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, np.float32).astype(np.float64)
 
 
-def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None,
-               one_launch=None) -> binding.Slots:
-    """Create a ctx for the workload's modules and load every slot's adapter.
-    one_launch: force bf16 lora_apply to one launch (True) or two (False)."""
-    prev = os.environ.get("LORA_MI355X_ONE_LAUNCH")
-    if one_launch is not None:
-        os.environ["LORA_MI355X_ONE_LAUNCH"] = "1" if one_launch else "0"
-    try:
-        S = binding.Slots(wl.max_loras, max_rank or wl.max_rank,
-                          [(m.d_in, m.d_out) for m in wl.modules], wl.dtype,
-                          max_tokens or max(wl.n_tokens, 1))
-    finally:
-        if one_launch is not None:
-            if prev is None:
-                del os.environ["LORA_MI355X_ONE_LAUNCH"]
-            else:
-                os.environ["LORA_MI355X_ONE_LAUNCH"] = prev
+def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None) -> binding.Slots:
+    """Create a ctx for the workload's modules and load every slot's adapter."""
+    S = binding.Slots(wl.max_loras, max_rank or wl.max_rank,
+                      [(m.d_in, m.d_out) for m in wl.modules], wl.dtype,
+                      max_tokens or max(wl.n_tokens, 1))
     pinned = [] if keep is None else keep
     for k, ad in enumerate(wl.adapters):
         if ad is None:
@@ -88,7 +75,7 @@ def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None,
 def run_gpu(wl: synth.Workload, S: binding.Slots, prepare=True, path="apply"):
     """Update every module once; returns {module name: y after (numpy bits)}.
 
-    path "apply": lora_apply per module (bf16: shrink and expand in one launch);
+    path "apply": lora_apply per module;
     "split": lora_shrink then lora_expand per module on a prepared plan.
     """
     idx = torch.from_numpy(wl.idx).cuda()

@@ -127,13 +127,12 @@ def test_sweep(case):
     Sl.close()
 
 
-# bf16 lora_apply runs shrink and expand in one launch (apply_bf16_kernel); the
-# split path (lora_shrink, lora_expand) runs the same arithmetic in two.  Cases:
-# K ranges that end in a partial K block, column counts that are not a multiple
-# of a wave's 64 columns, tiles of every length 1..64, 256 slots, one token, the
-# largest inline-planned batch, batches above it (plan kernels, segment path),
-# every padded-rank class.
-ONE_LAUNCH_SWEEP = [
+# lora_apply against the separate lora_shrink / lora_expand entry points and the
+# oracle: K ranges that end in a partial K block, column counts that are not a
+# multiple of a wave's 64 columns, tiles of every length 1..64, 256 slots, one
+# token, the largest inline-planned batch, batches above it (plan kernels,
+# segment path), every padded-rank class.
+APPLY_SWEEP = [
     # (d_in, d_out) list, max_loras, R, ranks, T, p_base_only, zipf_s
     ([(136, 264)], 8, 32, [1, 3, 16, 17, 31, 32, 8, 2], 300, 0.1, 1.1),
     ([(8, 8), (24, 1000)], 4, 16, [16, 1, 9, 4], 257, 0.05, 0.5),
@@ -148,40 +147,34 @@ ONE_LAUNCH_SWEEP = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(ONE_LAUNCH_SWEEP)))
-def test_one_launch_apply_matches_split_path_and_oracle(case):
-    shapes, S_, R, ranks, T, pb, zs = ONE_LAUNCH_SWEEP[case]
+@pytest.mark.parametrize("case", range(len(APPLY_SWEEP)))
+def test_apply_matches_split_entry_points_and_oracle(case):
+    shapes, S_, R, ranks, T, pb, zs = APPLY_SWEEP[case]
     mods = [synth.Module(f"m{i}", a, b) for i, (a, b) in enumerate(shapes)]
     wl = synth.random_case(200 + case, synth.BF16, mods, T, S_, R, ranks, p_base_only=pb,
                            zipf_s=zs)
-    log(f"case one-launch sweep {case}: {shapes} S={S_} R={R} T={T}")
-    Sl = make_slots(wl, one_launch=True)
-    one = run_gpu(wl, Sl)
-    assert Sl.stats()["applies_one_launch"] == len(mods)
+    log(f"case apply sweep {case}: {shapes} S={S_} R={R} T={T}")
+    Sl = make_slots(wl)
+    applied = run_gpu(wl, Sl)
     split = run_gpu(wl, Sl, path="split")
     assert Sl.flags() == 0
-    Sl.close()
-    Sl = make_slots(wl, one_launch=False)
-    two = run_gpu(wl, Sl)
-    assert Sl.stats()["applies_one_launch"] == 0
     for m in mods:
-        assert np.array_equal(one[m.name], split[m.name]), m.name
-        assert np.array_equal(two[m.name], split[m.name]), m.name
-        check_close(one[m.name], run_oracle(wl, m.name), wl.dtype, f"one-launch sweep {case} {m.name}")
+        assert np.array_equal(applied[m.name], split[m.name]), m.name
+        check_close(applied[m.name], run_oracle(wl, m.name), wl.dtype, f"apply sweep {case} {m.name}")
         skipped = np.ones(T, bool)
         for k, ad in enumerate(wl.adapters):
             if ad is not None and m.name in ad.At:
                 skipped &= wl.idx != k
-        assert np.array_equal(one[m.name][skipped], wl.y[m.name][skipped])
+        assert np.array_equal(applied[m.name][skipped], wl.y[m.name][skipped])
     Sl.close()
 
 
-def test_one_launch_counters_across_batch_sizes():
-    """Consecutive one-launch applies on one ctx with changing batch sizes (and so
-    changing grids) use alternating counter sets; each equals the split path."""
+def test_consecutive_batches_of_changing_size_on_one_ctx():
+    """Batches of changing sizes on one ctx switch between the in-kernel plan and
+    the plan kernels; every apply equals the separate entry points on its batch."""
     mods = [synth.Module("a", 640, 384)]
     wl = synth.random_case(31, synth.BF16, mods, 3000, 6, 32, [32, 16, 8, 4, 32, 1], p_base_only=0.05)
-    S = make_slots(wl, max_tokens=3000, one_launch=True)
+    S = make_slots(wl, max_tokens=3000)
     x = to_dev(wl.x["a"], wl.dtype)
     for T in (3000, 100, 1, 1024, 1025, 3000, 64, 700):
         idx = torch.from_numpy(wl.idx[:T]).cuda()
@@ -266,7 +259,7 @@ def test_padding_to_max_rank_changes_nothing(dtype, path, wide):
 def test_deterministic_and_prepared_plan_matches_unprepared(R):
     """Repeated runs are bit-identical, whether the plan is computed in the kernel
     or read from an earlier launch, and the separate shrink / expand entry points
-    equal the one-launch apply."""
+    equal lora_apply."""
     wl = synth.random_case(11, synth.BF16, [synth.Module("a", 1024, 2048)], 700, 8, R,
                            [32, 16, 8, 4, 32, 16, 8, 4])
     S = make_slots(wl)
@@ -495,12 +488,4 @@ def test_profile_times_every_dispatch():
     S.apply(xs[0], ys[0], idx, 0)
     p = S.profile_end()
     assert p["launches"]["shrink"] == 1 and p["untimed"] == 3
-    S.close()
-    S = make_slots(wl, one_launch=True)
-    S.profile_begin(1)
-    S.apply(xs[0], ys[0], idx, 0)                        # one dispatch per apply
-    S.apply(xs[0], ys[0], idx, 0)
-    p = S.profile_end()
-    assert p["launches"]["apply"] == 1 and p["untimed"] == 1
-    assert p["launches"]["shrink"] + p["launches"]["expand"] == 0
     S.close()
