@@ -117,6 +117,7 @@ struct ExpandArgs {
     int32_t R_pad;
     int32_t grid_tiles;
     int32_t grid_cols;                  // max column chunks over the members
+    int32_t xcd_group;                  // work items per XCD group (bf16 kernel)
 };
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,

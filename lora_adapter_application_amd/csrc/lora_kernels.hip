@@ -626,6 +626,20 @@ struct TilePlanLds {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// The chip dispatches the workgroups of a launch to its 8 XCDs in turn
+// (workgroup i to XCD i mod 8), and each XCD has an L2 of its own.  Work items
+// are taken in groups of G consecutive items; group k runs on XCD k mod 8, its
+// items one after the other, so they share that XCD's L2, while consecutive
+// groups still spread over all XCDs.  The launch has xcd_grid(n, G)
+// workgroups; items >= n are padding.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_item(int G)
+{
+    const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+    return ((j / G) * kXcds + xcd) * G + j % G;
+}
+
 constexpr int kPlanPerThread = kInlinePlanTokens / 256;
 
 // The batch's slot indices, thread tid holding tokens c*256 + tid (-1 past T).
@@ -787,39 +801,45 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int spli
 // path, shorter ones the gather path single-buffered.  Otherwise every tile
 // takes the gather path, double-buffered when the rank allows.  PLAN: how the
 // workgroup finds its tile (PlanMode).
+// Work item w = (tile * grid_splits + split) * n + member, in groups of n: the
+// members of one (tile, K split) run back to back on one XCD, so when they
+// share x (q, k and v of a layer) x comes from HBM once and from L2 after.
 template <int NB, bool MIXED, int PLAN>
 __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
 {
-    const int m = blockIdx.z;
+    const int w = xcd_item(a.n);
+    if (w >= a.grid_tiles * a.grid_splits * a.n)
+        return;
+    const int m = w % a.n, split = (w / a.n) % a.grid_splits, bt = w / (a.n * a.grid_splits);
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
     __shared__ __attribute__((aligned(16))) unsigned char lds[shrink_smem_bytes(NB, MIXED)];
     Tile tile;
     int tokv;
+    const bool lead = split == 0 && m == 0;     // publishes the tile
     if constexpr (PLAN == kPlanInline) {
         __shared__ TilePlanLds P;
-        const bool y0z0 = blockIdx.y == 0 && blockIdx.z == 0;
         int v[kPlanPerThread];
         plan_load_idx(a.idx, a.T, v);
-        if (!plan_tile(v, a.S, mr, a.plan, P, blockIdx.x, y0z0, y0z0 && blockIdx.x == 0, tile, tokv))
+        if (!plan_tile(v, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv))
             return;
     } else {
         const int n_tiles = *a.plan.n_tiles;
-        tile = a.plan.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
-        tokv = a.plan.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
-        if ((int)blockIdx.x >= n_tiles)
+        tile = a.plan.tiles[bt];              // in bounds: the tile buffer covers the grid
+        tokv = a.plan.tile_tok[(int64_t)bt * kTileTokens + lane];
+        if (bt >= n_tiles)
             return;
         // lookups in code every lane runs (see meta_scale), stores by one lane
         tile.rank = meta_rank(mr, tile.slot);
         tile.scale = meta_scale(mr, tile.slot);
-        if (blockIdx.y == 0 && m == 0 && threadIdx.x == 0) {
-            a.plan.tiles[blockIdx.x].rank = tile.rank;
-            a.plan.tiles[blockIdx.x].scale = tile.scale;
+        if (lead && threadIdx.x == 0) {
+            a.plan.tiles[bt].rank = tile.rank;
+            a.plan.tiles[bt].scale = tile.scale;
         }
     }
-    if ((int)blockIdx.y >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
+    if (split >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
-    shrink_tile<NB, MIXED>(a, m, blockIdx.y, tile, tokv, lds);
+    shrink_tile<NB, MIXED>(a, m, split, tile, tokv, lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -1032,31 +1052,39 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
         }
     }
     __syncthreads();
-    if (!cols_ok)
-        return;
-    expand_store<NB, 4, HS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase, d_out, cb);
+    if (cols_ok)
+        expand_store<NB, 4, HS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase, d_out, cb);
 }
 
 constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 
 // Tiles as the shrink published them, with rank and scale of the slot as that
-// shrink saw them.
+// shrink saw them.  Work item w = (member * grid_cols + chunk) * grid_tiles +
+// tile, in XCD groups of a.xcd_group: in a large batch, long runs of tiles
+// (mostly of one slot) of one column chunk run on one XCD and read that slot's
+// B columns from L2; a small batch keeps groups of 1 (plain round-robin), which
+// balances its few, uneven tiles over the XCDs.
 template <int NB>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
-    const int m = blockIdx.z;
+    const int n_items = a.grid_tiles * a.grid_cols * a.n;
+    const int w = xcd_item(a.xcd_group);
+    if (w >= n_items)
+        return;
+    const int bt = w % a.grid_tiles, chunk = (w / a.grid_tiles) % a.grid_cols;
+    const int m = w / (a.grid_tiles * a.grid_cols);
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
     const int n_tiles = *a.n_tiles;
-    const Tile tile = a.tiles[blockIdx.x];      // in bounds: the tile buffer covers the grid
-    const int tokv = a.tile_tok[(int64_t)blockIdx.x * kTileTokens + lane];
-    if ((int)blockIdx.x >= n_tiles || (int)blockIdx.y * kExpandCols >= a.d_out[m])
+    const Tile tile = a.tiles[bt];              // in bounds: the tile buffer covers the grid
+    const int tokv = a.tile_tok[(int64_t)bt * kTileTokens + lane];
+    if (bt >= n_tiles || chunk * kExpandCols >= a.d_out[m])
         return;
     if (tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
     __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB)];
     __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB)];
-    expand_tile<NB>(a, m, blockIdx.y, tile, tokv, hs_hi, hs_lo);
+    expand_tile<NB>(a, m, chunk, tile, tokv, hs_hi, hs_lo);
 }
 
 // ----------------------------------------------------------------------------
@@ -1177,6 +1205,14 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta 
 // ----------------------------------------------------------------------------
 // launches
 
+// Workgroups for n work items in XCD groups of G (xcd_item): whole rounds of
+// 8 groups.
+static dim3 xcd_grid(int64_t n, int G)
+{
+    const int64_t groups = (n + G - 1) / G;
+    return dim3((unsigned)((groups + kXcds - 1) / kXcds * kXcds * G));
+}
+
 template <bool MIXED, int PLAN>
 static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st,
                                const LaunchTiming &t)
@@ -1196,14 +1232,15 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
                          const LaunchTiming &t)
 {
     const dim3 grid(a.grid_tiles, a.grid_splits, a.n), block(256);
+    const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.grid_splits * a.n, a.n);
     if (!bf16)
         launch(shrink_f32_kernel, grid, block, 0, st, t, a, m);
     else if (a.plan_mode == kPlanInline)
-        launch_shrink_bf16<false, kPlanInline>(a, m, grid, st, t);
+        launch_shrink_bf16<false, kPlanInline>(a, m, g, st, t);
     else if (a.mixed)
-        launch_shrink_bf16<true, kPlanTiles>(a, m, grid, st, t);
+        launch_shrink_bf16<true, kPlanTiles>(a, m, g, st, t);
     else
-        launch_shrink_bf16<false, kPlanTiles>(a, m, grid, st, t);
+        launch_shrink_bf16<false, kPlanTiles>(a, m, g, st, t);
     return hipGetLastError();
 }
 
@@ -1214,15 +1251,16 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
     if (!bf16) {
         launch(expand_f32_kernel, grid, block, 0, st, t, a, m);
     } else {
+        const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.grid_cols * a.n, a.xcd_group);
         const int nbmax = a.R_pad / 16;
         if (nbmax <= 1)
-            launch(expand_bf16_kernel<1>, grid, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<1>, g, block, 0, st, t, a, m);
         else if (nbmax <= 2)
-            launch(expand_bf16_kernel<2>, grid, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<2>, g, block, 0, st, t, a, m);
         else if (nbmax <= 4)
-            launch(expand_bf16_kernel<4>, grid, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<4>, g, block, 0, st, t, a, m);
         else
-            launch(expand_bf16_kernel<8>, grid, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<8>, g, block, 0, st, t, a, m);
     }
     return hipGetLastError();
 }

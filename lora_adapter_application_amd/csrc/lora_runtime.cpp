@@ -361,6 +361,9 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
     a.grid_tiles = max_tiles_for(T, c->S);
+    // large batches: one contiguous run of tiles per XCD; small: round-robin
+    const int64_t items = (int64_t)a.grid_tiles * a.grid_cols * n;
+    a.xcd_group = T > kInlinePlanTokens ? (int)((items + 7) / 8) : 1;
     return a;
 }
 
