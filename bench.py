@@ -11,6 +11,13 @@ like the layers of a model) so that the bytes the kernels read come from HBM
 rather than from the 256 MB Infinity Cache.  Inputs are resident
 in HBM before timing starts.  Prints one JSON line.
 
+Launch: by default the library calls of the L steps of one rotation are
+captured once into a HIP graph (torch.cuda.graph over the library's own
+launches) and the timed region replays it, as a serving engine replays its
+decode step; the same K steps launched eagerly from Python are timed too and
+reported as "eager" (that rate includes the host cost of the Python binding).
+--launch eager times the eager calls instead.
+
 value      tokens of the batch (skipped tokens included) x K / wall time of K steps
 roofline   the kernel with the largest share of the step: its algorithmic bytes /
            its kernel time, from start / stop events the library attaches to each of
@@ -54,6 +61,8 @@ def parse():
                    help="minimum footprint of the rotated layer sets (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--launch", choices=["graph", "eager"], default="graph",
+                   help="timed region: replays of the captured steps, or eager calls")
     p.add_argument("--no-kernel-timing", action="store_true",
                    help="time the steps without per-dispatch kernel events (roofline then null)")
     p.add_argument("--calib-copy", action="store_true",
@@ -192,12 +201,41 @@ def main():
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    # timed region: K steps, nothing but the library calls
+    # eager: K steps, nothing but the library calls
     t0 = time.perf_counter()
     for i in range(K):
         step(args.warmup + i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    eager_s = time.perf_counter() - t0
+    if args.launch == "graph":
+        # the L steps of one rotation (and the K mod L first ones) captured once;
+        # K steps = K // L replays of the first graph and one of the second
+        slots.sync_loads()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for n_steps in (L, K % L):
+            if n_steps == 0 or (n_steps == L and K < L):
+                graphs.append(None)
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(n_steps):
+                    step(i)
+            graphs.append(g)
+        for g in graphs:                # one untimed replay each
+            if g is not None:
+                g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K // L):
+            graphs[0].replay()
+        if graphs[1] is not None:
+            graphs[1].replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        elapsed = eager_s
     ms_per_step = elapsed / K * 1e3
     value = T * K / elapsed
     if use_timing:
@@ -275,10 +313,12 @@ def main():
                    "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
                    "max_loras": S, "max_rank": R, "ranks": sorted({a.r for a in wl.adapters if a}),
                    "layer_sets_rotated": L, "groups": [[names[j] for j in g] for g in groups],
+                   "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "kernel_timing": "per-dispatch events" if use_timing else "none",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "eager": {"ms_per_step": round(eager_s / K * 1e3, 5), "value": round(T * K / eager_s, 1)},
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

@@ -30,6 +30,17 @@
  *  - Element type of x, y, A and B is the ctx dtype: bf16 (raw 16-bit
  *    patterns) or fp32.  Accumulation is always fp32; a bf16 y is rounded once,
  *    to nearest even.
+ *  - Graph capture: the launching calls may be captured into a HIP graph
+ *    (hipStreamBeginCapture on a non-null stream) and the graph replayed.
+ *    Each launch takes the slot metadata (rank, scale, target modules) by
+ *    value when it is enqueued, so a replay uses the metadata as of the
+ *    capture and the adapter weights as they are at the replay: reloading a
+ *    slot with an adapter of the same rank, lora_alpha and targets is seen by
+ *    later replays; any other load or clear needs a new capture.  Loads must be
+ *    complete before the capture starts (lora_sync_loads), else the first
+ *    captured launch fails with LORA_ERR_INVALID_ARGUMENT.  Launches under
+ *    capture are never timed (lora_profile_begin).  No load or clear may be
+ *    issued while a capture is open.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -129,7 +140,9 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
  * no device work is enqueued. */
 int lora_slot_clear(lora_ctx *ctx, int32_t slot);
 
-/* Host waits until every load issued so far has completed. */
+/* Host waits until every load issued so far has completed; launches after it
+ * need not wait for those loads on the device (required before a graph
+ * capture). */
 int lora_sync_loads(lora_ctx *ctx);
 
 /*

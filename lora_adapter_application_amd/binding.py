@@ -130,6 +130,9 @@ def _ptr(t) -> Optional[int]:
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:      # the raw handle, without building a Stream object
+            return int(raw(torch.cuda.current_device())) or None
         return int(torch.cuda.current_stream().cuda_stream) or None
     if isinstance(stream, int):
         return stream or None

@@ -87,6 +87,7 @@ struct lora_ctx {
     hipStream_t side = nullptr;
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
+    uint64_t synced_gen = 0;                 // loads the host has seen complete (lora_sync_loads)
     std::vector<StreamState> streams;
     // plan state; an inline plan is computed by every shrink launch itself
     bool plan_valid = false, plan_prepared = false;
@@ -150,12 +151,29 @@ StreamState *stream_state(lora_ctx *c, hipStream_t s)
 }
 
 // Make stream s wait for all loads issued so far, and mark it as in use.
+bool stream_capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();   // a query error must not surface at a later call
+        return false;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// A stream that is being captured into a graph cannot wait for the load event,
+// which was recorded outside the capture: loads must be complete (on the host,
+// lora_sync_loads) before a capture starts.
 int before_launch(lora_ctx *c, hipStream_t s)
 {
     StreamState *st = stream_state(c, s);
     if (!st)
         return fail(c, LORA_ERR_HIP, "hipEventCreateWithFlags failed");
-    if (st->waited_gen < c->load_gen) {
+    if (st->waited_gen < c->load_gen && c->synced_gen < c->load_gen) {
+        if (stream_capturing(s))
+            return fail(c, LORA_ERR_INVALID_ARGUMENT,
+                        "slot loads pending on a stream under graph capture: call lora_sync_loads "
+                        "before the capture");
         HIP_TRY(c, hipStreamWaitEvent(s, c->load_done, 0));
         st->waited_gen = c->load_gen;
     }
@@ -245,12 +263,13 @@ int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
 enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2 };
 
-// Events for the next dispatch while profiling (none once the reserve is used up).
-LaunchTiming next_timing(lora_ctx *c, int kind)
+// Events for the next dispatch while profiling (none once the reserve is used
+// up, and none for a dispatch captured into a graph).
+LaunchTiming next_timing(lora_ctx *c, int kind, hipStream_t s)
 {
     if (!c->profiling)
         return LaunchTiming{};
-    if (c->prof_used >= c->prof_cap) {
+    if (c->prof_used >= c->prof_cap || stream_capturing(s)) {
         c->prof_untimed += 1;
         return LaunchTiming{};
     }
@@ -283,9 +302,9 @@ int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
         if (rc)
             return rc;
         LaunchTiming t[2];
-        t[0] = next_timing(c, PROF_PLAN);
+        t[0] = next_timing(c, PROF_PLAN, s);
         if (T > 1024)
-            t[1] = next_timing(c, PROF_PLAN);
+            t[1] = next_timing(c, PROF_PLAN, s);
         HIP_TRY(c, launch_plan(idx, T, c->S, c->plan, s, t));
     }
     if (T > 0)
@@ -376,7 +395,7 @@ int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x,
             return rc;
         const ShrinkArgs a = shrink_args(c, n, modules, x);
         HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
-                                 next_timing(c, PROF_SHRINK)));
+                                 next_timing(c, PROF_SHRINK, s)));
         if (c->plan_mode == kPlanInline)
             c->plan_mode = kPlanTiles;   // later launches read the plan this one published
         c->stats.shrinks += n;
@@ -397,7 +416,7 @@ int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipSt
             return rc;
         const ExpandArgs a = expand_args(c, n, modules, y);
         HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
-                                 next_timing(c, PROF_EXPAND)));
+                                 next_timing(c, PROF_EXPAND, s)));
         c->stats.expands += n;
     }
     return LORA_OK;
@@ -657,6 +676,7 @@ int lora_sync_loads(lora_ctx *ctx)
         return LORA_ERR_INVALID_ARGUMENT;
     DeviceGuard guard(ctx->device);
     HIP_TRY(ctx, hipStreamSynchronize(ctx->side));
+    ctx->synced_gen = ctx->load_gen;
     return LORA_OK;
 }
 
