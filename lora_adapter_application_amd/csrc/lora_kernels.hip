@@ -510,7 +510,7 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
     }
 }
 
-// Segment path (SGMV) for tiles of 33..64 tokens: wave w owns subtile w over
+// Segment path (SGMV) for tiles of 17..64 tokens: wave w owns subtile w over
 // the whole K range.  Each K block of A^T (nb*16 ranks x 128) is loaded once per
 // workgroup into LDS (double buffered) and shared by the 4 waves; x is
 // prefetched two K blocks ahead in registers.
@@ -770,10 +770,15 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs 
     return true;
 }
 
+// Tiles of more than this many tokens take the segment path: their A^T blocks
+// are shared by two to four waves, so staging them once in LDS saves the L2
+// reads of the other waves.
+constexpr int kSegmentMinTokens = 16;
+
 // LDS of a shrink workgroup: K-split reduction, or the segment path's A stage.
-constexpr int shrink_smem_bytes(int NB, bool MIXED)
+constexpr int shrink_smem_bytes(int NB)
 {
-    return cmax(4 * NB * 64 * 16, MIXED ? 2 * NB * 16 * kLdsRow * 2 : 0);
+    return cmax(4 * NB * 64 * 16, 2 * NB * 16 * kLdsRow * 2);
 }
 
 // The shrink of one tile for K split `split` of member m: writes the member's h
@@ -791,16 +796,15 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int spli
     v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
     v.h = a.hpart + m * a.member_stride + (int64_t)split * a.split_stride;
     v.R_pad = a.R_pad;
-    if (MIXED && tile.len > 32)
+    if (tile.len > kSegmentMinTokens)
         shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
     else
         shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
 }
 
-// MIXED: batches above 1024 tokens; tiles of 33..64 tokens take the segment
-// path, shorter ones the gather path single-buffered.  Otherwise every tile
-// takes the gather path, double-buffered when the rank allows.  PLAN: how the
-// workgroup finds its tile (PlanMode).
+// Tiles of 17..64 tokens take the segment path, shorter ones the gather path:
+// single-buffered when MIXED (batches above 1024 tokens), else double-buffered
+// when the rank allows.  PLAN: how the workgroup finds its tile (PlanMode).
 // Work item w = (tile * grid_splits + split) * n + member, in groups of n: the
 // members of one (tile, K split) run back to back on one XCD, so when they
 // share x (q, k and v of a layer) x comes from HBM once and from L2 after.
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
     const int m = w % a.n, split = (w / a.n) % a.grid_splits, bt = w / (a.n * a.grid_splits);
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
-    __shared__ __attribute__((aligned(16))) unsigned char lds[shrink_smem_bytes(NB, MIXED)];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[shrink_smem_bytes(NB)];
     Tile tile;
     int tokv;
     const bool lead = split == 0 && m == 0;     // publishes the tile
@@ -854,7 +858,10 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
 // and y is read and written 32 bytes per lane.  Every global load of the wave
 // (token ids, B, y, h partials) is issued before any arithmetic.  The K-split
 // partials of h are summed once per workgroup and split into a bf16 high part
-// and a bf16 low part (h - high) in LDS; two MFMAs per step keep ~16 bits of h.
+// and a bf16 low part (h - high) in LDS.  One v_mfma_f32_16x16x32_bf16 covers a
+// block of 16 ranks with both parts stacked along K (lane groups 0-1 the high
+// part of ranks 0-7 / 8-15, lane groups 2-3 the low part, against the same B
+// values), which keeps ~16 bits of h.
 
 // Operand loads of the expand are unconditional: a lane whose element lies
 // outside the data reads the first element instead, and that value only reaches
@@ -864,20 +871,21 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
 // instruction needs.
 
 // B operands of one wave's 64 columns cb..cb+63: lane row -> column
-// cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 4g..4g+3.
+// cb + (row/4)*16 + b*4 + row%4, ranks kst*16 + 8(g&1) .. +7 (one 16-byte
+// group of the repacked B; lane groups g and g+2 read the same bytes).
 template <int NB>
-__device__ __forceinline__ void load_b_ops(uint2 (&bop)[NB][4], const uint16_t *Bslot, int d_out,
+__device__ __forceinline__ void load_b_ops(uint4 (&bop)[NB][4], const uint16_t *Bslot, int d_out,
                                            int cb, int nb, bool cols_ok)
 {
     const int lane = threadIdx.x & 63, row = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kst = 0; kst < NB; ++kst) {
-        const int G = kst * 2 + (g >> 1);
+        const int G = kst * 2 + (g & 1);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int n = cb + (row >> 2) * 16 + b * 4 + (row & 3);
             const bool ok = kst < nb && cols_ok && n < d_out;
-            bop[kst][b] = *(const uint2 *)(Bslot + (ok ? ((int64_t)G * d_out + n) * 8 + (g & 1) * 4 : 0));
+            bop[kst][b] = *(const uint4 *)(Bslot + (ok ? ((int64_t)G * d_out + n) * 8 : 0));
         }
     }
 }
@@ -915,7 +923,7 @@ __device__ __forceinline__ void split_hi_lo(const f32x4_t h, uint2 &hi, uint2 &l
 // are not stored.
 template <int NB, int NSUB, int HS>
 __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16_t *hs_lo,
-                                             const uint2 (&bop)[NB][4], const uint4 (&yv)[NSUB][2],
+                                             const uint4 (&bop)[NB][4], const uint4 (&yv)[NSUB][2],
                                              const int (&tok)[NSUB], const bool (&tok_ok)[NSUB],
                                              int nsub, int nb, float s, uint16_t *ybase, int d_out,
                                              int cb)
@@ -932,15 +940,13 @@ __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16
 #pragma unroll
         for (int kst = 0; kst < NB; ++kst) {
             if (kst < nb) {
-                const int o = (st * 16 + row) * HS + kst * 16 + g * 4;
-                const s16x4_t hhi = __builtin_bit_cast(s16x4_t, *(const uint2 *)(hs_hi + o));
-                const s16x4_t hlo = __builtin_bit_cast(s16x4_t, *(const uint2 *)(hs_lo + o));
+                // lane groups 0-1: high part, 2-3: low part, of ranks kst*16 + 8(g&1) ..
+                const int o = (st * 16 + row) * HS + kst * 16 + (g & 1) * 8;
+                const bf16x8_t hv = __builtin_bit_cast(bf16x8_t, *(const uint4 *)((g < 2 ? hs_hi : hs_lo) + o));
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const s16x4_t bo = __builtin_bit_cast(s16x4_t, bop[kst][b]);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hhi, acc[b], 0, 0, 0);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bo, hlo, acc[b], 0, 0, 0);
-                }
+                for (int b = 0; b < 4; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bop[kst][b]),
+                                                                     hv, acc[b], 0, 0, 0);
             }
         }
         if (tok_ok[st]) {
@@ -1034,7 +1040,7 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
     }
     f32x4_t hsum[NB];
     load_h_sums<NB>(hsum, a, m, tile, nb);
-    uint2 bop[NB][4];
+    uint4 bop[NB][4];
     load_b_ops<NB>(bop, (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m], d_out,
                    cb, nb, cols_ok);
     uint4 yv[4][2];
