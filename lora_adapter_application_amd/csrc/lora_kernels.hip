@@ -512,14 +512,23 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
 
 // Segment path (SGMV) for tiles of 17..64 tokens: wave w owns subtile w over
 // the whole K range.  Each K block of A^T (nb*16 ranks x 128) is loaded once per
-// workgroup into LDS (double buffered) and shared by the 4 waves; x is
-// prefetched two K blocks ahead in registers.
+// workgroup into LDS (double buffered) and shared by the 4 waves.  The loads of
+// the next D blocks (x in registers, A^T in registers until staged) are in
+// flight while a block is multiplied, so a workgroup keeps D blocks of memory
+// requests outstanding instead of waiting one round trip per block.  The ring
+// of D register sets is indexed statically (the loop is unrolled by D), so no
+// register holding an outstanding load is ever copied.
 constexpr int kLdsRow = kShrinkKBlock + 8;   // bf16 elements per staged A row (padded)
+
+// Blocks in flight of the segment path: deeper for low rank, where the
+// register sets are small.
+constexpr int sgmv_depth(int NB) { return NB <= 2 ? 4 : NB == 4 ? 3 : 2; }
 
 template <int NB>
 __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
                                             uint16_t *lds)
 {
+    constexpr int D = sgmv_depth(NB);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row = lane & 15, g = lane >> 4;
     const int t_in = wave * 16 + row;
@@ -530,75 +539,84 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &til
     const int nkb = (k1 - k0 + kShrinkKBlock - 1) / kShrinkKBlock;
     constexpr int buf_elems = NB * 16 * kLdsRow;
 
-    uint4 ra[NB];
-    auto load_a = [&](int kb) {
+    // Loads are unconditional, with addresses clamped into the operands (rank
+    // rows below nb*16, K below k1): a branch around a load would make the
+    // compiler wait for every outstanding load at the loop head.  A^T values
+    // past k1 are zeroed when staged, so the x values read there (clamped, finite)
+    // contribute nothing; rows past the tile read token 0 and are not stored.
+    const int r_last = nb * 16 - 1;
+    auto load_a = [&](uint4 (&ra)[NB], int kb) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int c = tid + 256 * i;
-            const int r = c >> 4, col = (c & 15) * 8;
-            ra[i] = (i < nb && kb + col < k1) ? ld16(v.A + (int64_t)r * v.d_in + kb + col)
-                                              : make_uint4(0, 0, 0, 0);
+            const int r = min(c >> 4, r_last), col = (c & 15) * 8;
+            ra[i] = ld16(v.A + (int64_t)r * v.d_in + min(kb + col, k1 - 8));
         }
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](const uint4 (&ra)[NB], int buf, int kb) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i < nb) {
                 const int c = tid + 256 * i;
                 const int r = c >> 4, col = (c & 15) * 8;
-                *(uint4 *)(lds + buf * buf_elems + r * kLdsRow + col) = ra[i];
+                *(uint4 *)(lds + buf * buf_elems + r * kLdsRow + col) =
+                    kb + col < k1 ? ra[i] : make_uint4(0, 0, 0, 0);
             }
         }
     };
     auto load_x = [&](uint4 (&xv)[4], int kb) {
         const int kk = kb + g * 32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ke = kk + q * 8;
-            xv[q] = (tok_ok && ke < k1) ? ld16(xrow + ke) : make_uint4(0, 0, 0, 0);
-        }
+        for (int q = 0; q < 4; ++q)
+            xv[q] = ld16(xrow + min(kk + q * 8, k1 - 8));
     };
 
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 x0[4], x1[4], x2[4];
-    load_a(k0);
-    load_x(x0, k0);
-    if (nkb > 1)
-        load_x(x1, k0 + kShrinkKBlock);
-    store_a(0);
-    if (nkb > 1)
-        load_a(k0 + kShrinkKBlock);
+    // ring slot j holds block i + j of the current pass (x) and, for A^T, the
+    // block after the one staged in LDS
+    uint4 xr[D][4], ar[D][NB];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        if (j < nkb) {
+            load_a(ar[j], k0 + j * kShrinkKBlock);
+            load_x(xr[j], k0 + j * kShrinkKBlock);
+        }
+    }
+    store_a(ar[0], 0, k0);
     __syncthreads();
-    for (int i = 0; i < nkb; ++i) {
-        const int kb = k0 + i * kShrinkKBlock;
-        if (i + 2 < nkb)
-            load_x(x2, kb + 2 * kShrinkKBlock);
-        const uint16_t *L = lds + (i & 1) * buf_elems;
+    for (int i = 0; i < nkb; i += D) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (b < nb) {
+        for (int j = 0; j < D; ++j) {
+            const int b = i + j;          // block multiplied in this step
+            if (b < nkb) {
+                const uint16_t *L = lds + (b & 1) * buf_elems;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 av = *(const uint4 *)(L + (b * 16 + row) * kLdsRow + g * 32 + q * 8);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, x0[q]),
-                        acc[b], 0, 0, 0);
+                for (int rb = 0; rb < NB; ++rb) {
+                    if (rb < nb) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint4 av = *(const uint4 *)(L + (rb * 16 + row) * kLdsRow + g * 32 + q * 8);
+                            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xr[j][q]),
+                                acc[rb], 0, 0, 0);
+                        }
+                    }
                 }
+                // slot j is free (A^T block b is in LDS, x block b consumed):
+                // refill it with block b + D
+                if (b + D < nkb) {
+                    load_x(xr[j], k0 + (b + D) * kShrinkKBlock);
+                }
+                // stage block b + 1 (slot j + 1) into the other LDS buffer
+                if (b + 1 < nkb)
+                    store_a(ar[(j + 1) % D], (b + 1) & 1, k0 + (b + 1) * kShrinkKBlock);
+                if (b + D < nkb)
+                    load_a(ar[j], k0 + (b + D) * kShrinkKBlock);
+                __syncthreads();
             }
-        }
-        if (i + 1 < nkb) {
-            store_a((i + 1) & 1);
-            if (i + 2 < nkb)
-                load_a(kb + 2 * kShrinkKBlock);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            x0[q] = x1[q];
-            x1[q] = x2[q];
         }
     }
     if (tok_ok) {
