@@ -60,6 +60,9 @@ def parse():
                    help="minimum footprint of the rotated layer sets (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--shared-x", action="store_true",
+                   help="the members of a group read one x buffer, as q, k and v read the layer "
+                        "input (the grouped shrink then fetches x from HBM once per group)")
     p.add_argument("--launch", choices=["graph", "eager"], default="eager",
                    help="which timed pass gives value: eager calls or graph replays")
     p.add_argument("--no-kernel-timing", action="store_true",
@@ -142,8 +145,18 @@ def main():
     S, R = wl.max_loras, wl.max_rank
     mods = wl.modules
     b = 2                                                   # bf16
+    names = [m.name for m in mods]
+    groups = [[names.index(n) for n in g] for g in GROUPS[wl.name]]
+    # with --shared-x, the first member of each group whose members have one d_in
+    # owns the x buffer the whole group reads
+    x_owner = list(range(len(mods)))
+    for g in groups:
+        if args.shared_x and len({mods[j].d_in for j in g}) == 1:
+            for j in g:
+                x_owner[j] = g[0]
     # rotation depth
-    per_set = sum(S * R * (m.d_in + m.d_out) * b + T * (m.d_in + 2 * m.d_out) * b for m in mods)
+    per_set = sum(S * R * (m.d_in + m.d_out) * b + T * 2 * m.d_out * b
+                  + (T * m.d_in * b if x_owner[j] == j else 0) for j, m in enumerate(mods))
     L = max(1, math.ceil(args.layer_bytes / per_set))
     log(f"workload {wl.name}: T={T} S={S} R={R} modules={[(m.name, m.d_in, m.d_out) for m in mods]}"
         f" layer sets={L} ({L * per_set / 1e9:.2f} GB)")
@@ -174,18 +187,20 @@ def main():
     idx = torch.from_numpy(wl.idx).to(dev)
     xs, ys = [], []
     for l in range(L):
-        for m in mods:
-            if l == 0:
+        for j, m in enumerate(mods):
+            if x_owner[j] != j:
+                xs.append(xs[l * len(mods) + x_owner[j]])
+            elif l == 0:
                 xs.append(dev_bits(wl.x[m.name]))
-                ys.append(dev_bits(wl.y[m.name]))
             else:
                 xs.append(torch.randn(T, m.d_in, generator=gen, device=dev).to(torch.bfloat16))
+            if l == 0:
+                ys.append(dev_bits(wl.y[m.name]))
+            else:
                 ys.append(torch.randn(T, m.d_out, generator=gen, device=dev).to(torch.bfloat16))
     torch.cuda.synchronize()
 
     nm = len(mods)
-    names = [m.name for m in mods]
-    groups = [[names.index(n) for n in g] for g in GROUPS[wl.name]]
     ng = len(groups)
     use_timing = not args.no_kernel_timing
 
@@ -256,7 +271,9 @@ def main():
         n = prof["launches"]
         tot = prof["total_ms"]
         # algorithmic bytes of one launch of each group
-        shrink_bytes = [sum(b * mods[j].d_in * (T_act + sum_r) for j in g) for g in groups]
+        # x once per buffer read (once per group with --shared-x) plus each used slot's A^T
+        shrink_bytes = [sum(b * mods[j].d_in * ((T_act if x_owner[j] == j else 0) + sum_r) for j in g)
+                        for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
         group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes}
         flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
@@ -311,6 +328,7 @@ def main():
                    "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
                    "max_loras": S, "max_rank": R, "ranks": sorted({a.r for a in wl.adapters if a}),
                    "layer_sets_rotated": L, "groups": [[names[j] for j in g] for g in groups],
+                   "shared_x": bool(args.shared_x),
                    "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "kernel_timing": "per-dispatch events" if use_timing else "none",
                    "parallelism": "none (1 GPU)"},
