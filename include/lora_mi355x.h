@@ -161,6 +161,28 @@ int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_to
                       void *stream);
 
 /*
+ * lora_plan_prepare, and a declaration of the slots the batch reads:
+ * used_slots is a host array of n_used slot indices (0..max_loras-1; repeats
+ * allowed).  The launches of this plan treat every other slot as empty (its
+ * tokens leave y untouched), so they read only the listed slots.  The library
+ * then records, per listed slot, an event after each lora_expand of the plan,
+ * and a later lora_slot_load into a slot waits only for the last such event of
+ * that slot instead of for every launch issued since the previous load.  A
+ * load into a slot that the batches in flight do not read therefore overlaps
+ * them: the next step's misses can be uploaded while this step computes.  The
+ * rule kept is that of "Multi-LoRA adapter cache in production" (oh-bug.com),
+ * section "GPU, CPU and disk form the adapter storage hierarchy": an adapter
+ * that in-flight work uses is never overwritten; the upload of a CPU hit is
+ * the H2D tier of the same section.
+ * Errors: a used_slots entry out of range -> LORA_ERR_SLOT_OUT_OF_RANGE;
+ * used_slots NULL with n_used > 0, or n_used < 0 -> LORA_ERR_INVALID_ARGUMENT.
+ * Under graph capture the declaration still limits the slots read, and loads
+ * fall back to waiting for every launch on the capturing stream.
+ */
+int lora_plan_prepare_slots(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_tokens,
+                            const int32_t *used_slots, int32_t n_used, void *stream);
+
+/*
  * lora_shrink: h = x . A_k for every planned token (fp32 intermediate of rank
  * R, held in the ctx).  x is [n_tokens][d_in] of the prepared plan.
  * Requires a prepared plan (else LORA_ERR_NO_PLAN).

@@ -37,7 +37,8 @@ LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_clear",
-           "lora_sync_loads", "lora_plan_prepare", "lora_shrink", "lora_expand", "lora_apply",
+           "lora_sync_loads", "lora_plan_prepare", "lora_plan_prepare_slots", "lora_shrink",
+           "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
            "lora_get_device_flags", "lora_get_stats", "lora_profile_begin", "lora_profile_end",
            "lora_status_string", "lora_last_error")
@@ -87,6 +88,7 @@ def load_library(path: str = LIB_PATH):
         "lora_slot_clear": ([P, I32], ctypes.c_int),
         "lora_sync_loads": ([P], ctypes.c_int),
         "lora_plan_prepare": ([P, P, I32, P], ctypes.c_int),
+        "lora_plan_prepare_slots": ([P, P, I32, P, I32, P], ctypes.c_int),
         "lora_shrink": ([P, P, I32, P], ctypes.c_int),
         "lora_expand": ([P, P, I32, P], ctypes.c_int),
         "lora_apply": ([P, P, P, P, I32, I32, P], ctypes.c_int),
@@ -209,6 +211,20 @@ def lora_plan_prepare(ctx, token_slot_idx, n_tokens: Optional[int] = None, strea
                                             int(n_tokens), _stream(stream)), ctx)
 
 
+def lora_plan_prepare_slots(ctx, token_slot_idx, used_slots: Sequence[int],
+                            n_tokens: Optional[int] = None, stream=None) -> None:
+    """lora_plan_prepare, declaring the (host) list of slots the batch reads."""
+    import torch
+    if n_tokens is None:
+        n_tokens = token_slot_idx.numel()
+    if n_tokens:
+        _require_cuda(token_slot_idx, "token_slot_idx", torch.int32, n_tokens)
+    used = [int(k) for k in used_slots]
+    arr = (ctypes.c_int32 * max(len(used), 1))(*used)
+    _check(load_library().lora_plan_prepare_slots(ctx, _ptr(token_slot_idx) if n_tokens else None,
+                                                  int(n_tokens), arr, len(used), _stream(stream)), ctx)
+
+
 def lora_shrink(ctx, x, module: int, stream=None) -> None:
     if x is not None:
         _require_cuda(x, "x")
@@ -318,8 +334,11 @@ class Slots:
     def sync_loads(self):
         lora_sync_loads(self.ctx)
 
-    def prepare(self, idx, n_tokens=None, stream=None):
-        lora_plan_prepare(self.ctx, idx, n_tokens, stream)
+    def prepare(self, idx, n_tokens=None, stream=None, used_slots=None):
+        if used_slots is None:
+            lora_plan_prepare(self.ctx, idx, n_tokens, stream)
+        else:
+            lora_plan_prepare_slots(self.ctx, idx, used_slots, n_tokens, stream)
 
     def shrink(self, x, module, stream=None):
         lora_shrink(self.ctx, x, module, stream)

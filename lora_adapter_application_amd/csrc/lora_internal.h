@@ -125,9 +125,20 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
 hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);
 
-// Slot maintenance, on the side stream.
-hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_slot,
-                                const void *B_stage, int32_t d_out, int32_t r, int32_t R_pad,
-                                hipStream_t st);
+// Slot maintenance, on the side stream: one launch finishes the loads of up to
+// kFinalizeBatch modules (B repack from its staged copy, zero padding rows).
+constexpr int kFinalizeBatch = 16;
+struct FinalizeItem {
+    void *A_slot;            // the slot's A^T block of the module
+    void *Bi_slot;           // the slot's repacked B block
+    const void *A_stage;     // r x d_in, row-major, staged on the device
+    const void *B_stage;     // r x d_out, row-major, staged on the device
+    int32_t d_in, d_out;
+};
+struct FinalizeBatch {
+    int32_t n, r, R_pad;
+    FinalizeItem it[kFinalizeBatch];
+};
+hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st);
 
 }  // namespace lora

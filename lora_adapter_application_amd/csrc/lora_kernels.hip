@@ -1292,14 +1292,22 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
 // ----------------------------------------------------------------------------
 // slot maintenance
 
-// Repack B (r x d_out, row-major, staged on the device) into groups of 8 ranks,
-// Bi[j/8][n][j%8], and zero ranks r..R_pad-1 of both A^T and B.
+// Copy A^T (r x d_in) from the stage into the slot, repack B (r x d_out,
+// row-major, staged) into groups of 8 ranks, Bi[j/8][n][j%8], and zero ranks
+// r..R_pad-1 of both; module blockIdx.y of the batch.  Rows are 16-byte
+// multiples (d_in, d_out multiples of 8), so A^T moves in 16-byte pieces.
 template <typename E>
-__global__ void slot_finalize_kernel(E *A_slot, int32_t d_in, E *Bi_slot, const E *B_stage,
-                                     int32_t d_out, int32_t r, int32_t R_pad)
+__global__ void slot_finalize_kernel(FinalizeBatch fb)
 {
+    const FinalizeItem &it = fb.it[blockIdx.y];
+    E *A_slot = (E *)it.A_slot, *Bi_slot = (E *)it.Bi_slot;
+    const E *B_stage = (const E *)it.B_stage;
+    const int d_in = it.d_in, d_out = it.d_out, r = fb.r, R_pad = fb.R_pad;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nA16 = (int64_t)r * d_in * (int64_t)sizeof(E) / 16;
+    for (int64_t o = first; o < nA16; o += stride)
+        ((uint4 *)A_slot)[o] = ((const uint4 *)it.A_stage)[o];
     const int64_t per_group = (int64_t)d_out * 8;
     const int64_t nB = (int64_t)R_pad * d_out;
     for (int64_t o = first; o < nB; o += stride) {
@@ -1309,27 +1317,28 @@ __global__ void slot_finalize_kernel(E *A_slot, int32_t d_in, E *Bi_slot, const 
         const int j = G * 8 + w;
         Bi_slot[o] = j < r ? B_stage[(int64_t)j * d_out + n] : E(0);
     }
-    const int64_t nA = (int64_t)(R_pad - r) * d_in;
-    for (int64_t o = first; o < nA; o += stride)
-        A_slot[(int64_t)r * d_in + o] = E(0);
+    const int64_t nZ16 = (int64_t)(R_pad - r) * d_in * (int64_t)sizeof(E) / 16;
+    uint4 *A_pad = (uint4 *)(A_slot + (int64_t)r * d_in);
+    for (int64_t o = first; o < nZ16; o += stride)
+        A_pad[o] = make_uint4(0, 0, 0, 0);
 }
 
-hipError_t launch_slot_finalize(bool bf16, void *A_slot, int32_t d_in, void *Bi_slot,
-                                const void *B_stage, int32_t d_out, int32_t r, int32_t R_pad,
-                                hipStream_t st)
+hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st)
 {
-    const int64_t work = (int64_t)R_pad * (d_out > d_in ? d_out : d_in);
+    if (b.n <= 0)
+        return hipSuccess;
+    int64_t work = 0;
+    for (int i = 0; i < b.n; ++i) {
+        const int64_t w = (int64_t)b.R_pad * (b.it[i].d_out > b.it[i].d_in ? b.it[i].d_out : b.it[i].d_in);
+        work = w > work ? w : work;
+    }
     int blocks = (int)((work + 255) / 256);
-    if (blocks > 2048)
-        blocks = 2048;
+    if (blocks > 1024)
+        blocks = 1024;
     if (bf16)
-        hipLaunchKernelGGL(slot_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
-                           (uint16_t *)A_slot, d_in, (uint16_t *)Bi_slot,
-                           (const uint16_t *)B_stage, d_out, r, R_pad);
+        hipLaunchKernelGGL(slot_finalize_kernel<uint16_t>, dim3(blocks, b.n), dim3(256), 0, st, b);
     else
-        hipLaunchKernelGGL(slot_finalize_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                           (float *)A_slot, d_in, (float *)Bi_slot, (const float *)B_stage, d_out,
-                           r, R_pad);
+        hipLaunchKernelGGL(slot_finalize_kernel<float>, dim3(blocks, b.n), dim3(256), 0, st, b);
     return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ struct lora_ctx {
     std::vector<int32_t> rank_host;          // [n_modules][S]: r if the slot's adapter targets m
     std::vector<int32_t> slot_rank;          // [S]: rank of the adapter in the slot (0 = empty)
     std::vector<float> scale_host;
-    void *stage = nullptr;                   // B staging, R_pad * max d_out elements
+    void *stage = nullptr;                   // A^T and B staging for the modules of one load
+    int64_t stage_elems = 0;
     float *hpart = nullptr;
     int hbuf_rows = 0;
     int max_splits = 16;                     // K-split cap of the shrink (tuning)
@@ -88,6 +89,15 @@ struct lora_ctx {
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
     uint64_t synced_gen = 0;                 // loads the host has seen complete (lora_sync_loads)
+    // slots the prepared plan reads (lora_plan_prepare_slots); else every slot
+    bool plan_hinted = false;
+    std::vector<uint8_t> hint;               // [S]
+    // per slot, the number of the last use event recorded after a launch of a
+    // declared plan that reads it (0: none since the slot's last load)
+    std::vector<uint64_t> last_use;          // [S]
+    static constexpr int kUseEvents = 64;    // ring; a reused entry only waits longer
+    hipEvent_t use_ev[kUseEvents] = {};
+    uint64_t use_seq = 0;
     std::vector<StreamState> streams;
     // plan state; an inline plan is computed by every shrink launch itself
     bool plan_valid = false, plan_prepared = false;
@@ -164,7 +174,9 @@ bool stream_capturing(hipStream_t s)
 // A stream that is being captured into a graph cannot wait for the load event,
 // which was recorded outside the capture: loads must be complete (on the host,
 // lora_sync_loads) before a capture starts.
-int before_launch(lora_ctx *c, hipStream_t s)
+// reads_slots: the launch reads slot data (shrink, expand); plan kernels read
+// only the slot indices, so a later load need not wait for them.
+int before_launch(lora_ctx *c, hipStream_t s, bool reads_slots = true)
 {
     StreamState *st = stream_state(c, s);
     if (!st)
@@ -177,7 +189,26 @@ int before_launch(lora_ctx *c, hipStream_t s)
         HIP_TRY(c, hipStreamWaitEvent(s, c->load_done, 0));
         st->waited_gen = c->load_gen;
     }
-    st->used_since_load = true;
+    // a launch of a declared plan is fenced per slot (after its expand), except
+    // under capture, where no event is recorded
+    if (reads_slots && (!c->plan_hinted || stream_capturing(s)))
+        st->used_since_load = true;
+    return LORA_OK;
+}
+
+// After an expand of a declared plan: one event, the last use of every declared slot.
+int record_slot_use(lora_ctx *c, hipStream_t s)
+{
+    if (!c->plan_hinted || stream_capturing(s))
+        return LORA_OK;
+    const uint64_t seq = ++c->use_seq;
+    hipEvent_t &ev = c->use_ev[seq % lora_ctx::kUseEvents];
+    if (!ev)
+        HIP_TRY(c, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    HIP_TRY(c, hipEventRecord(ev, s));
+    for (int k = 0; k < c->S; ++k)
+        if (c->hint[k])
+            c->last_use[k] = seq;
     return LORA_OK;
 }
 
@@ -223,6 +254,11 @@ void free_all(lora_ctx *c)
         if (st.tail)
             (void)hipEventDestroy(st.tail);
     c->streams.clear();
+    for (auto &ev : c->use_ev)
+        if (ev) {
+            (void)hipEventDestroy(ev);
+            ev = nullptr;
+        }
     if (c->load_done)
         (void)hipEventDestroy(c->load_done);
     if (c->side)
@@ -282,13 +318,14 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
     SlotMeta m;
     std::memset(&m, 0, sizeof m);
     for (int k = 0; k < c->S; ++k) {
+        const bool readable = !c->plan_hinted || c->hint[k];
         m.scale[k] = c->scale_host[k];
-        m.rank[k] = (uint8_t)c->slot_rank[k];
+        m.rank[k] = readable ? (uint8_t)c->slot_rank[k] : 0;
     }
     for (int i = 0; i < n; ++i) {
         const int32_t *r = c->rank_host.data() + (size_t)modules[i] * c->S;
         for (int k = 0; k < c->S; ++k)
-            if (r[k] > 0)
+            if (r[k] > 0 && (!c->plan_hinted || c->hint[k]))
                 m.target[i][k >> 5] |= 1u << (k & 31);
     }
     return m;
@@ -296,9 +333,10 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
 
 int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
 {
+    c->plan_hinted = false;
     c->plan_mode = c->dtype == LORA_BF16 && T <= kInlinePlanTokens ? kPlanInline : kPlanTiles;
     if (T > 0 && c->plan_mode == kPlanTiles) {
-        int rc = before_launch(c, s);
+        int rc = before_launch(c, s, false);
         if (rc)
             return rc;
         LaunchTiming t[2];
@@ -418,6 +456,9 @@ int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipSt
         HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
                                  next_timing(c, PROF_EXPAND, s)));
         c->stats.expands += n;
+        int rc2 = record_slot_use(c, s);
+        if (rc2)
+            return rc2;
     }
     return LORA_OK;
 }
@@ -544,13 +585,25 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     }
     c->hbuf_rows = std::max(max_tokens, 16384);
     c->slot_rank.assign(max_loras, 0);
+    c->hint.assign(max_loras, 0);
+    c->last_use.assign(max_loras, 0);
     if (const char *env = std::getenv("LORA_MI355X_MAX_SPLITS")) {
         const int v = std::atoi(env);
         if (v >= 1 && v <= kMaxSplits)
             c->max_splits = v;
     }
     c->max_tiles = max_tiles_for(max_tokens, max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->R_pad * max_out * c->elem);
+    // A^T and B of every module of a load side by side, within 64 MB (at least
+    // one module)
+    int64_t sum_io = 0, max_io = 0;
+    for (int m = 0; m < n_modules; ++m) {
+        sum_io += modules[m].d_in + modules[m].d_out;
+        max_io = std::max<int64_t>(max_io, modules[m].d_in + modules[m].d_out);
+    }
+    c->stage_elems = std::max<int64_t>((int64_t)c->R_pad * max_io,
+                                       std::min<int64_t>((int64_t)c->R_pad * sum_io,
+                                                         (64ll << 20) / c->elem));
+    if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->stage_elems * c->elem);
     if (e == hipSuccess)
         e = dalloc(c, &c->hpart, sizeof(float) * (size_t)kMaxGroup * c->hbuf_rows * c->R_pad);
     if (e == hipSuccess) e = dalloc(c, &c->plan.counts, sizeof(int32_t) * (size_t)max_loras);
@@ -625,22 +678,68 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
     int rc = fence_compute_streams(ctx);
     if (rc)
         return rc;
+    if (ctx->last_use[slot]) {
+        HIP_TRY(ctx, hipStreamWaitEvent(ctx->side, ctx->use_ev[ctx->last_use[slot] % lora_ctx::kUseEvents], 0));
+        ctx->last_use[slot] = 0;
+    }
     int64_t bytes = 0;
     const bool bf16 = ctx->dtype == LORA_BF16;
+    // Every targeted module's A^T and B go to the stage, in module order, A^T
+    // then B; ranges that follow each other both in the source and in the stage
+    // are moved by one copy (an adapter read into one buffer takes one transfer,
+    // where the link is fastest).  One finalize launch per batch of modules (or
+    // when the stage is full) moves A^T into the slot and repacks B, in stream
+    // order after its copies.
+    FinalizeBatch fb;
+    std::memset(&fb, 0, sizeof fb);
+    fb.r = r;
+    fb.R_pad = ctx->R_pad;
+    int64_t stage_used = 0;
+    const char *run_src = nullptr;
+    char *run_dst = nullptr;
+    size_t run_bytes = 0;
+    auto flush_run = [&]() -> hipError_t {
+        hipError_t e = hipSuccess;
+        if (run_bytes)
+            e = hipMemcpyAsync(run_dst, run_src, run_bytes, hipMemcpyDefault, ctx->side);
+        run_bytes = 0;
+        return e;
+    };
+    auto add_range = [&](const void *src, char *dst, size_t n) -> hipError_t {
+        if (run_bytes && (const char *)src == run_src + run_bytes && dst == run_dst + run_bytes) {
+            run_bytes += n;
+            return hipSuccess;
+        }
+        hipError_t e = flush_run();
+        run_src = (const char *)src;
+        run_dst = dst;
+        run_bytes = n;
+        return e;
+    };
     for (int m = 0; m < ctx->n_modules; ++m) {
         if (!A_t[m])
             continue;
         const auto sh = ctx->shapes[m];
+        const int64_t a_elems = (int64_t)r * sh.d_in, b_elems = (int64_t)r * sh.d_out;
+        if (fb.n == kFinalizeBatch || stage_used + a_elems + b_elems > ctx->stage_elems) {
+            HIP_TRY(ctx, flush_run());
+            HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
+            fb.n = 0;
+            stage_used = 0;
+        }
         char *Aslot = (char *)ctx->A[m] + (size_t)slot * ctx->strideA[m] * ctx->elem;
         char *Bslot = (char *)ctx->Bi[m] + (size_t)slot * ctx->strideB[m] * ctx->elem;
-        const size_t abytes = (size_t)r * sh.d_in * ctx->elem;
-        const size_t bbytes = (size_t)r * sh.d_out * ctx->elem;
-        HIP_TRY(ctx, hipMemcpyAsync(Aslot, A_t[m], abytes, hipMemcpyDefault, ctx->side));
-        HIP_TRY(ctx, hipMemcpyAsync(ctx->stage, B[m], bbytes, hipMemcpyDefault, ctx->side));
-        HIP_TRY(ctx, launch_slot_finalize(bf16, Aslot, sh.d_in, Bslot, ctx->stage, sh.d_out, r,
-                                          ctx->R_pad, ctx->side));
+        char *Ast = (char *)ctx->stage + (size_t)stage_used * ctx->elem;
+        char *Bst = Ast + (size_t)a_elems * ctx->elem;
+        const size_t abytes = (size_t)a_elems * ctx->elem, bbytes = (size_t)b_elems * ctx->elem;
+        HIP_TRY(ctx, add_range(A_t[m], Ast, abytes));
+        HIP_TRY(ctx, add_range(B[m], Bst, bbytes));
+        fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, Ast, Bst, sh.d_in, sh.d_out};
+        stage_used += a_elems + b_elems;
         bytes += (int64_t)abytes + (int64_t)bbytes;
     }
+    HIP_TRY(ctx, flush_run());
+    HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
     HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
     ctx->load_gen += 1;
     for (int m = 0; m < ctx->n_modules; ++m)
@@ -700,6 +799,29 @@ int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_to
         return rc;
     }
     ctx->plan_prepared = true;
+    return LORA_OK;
+}
+
+int lora_plan_prepare_slots(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_tokens,
+                            const int32_t *used_slots, int32_t n_used, void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (n_used < 0 || (n_used > 0 && !used_slots))
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "used_slots: %d entries at %p", n_used,
+                    (const void *)used_slots);
+    for (int i = 0; i < n_used; ++i)
+        if (used_slots[i] < 0 || used_slots[i] >= ctx->S)
+            return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "used_slots[%d] = %d not in 0..%d", i,
+                        used_slots[i], ctx->S - 1);
+    int rc = lora_plan_prepare(ctx, token_slot_idx, n_tokens, stream);
+    if (rc)
+        return rc;
+    std::fill(ctx->hint.begin(), ctx->hint.end(), 0);
+    for (int i = 0; i < n_used; ++i)
+        ctx->hint[used_slots[i]] = 1;
+    ctx->plan_hinted = true;
     return LORA_OK;
 }
 

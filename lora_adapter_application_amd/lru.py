@@ -19,7 +19,9 @@ runs:
 1. adapters already resident are hits and are touched;
 2. the others are misses, loaded in order of first appearance;
 3. a miss takes an empty slot (lowest index first), or else evicts the least
-   recently used slot that the step itself does not use.
+   recently used slot that the step itself does not use; slots passed as
+   `avoid` (read by batches still in flight) are taken only when no other slot
+   is left, since a load into them has to wait for those batches.
 
 A step with more distinct adapters than slots is refused.
 """
@@ -67,12 +69,14 @@ class SlotLRU:
         self.tick += 1
         self.last_use[slot] = self.tick
 
-    def plan_step(self, adapter_ids: np.ndarray) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+    def plan_step(self, adapter_ids: np.ndarray, avoid=()) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
         """Map one batch's per-token adapter ids (-1 = base only) to slots.
 
         Returns (slot per token, int32 with -1 kept) and the loads to issue
         before the batch, as (slot, adapter id) in order of first appearance.
+        `avoid`: slots to evict only as a last resort.
         """
+        avoid = set(avoid)
         ids = np.asarray(adapter_ids)
         act = ids >= 0
         uniq, first = np.unique(ids[act], return_index=True)
@@ -94,7 +98,8 @@ class SlotLRU:
                 slot = empty[0]
             else:
                 cands = [s for s in range(self.n_slots) if s not in protected]
-                slot = min(cands, key=lambda s: self.last_use[s])
+                free = [s for s in cands if s not in avoid]
+                slot = min(free or cands, key=lambda s: self.last_use[s])
                 old = self.adapter_in[slot]
                 del self.slot_of[old]
                 self.evicted_at[old] = self.step_no

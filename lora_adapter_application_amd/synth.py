@@ -300,7 +300,11 @@ def oracle_adapters(wl: Workload, module: str, adapters=None):
 
 @dataclass
 class DevicePool:
-    """Adapter pool in pinned host memory: At[name] is [n][r][d_in], B[name] [n][r][d_out] (bf16)."""
+    """Adapter pool in pinned host memory: At[name] is [n][r][d_in], B[name] [n][r][d_out] (bf16).
+
+    Each adapter's weights are one contiguous block, module after module (A^T
+    then B), the way an adapter file is read into one buffer; At and B are
+    views into the blocks."""
     r: int
     lora_alpha: float
     At: Dict[str, "object"]
@@ -330,9 +334,14 @@ def churn_pool_device(n_adapters: int = 200, rank: int = 64, modules=None, seed:
     base = SEEDS["churn"] if seed is None else seed
     g = _dev_gen(base * 7919 + 11, device)
     At, B = {}, {}
+    per = sum(rank * (m.d_in + m.d_out) for m in mods)      # elements per adapter block
+    packed = torch.empty((n_adapters, per), dtype=torch.bfloat16, pin_memory=True)
+    off = 0
     for m in mods:
-        a = torch.empty((n_adapters, rank, m.d_in), dtype=torch.bfloat16, pin_memory=True)
-        b = torch.empty((n_adapters, rank, m.d_out), dtype=torch.bfloat16, pin_memory=True)
+        a = packed.as_strided((n_adapters, rank, m.d_in), (per, m.d_in, 1), off)
+        off += rank * m.d_in
+        b = packed.as_strided((n_adapters, rank, m.d_out), (per, m.d_out, 1), off)
+        off += rank * m.d_out
         bound = 1.0 / np.sqrt(m.d_in)
         a.copy_(((torch.rand((n_adapters, rank, m.d_in), generator=g, device=device) * 2 - 1)
                  * bound).to(torch.bfloat16))

@@ -63,3 +63,16 @@ def test_churn_steps_respect_cap_and_mapping():
         assert np.array_equal(slots, np.array([res[int(a)] for a in ids], dtype=np.int32))
         assert len(set(res.values())) == len(res) <= 128
     assert lru.stats.misses >= 128 and lru.stats.hits > 0
+
+
+def test_avoided_slots_are_evicted_last():
+    lru = SlotLRU(4)
+    lru.plan_step(np.array([1, 2, 3, 4]))        # slots 0..3, use order 1,2,3,4
+    # slots 0 and 1 (adapters 1, 2) are read by a batch in flight: the miss takes
+    # the least recently used slot outside them, slot 2
+    slots, loads = lru.plan_step(np.array([5]), avoid={0, 1})
+    assert loads == [(2, 5)]
+    # with every other slot protected or avoided, an avoided slot is still taken
+    slots, loads = lru.plan_step(np.array([5, 4, 6]), avoid={0, 1})
+    assert loads == [(0, 6)]
+    assert lru.resident() == {2: 1, 5: 2, 4: 3, 6: 0}
