@@ -69,6 +69,9 @@ def _load():
     lib.lora_oracle_apply.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3 + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    lib.lora_oracle_apply_ex.restype = ctypes.c_int64
+    lib.lora_oracle_apply_ex.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3 + [
+        ctypes.c_int32] + [ctypes.c_void_p] * 7 + [ctypes.c_int32]
     lib.lora_oracle_max_threads.restype = ctypes.c_int32
     lib.lora_oracle_max_threads.argtypes = []
     _lib = lib
@@ -108,7 +111,9 @@ def apply(dtype: int, x: np.ndarray, y: np.ndarray, idx: np.ndarray,
     x         [T, d_in];  y  [T, d_out];  idx  int32 [T]
     adapters  one entry per slot (or per adapter id): None when the slot is empty
               or the module is not targeted, else a dict with keys
-              ``r``, ``lora_alpha``, ``use_rslora``, ``At`` (r x d_in) and ``B`` (r x d_out)
+              ``r``, ``lora_alpha``, ``use_rslora``, ``At`` (r x d_in) and ``B`` (r x d_out),
+              and optionally ``bias`` (d_out values of the data dtype) and
+              ``dora_scale`` (d_out floats): y <- round(g * (y + s * x A B) + c)
     """
     lib = _load()
     elem = np.uint16 if dtype == BF16 else np.float32
@@ -125,6 +130,9 @@ def apply(dtype: int, x: np.ndarray, y: np.ndarray, idx: np.ndarray,
     keep = []
     At_ptrs = (ctypes.c_void_p * max(n, 1))()
     B_ptrs = (ctypes.c_void_p * max(n, 1))()
+    c_ptrs = (ctypes.c_void_p * max(n, 1))()
+    g_ptrs = (ctypes.c_void_p * max(n, 1))()
+    extras = False
     for k, a in enumerate(adapters):
         if a is None:
             continue
@@ -138,11 +146,31 @@ def apply(dtype: int, x: np.ndarray, y: np.ndarray, idx: np.ndarray,
         At_ptrs[k] = At.ctypes.data
         B_ptrs[k] = B.ctypes.data
         keep.append((At, B))
+        if a.get("bias") is not None:
+            c = np.ascontiguousarray(a["bias"], dtype=elem)
+            assert c.shape == (d_out,), c.shape
+            c_ptrs[k] = c.ctypes.data
+            keep.append(c)
+            extras = True
+        if a.get("dora_scale") is not None:
+            g = np.ascontiguousarray(a["dora_scale"], dtype=np.float64)
+            assert g.shape == (d_out,), g.shape
+            g_ptrs[k] = g.ctypes.data
+            keep.append(g)
+            extras = True
     if T == 0:
         return out
-    lib.lora_oracle_apply(dtype, T, d_in, d_out, x.ctypes.data, out.ctypes.data,
-                          idx.ctypes.data, n, rank.ctypes.data, alpha.ctypes.data,
-                          rs.ctypes.data, ctypes.cast(At_ptrs, ctypes.c_void_p),
-                          ctypes.cast(B_ptrs, ctypes.c_void_p), int(n_threads))
+    if extras:
+        lib.lora_oracle_apply_ex(dtype, T, d_in, d_out, x.ctypes.data, out.ctypes.data,
+                                 idx.ctypes.data, n, rank.ctypes.data, alpha.ctypes.data,
+                                 rs.ctypes.data, ctypes.cast(At_ptrs, ctypes.c_void_p),
+                                 ctypes.cast(B_ptrs, ctypes.c_void_p),
+                                 ctypes.cast(c_ptrs, ctypes.c_void_p),
+                                 ctypes.cast(g_ptrs, ctypes.c_void_p), int(n_threads))
+    else:
+        lib.lora_oracle_apply(dtype, T, d_in, d_out, x.ctypes.data, out.ctypes.data,
+                              idx.ctypes.data, n, rank.ctypes.data, alpha.ctypes.data,
+                              rs.ctypes.data, ctypes.cast(At_ptrs, ctypes.c_void_p),
+                              ctypes.cast(B_ptrs, ctypes.c_void_p), int(n_threads))
     del keep
     return out

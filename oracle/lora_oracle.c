@@ -178,6 +178,75 @@ int64_t lora_oracle_apply(int32_t dtype, int32_t n_tokens, int32_t d_in, int32_t
     return applied;
 }
 
+/*
+ * The same update with the two per-adapter output terms an adapter_config can
+ * switch on ("vLLM LoRA Resolver plugins explained", section 3.2: the fields
+ * "bias" and "use_dora" of the example config, both off there):
+ *
+ *   y[t,n] <- round( g_k[n] * ( y[t,n] + s * sum_j h_j * B_k[j,n] ) + c_k[n] )
+ *
+ *   c_k  (bias[k], d_out values of the data dtype, NULL = 0): an output bias the
+ *        adapter brings for the module, added as given (a bias trained with the
+ *        adapter enters as its difference to the base bias; a bias of lora_B
+ *        enters scaled by s);
+ *   g_k  (dora[k], d_out doubles, NULL = 1): DoRA's per-output-feature factor
+ *        m_n / ||W0 + s B^T A||_n of "DoRA: Weight-Decomposed Low-Rank
+ *        Adaptation" (Liu et al., 2024), with y the base product x W0^T without
+ *        the base bias; the caller forms it from W0, which the library never
+ *        holds.
+ * The pages name the two fields and nothing more; this is the plain reading of
+ * them written in the order the definition applies (scale the low-rank sum,
+ * add it to the base product, apply the magnitude factor, add the bias).
+ * Same precision rules as lora_oracle_apply: double, ascending order, no FMA,
+ * one rounding.
+ */
+int64_t lora_oracle_apply_ex(int32_t dtype, int32_t n_tokens, int32_t d_in, int32_t d_out,
+                             const void *x, void *y, const int32_t *idx, int32_t n_slots,
+                             const int32_t *rank, const double *lora_alpha,
+                             const int32_t *use_rslora, const void *const *At,
+                             const void *const *B, const void *const *bias,
+                             const double *const *dora, int32_t n_threads)
+{
+    int64_t applied = 0;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : applied)
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        int32_t k = idx[t];
+        if (k < 0 || k >= n_slots || rank[k] <= 0)
+            continue;
+        int32_t r = rank[k];
+        double s = lora_oracle_scale(lora_alpha[k], r, use_rslora[k]);
+        double *h = (double *)malloc(sizeof(double) * (size_t)r);
+        for (int32_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < d_in; ++i)
+                acc = acc + load_elem(x, dtype, (int64_t)t * d_in + i) *
+                                load_elem(At[k], dtype, (int64_t)j * d_in + i);
+            h[j] = acc;
+        }
+        for (int32_t n = 0; n < d_out; ++n) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < r; ++j)
+                acc = acc + h[j] * load_elem(B[k], dtype, (int64_t)j * d_out + n);
+            int64_t o = (int64_t)t * d_out + n;
+            double v = load_elem(y, dtype, o) + s * acc;
+            if (dora && dora[k])
+                v = dora[k][n] * v;
+            if (bias && bias[k])
+                v = v + load_elem(bias[k], dtype, n);
+            store_elem(y, dtype, o, v);
+        }
+        free(h);
+        applied += 1;
+    }
+    return applied;
+}
+
 int32_t lora_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -401,3 +401,93 @@ def test_adapter_bytes_formula():
     # the manifest's estimated_bytes is not a whole number of such layers, so it
     # cannot be reproduced from the page's own formula and is not used as a pin
     assert man["estimated_bytes"] % per_layer != 0
+
+
+# ---------------------------------------------------------------------------
+# adapter bias and DoRA magnitude (the "bias" and "use_dora" fields)
+
+def test_neutral_bias_and_magnitude_leave_the_update_bit_identical():
+    rng = np.random.default_rng(41)
+    T, d_in, d_out = 20, 24, 40
+    ads = _rand_adapters(rng, 3, d_in, d_out, [4, 2, 6])
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = rng.integers(-1, 3, size=T).astype(np.int32)
+    plain = oracle.apply(oracle.FP32, x, y, idx, ads)
+    ext = [dict(a, bias=np.zeros(d_out, np.float32), dora_scale=np.ones(d_out)) for a in ads]
+    assert np.array_equal(oracle.apply(oracle.FP32, x, y, idx, ext).view(np.uint32), plain.view(np.uint32))
+
+
+def test_dora_equals_the_weight_decomposed_merge():
+    """DoRA (Liu et al., 2024): W' = m * V / ||V|| per output feature, V = W0 + s B^T A.
+    With y = x W0^T and g = m / ||V||, the oracle must give x W'^T."""
+    rng = np.random.default_rng(43)
+    T, d_in, d_out = 16, 36, 28
+    ads = _rand_adapters(rng, 2, d_in, d_out, [3, 5])
+    W0 = rng.standard_normal((d_out, d_in)) * 0.3                   # [out, in]
+    m = rng.uniform(0.5, 2.0, size=(2, d_out))
+    x = _f32(rng.standard_normal((T, d_in)))
+    idx = np.array([0, 1] * (T // 2), dtype=np.int32)
+    ext, Wp = [], []
+    for k, a in enumerate(ads):
+        s = a["lora_alpha"] / a["r"]
+        V = W0 + s * (a["B"].astype(np.float64).T @ a["At"].astype(np.float64))
+        norm = np.linalg.norm(V, axis=1)
+        Wp.append(m[k][:, None] * V / norm[:, None])
+        ext.append(dict(a, dora_scale=m[k] / norm))
+    y_base = _f32(x.astype(np.float64) @ W0.T)
+    got = oracle.apply(oracle.FP32, x, y_base, idx, ext).astype(np.float64)
+    ref = np.stack([x[t].astype(np.float64) @ Wp[idx[t]].T for t in range(T)])
+    np.testing.assert_allclose(got, ref, rtol=5e-6, atol=5e-6)
+
+
+def test_bias_is_added_after_the_magnitude_factor_exactly():
+    """With A^T = 0 the update is g*y + c; small integers make it exact."""
+    T, d_in, d_out = 4, 8, 6
+    a = {"r": 2, "lora_alpha": 4.0, "At": np.zeros((2, d_in), np.float32),
+         "B": np.ones((2, d_out), np.float32),
+         "bias": np.arange(d_out, dtype=np.float32) - 2.0, "dora_scale": np.full(d_out, 3.0)}
+    x = np.ones((T, d_in), np.float32)
+    y = np.arange(T * d_out, dtype=np.float32).reshape(T, d_out)
+    idx = np.array([0, -1, 0, 0], np.int32)
+    got = oracle.apply(oracle.FP32, x, y, idx, [a])
+    want = y.copy()
+    for t in (0, 2, 3):
+        want[t] = 3.0 * y[t] + a["bias"]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP32, oracle.BF16])
+def test_bias_matches_dense_merge_plus_bias(dtype):
+    rng = np.random.default_rng(47)
+    T, d_in, d_out = 18, 32, 24
+    ads = _rand_adapters(rng, 3, d_in, d_out, [2, 0, 7])
+    if dtype == oracle.BF16:
+        cast = lambda a: synth.bf16_bits_to_f32(synth.to_bf16_bits(np.asarray(a, np.float32)))
+        for a in ads:
+            if a:
+                a["At"], a["B"] = cast(a["At"]), cast(a["B"])
+        x = cast(rng.standard_normal((T, d_in)))
+        y = cast(rng.standard_normal((T, d_out)))
+    else:
+        x = _f32(rng.standard_normal((T, d_in)))
+        y = _f32(rng.standard_normal((T, d_out)))
+    biases = [_f32(rng.standard_normal(d_out)) if a else None for a in ads]
+    if dtype == oracle.BF16:
+        biases = [cast(b) if b is not None else None for b in biases]
+    ext = [dict(a, bias=b) if a else None for a, b in zip(ads, biases)]
+    idx = rng.integers(-1, 3, size=T).astype(np.int32)
+    ref = _brute_dense_merge(x, y, idx, ads)
+    for t in range(T):
+        if 0 <= idx[t] < 3 and ads[idx[t]] is not None:
+            ref[t] = ref[t] + biases[idx[t]]
+    if dtype == oracle.BF16:
+        bits = lambda a: synth.to_bf16_bits(np.asarray(a, np.float32))
+        e2 = [dict(a, At=bits(a["At"]), B=bits(a["B"]), bias=bits(a["bias"])) if a else None for a in ext]
+        got = synth.bf16_bits_to_f32(oracle.apply(oracle.BF16, bits(x), bits(y), idx, e2)).astype(np.float64)
+        # one bf16 rounding of the exact value
+        tol = np.abs(ref) * 2.0 ** -8 + 1e-30
+        assert np.all(np.abs(got - ref) <= tol)
+    else:
+        got = oracle.apply(oracle.FP32, x, y, idx, ext).astype(np.float64)
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
