@@ -135,6 +135,32 @@ int lora_slots_destroy(lora_ctx *ctx);
 int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
                    int32_t r, double lora_alpha, int32_t use_rslora);
 
+/*
+ * lora_slot_load with the two per-adapter output terms of the "bias" and
+ * "use_dora" fields of the example adapter_config.json ("vLLM LoRA Resolver
+ * plugins explained", section 3.2; off in that example).  For a token of this
+ * slot the update of module m becomes
+ *
+ *     y[t,n] = round( g_m[n] * ( y[t,n] + s * (x[t,:] . A) . B[:,n] ) + c_m[n] )
+ *
+ *   bias        NULL (c = 0), or [n_modules] pointers: c_m, d_out_m values of
+ *               the ctx dtype, non-NULL for every targeted module.  The bias is
+ *               added as given: a bias trained with the adapter enters as its
+ *               difference to the base bias, a bias of lora_B scaled by s.
+ *   dora_scale  NULL (g = 1), or [n_modules] pointers: g_m, d_out_m floats,
+ *               non-NULL for every targeted module: DoRA's factor
+ *               m[n] / ||W0 + s B^T A||_n per output feature ("DoRA:
+ *               Weight-Decomposed Low-Rank Adaptation", Liu et al. 2024), which
+ *               the caller forms from the base weight W0.  With DoRA, y must be
+ *               the base product x W0^T without the base bias.
+ * Same memory rules, ordering and errors as lora_slot_load; a NULL entry for a
+ * targeted module -> LORA_ERR_INVALID_ARGUMENT.  The extra bytes are not part of
+ * the page's size estimate and are not counted in bytes_loaded.
+ */
+int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
+                      const void *const *bias, const float *const *dora_scale, int32_t r,
+                      double lora_alpha, int32_t use_rslora);
+
 /* Mark `slot` empty for every module.  Batches enqueued after this call skip
  * the slot; batches already enqueued still apply the adapter it held.  Host-only:
  * no device work is enqueued. */

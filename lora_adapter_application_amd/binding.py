@@ -36,7 +36,8 @@ LORA_ERR_NO_PLAN = -9
 LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
 
 # Every symbol the header declares, for the export check.
-EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_clear",
+EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_load_ex",
+           "lora_slot_clear",
            "lora_sync_loads", "lora_plan_prepare", "lora_plan_prepare_slots", "lora_shrink",
            "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH):
         "lora_slots_create": ([ctypes.POINTER(P), I32, I32, ctypes.POINTER(_ModuleShape), I32,
                                I32, I32, I32], ctypes.c_int),
         "lora_slots_destroy": ([P], ctypes.c_int),
+        "lora_slot_load_ex": ([P, I32, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
+                               ctypes.POINTER(P), I32, D, I32], ctypes.c_int),
         "lora_slot_load": ([P, I32, ctypes.POINTER(P), ctypes.POINTER(P), I32, D, I32],
                            ctypes.c_int),
         "lora_slot_clear": ([P, I32], ctypes.c_int),
@@ -191,6 +194,21 @@ def lora_slot_load(ctx, slot: int, A_t: Sequence, B: Sequence, r: int, lora_alph
     b_arr = (ctypes.c_void_p * n)(*[_ptr(b) for b in B])
     _check(load_library().lora_slot_load(ctx, int(slot), a_arr, b_arr, int(r), float(lora_alpha),
                                          int(bool(use_rslora))), ctx)
+
+
+def lora_slot_load_ex(ctx, slot: int, A_t: Sequence, B: Sequence, bias: Optional[Sequence],
+                      dora_scale: Optional[Sequence], r: int, lora_alpha: float,
+                      use_rslora: bool = False) -> None:
+    """lora_slot_load with per-module output bias (ctx dtype) and DoRA factors (float32),
+    each a sequence with one entry per module, or None."""
+    n = len(A_t)
+    if len(B) != n or (bias is not None and len(bias) != n) or \
+            (dora_scale is not None and len(dora_scale) != n):
+        raise ValueError("one entry per module in A_t, B, bias and dora_scale")
+    arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts]) if ts is not None else None
+    _check(load_library().lora_slot_load_ex(ctx, int(slot), arr(A_t), arr(B), arr(bias),
+                                            arr(dora_scale), int(r), float(lora_alpha),
+                                            int(bool(use_rslora))), ctx)
 
 
 def lora_slot_clear(ctx, slot: int) -> None:
@@ -325,8 +343,11 @@ class Slots:
                                      LORA_BF16 if dtype == "bf16" else LORA_FP32, max_tokens,
                                      device)
 
-    def load(self, slot, A_t, B, r, lora_alpha, use_rslora=False):
-        lora_slot_load(self.ctx, slot, A_t, B, r, lora_alpha, use_rslora)
+    def load(self, slot, A_t, B, r, lora_alpha, use_rslora=False, bias=None, dora_scale=None):
+        if bias is None and dora_scale is None:
+            lora_slot_load(self.ctx, slot, A_t, B, r, lora_alpha, use_rslora)
+        else:
+            lora_slot_load_ex(self.ctx, slot, A_t, B, bias, dora_scale, r, lora_alpha, use_rslora)
 
     def clear(self, slot):
         lora_slot_clear(self.ctx, slot)

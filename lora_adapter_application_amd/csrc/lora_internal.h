@@ -62,8 +62,11 @@ constexpr int kMaxGroup = 8;
 struct SlotMeta {
     float scale[LORA_MAX_SLOTS];
     uint8_t rank[LORA_MAX_SLOTS];
+    uint8_t flags[LORA_MAX_SLOTS];      // kSlotBias | kSlotDora
     uint32_t target[kMaxGroup][LORA_MAX_SLOTS / 32];
 };
+// Output terms an adapter may carry (lora_slot_load_ex).
+enum SlotFlags { kSlotBias = 1, kSlotDora = 2 };
 
 // Optional events around one dispatch (both null: untimed), recorded with the
 // dispatch itself so they bracket exactly the kernel's execution.
@@ -118,6 +121,9 @@ struct ExpandArgs {
     int32_t grid_tiles;
     int32_t grid_cols;                  // max column chunks over the members
     int32_t xcd_group;                  // work items per XCD group (bf16 kernel)
+    const void *bias[kMaxGroup];        // module base: [S][d_out], ctx dtype
+    const float *dora[kMaxGroup];       // module base: [S][d_out]
+    int32_t terms;                      // some slot of the launch has output terms
 };
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,

@@ -322,11 +322,13 @@ __device__ __forceinline__ int member_rank(const SlotMeta &meta, int m, int slot
 }
 
 // Slot metadata fetched at kernel start, independent of the tile: lane l holds
-// the ranks of slots 4l .. 4l+3 (rk), word l % 8 of group member l / 8's target
-// mask (tw) and the scales of slots l, l+64, l+128, l+192 (sc).  A lookup for a
+// the ranks and the output-term flags of slots 4l .. 4l+3 (rk, fl), word l % 8
+// of group member l / 8's target mask (tw) and the scales of slots l, l+64,
+// l+128, l+192 (sc).  A lookup for a
 // wave-uniform slot reads one lane (v_readlane), with no memory access.
 struct MetaRegs {
     uint32_t rk;
+    uint32_t fl;
     uint32_t tw;
     float sc[LORA_MAX_SLOTS / 64];
 };
@@ -336,6 +338,7 @@ __device__ __forceinline__ MetaRegs load_meta_regs(const SlotMeta &meta)
     const int lane = threadIdx.x & 63;
     MetaRegs r;
     r.rk = ((const uint32_t *)meta.rank)[lane];
+    r.fl = ((const uint32_t *)meta.flags)[lane];
     r.tw = ((const uint32_t *)meta.target)[lane];
 #pragma unroll
     for (int i = 0; i < LORA_MAX_SLOTS / 64; ++i)
@@ -347,6 +350,12 @@ __device__ __forceinline__ int meta_rank(const MetaRegs &r, int slot)
 {
     slot = __builtin_amdgcn_readfirstlane(slot);
     return (__builtin_amdgcn_readlane(r.rk, slot >> 2) >> ((slot & 3) * 8)) & 0xff;
+}
+
+__device__ __forceinline__ int meta_flags(const MetaRegs &r, int slot)
+{
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    return (__builtin_amdgcn_readlane(r.fl, slot >> 2) >> ((slot & 3) * 8)) & 0xff;
 }
 
 __device__ __forceinline__ bool meta_targets(const MetaRegs &r, int m, int slot)
@@ -939,12 +948,20 @@ __device__ __forceinline__ void split_hi_lo(const f32x4_t h, uint2 &hi, uint2 &l
 // the tile's h as bf16 high / low halves in LDS, row stride HS elements.  Rows
 // beyond the tile hold stale LDS; they only reach output columns of tokens that
 // are not stored.
-template <int NB, int NSUB, int HS>
+// The output terms of an adapter for the 16 columns cb + 16g .. of a lane:
+// DoRA factors (fp32) and bias (bf16), loaded only when the slot has them.
+struct OutTerms {
+    int fl;
+    float g[16];
+    uint4 c[2];
+};
+
+template <int NB, int NSUB, int HS, bool TERMS>
 __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16_t *hs_lo,
                                              const uint4 (&bop)[NB][4], const uint4 (&yv)[NSUB][2],
                                              const int (&tok)[NSUB], const bool (&tok_ok)[NSUB],
                                              int nsub, int nb, float s, uint16_t *ybase, int d_out,
-                                             int cb)
+                                             int cb, const OutTerms &ot)
 {
     const int lane = threadIdx.x & 63, row = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -975,11 +992,22 @@ __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16
                 if (col < d_out) {
                     const uint4 yw = yv[st][piece];
                     uint32_t w[4] = {yw.x, yw.y, yw.z, yw.w};
+                    const uint32_t cws[4] = {ot.c[piece].x, ot.c[piece].y, ot.c[piece].z, ot.c[piece].w};
 #pragma unroll
                     for (int h2 = 0; h2 < 4; ++h2) {
                         const int e0 = piece * 8 + h2 * 2, e1 = e0 + 1;
-                        const float v0 = bf16_bits_to_f32(w[h2] & 0xffffu) + s * acc[e0 >> 2][e0 & 3];
-                        const float v1 = bf16_bits_to_f32(w[h2] >> 16) + s * acc[e1 >> 2][e1 & 3];
+                        float v0 = bf16_bits_to_f32(w[h2] & 0xffffu) + s * acc[e0 >> 2][e0 & 3];
+                        float v1 = bf16_bits_to_f32(w[h2] >> 16) + s * acc[e1 >> 2][e1 & 3];
+                        if constexpr (TERMS) {
+                            if (ot.fl & kSlotDora) {
+                                v0 = ot.g[e0] * v0;
+                                v1 = ot.g[e1] * v1;
+                            }
+                            if (ot.fl & kSlotBias) {
+                                v0 = v0 + bf16_bits_to_f32(cws[h2] & 0xffffu);
+                                v1 = v1 + bf16_bits_to_f32(cws[h2] >> 16);
+                            }
+                        }
                         w[h2] = pack_bf16x2(v0, v1);
                     }
                     *(uint4 *)(yrow + col) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -1033,9 +1061,9 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
 // The expand of one tile for the 256 columns of chunk `chunk` of member m.
 // Requires 0 < tile.rank and an adapter that targets the member.  Every global
 // load (h partials, B, y) is issued before any arithmetic.
-template <int NB>
+template <int NB, bool TERMS>
 __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chunk, const Tile &tile,
-                                            int tokv, uint16_t *hs_hi, uint16_t *hs_lo)
+                                            int tokv, int flags, uint16_t *hs_hi, uint16_t *hs_lo)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int d_out = a.d_out[m];
@@ -1063,6 +1091,28 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
                    cb, nb, cols_ok);
     uint4 yv[4][2];
     load_y<4>(yv, ybase, d_out, cb, tok, tok_ok);
+    // output terms of the slot for this lane's 16 columns (clamped like y)
+    OutTerms ot;
+    ot.fl = flags;
+    ot.c[0] = ot.c[1] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int piece = 0; piece < (TERMS ? 2 : 0); ++piece) {
+        // columns col .. col+7; past d_out the slot's first columns are read
+        // instead, and those outputs are not stored
+        const int col = cb + (lane >> 4) * 16 + piece * 8;
+        const int64_t o = (int64_t)tile.slot * d_out + (cols_ok && col < d_out ? col : 0);
+        if (flags & kSlotDora) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const f32x4_t gq = *(const f32x4_t *)(a.dora[m] + o + q * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ot.g[piece * 8 + q * 4 + e] = gq[e];
+            }
+        }
+        if (flags & kSlotBias)
+            ot.c[piece] = *(const uint4 *)((const uint16_t *)a.bias[m] + o);
+    }
     // h -> bf16 high and low halves in LDS
     constexpr int HS = NB * 16 + 8;             // row stride (bf16 elements, 16-byte multiple)
     const int quads = nb * 4;
@@ -1077,7 +1127,8 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
     }
     __syncthreads();
     if (cols_ok)
-        expand_store<NB, 4, HS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase, d_out, cb);
+        expand_store<NB, 4, HS, TERMS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase,
+                                       d_out, cb, ot);
 }
 
 constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
@@ -1088,7 +1139,7 @@ constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 // (mostly of one slot) of one column chunk run on one XCD and read that slot's
 // B columns from L2; a small batch keeps groups of 1 (plain round-robin), which
 // balances its few, uneven tiles over the XCDs.
-template <int NB>
+template <int NB, bool TERMS>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
     const int n_items = a.grid_tiles * a.grid_cols * a.n;
@@ -1104,11 +1155,12 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
     const int tokv = a.tile_tok[(int64_t)bt * kTileTokens + lane];
     if (bt >= n_tiles || chunk * kExpandCols >= a.d_out[m])
         return;
+    const int flags = meta_flags(mr, tile.slot);
     if (tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
     __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB)];
     __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB)];
-    expand_tile<NB>(a, m, chunk, tile, tokv, hs_hi, hs_lo);
+    expand_tile<NB, TERMS>(a, m, chunk, tile, tokv, flags, hs_hi, hs_lo);
 }
 
 // ----------------------------------------------------------------------------
@@ -1217,11 +1269,19 @@ __global__ __launch_bounds__(256) void expand_f32_kernel(ExpandArgs a, SlotMeta 
                 acc[t] += hs[t][j] * bj;
     }
     float *y = (float *)a.y[m];
+    const int fl = meta.flags[tile.slot];
+    const float gn = (fl & kSlotDora) ? a.dora[m][(int64_t)tile.slot * d_out + n] : 1.f;
+    const float cn = (fl & kSlotBias) ? ((const float *)a.bias[m])[(int64_t)tile.slot * d_out + n] : 0.f;
 #pragma unroll
     for (int t = 0; t < kTileTokens; ++t) {
         if (t < tile.len) {
             const int64_t o = (int64_t)tok_row[t] * d_out + n;
-            y[o] = y[o] + s * acc[t];
+            float v = y[o] + s * acc[t];
+            if (fl & kSlotDora)
+                v = gn * v;
+            if (fl & kSlotBias)
+                v = v + cn;
+            y[o] = v;
         }
     }
 }
@@ -1277,14 +1337,24 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
     } else {
         const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.grid_cols * a.n, a.xcd_group);
         const int nbmax = a.R_pad / 16;
-        if (nbmax <= 1)
-            launch(expand_bf16_kernel<1>, g, block, 0, st, t, a, m);
+        // the output-term epilogue only in launches where some slot has terms
+        if (a.terms) {
+            if (nbmax <= 1)
+                launch(expand_bf16_kernel<1, true>, g, block, 0, st, t, a, m);
+            else if (nbmax <= 2)
+                launch(expand_bf16_kernel<2, true>, g, block, 0, st, t, a, m);
+            else if (nbmax <= 4)
+                launch(expand_bf16_kernel<4, true>, g, block, 0, st, t, a, m);
+            else
+                launch(expand_bf16_kernel<8, true>, g, block, 0, st, t, a, m);
+        } else if (nbmax <= 1)
+            launch(expand_bf16_kernel<1, false>, g, block, 0, st, t, a, m);
         else if (nbmax <= 2)
-            launch(expand_bf16_kernel<2>, g, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<2, false>, g, block, 0, st, t, a, m);
         else if (nbmax <= 4)
-            launch(expand_bf16_kernel<4>, g, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<4, false>, g, block, 0, st, t, a, m);
         else
-            launch(expand_bf16_kernel<8>, g, block, 0, st, t, a, m);
+            launch(expand_bf16_kernel<8, false>, g, block, 0, st, t, a, m);
     }
     return hipGetLastError();
 }

@@ -74,6 +74,9 @@ struct lora_ctx {
     int S = 0, R = 0, R_pad = 0, n_modules = 0, max_tokens = 0, elem = 2;
     std::vector<lora_module_shape> shapes;
     std::vector<void *> A, Bi;
+    std::vector<void *> bias;                // per module: [max_loras][d_out], ctx dtype
+    std::vector<float *> dora;               // per module: [max_loras][d_out]
+    std::vector<uint8_t> slot_flags;         // [S]: kSlotBias | kSlotDora
     std::vector<int64_t> strideA, strideB;   // per-slot element strides
     std::vector<int32_t> rank_host;          // [n_modules][S]: r if the slot's adapter targets m
     std::vector<int32_t> slot_rank;          // [S]: rank of the adapter in the slot (0 = empty)
@@ -321,6 +324,7 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
         const bool readable = !c->plan_hinted || c->hint[k];
         m.scale[k] = c->scale_host[k];
         m.rank[k] = readable ? (uint8_t)c->slot_rank[k] : 0;
+        m.flags[k] = readable ? c->slot_flags[k] : 0;
     }
     for (int i = 0; i < n; ++i) {
         const int32_t *r = c->rank_host.data() + (size_t)modules[i] * c->S;
@@ -405,6 +409,8 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
         const lora_module_shape sh = c->shapes[mod];
         a.y[i] = y[i];
         a.Bi[i] = c->Bi[mod];
+        a.bias[i] = c->bias[mod];
+        a.dora[i] = c->dora[mod];
         a.slot_stride_B[i] = c->strideB[mod];
         a.d_out[i] = sh.d_out;
         a.splits[i] = c->last_splits[i];
@@ -421,6 +427,10 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     // large batches: one contiguous run of tiles per XCD; small: round-robin
     const int64_t items = (int64_t)a.grid_tiles * a.grid_cols * n;
     a.xcd_group = T > kInlinePlanTokens ? (int)((items + 7) / 8) : 1;
+    a.terms = 0;
+    for (int k = 0; k < c->S; ++k)
+        if (c->slot_flags[k] && (!c->plan_hinted || c->hint[k]))
+            a.terms = 1;
     return a;
 }
 
@@ -577,14 +587,23 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         e = dalloc(c, &a, (size_t)(sa * max_loras * c->elem));
         if (e == hipSuccess)
             e = dalloc(c, &b, (size_t)(sb * max_loras * c->elem));
+        void *cb = nullptr;
+        float *gb = nullptr;
+        if (e == hipSuccess)
+            e = dalloc(c, &cb, (size_t)sh.d_out * max_loras * c->elem);
+        if (e == hipSuccess)
+            e = dalloc(c, &gb, sizeof(float) * (size_t)sh.d_out * max_loras);
         c->A.push_back(a);
         c->Bi.push_back(b);
+        c->bias.push_back(cb);
+        c->dora.push_back(gb);
         c->strideA.push_back(sa);
         c->strideB.push_back(sb);
         max_out = std::max(max_out, sh.d_out);
     }
     c->hbuf_rows = std::max(max_tokens, 16384);
     c->slot_rank.assign(max_loras, 0);
+    c->slot_flags.assign(max_loras, 0);
     c->hint.assign(max_loras, 0);
     c->last_use.assign(max_loras, 0);
     if (const char *env = std::getenv("LORA_MI355X_MAX_SPLITS")) {
@@ -647,6 +666,13 @@ int lora_slots_destroy(lora_ctx *ctx)
 int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
                    int32_t r, double lora_alpha, int32_t use_rslora)
 {
+    return lora_slot_load_ex(ctx, slot, A_t, B, nullptr, nullptr, r, lora_alpha, use_rslora);
+}
+
+int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const void *const *B,
+                      const void *const *bias, const float *const *dora_scale, int32_t r,
+                      double lora_alpha, int32_t use_rslora)
+{
     if (check_ctx(ctx))
         return LORA_ERR_INVALID_ARGUMENT;
     ctx->last_error.clear();
@@ -672,6 +698,13 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
             if (A_t[m] && (check_source(A_t[m]) || check_source(B[m])))
                 return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
                             "module %d: weights must be pinned host or device memory", m);
+            if (A_t[m] && bias && !bias[m])
+                return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: bias entry is NULL", m);
+            if (A_t[m] && dora_scale && !dora_scale[m])
+                return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: dora_scale entry is NULL", m);
+            if (A_t[m] && ((bias && check_source(bias[m])) || (dora_scale && check_source(dora_scale[m]))))
+                return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
+                            "module %d: bias / dora_scale must be pinned host or device memory", m);
         }
     }
     DeviceGuard guard(ctx->device);
@@ -740,11 +773,24 @@ int lora_slot_load(lora_ctx *ctx, int32_t slot, const void *const *A_t, const vo
     }
     HIP_TRY(ctx, flush_run());
     HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
+    // output terms straight into the slot's rows
+    for (int m = 0; m < ctx->n_modules && (bias || dora_scale); ++m) {
+        if (!A_t[m])
+            continue;
+        const int d_out = ctx->shapes[m].d_out;
+        if (bias)
+            HIP_TRY(ctx, hipMemcpyAsync((char *)ctx->bias[m] + (size_t)slot * d_out * ctx->elem, bias[m],
+                                        (size_t)d_out * ctx->elem, hipMemcpyDefault, ctx->side));
+        if (dora_scale)
+            HIP_TRY(ctx, hipMemcpyAsync(ctx->dora[m] + (size_t)slot * d_out, dora_scale[m],
+                                        sizeof(float) * (size_t)d_out, hipMemcpyDefault, ctx->side));
+    }
     HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
     ctx->load_gen += 1;
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = A_t[m] ? r : 0;
     ctx->slot_rank[slot] = r;
+    ctx->slot_flags[slot] = (uint8_t)((bias ? kSlotBias : 0) | (dora_scale ? kSlotDora : 0));
     ctx->scale_host[slot] = s;
     ctx->slot_epoch += 1;
     ctx->stats.loads += 1;
@@ -764,6 +810,7 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot)
     for (int m = 0; m < ctx->n_modules; ++m)
         ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
     ctx->slot_rank[slot] = 0;
+    ctx->slot_flags[slot] = 0;
     ctx->slot_epoch += 1;
     ctx->stats.clears += 1;
     return LORA_OK;

@@ -54,12 +54,15 @@ class Module:
 
 @dataclass
 class Adapter:
-    """One adapter: per targeted module, At (r x d_in) and B (r x d_out)."""
+    """One adapter: per targeted module, At (r x d_in) and B (r x d_out); optionally
+    an output bias (d_out, data dtype) and a DoRA factor (d_out, float32)."""
     r: int
     lora_alpha: float
     use_rslora: bool
     At: Dict[str, np.ndarray] = field(default_factory=dict)
     B: Dict[str, np.ndarray] = field(default_factory=dict)
+    bias: Optional[Dict[str, np.ndarray]] = None
+    dora_scale: Optional[Dict[str, np.ndarray]] = None
 
 
 @dataclass
@@ -290,9 +293,29 @@ def oracle_adapters(wl: Workload, module: str, adapters=None):
         if ad is None or module not in ad.At:
             out.append(None)
         else:
-            out.append({"r": ad.r, "lora_alpha": ad.lora_alpha, "use_rslora": ad.use_rslora,
-                        "At": ad.At[module], "B": ad.B[module]})
+            rec = {"r": ad.r, "lora_alpha": ad.lora_alpha, "use_rslora": ad.use_rslora,
+                   "At": ad.At[module], "B": ad.B[module]}
+            if ad.bias is not None:
+                rec["bias"] = ad.bias[module]
+            if ad.dora_scale is not None:
+                rec["dora_scale"] = ad.dora_scale[module].astype(np.float64)
+            out.append(rec)
     return out
+
+
+def add_output_terms(wl: Workload, seed: int, bias_slots=(), dora_slots=()) -> Workload:
+    """Give the listed slots an output bias c ~ N(0, 0.05) and / or a DoRA factor
+    g ~ U(0.5, 1.5) per targeted module (seeded; c in the workload's dtype)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
+    for k, ad in enumerate(wl.adapters):
+        if ad is None:
+            continue
+        if k in bias_slots:
+            ad.bias = {m: _cast(rng.standard_normal(ad.B[m].shape[1]).astype(np.float32) * 0.05, wl.dtype)
+                       for m in ad.At}
+        if k in dora_slots:
+            ad.dora_scale = {m: rng.uniform(0.5, 1.5, ad.B[m].shape[1]).astype(np.float32) for m in ad.At}
+    return wl
 
 
 # ----------------------------------------------------------------------------

@@ -56,7 +56,7 @@ def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None) ->
     for k, ad in enumerate(wl.adapters):
         if ad is None:
             continue
-        A_t, B = [], []
+        A_t, B, C, G = [], [], [], []
         for m in wl.modules:
             if m.name in ad.At:
                 a = to_pinned(ad.At[m.name], wl.dtype)
@@ -64,10 +64,20 @@ def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None) ->
                 pinned += [a, b]
                 A_t.append(a)
                 B.append(b)
+                if ad.bias is not None:
+                    C.append(to_pinned(ad.bias[m.name], wl.dtype))
+                    pinned.append(C[-1])
+                if ad.dora_scale is not None:
+                    G.append(torch.from_numpy(np.ascontiguousarray(ad.dora_scale[m.name], np.float32)).pin_memory())
+                    pinned.append(G[-1])
             else:
                 A_t.append(None)
                 B.append(None)
-        S.load(k, A_t, B, ad.r, ad.lora_alpha, ad.use_rslora)
+                C.append(None)
+                G.append(None)
+        S.load(k, A_t, B, ad.r, ad.lora_alpha, ad.use_rslora,
+               bias=C if ad.bias is not None else None,
+               dora_scale=G if ad.dora_scale is not None else None)
     S.sync_loads()
     return S
 
