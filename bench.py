@@ -212,12 +212,16 @@ def main():
     ng = len(groups)
     use_timing = not args.no_kernel_timing
 
+    # the library calls of one step per layer set, arguments marshalled once
+    # (per stream: the eager passes use the current stream, the graph capture its own)
+    def bind_all(stream=None):
+        return [slots.bind_step([([l * nm + j for j in g], [xs[l * nm + j] for j in g],
+                                  [ys[l * nm + j] for j in g]) for g in groups], idx, stream)
+                for l in range(L)]
+    bound = bind_all()
+
     def step(i):
-        l = i % L
-        slots.prepare(idx)
-        for g in groups:
-            mis = [l * nm + j for j in g]
-            slots.apply_group(mis, [xs[mi] for mi in mis], [ys[mi] for mi in mis], idx)
+        bound[i % L]()
 
     for i in range(args.warmup):
         step(i)
@@ -234,6 +238,7 @@ def main():
     slots.sync_loads()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
+    bound_cap = bind_all(cap)
     graphs = []
     for n_steps in (L, K % L):
         if n_steps == 0 or (n_steps == L and K < L):
@@ -242,7 +247,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             for i in range(n_steps):
-                step(i)
+                bound_cap[i % L]()
         graphs.append(g)
     for g in graphs:                # one untimed replay each
         if g is not None:

@@ -121,3 +121,21 @@ def test_capture_with_pending_load_is_rejected():
         assert not np.array_equal(from_dev(ys[mi], wl.dtype), before[mi]) or \
             np.array_equal(ref, before[mi])
     S.close()
+
+
+def test_bound_step_matches_direct_calls():
+    """Slots.bind_step marshals the arguments once; its calls give the same bits."""
+    wl = _case(300, 9300)
+    S = make_slots(wl)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in MODS]
+    y0 = [to_dev(wl.y[m.name], wl.dtype) for m in MODS]
+    yd = [y.clone() for y in y0]
+    _steps(S, idx, xs, yd)
+    yb = [y.clone() for y in y0]
+    step = S.bind_step([(g, [xs[i] for i in g], [yb[i] for i in g]) for g in GROUPS], idx)
+    step()
+    torch.cuda.synchronize()
+    for mi in range(len(MODS)):
+        assert torch.equal(yb[mi], yd[mi])
+    S.close()
