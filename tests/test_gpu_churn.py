@@ -74,3 +74,57 @@ def test_churn_all_steps_match_oracle(pool):
     assert S.stats()["bytes_loaded"] == st.misses * oracle.adapter_bytes(
         [(m.d_in, m.d_out) for m in mods], [True] * 5, 64, 2)
     S.close()
+
+
+def test_churn_pipelined_uploads_match_oracle(pool):
+    """The churn as a pipeline: step s+1's misses are uploaded while step s runs
+    (declared slots, 144 slots for a per-step cap of 128), with no host wait
+    between steps; every step's sampled rows must match the oracle."""
+    mods = synth.CHURN_MODULES
+    names = [m.name for m in mods]
+    n_steps = 16
+    S = binding.Slots(144, 64, [(m.d_in, m.d_out) for m in mods], "bf16", max_tokens=8192)
+    lru = SlotLRU(144)
+    rng = np.random.default_rng(1)
+    sched, prev = [], set()
+    for step in range(n_steps):
+        ids, _, x, y = synth.churn_step_device(100 + step)
+        slots, loads = lru.plan_step(ids, avoid=prev)
+        used = sorted({int(v) for v in slots[slots >= 0]})
+        prev = set(used)
+        T = ids.shape[0]
+        rows = np.unique(np.concatenate([[0, 1023, 1024, T - 1], rng.integers(0, T, 16)]))
+        rows_t = torch.from_numpy(rows).cuda()
+        y0 = {n: bits(y[n][rows_t]) for n in names}
+        sched.append((ids, torch.from_numpy(slots).cuda(), used, loads, x, y, rows, rows_t, y0))
+    torch.cuda.synchronize()
+
+    def issue(loads):
+        for slot, a in loads:
+            S.load(slot, [pool.At[n][a] for n in names], [pool.B[n][a] for n in names], 64, 128.0)
+
+    issue(sched[0][3])
+    for step in range(n_steps):
+        _, idx, used, _, x, y, _, _, _ = sched[step]
+        S.prepare(idx, used_slots=used)
+        for g in GROUPS:
+            mi = [names.index(n) for n in g]
+            S.apply_group(mi, [x[n] for n in g], [y[n] for n in g], idx)
+        if step + 1 < n_steps:
+            issue(sched[step + 1][3])
+    torch.cuda.synchronize()
+    worst = 0.0
+    for step in range(n_steps):
+        ids, _, _, _, x, y, rows, rows_t, y0 = sched[step]
+        for n in names:
+            adapters = [None] * 200
+            for a in np.unique(ids[rows]):
+                adapters[int(a)] = pool.adapter(n, int(a))
+            ref = oracle.apply(oracle.BF16, bits(x[n][rows_t]), y0[n], ids[rows], adapters)
+            got = bits(y[n][rows_t])
+            g64, r64 = as_f64(got, synth.BF16), as_f64(ref, synth.BF16)
+            w = float((np.abs(g64 - r64) / (2e-2 * (1 + np.abs(r64)))).max())
+            worst = max(worst, w)
+            assert w <= 1.0, f"pipelined step {step} {n}: err/bound {w:.3f}"
+    log(f"pipelined churn: {lru.stats.misses} misses, worst err/bound {worst:.3f}")
+    S.close()
