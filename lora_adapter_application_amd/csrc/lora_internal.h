@@ -102,7 +102,12 @@ struct ShrinkArgs {
     int32_t grid_tiles;
     int32_t grid_splits;                // max splits over the members
     int32_t mixed;                      // batch above 1024 tokens: long tiles take the segment path
+    int32_t warm;                       // kWarmX | kWarmA: L2 warm-up of the split's blocks (inline plan)
+    int32_t warm_rows;                  // rows of the warm-up block per workgroup
 };
+
+// What the inline-plan shrink warms in L2 while its plan is formed.
+enum WarmFlags { kWarmX = 1, kWarmA = 2 };
 
 struct ExpandArgs {
     int32_t n;
@@ -121,6 +126,7 @@ struct ExpandArgs {
     int32_t grid_tiles;
     int32_t grid_cols;                  // max column chunks over the members
     int32_t xcd_group;                  // work items per XCD group (bf16 kernel)
+    int32_t tile_major;                 // bf16 kernel: chunks of a tile are consecutive items
     const void *bias[kMaxGroup];        // module base: [S][d_out], ctx dtype
     const float *dora[kMaxGroup];       // module base: [S][d_out]
     int32_t terms;                      // some slot of the launch has output terms

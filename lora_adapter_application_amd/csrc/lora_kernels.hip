@@ -669,13 +669,33 @@ __device__ __forceinline__ int xcd_item(int G)
 
 constexpr int kPlanPerThread = kInlinePlanTokens / 256;
 
+// Kernel arguments are read with scalar loads where the code first needs a
+// field, and a field whose 64-byte line is not yet in the scalar cache costs a
+// memory round trip at that point; the compiler spreads these loads through
+// the plan and the tile code.  Touching every line of the argument struct at
+// entry brings them all in behind a single wait.
+template <typename Args>
+__device__ __forceinline__ void touch_args()
+{
+    const __attribute__((address_space(4))) uint32_t *p =
+        (const __attribute__((address_space(4))) uint32_t *)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < (int)((sizeof(Args) + 63) / 64); ++i)
+        s ^= p[i * 16];
+    asm volatile("" ::"s"(s));
+}
+
 // The batch's slot indices, thread tid holding tokens c*256 + tid (-1 past T).
 __device__ __forceinline__ void plan_load_idx(const int32_t *idx, int T, int (&v)[kPlanPerThread])
 {
 #pragma unroll
     for (int c = 0; c < kPlanPerThread; ++c) {
+        // unconditional load (clamped index), so that waiting for these
+        // loads need not wait for loads issued after them
         const int i = c * 256 + threadIdx.x;
-        v[c] = i < T ? idx[i] : -1;
+        const int raw = idx[min(i, T - 1)];
+        v[c] = i < T ? raw : -1;
     }
 }
 
@@ -829,15 +849,65 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int spli
         shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
 }
 
+// L2 warm-up of one (K split, member) block while the inline plan is formed.
+// The workgroups of a split all run on one XCD (the host asks for this only
+// when the split count is a multiple of 8), so what they touch here is in that
+// XCD's L2 when their tiles load x and A^T after the plan.  The block is a list
+// of rows over the split's K range: x rows of every token, then A^T rows of
+// every slot (slot s, rank j is row s * R_pad + j, contiguous at stride d_in).
+// Workgroup bt takes a.warm_rows of them; lane l touches one 4-byte word in
+// 64-byte piece (l & 7) + 8 pj of row (l >> 3) + 32 ri.  Returns the words
+// read, to be consumed by keep_warm.
+constexpr int kWarmRowIters = 4, kWarmPieceIters = 2;
+constexpr int kWarmLoads = kWarmRowIters * kWarmPieceIters;
+
+__device__ __forceinline__ void warm_split(const ShrinkArgs &a, int m, int split, int bt,
+                                           uint32_t (&wv)[kWarmLoads])
+{
+    const int d_in = a.d_in[m];
+    const int k0 = split * a.k_chunk[m];
+    const int lpr = split < a.splits[m] ? (min(d_in, k0 + a.k_chunk[m]) - k0 + 31) >> 5 : 0;
+    const int nx = (a.warm & kWarmX) ? a.T : 0;
+    const int rows = nx + ((a.warm & kWarmA) ? a.S * a.R_pad : 0);
+    const int r0 = bt * a.warm_rows, r1 = min(rows, r0 + a.warm_rows);
+    const uint16_t *x = (const uint16_t *)a.x[m] + k0;
+    const uint16_t *A = (const uint16_t *)a.A[m] + k0;
+#pragma unroll
+    for (int ri = 0; ri < kWarmRowIters; ++ri) {
+#pragma unroll
+        for (int pj = 0; pj < kWarmPieceIters; ++pj) {
+            const int row = r0 + (threadIdx.x >> 3) + 32 * ri;
+            const int piece = (threadIdx.x & 7) + 8 * pj;
+            // unconditional (a lane with nothing to touch reads x's first
+            // word), so that the plan's wait for the slot indices need not
+            // wait for these loads as well
+            const bool ok = row < r1 && piece < lpr;
+            const uint16_t *p = !ok ? (const uint16_t *)a.x[m]
+                                : row < nx ? x + (int64_t)row * d_in + piece * 32
+                                           : A + (int64_t)(row - nx) * d_in + piece * 32;
+            wv[ri * kWarmPieceIters + pj] = *(const uint32_t *)p;
+        }
+    }
+}
+
+// Consumes the warm-up words (waits for them; no instruction is emitted).
+__device__ __forceinline__ void keep_warm(const uint32_t (&wv)[kWarmLoads])
+{
+#pragma unroll
+    for (int i = 0; i < kWarmLoads; ++i)
+        asm volatile("" ::"v"(wv[i]));
+}
+
 // Tiles of 17..64 tokens take the segment path, shorter ones the gather path:
 // single-buffered when MIXED (batches above 1024 tokens), else double-buffered
 // when the rank allows.  PLAN: how the workgroup finds its tile (PlanMode).
 // Work item w = (tile * grid_splits + split) * n + member, in groups of n: the
 // members of one (tile, K split) run back to back on one XCD, so when they
 // share x (q, k and v of a layer) x comes from HBM once and from L2 after.
-template <int NB, bool MIXED, int PLAN>
+template <int NB, bool MIXED, int PLAN, bool WARM>
 __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta meta)
 {
+    touch_args<ShrinkArgs>();
     const int w = xcd_item(a.n);
     if (w >= a.grid_tiles * a.grid_splits * a.n)
         return;
@@ -852,7 +922,13 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
         __shared__ TilePlanLds P;
         int v[kPlanPerThread];
         plan_load_idx(a.idx, a.T, v);
-        if (!plan_tile(v, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv))
+        uint32_t wv[kWarmLoads];
+        if constexpr (WARM)
+            warm_split(a, m, split, bt, wv);
+        const bool has_tile = plan_tile(v, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
+        if constexpr (WARM)
+            keep_warm(wv);
+        if (!has_tile)
             return;
     } else {
         const int n_tiles = *a.plan.n_tiles;
@@ -1134,11 +1210,14 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
 constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 
 // Tiles as the shrink published them, with rank and scale of the slot as that
-// shrink saw them.  Work item w = (member * grid_cols + chunk) * grid_tiles +
-// tile, in XCD groups of a.xcd_group: in a large batch, long runs of tiles
-// (mostly of one slot) of one column chunk run on one XCD and read that slot's
-// B columns from L2; a small batch keeps groups of 1 (plain round-robin), which
-// balances its few, uneven tiles over the XCDs.
+// shrink saw them.  Work items are taken in XCD groups of a.xcd_group.  A small
+// batch numbers them w = (member * grid_cols + chunk) * grid_tiles + tile in
+// groups of 1 (plain round-robin), which balances its few, uneven tiles over
+// the XCDs.  A large batch (a.tile_major) numbers them w = (member *
+// grid_tiles + tile) * grid_cols + chunk and gives each XCD one contiguous
+// run: all column chunks of a tile run on one XCD, so the tile's h is fetched
+// from HBM once, and consecutive tiles (mostly of one slot) read that slot's B
+// from the same L2.
 template <int NB, bool TERMS>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
@@ -1146,7 +1225,8 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
     const int w = xcd_item(a.xcd_group);
     if (w >= n_items)
         return;
-    const int bt = w % a.grid_tiles, chunk = (w / a.grid_tiles) % a.grid_cols;
+    const int bt = a.tile_major ? (w / a.grid_cols) % a.grid_tiles : w % a.grid_tiles;
+    const int chunk = a.tile_major ? w % a.grid_cols : (w / a.grid_tiles) % a.grid_cols;
     const int m = w / (a.grid_tiles * a.grid_cols);
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
@@ -1297,19 +1377,19 @@ static dim3 xcd_grid(int64_t n, int G)
     return dim3((unsigned)((groups + kXcds - 1) / kXcds * kXcds * G));
 }
 
-template <bool MIXED, int PLAN>
+template <bool MIXED, int PLAN, bool WARM = false>
 static void launch_shrink_bf16(const ShrinkArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st,
                                const LaunchTiming &t)
 {
     const int nbmax = a.R_pad / 16;
     if (nbmax <= 1)
-        launch(shrink_bf16_kernel<1, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<1, MIXED, PLAN, WARM>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 2)
-        launch(shrink_bf16_kernel<2, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<2, MIXED, PLAN, WARM>, grid, dim3(256), 0, st, t, a, m);
     else if (nbmax <= 4)
-        launch(shrink_bf16_kernel<4, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<4, MIXED, PLAN, WARM>, grid, dim3(256), 0, st, t, a, m);
     else
-        launch(shrink_bf16_kernel<8, MIXED, PLAN>, grid, dim3(256), 0, st, t, a, m);
+        launch(shrink_bf16_kernel<8, MIXED, PLAN, WARM>, grid, dim3(256), 0, st, t, a, m);
 }
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
@@ -1320,7 +1400,8 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
     if (!bf16)
         launch(shrink_f32_kernel, grid, block, 0, st, t, a, m);
     else if (a.plan_mode == kPlanInline)
-        launch_shrink_bf16<false, kPlanInline>(a, m, g, st, t);
+        a.warm ? launch_shrink_bf16<false, kPlanInline, true>(a, m, g, st, t)
+               : launch_shrink_bf16<false, kPlanInline, false>(a, m, g, st, t);
     else if (a.mixed)
         launch_shrink_bf16<true, kPlanTiles>(a, m, g, st, t);
     else

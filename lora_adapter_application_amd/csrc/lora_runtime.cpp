@@ -393,6 +393,21 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
     a.R_pad = c->R_pad;
     a.grid_tiles = max_tiles_for(T, c->S);
     a.mixed = T > 1024;
+    // With the inline plan and a multiple of 8 K-splits, every tile of one
+    // split runs on one XCD: its workgroups warm that split's x block (all
+    // tokens) and, when it is small, its A^T block (all slots) in that XCD's L2
+    // while they form the plan.
+    a.warm = 0;
+    if (c->plan_mode == kPlanInline && a.grid_splits % 8 == 0) {
+        a.warm = kWarmX;
+        int64_t a_bytes = 0;
+        for (int i = 0; i < n; ++i)
+            a_bytes = std::max<int64_t>(a_bytes, (int64_t)c->S * c->R_pad * a.k_chunk[i] * c->elem);
+        if (a_bytes <= (256 << 10))
+            a.warm |= kWarmA;
+        const int rows = T + ((a.warm & kWarmA) ? c->S * c->R_pad : 0);
+        a.warm_rows = ceil_div(rows, a.grid_tiles);
+    }
     return a;
 }
 
@@ -424,9 +439,11 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
     a.grid_tiles = max_tiles_for(T, c->S);
-    // large batches: one contiguous run of tiles per XCD; small: round-robin
+    // large batches: one contiguous run of tiles per XCD, every column chunk of
+    // a tile on the same XCD; small: round-robin
     const int64_t items = (int64_t)a.grid_tiles * a.grid_cols * n;
-    a.xcd_group = T > kInlinePlanTokens ? (int)((items + 7) / 8) : 1;
+    a.tile_major = T > kInlinePlanTokens;
+    a.xcd_group = a.tile_major ? (int)((items + 7) / 8) : 1;
     a.terms = 0;
     for (int k = 0; k < c->S; ++k)
         if (c->slot_flags[k] && (!c->plan_hinted || c->hint[k]))
