@@ -702,22 +702,25 @@ __device__ __forceinline__ void plan_load_idx(const int32_t *idx, int T, int (&v
 // Tile b of the plan, from the slot indices v (plan_load_idx).  publish: write
 // the tile and its token ids to the plan buffers; first: write the totals and
 // the flag.  Returns false past the last tile.
-__device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs &mr,
+__device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, const MetaRegs &mr,
                           const PlanBuffers &pb, TilePlanLds &L, int b, bool publish, bool first,
                           Tile &tile, int &tokv)
 {
     constexpr int NC = kPlanPerThread;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ncu = (T + 255) >> 8;             // entries c of v that hold tokens
     if (tid < S)
         L.cnt[tid] = 0;
     __syncthreads();
     bool big = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (v[c] >= 0 && v[c] < S)
-            atomicAdd(&L.cnt[v[c]], 1);
-        big |= v[c] >= S;
+        if (c < ncu) {
+            if (v[c] >= 0 && v[c] < S)
+                atomicAdd(&L.cnt[v[c]], 1);
+            big |= v[c] >= S;
+        }
     }
     if (first) {
         const uint64_t bigm = __ballot(big);
@@ -726,41 +729,66 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs 
     }
     __syncthreads();
     if (wave == 0) {
-        // lane l takes slots 4l .. 4l+3: counts, tiles, and exclusive prefixes
-        int c4[4], n4[4], sc = 0, sn = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int sl = 4 * lane + k;
-            c4[k] = sl < S ? L.cnt[sl] : 0;
-            n4[k] = (c4[k] + kTileTokens - 1) / kTileTokens;
-            sc += c4[k];
-            sn += n4[k];
-        }
-        const int ic = wave_incl_scan(sc), in = wave_incl_scan(sn);
-        int pc = ic - sc, pn = in - sn;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int sl = 4 * lane + k;
-            if (sl < S) {
-                if (b >= pn && b < pn + n4[k]) {
-                    L.slot = sl;
-                    L.j = b - pn;
-                    L.start = pc;
-                    L.count = c4[k];
-                }
+        if (S <= 64) {
+            // lane l takes slot l: count, tiles, and exclusive prefixes
+            const int c1 = lane < S ? L.cnt[lane] : 0;
+            const int n1 = (c1 + kTileTokens - 1) / kTileTokens;
+            const int ic = wave_incl_scan(c1), in = wave_incl_scan(n1);
+            const int pc = ic - c1, pn = in - n1;
+            if (lane < S && b >= pn && b < pn + n1) {
+                L.slot = lane;
+                L.j = b - pn;
+                L.start = pc;
+                L.count = c1;
+            }
+            if (first && lane < S) {
+                pb.counts[lane] = c1;
+                pb.seg_start[lane] = pc;
+            }
+            if (lane == 63) {
+                L.n_tiles = in;
                 if (first) {
-                    pb.counts[sl] = c4[k];
-                    pb.seg_start[sl] = pc;
+                    *pb.n_tiles = in;
+                    *pb.n_active = ic;
                 }
             }
-            pc += c4[k];
-            pn += n4[k];
-        }
-        if (lane == 63) {
-            L.n_tiles = in;
-            if (first) {
-                *pb.n_tiles = in;
-                *pb.n_active = ic;
+        } else {
+            // lane l takes slots 4l .. 4l+3
+            int c4[4], n4[4], sc = 0, sn = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int sl = 4 * lane + k;
+                c4[k] = sl < S ? L.cnt[sl] : 0;
+                n4[k] = (c4[k] + kTileTokens - 1) / kTileTokens;
+                sc += c4[k];
+                sn += n4[k];
+            }
+            const int ic = wave_incl_scan(sc), in = wave_incl_scan(sn);
+            int pc = ic - sc, pn = in - sn;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int sl = 4 * lane + k;
+                if (sl < S) {
+                    if (b >= pn && b < pn + n4[k]) {
+                        L.slot = sl;
+                        L.j = b - pn;
+                        L.start = pc;
+                        L.count = c4[k];
+                    }
+                    if (first) {
+                        pb.counts[sl] = c4[k];
+                        pb.seg_start[sl] = pc;
+                    }
+                }
+                pc += c4[k];
+                pn += n4[k];
+            }
+            if (lane == 63) {
+                L.n_tiles = in;
+                if (first) {
+                    *pb.n_tiles = in;
+                    *pb.n_active = ic;
+                }
             }
         }
     }
@@ -771,9 +799,12 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs 
     uint64_t mk[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        mk[c] = __ballot(v[c] == sl);
-        if (lane == 0)
-            L.wc[c * 4 + wave] = __popcll(mk[c]);
+        mk[c] = 0;
+        if (c < ncu) {
+            mk[c] = __ballot(v[c] == sl);
+            if (lane == 0)
+                L.wc[c * 4 + wave] = __popcll(mk[c]);
+        }
     }
     __syncthreads();
     // window c*4 + wave holds tokens c*256 + 64*wave .. +63, so windows in index
@@ -784,16 +815,18 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int S, const MetaRegs 
         pre[c] = 0;
 #pragma unroll
     for (int w = 0; w < kInlinePlanTokens / 64; ++w) {
-        const int k = L.wc[w];
+        if (w < 4 * ncu) {
+            const int k = L.wc[w];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            if (w == c * 4 + wave)
-                pre[c] = before;
-        before += k;
+            for (int c = 0; c < NC; ++c)
+                if (w == c * 4 + wave)
+                    pre[c] = before;
+            before += k;
+        }
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (v[c] == sl) {
+        if (c < ncu && v[c] == sl) {
             const int r = pre[c] - j * kTileTokens +
                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk[c] >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[c], 0u));
@@ -925,7 +958,7 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
         uint32_t wv[kWarmLoads];
         if constexpr (WARM)
             warm_split(a, m, split, bt, wv);
-        const bool has_tile = plan_tile(v, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
+        const bool has_tile = plan_tile(v, a.T, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
         if constexpr (WARM)
             keep_warm(wv);
         if (!has_tile)
@@ -1210,24 +1243,31 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
 constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 
 // Tiles as the shrink published them, with rank and scale of the slot as that
-// shrink saw them.  Work items are taken in XCD groups of a.xcd_group.  A small
-// batch numbers them w = (member * grid_cols + chunk) * grid_tiles + tile in
-// groups of 1 (plain round-robin), which balances its few, uneven tiles over
-// the XCDs.  A large batch (a.tile_major) numbers them w = (member *
-// grid_tiles + tile) * grid_cols + chunk and gives each XCD one contiguous
-// run: all column chunks of a tile run on one XCD, so the tile's h is fetched
-// from HBM once, and consecutive tiles (mostly of one slot) read that slot's B
-// from the same L2.
+// shrink saw them.  Member m has its own number of 256-column chunks,
+// a.col_start[m + 1] - a.col_start[m]; work items cover exactly the (tile,
+// member, chunk) triples, member by member, so a group of members of unequal
+// widths (q next to k and v) launches no empty workgroups.  Items are taken in
+// XCD groups of a.xcd_group.  Within a member a small batch numbers them
+// chunk * grid_tiles + tile in groups of 1 (plain round-robin), which balances
+// its few, uneven tiles over the XCDs.  A large batch (a.tile_major) numbers
+// them tile * chunks + chunk and gives each XCD one contiguous run: all column
+// chunks of a tile run on one XCD, so the tile's h is fetched from HBM once,
+// and consecutive tiles (mostly of one slot) read that slot's B from the same
+// L2.
 template <int NB, bool TERMS>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
-    const int n_items = a.grid_tiles * a.grid_cols * a.n;
+    const int n_items = a.grid_tiles * a.col_start[a.n];
     const int w = xcd_item(a.xcd_group);
     if (w >= n_items)
         return;
-    const int bt = a.tile_major ? (w / a.grid_cols) % a.grid_tiles : w % a.grid_tiles;
-    const int chunk = a.tile_major ? w % a.grid_cols : (w / a.grid_tiles) % a.grid_cols;
-    const int m = w / (a.grid_tiles * a.grid_cols);
+    int m = 0;
+    while (m + 1 < a.n && w >= a.grid_tiles * a.col_start[m + 1])
+        ++m;
+    const int local = w - a.grid_tiles * a.col_start[m];
+    const int chunks = a.col_start[m + 1] - a.col_start[m];
+    const int bt = a.tile_major ? local / chunks : local % a.grid_tiles;
+    const int chunk = a.tile_major ? local % chunks : local / a.grid_tiles;
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
     const int n_tiles = *a.n_tiles;
@@ -1416,7 +1456,7 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
     if (!bf16) {
         launch(expand_f32_kernel, grid, block, 0, st, t, a, m);
     } else {
-        const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.grid_cols * a.n, a.xcd_group);
+        const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.col_start[a.n], a.xcd_group);
         const int nbmax = a.R_pad / 16;
         // the output-term epilogue only in launches where some slot has terms
         if (a.terms) {

@@ -430,6 +430,7 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
         a.d_out[i] = sh.d_out;
         a.splits[i] = c->last_splits[i];
         a.grid_cols = std::max(a.grid_cols, ceil_div(sh.d_out, kExpandCols));
+        a.col_start[i + 1] = a.col_start[i] + ceil_div(sh.d_out, kExpandCols);
     }
     a.tiles = c->plan.tiles;
     a.tile_tok = c->plan.tile_tok;
@@ -441,7 +442,7 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     a.grid_tiles = max_tiles_for(T, c->S);
     // large batches: one contiguous run of tiles per XCD, every column chunk of
     // a tile on the same XCD; small: round-robin
-    const int64_t items = (int64_t)a.grid_tiles * a.grid_cols * n;
+    const int64_t items = (int64_t)a.grid_tiles * a.col_start[n];
     a.tile_major = T > kInlinePlanTokens;
     a.xcd_group = a.tile_major ? (int)((items + 7) / 8) : 1;
     a.terms = 0;
