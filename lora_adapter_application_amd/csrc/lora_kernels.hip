@@ -876,9 +876,18 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int spli
     v.k1 = min((int)v.d_in, v.k0 + a.k_chunk[m]);
     v.h = a.hpart + m * a.member_stride + (int64_t)split * a.split_stride;
     v.R_pad = a.R_pad;
-    if (tile.len > kSegmentMinTokens)
-        shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
-    else
+    if (tile.len > kSegmentMinTokens) {
+        // the segment loop sized to the tile's own rank blocks: a wider one
+        // would load (clamped) A^T rows past them on every K block
+        if (NB >= 2 && nb <= 1)
+            shrink_sgmv<1>(v, tile, tokv, nb, (uint16_t *)smem);
+        else if (NB >= 4 && nb <= 2)
+            shrink_sgmv<(NB >= 4 ? 2 : NB)>(v, tile, tokv, nb, (uint16_t *)smem);
+        else if (NB >= 8 && nb <= 4)
+            shrink_sgmv<(NB >= 8 ? 4 : NB)>(v, tile, tokv, nb, (uint16_t *)smem);
+        else
+            shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
+    } else
         shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
 }
 
