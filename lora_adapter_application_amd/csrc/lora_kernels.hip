@@ -587,38 +587,68 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &til
     // ring slot j holds block i + j of the current pass (x) and, for A^T, the
     // block after the one staged in LDS
     uint4 xr[D][4], ar[D][NB];
+    auto mma = [&](int b, const uint4 (&xv)[4]) {
+        const uint16_t *L = lds + (b & 1) * buf_elems;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-        if (j < nkb) {
-            load_a(ar[j], k0 + j * kShrinkKBlock);
-            load_x(xr[j], k0 + j * kShrinkKBlock);
+        for (int rb = 0; rb < NB; ++rb) {
+            if (rb < nb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 av = *(const uint4 *)(L + (rb * 16 + row) * kLdsRow + g * 32 + q * 8);
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv[q]), acc[rb], 0,
+                        0, 0);
+                }
+            }
         }
+    };
+    int i = 0;
+    if (nkb >= 2 * D) {
+        // Steady state: every refill of the first nkb - D blocks is in range,
+        // so the prologue and the loop issue their loads without a branch, in
+        // a fixed order, and the compiler counts them exactly; a branch around
+        // a load would make it wait for all of them at the loop head.
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            load_x(xr[j], k0 + j * kShrinkKBlock);
+            load_a(ar[j], k0 + j * kShrinkKBlock);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store_a(ar[0], 0, k0);
+        __syncthreads();
+        for (; i + 2 * D <= nkb; i += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int b = i + j;
+                mma(b, xr[j]);
+                load_x(xr[j], k0 + (b + D) * kShrinkKBlock);
+                store_a(ar[(j + 1) % D], (b + 1) & 1, k0 + (b + 1) * kShrinkKBlock);
+                load_a(ar[j], k0 + (b + D) * kShrinkKBlock);
+                __syncthreads();
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            if (j < nkb) {
+                load_a(ar[j], k0 + j * kShrinkKBlock);
+                load_x(xr[j], k0 + j * kShrinkKBlock);
+            }
+        }
+        store_a(ar[0], 0, k0);
+        __syncthreads();
     }
-    store_a(ar[0], 0, k0);
-    __syncthreads();
-    for (int i = 0; i < nkb; i += D) {
+    // the last blocks: refills only while in range
+    for (; i < nkb; i += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int b = i + j;          // block multiplied in this step
             if (b < nkb) {
-                const uint16_t *L = lds + (b & 1) * buf_elems;
-#pragma unroll
-                for (int rb = 0; rb < NB; ++rb) {
-                    if (rb < nb) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint4 av = *(const uint4 *)(L + (rb * 16 + row) * kLdsRow + g * 32 + q * 8);
-                            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xr[j][q]),
-                                acc[rb], 0, 0, 0);
-                        }
-                    }
-                }
+                mma(b, xr[j]);
                 // slot j is free (A^T block b is in LDS, x block b consumed):
                 // refill it with block b + D
-                if (b + D < nkb) {
+                if (b + D < nkb)
                     load_x(xr[j], k0 + (b + D) * kShrinkKBlock);
-                }
                 // stage block b + 1 (slot j + 1) into the other LDS buffer
                 if (b + 1 < nkb)
                     store_a(ar[(j + 1) % D], (b + 1) & 1, k0 + (b + 1) * kShrinkKBlock);
