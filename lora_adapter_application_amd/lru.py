@@ -11,7 +11,11 @@ adapter cache in production" (oh-bug.com):
   - an adapter that in-flight work is using is never evicted;
 - the parameter table: max_loras bounds the adapters one batch uses;
 - the metrics section: the thrash ratio is reloads shortly after an eviction,
-  divided by evictions.
+  divided by evictions;
+- section "why pure LRU fails in multi-tenant settings": a burst of rarely used
+  adapters must not push the hot ones out.  Two of its platform rules are here:
+  a warm set of pinned adapters that are never evicted while resident, and a
+  minimum residency (in steps) before a newly loaded adapter may be evicted.
 
 One step is one batch.  Every adapter it uses must be resident before the batch
 runs:
@@ -19,11 +23,14 @@ runs:
 1. adapters already resident are hits and are touched;
 2. the others are misses, loaded in order of first appearance;
 3. a miss takes an empty slot (lowest index first), or else evicts the least
-   recently used slot that the step itself does not use; slots passed as
-   `avoid` (read by batches still in flight) are taken only when no other slot
-   is left, since a load into them has to wait for those batches.
+   recently used slot that the step itself does not use and that holds no
+   pinned adapter.  Among those, slots whose adapter is younger than
+   `min_residency` steps are taken only when no older one is left, and slots
+   passed as `avoid` (read by batches still in flight, so a load into them has
+   to wait for those batches) only when nothing else is.
 
-A step with more distinct adapters than slots is refused.
+A step with more distinct adapters than slots, or one that would have to evict
+a pinned adapter, is refused.
 """
 from __future__ import annotations
 
@@ -48,11 +55,16 @@ class LruStats:
 
 
 class SlotLRU:
-    def __init__(self, n_slots: int, thrash_window: int = 10):
+    def __init__(self, n_slots: int, thrash_window: int = 10, min_residency: int = 0):
         if n_slots < 1:
             raise ValueError("n_slots must be >= 1")
+        if min_residency < 0:
+            raise ValueError("min_residency must be >= 0")
         self.n_slots = n_slots
         self.thrash_window = thrash_window
+        self.min_residency = min_residency
+        self.pinned: set = set()
+        self.loaded_at = [-1] * n_slots
         self.adapter_in: List[Optional[int]] = [None] * n_slots
         self.slot_of: Dict[int, int] = {}
         self.last_use = [-1] * n_slots
@@ -64,6 +76,17 @@ class SlotLRU:
     def resident(self) -> Dict[int, int]:
         """adapter id -> slot for every resident adapter."""
         return dict(self.slot_of)
+
+    def pin(self, adapter_ids) -> None:
+        """Add adapters to the warm set: once resident they are never evicted.
+        At least one slot must stay free of pinned adapters."""
+        new = self.pinned | {int(a) for a in adapter_ids}
+        if len(new) >= self.n_slots:
+            raise ValueError(f"{len(new)} pinned adapters leave no evictable slot of {self.n_slots}")
+        self.pinned = new
+
+    def unpin(self, adapter_ids) -> None:
+        self.pinned -= {int(a) for a in adapter_ids}
 
     def _touch(self, slot: int) -> None:
         self.tick += 1
@@ -84,6 +107,12 @@ class SlotLRU:
         if len(distinct) > self.n_slots:
             raise ValueError(f"step uses {len(distinct)} adapters but only {self.n_slots} slots exist")
         protected = {self.slot_of[a] for a in distinct if a in self.slot_of}
+        n_miss = sum(1 for a in distinct if a not in self.slot_of)
+        usable = sum(1 for s in range(self.n_slots)
+                     if s not in protected and self.adapter_in[s] not in self.pinned)
+        if n_miss > usable:
+            raise ValueError(f"step needs {n_miss} slots but only {usable} hold no pinned "
+                             "adapter and no adapter of the step")
         loads: List[Tuple[int, int]] = []
         for a in distinct:
             if a in self.slot_of:
@@ -97,15 +126,19 @@ class SlotLRU:
             if empty:
                 slot = empty[0]
             else:
-                cands = [s for s in range(self.n_slots) if s not in protected]
-                free = [s for s in cands if s not in avoid]
-                slot = min(free or cands, key=lambda s: self.last_use[s])
+                cands = [s for s in range(self.n_slots)
+                         if s not in protected and self.adapter_in[s] not in self.pinned]
+                young = {s for s in cands if self.step_no - self.loaded_at[s] < self.min_residency}
+                free = [s for s in cands if s not in avoid and s not in young]
+                free = free or [s for s in cands if s not in avoid] or cands
+                slot = min(free, key=lambda s: self.last_use[s])
                 old = self.adapter_in[slot]
                 del self.slot_of[old]
                 self.evicted_at[old] = self.step_no
                 self.stats.evictions += 1
             self.adapter_in[slot] = a
             self.slot_of[a] = slot
+            self.loaded_at[slot] = self.step_no
             protected.add(slot)
             self._touch(slot)
             loads.append((slot, a))

@@ -76,3 +76,63 @@ def test_avoided_slots_are_evicted_last():
     slots, loads = lru.plan_step(np.array([5, 4, 6]), avoid={0, 1})
     assert loads == [(0, 6)]
     assert lru.resident() == {2: 1, 5: 2, 4: 3, 6: 0}
+
+
+def test_pinned_adapter_survives_a_burst_of_cold_adapters():
+    """The pages' thrashing case: 4 slots, a hot adapter, and a burst of 20 rarely used
+    ones touched one per step.  Plain LRU evicts the hot adapter; a pinned one stays."""
+    burst = [np.array([100 + k]) for k in range(20)]
+    plain = SlotLRU(4)
+    plain.plan_step(np.array([1]))
+    for ids in burst:
+        plain.plan_step(ids)
+    assert 1 not in plain.resident()
+    warm = SlotLRU(4)
+    warm.pin([1])
+    warm.plan_step(np.array([1]))
+    slot_of_1 = warm.resident()[1]
+    for ids in burst:
+        _, loads = warm.plan_step(ids)
+        assert all(s != slot_of_1 for s, _ in loads)
+    assert warm.resident()[1] == slot_of_1
+    _, loads = warm.plan_step(np.array([1]))
+    assert loads == [] and warm.stats.hits == 1
+    # unpinned, it is an ordinary LRU entry again
+    warm.unpin([1])
+    for ids in burst[:4]:
+        warm.plan_step(ids)
+    assert 1 not in warm.resident()
+
+
+def test_pinning_must_leave_an_evictable_slot_and_a_step_may_not_need_a_pinned_one():
+    lru = SlotLRU(3)
+    with pytest.raises(ValueError):
+        lru.pin([1, 2, 3])
+    lru.pin([1, 2])
+    lru.plan_step(np.array([1, 2, 3]))
+    before = (lru.resident(), lru.stats.misses, lru.stats.evictions)
+    # 4 and 5 need two slots; only slot of 3 is evictable: refused, state unchanged
+    with pytest.raises(ValueError):
+        lru.plan_step(np.array([4, 5]))
+    assert (lru.resident(), lru.stats.misses, lru.stats.evictions) == before
+    slots, loads = lru.plan_step(np.array([4, 1]))
+    assert loads == [(2, 4)] and list(slots) == [2, 0]
+
+
+def test_minimum_residency_keeps_new_adapters_until_older_ones_are_gone():
+    lru = SlotLRU(3, min_residency=3)
+    lru.plan_step(np.array([1, 2, 3]))            # step 0: slots 0,1,2
+    lru.plan_step(np.array([1, 2]))               # step 1: 3 is least recently used
+    # step 2: every resident adapter is younger than 3 steps; with nothing older,
+    # the least recently used one (3, slot 2) is still taken
+    _, loads = lru.plan_step(np.array([4]))
+    assert loads == [(2, 4)]
+    lru.plan_step(np.array([1, 2]))               # step 3: 4 is now least recently used
+    # step 4: 4 (loaded at step 2) is younger than 3 steps, so the older LRU entry
+    # outside the step goes instead
+    _, loads = lru.plan_step(np.array([5, 2]))
+    assert loads == [(0, 5)]
+    assert 4 in lru.resident() and 1 not in lru.resident()
+    # step 5: 4 has reached the minimum residency and is the only candidate
+    _, loads = lru.plan_step(np.array([6, 2, 5]))
+    assert loads == [(2, 6)]
