@@ -990,11 +990,11 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
     Tile tile;
     int tokv;
     const bool lead = split == 0 && m == 0;     // publishes the tile
+    uint32_t wv[kWarmLoads];
     if constexpr (PLAN == kPlanInline) {
         __shared__ TilePlanLds P;
         int v[kPlanPerThread];
         plan_load_idx(a.idx, a.T, v);
-        uint32_t wv[kWarmLoads];
         if constexpr (WARM)
             warm_split(a, m, split, bt, wv);
         const bool has_tile = plan_tile(v, a.T, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
@@ -1006,8 +1006,15 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
         const int n_tiles = *a.plan.n_tiles;
         tile = a.plan.tiles[bt];              // in bounds: the tile buffer covers the grid
         tokv = a.plan.tile_tok[(int64_t)bt * kTileTokens + lane];
-        if (bt >= n_tiles)
+        // warm the split while the tile record arrives; the words are consumed
+        // at the end, so no wait is added
+        if constexpr (WARM)
+            warm_split(a, m, split, bt, wv);
+        if (bt >= n_tiles) {
+            if constexpr (WARM)
+                keep_warm(wv);
             return;
+        }
         // lookups in code every lane runs (see meta_scale), stores by one lane
         tile.rank = meta_rank(mr, tile.slot);
         tile.scale = meta_scale(mr, tile.slot);
@@ -1016,9 +1023,14 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
             a.plan.tiles[bt].scale = tile.scale;
         }
     }
-    if (split >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
+    if (split >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot)) {
+        if constexpr (WARM && PLAN != kPlanInline)
+            keep_warm(wv);
         return;
+    }
     shrink_tile<NB, MIXED>(a, m, split, tile, tokv, lds);
+    if constexpr (WARM && PLAN != kPlanInline)
+        keep_warm(wv);
 }
 
 // ----------------------------------------------------------------------------
@@ -1483,6 +1495,8 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
                : launch_shrink_bf16<false, kPlanInline, false>(a, m, g, st, t);
     else if (a.mixed)
         launch_shrink_bf16<true, kPlanTiles>(a, m, g, st, t);
+    else if (a.warm)
+        launch_shrink_bf16<false, kPlanTiles, true>(a, m, g, st, t);
     else
         launch_shrink_bf16<false, kPlanTiles>(a, m, g, st, t);
     return hipGetLastError();

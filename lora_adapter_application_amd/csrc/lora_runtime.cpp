@@ -393,12 +393,12 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
     a.R_pad = c->R_pad;
     a.grid_tiles = max_tiles_for(T, c->S);
     a.mixed = T > 1024;
-    // With the inline plan and a multiple of 8 K-splits, every tile of one
-    // split runs on one XCD: its workgroups warm that split's x block (all
-    // tokens) and, when it is small, its A^T block (all slots) in that XCD's L2
-    // while they form the plan.
+    // A small batch with a multiple of 8 K-splits runs every tile of one split
+    // on one XCD: its workgroups warm that split's x block (all tokens) and,
+    // when it is small, its A^T block (all slots) in that XCD's L2 while they
+    // form the plan or read the published tile.
     a.warm = 0;
-    if (c->plan_mode == kPlanInline && a.grid_splits % 8 == 0) {
+    if (c->dtype == LORA_BF16 && T <= kInlinePlanTokens && a.grid_splits % 8 == 0) {
         a.warm = kWarmX;
         int64_t a_bytes = 0;
         for (int i = 0; i < n; ++i)
