@@ -21,9 +21,11 @@ value      tokens of the batch (skipped tokens included) x K / wall time of K st
 roofline   the kernel with the largest share of the step: its algorithmic bytes /
            its kernel time, from start / stop events the library attaches to each of
            its dispatches (hipExtLaunchKernelGGL) during a second pass of the same K
-           steps right after the timed one
+           steps right after the timed one; also its fraction of a measured 1 GiB
+           device copy (copy_GBps, read plus write) beside the 8 TB/s spec
 cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
-           same workload (rank 0, one GPU only)
+           same workload (rank 0, one GPU only): all threads, and one thread on
+           a smaller sample; nproc and the CPU model
 """
 from __future__ import annotations
 
@@ -105,6 +107,27 @@ def calib_copy(steps):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
                       "ms_per_copy": dt * 1e3, "GBps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def measured_copy_gbps(reps=10):
+    """Read-plus-write rate of a 1 GiB device copy (torch), the practical ceiling
+    the dominant kernel is also compared with, beside the 8 TB/s spec."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    gbps = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def kernel_source_sha():
@@ -313,11 +336,14 @@ def main():
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
         kname = "lora_" + dom
         traffic = traffic_from_profiles(kname, wl.name)
+        copy_gbps = measured_copy_gbps()
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic,
                     "alg_bytes_per_launch": float(np.mean(dom_bytes)),
-                    "avg_launch_us": avg_us(dom)}
+                    "avg_launch_us": avg_us(dom),
+                    "copy_GBps": round(copy_gbps, 1),
+                    "frac_of_copy": round(achieved / copy_gbps, 4)}
         log("kernels:", json.dumps(kernels))
 
     cpu = None
@@ -534,11 +560,36 @@ def cpu_baseline(wl, seconds):
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
+    # one thread on a smaller sample, about a third of the time
+    rows1 = rows[:256]
+    layers1 = 0
+    t1 = time.perf_counter()
+    while True:
+        for m in wl.modules:
+            oracle.apply(oracle.BF16, wl.x[m.name][rows1], wl.y[m.name][rows1], wl.idx[rows1],
+                         ads[m.name], n_threads=1)
+        layers1 += 1
+        dt1 = time.perf_counter() - t1
+        if dt1 >= seconds / 3:
+            break
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(layers * len(rows) / dt, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{layers} layer passes of {len(rows)} tokens of {wl.name} "
                       f"({len(wl.modules)} modules each), fp64 scalar C, OpenMP over tokens, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "single_thread": {"value": round(layers1 * len(rows1) / dt1, 1), "unit": "tokens/s",
+                              "sample": f"{layers1} layer passes of {len(rows1)} tokens, 1 thread, "
+                                        f"{dt1:.1f} s"},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model}
 
 
 if __name__ == "__main__":
