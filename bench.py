@@ -284,6 +284,22 @@ def main():
     torch.cuda.synchronize()
     graph_s = time.perf_counter() - t0
     del graphs
+    # step-time spread: the K steps once more, an event recorded after each
+    # (events made before the pass); each step's time is the gap to the
+    # previous event, so the distribution includes one event's cost per step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(K):
+        step(args.warmup + i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K)])
+    step_spread = {"p10_us": round(float(np.percentile(per_step, 10)), 3),
+                   "p50_us": round(float(np.percentile(per_step, 50)), 3),
+                   "p90_us": round(float(np.percentile(per_step, 90)), 3),
+                   "pass": "eager, an event after each step"}
+    del evs
     elapsed = graph_s if args.launch == "graph" else eager_s
     ms_per_step = elapsed / K * 1e3
     value = T * K / elapsed
@@ -375,6 +391,7 @@ def main():
         "cpu_baseline": cpu,
         "eager": {"ms_per_step": round(eager_s / K * 1e3, 5), "value": round(T * K / eager_s, 1)},
         "graph": {"ms_per_step": round(graph_s / K * 1e3, 5), "value": round(T * K / graph_s, 1)},
+        "step_spread": step_spread,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
