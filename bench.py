@@ -151,8 +151,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
-              "by replicating slot pools per GPU with no exchange, which this build does not "
-              "measure.", file=sys.stderr)
+              "by replicating slot pools per GPU with no exchange, which this benchmark does "
+              "not measure.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
