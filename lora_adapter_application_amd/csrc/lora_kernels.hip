@@ -1300,11 +1300,11 @@ constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 // widths (q next to k and v) launches no empty workgroups.  Items are taken in
 // XCD groups of a.xcd_group.  Within a member a small batch numbers them
 // chunk * grid_tiles + tile in groups of 1 (plain round-robin), which balances
-// its few, uneven tiles over the XCDs.  A large batch (a.tile_major) numbers
-// them tile * chunks + chunk and gives each XCD one contiguous run: all column
-// chunks of a tile run on one XCD, so the tile's h is fetched from HBM once,
-// and consecutive tiles (mostly of one slot) read that slot's B from the same
-// L2.
+// its few, uneven tiles over the XCDs.  A large batch gives each XCD one
+// contiguous run of items, numbered chunk * grid_tiles + tile, or, with long
+// slot segments (a.tile_major), tile * chunks + chunk: then all column chunks
+// of a tile run on one XCD, so the tile's h is fetched from HBM once, and
+// consecutive tiles (mostly of one slot) read that slot's B from the same L2.
 template <int NB, bool TERMS>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {

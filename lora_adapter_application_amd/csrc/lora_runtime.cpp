@@ -440,11 +440,16 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
     a.grid_tiles = max_tiles_for(T, c->S);
-    // large batches: one contiguous run of tiles per XCD, every column chunk of
-    // a tile on the same XCD; small: round-robin
+    // large batches: one contiguous run of items per XCD.  With long slot
+    // segments (prefill) the run is tile-major, every column chunk of a tile on
+    // one XCD: the tile's h comes from HBM once and consecutive tiles of a slot
+    // share its B in L2 (0.74 vs 0.81 ms per Llama-7B prefill step).  With about
+    // one tile per slot it is chunk-major, which measured 4% faster on the churn
+    // workload (8192 tokens over 128 slots).  Small batches: round-robin.
     const int64_t items = (int64_t)a.grid_tiles * a.col_start[n];
-    a.tile_major = T > kInlinePlanTokens;
-    a.xcd_group = a.tile_major ? (int)((items + 7) / 8) : 1;
+    const bool large = T > kInlinePlanTokens;
+    a.tile_major = large && T >= 128 * c->S;
+    a.xcd_group = large ? (int)((items + 7) / 8) : 1;
     a.terms = 0;
     for (int k = 0; k < c->S; ++k)
         if (c->slot_flags[k] && (!c->plan_hinted || c->hint[k]))
