@@ -11,6 +11,13 @@ namespace lora {
 
 // Tokens per tile: a tile is a run of at most kTileTokens tokens of one slot.
 constexpr int kTileTokens = 64;
+// Tiles of the plan a bf16 shrink forms inline (batches of at most
+// kInlinePlanTokens tokens) hold at most inline_tile_tokens(R_pad) tokens: a
+// decode kernel ends with its slowest workgroup, and a 64-token tile moves four
+// times the x bytes of a 16-token one; every tile also re-reads its slot's A^T,
+// a larger share of the bytes at higher rank.
+constexpr int kInlineTileTokensMax = 48;
+inline int inline_tile_tokens(int R_pad) { return R_pad <= 16 ? 32 : 48; }
 // Columns of y one expand workgroup covers.
 constexpr int kExpandCols = 256;
 // K elements one shrink wave consumes per step (4 MFMA steps of 32).
@@ -75,7 +82,10 @@ struct LaunchTiming {
     hipEvent_t stop = nullptr;
 };
 
-inline int max_tiles_for(int T, int S) { return (T + kTileTokens - 1) / kTileTokens + (S < T ? S : T); }
+inline int max_tiles_for(int T, int S, int cap = kTileTokens)
+{
+    return (T + cap - 1) / cap + (S < T ? S : T);
+}
 
 // A plan of more than 1024 tokens takes two launches; t[0] and t[1] time them.
 hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffers &pb,
@@ -104,6 +114,7 @@ struct ShrinkArgs {
     int32_t mixed;                      // batch above 1024 tokens: long tiles take the segment path
     int32_t warm;                       // kWarmX | kWarmA: L2 warm-up of the split's blocks (inline plan)
     int32_t warm_rows;                  // rows of the warm-up block per workgroup
+    int32_t tile_cap;                   // inline plan: tokens per tile
 };
 
 // What the inline-plan shrink warms in L2 while its plan is formed.

@@ -729,10 +729,11 @@ __device__ __forceinline__ void plan_load_idx(const int32_t *idx, int T, int (&v
     }
 }
 
-// Tile b of the plan, from the slot indices v (plan_load_idx).  publish: write
-// the tile and its token ids to the plan buffers; first: write the totals and
-// the flag.  Returns false past the last tile.
-__device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, const MetaRegs &mr,
+// Tile b of the plan, from the slot indices v (plan_load_idx); a slot's tokens
+// are cut into tiles of at most cap tokens.  publish: write the tile and its
+// token ids to the plan buffers; first: write the totals and the flag.  Returns
+// false past the last tile.
+__device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, int cap, const MetaRegs &mr,
                           const PlanBuffers &pb, TilePlanLds &L, int b, bool publish, bool first,
                           Tile &tile, int &tokv)
 {
@@ -762,7 +763,7 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, const Me
         if (S <= 64) {
             // lane l takes slot l: count, tiles, and exclusive prefixes
             const int c1 = lane < S ? L.cnt[lane] : 0;
-            const int n1 = (c1 + kTileTokens - 1) / kTileTokens;
+            const int n1 = (c1 + cap - 1) / cap;
             const int ic = wave_incl_scan(c1), in = wave_incl_scan(n1);
             const int pc = ic - c1, pn = in - n1;
             if (lane < S && b >= pn && b < pn + n1) {
@@ -789,7 +790,7 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, const Me
             for (int k = 0; k < 4; ++k) {
                 const int sl = 4 * lane + k;
                 c4[k] = sl < S ? L.cnt[sl] : 0;
-                n4[k] = (c4[k] + kTileTokens - 1) / kTileTokens;
+                n4[k] = (c4[k] + cap - 1) / cap;
                 sc += c4[k];
                 sn += n4[k];
             }
@@ -857,17 +858,17 @@ __device__ bool plan_tile(const int (&v)[kPlanPerThread], int T, int S, const Me
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         if (c < ncu && v[c] == sl) {
-            const int r = pre[c] - j * kTileTokens +
+            const int r = pre[c] - j * cap +
                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk[c] >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[c], 0u));
-            if (r >= 0 && r < kTileTokens)
+            if (r >= 0 && r < cap)
                 L.list[r] = c * 256 + tid;
         }
     }
     __syncthreads();
     tile.slot = sl;
-    tile.start = L.start + j * kTileTokens;
-    tile.len = min(kTileTokens, L.count - j * kTileTokens);
+    tile.start = L.start + j * cap;
+    tile.len = min(cap, L.count - j * cap);
     tile.rank = meta_rank(mr, sl);
     tile.scale = meta_scale(mr, sl);
     tokv = lane < tile.len ? L.list[lane] : 0;
@@ -997,7 +998,7 @@ __global__ __launch_bounds__(256) void shrink_bf16_kernel(ShrinkArgs a, SlotMeta
         plan_load_idx(a.idx, a.T, v);
         if constexpr (WARM)
             warm_split(a, m, split, bt, wv);
-        const bool has_tile = plan_tile(v, a.T, a.S, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
+        const bool has_tile = plan_tile(v, a.T, a.S, a.tile_cap, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv);
         if constexpr (WARM)
             keep_warm(wv);
         if (!has_tile)

@@ -105,6 +105,7 @@ struct lora_ctx {
     // plan state; an inline plan is computed by every shrink launch itself
     bool plan_valid = false, plan_prepared = false;
     int plan_mode = kPlanTiles;  // PlanMode of the next bf16 launch on this plan
+    int plan_tile_cap = kTileTokens;  // tokens per tile of the current plan
     uint64_t slot_epoch = 0, shrink_epoch = 0;   // loads + clears, and their count at the last shrink
     const int32_t *plan_idx = nullptr;
     int32_t plan_T = 0;
@@ -287,7 +288,7 @@ hipError_t dalloc(lora_ctx *c, T **p, size_t bytes)
 // the chip when the batch is small, none when it is large.
 void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 {
-    const int tiles = max_tiles_for(T, c->S);
+    const int tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
     int want = ceil_div(1024, std::max(tiles, 1));
     int cap = std::min(c->max_splits, std::max(1, d_in / 256));
     cap = std::min(cap, splits_cap(nb_template(c->R_pad)));
@@ -339,6 +340,7 @@ int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
 {
     c->plan_hinted = false;
     c->plan_mode = c->dtype == LORA_BF16 && T <= kInlinePlanTokens ? kPlanInline : kPlanTiles;
+    c->plan_tile_cap = c->plan_mode == kPlanInline ? inline_tile_tokens(c->R_pad) : kTileTokens;
     if (T > 0 && c->plan_mode == kPlanTiles) {
         int rc = before_launch(c, s, false);
         if (rc)
@@ -391,7 +393,8 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
     a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
-    a.grid_tiles = max_tiles_for(T, c->S);
+    a.grid_tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
+    a.tile_cap = c->plan_tile_cap;
     a.mixed = T > 1024;
     // A small batch with a multiple of 8 K-splits runs every tile of one split
     // on one XCD: its workgroups warm that split's x block (all tokens) and,
@@ -439,7 +442,7 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
-    a.grid_tiles = max_tiles_for(T, c->S);
+    a.grid_tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
     // large batches: one contiguous run of items per XCD.  With long slot
     // segments (prefill) the run is tile-major, every column chunk of a tile on
     // one XCD: the tile's h comes from HBM once and consecutive tiles of a slot
@@ -634,7 +637,9 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         if (v >= 1 && v <= kMaxSplits)
             c->max_splits = v;
     }
-    c->max_tiles = max_tiles_for(max_tokens, max_loras);
+    c->max_tiles = std::max(max_tiles_for(max_tokens, max_loras),
+                            max_tiles_for(std::min(max_tokens, (int)kInlinePlanTokens), max_loras,
+                                          inline_tile_tokens(c->R_pad)));
     // A^T and B of every module of a load side by side, within 64 MB (at least
     // one module)
     int64_t sum_io = 0, max_io = 0;
