@@ -142,6 +142,7 @@ struct ExpandArgs {
     const void *bias[kMaxGroup];        // module base: [S][d_out], ctx dtype
     const float *dora[kMaxGroup];       // module base: [S][d_out]
     int32_t terms;                      // some slot of the launch has output terms
+    int32_t tile_cap;                   // tokens per tile of the plan (at most kTileTokens)
 };
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,

@@ -1222,7 +1222,7 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
 // The expand of one tile for the 256 columns of chunk `chunk` of member m.
 // Requires 0 < tile.rank and an adapter that targets the member.  Every global
 // load (h partials, B, y) is issued before any arithmetic.
-template <int NB, bool TERMS>
+template <int NB, bool TERMS, int SUB>
 __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chunk, const Tile &tile,
                                             int tokv, int flags, uint16_t *hs_hi, uint16_t *hs_lo)
 {
@@ -1236,10 +1236,10 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
     uint16_t *ybase = (uint16_t *)a.y[m];
 
     // tokens of this lane in each subtile
-    int tok[4];
-    bool tok_ok[4];
+    int tok[SUB];
+    bool tok_ok[SUB];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < SUB; ++st) {
         const int t = st * 16 + row;
         tok_ok[st] = cols_ok && t < tile.len;
         const int tv = __shfl(tokv, t, 64);
@@ -1250,8 +1250,8 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
     uint4 bop[NB][4];
     load_b_ops<NB>(bop, (const uint16_t *)a.Bi[m] + (int64_t)tile.slot * a.slot_stride_B[m], d_out,
                    cb, nb, cols_ok);
-    uint4 yv[4][2];
-    load_y<4>(yv, ybase, d_out, cb, tok, tok_ok);
+    uint4 yv[SUB][2];
+    load_y<SUB>(yv, ybase, d_out, cb, tok, tok_ok);
     // output terms of the slot for this lane's 16 columns (clamped like y)
     OutTerms ot;
     ot.fl = flags;
@@ -1288,11 +1288,12 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
     }
     __syncthreads();
     if (cols_ok)
-        expand_store<NB, 4, HS, TERMS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase,
+        expand_store<NB, SUB, HS, TERMS>(hs_hi, hs_lo, bop, yv, tok, tok_ok, nsub, nb, tile.scale, ybase,
                                        d_out, cb, ot);
 }
 
-constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
+// LDS rows of h for SUB subtiles of 16 tokens
+constexpr int expand_hs_elems(int NB, int SUB) { return SUB * 16 * (NB * 16 + 8); }
 
 // Tiles as the shrink published them, with rank and scale of the slot as that
 // shrink saw them.  Member m has its own number of 256-column chunks,
@@ -1306,7 +1307,7 @@ constexpr int expand_hs_elems(int NB) { return kTileTokens * (NB * 16 + 8); }
 // slot segments (a.tile_major), tile * chunks + chunk: then all column chunks
 // of a tile run on one XCD, so the tile's h is fetched from HBM once, and
 // consecutive tiles (mostly of one slot) read that slot's B from the same L2.
-template <int NB, bool TERMS>
+template <int NB, bool TERMS, int SUB>
 __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta meta)
 {
     const int n_items = a.grid_tiles * a.col_start[a.n];
@@ -1330,9 +1331,9 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
     const int flags = meta_flags(mr, tile.slot);
     if (tile.rank == 0 || !meta_targets(mr, m, tile.slot))
         return;
-    __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB)];
-    __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB)];
-    expand_tile<NB, TERMS>(a, m, chunk, tile, tokv, flags, hs_hi, hs_lo);
+    __shared__ __attribute__((aligned(16))) uint16_t hs_hi[expand_hs_elems(NB, SUB)];
+    __shared__ __attribute__((aligned(16))) uint16_t hs_lo[expand_hs_elems(NB, SUB)];
+    expand_tile<NB, TERMS, SUB>(a, m, chunk, tile, tokv, flags, hs_hi, hs_lo);
 }
 
 // ----------------------------------------------------------------------------
@@ -1503,6 +1504,39 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
     return hipGetLastError();
 }
 
+// SUB: 16-token subtiles per tile, from the plan's tile size (a tile never
+// holds more than 16 SUB tokens).  Tiles of 32 tokens come only with rank 16
+// (one rank block), tiles of 48 only above it.
+template <bool TERMS>
+static void launch_expand_bf16(const ExpandArgs &a, const SlotMeta &m, dim3 grid, hipStream_t st,
+                               const LaunchTiming &t)
+{
+    const int nbmax = a.R_pad / 16;
+    const int sub = (a.tile_cap + 15) / 16;
+    const dim3 block(256);
+    if (nbmax <= 1) {
+        if (sub <= 2)
+            launch(expand_bf16_kernel<1, TERMS, 2>, grid, block, 0, st, t, a, m);
+        else
+            launch(expand_bf16_kernel<1, TERMS, 4>, grid, block, 0, st, t, a, m);
+    } else if (nbmax <= 2) {
+        if (sub <= 3)
+            launch(expand_bf16_kernel<2, TERMS, 3>, grid, block, 0, st, t, a, m);
+        else
+            launch(expand_bf16_kernel<2, TERMS, 4>, grid, block, 0, st, t, a, m);
+    } else if (nbmax <= 4) {
+        if (sub <= 3)
+            launch(expand_bf16_kernel<4, TERMS, 3>, grid, block, 0, st, t, a, m);
+        else
+            launch(expand_bf16_kernel<4, TERMS, 4>, grid, block, 0, st, t, a, m);
+    } else {
+        if (sub <= 3)
+            launch(expand_bf16_kernel<8, TERMS, 3>, grid, block, 0, st, t, a, m);
+        else
+            launch(expand_bf16_kernel<8, TERMS, 4>, grid, block, 0, st, t, a, m);
+    }
+}
+
 hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t)
 {
@@ -1511,25 +1545,11 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
         launch(expand_f32_kernel, grid, block, 0, st, t, a, m);
     } else {
         const dim3 g = xcd_grid((int64_t)a.grid_tiles * a.col_start[a.n], a.xcd_group);
-        const int nbmax = a.R_pad / 16;
         // the output-term epilogue only in launches where some slot has terms
-        if (a.terms) {
-            if (nbmax <= 1)
-                launch(expand_bf16_kernel<1, true>, g, block, 0, st, t, a, m);
-            else if (nbmax <= 2)
-                launch(expand_bf16_kernel<2, true>, g, block, 0, st, t, a, m);
-            else if (nbmax <= 4)
-                launch(expand_bf16_kernel<4, true>, g, block, 0, st, t, a, m);
-            else
-                launch(expand_bf16_kernel<8, true>, g, block, 0, st, t, a, m);
-        } else if (nbmax <= 1)
-            launch(expand_bf16_kernel<1, false>, g, block, 0, st, t, a, m);
-        else if (nbmax <= 2)
-            launch(expand_bf16_kernel<2, false>, g, block, 0, st, t, a, m);
-        else if (nbmax <= 4)
-            launch(expand_bf16_kernel<4, false>, g, block, 0, st, t, a, m);
+        if (a.terms)
+            launch_expand_bf16<true>(a, m, g, st, t);
         else
-            launch(expand_bf16_kernel<8, false>, g, block, 0, st, t, a, m);
+            launch_expand_bf16<false>(a, m, g, st, t);
     }
     return hipGetLastError();
 }

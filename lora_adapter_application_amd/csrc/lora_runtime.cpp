@@ -452,6 +452,7 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     const int64_t items = (int64_t)a.grid_tiles * a.col_start[n];
     const bool large = T > kInlinePlanTokens;
     a.tile_major = large && T >= 128 * c->S;
+    a.tile_cap = c->plan_tile_cap;
     a.xcd_group = large ? (int)((items + 7) / 8) : 1;
     a.terms = 0;
     for (int k = 0; k < c->S; ++k)
