@@ -177,7 +177,8 @@ int lora_sync_loads(lora_ctx *ctx);
  * permutation, per-slot segments and tiles of up to 64 tokens.  Tokens with
  * idx < 0 are not listed; idx >= max_loras are not listed and set
  * LORA_FLAG_SLOT_INDEX_TOO_LARGE.  For bf16 batches of at most 1024 tokens the
- * grouping runs inside each lora_shrink launch instead of a launch of its own.
+ * grouping runs inside each lora_shrink launch instead of a launch of its own,
+ * with tiles of up to 32 tokens (max_rank up to 16) or 48 (above).
  * The plan stays valid for lora_shrink,
  * lora_expand and lora_apply calls with the same (token_slot_idx, n_tokens)
  * until the next lora_plan_prepare; the caller must not change the contents of
