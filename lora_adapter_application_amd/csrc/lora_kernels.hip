@@ -1,8 +1,9 @@
 // lora_kernels.hip -- gfx950 kernels of the multi-adapter LoRA update
 //
 //   plan     stable counting sort of the per-token slot index into runs of one
-//            slot, cut into tiles of up to 64 tokens; each tile record lists its
-//            token indices (device only, no host sync)
+//            slot, cut into tiles of up to 64 tokens (32 or 48 when the shrink
+//            forms the plan inline); each tile record lists its token indices
+//            (device only, no host sync)
 //   shrink   h[p, :] = x[tok(p), :] . A_k^T over a K range (fp32 partials)
 //   expand   y[t, :] = round(y[t, :] + s_k * h[p, :] . B_k)
 //
@@ -11,12 +12,13 @@
 // section 3.2; the slot count and padded rank are max_loras / max_lora_rank of
 // the parameter table in "Multi-LoRA adapter cache in production".
 //
-// bf16 data runs on the matrix cores: v_mfma_f32_16x16x32_bf16 for shrink
-// (K = d_in) and v_mfma_f32_16x16x16_bf16 for expand (K = rank), with the fp32
-// intermediate split into a bf16 high and low part so the expand keeps ~16
-// bits of h; results are rounded to bf16 by v_cvt_pk_bf16_f32 (round to
-// nearest even).  fp32 data runs on plain VALU loops.  One shrink or expand
-// launch covers a group of up to kMaxGroup modules (blockIdx.z).
+// bf16 data runs on the matrix cores: v_mfma_f32_16x16x32_bf16 for the shrink
+// (K = d_in) and for the expand (K = a block of 16 ranks, with the fp32
+// intermediate split into a bf16 high and low part stacked along K, so the
+// expand keeps ~16 bits of h); results are rounded to bf16 by
+// v_cvt_pk_bf16_f32 (round to nearest even).  fp32 data runs on plain VALU
+// loops.  One shrink or expand launch covers a group of up to kMaxGroup
+// modules.
 //
 // Operand layout of a 16x16xK MFMA on a 64-wide wave, as used below: lane l
 // supplies row (l & 15) of A and column (l & 15) of B, each with the K slice of
@@ -301,7 +303,7 @@ hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffe
 // shrink, bf16 on MFMA
 //
 // One workgroup (4 waves) = one tile (<= 64 tokens of one slot) x one K split x
-// one group member (blockIdx.z).  Output: the member's h partial of the split
+// one group member.  Output: the member's h partial of the split
 // as [rank][token] blocks, lane l holding ranks 4g..4g+3 of token (l & 15),
 // stored as one 16-byte write.
 
@@ -974,6 +976,7 @@ __device__ __forceinline__ void keep_warm(const uint32_t (&wv)[kWarmLoads])
 // Tiles of 17..64 tokens take the segment path, shorter ones the gather path:
 // single-buffered when MIXED (batches above 1024 tokens), else double-buffered
 // when the rank allows.  PLAN: how the workgroup finds its tile (PlanMode).
+// WARM: the split's block is warmed in L2 meanwhile (warm_split).
 // Work item w = (tile * grid_splits + split) * n + member, in groups of n: the
 // members of one (tile, K split) run back to back on one XCD, so when they
 // share x (q, k and v of a layer) x comes from HBM once and from L2 after.
