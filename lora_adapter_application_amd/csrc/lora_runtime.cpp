@@ -164,7 +164,7 @@ StreamState *stream_state(lora_ctx *c, hipStream_t s)
     return &c->streams.back();
 }
 
-// Make stream s wait for all loads issued so far, and mark it as in use.
+// Whether s is being captured into a graph.
 bool stream_capturing(hipStream_t s)
 {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -175,7 +175,8 @@ bool stream_capturing(hipStream_t s)
     return cs != hipStreamCaptureStatusNone;
 }
 
-// A stream that is being captured into a graph cannot wait for the load event,
+// Make stream s wait for all loads issued so far, and mark it as in use.  A
+// stream that is being captured into a graph cannot wait for the load event,
 // which was recorded outside the capture: loads must be complete (on the host,
 // lora_sync_loads) before a capture starts.
 // reads_slots: the launch reads slot data (shrink, expand); plan kernels read
