@@ -123,8 +123,12 @@ int lora_slots_destroy(lora_ctx *ctx);
  *   r        adapter rank, 1..max_rank (r > max_rank -> LORA_ERR_RANK_EXCEEDS_MAX)
  *   lora_alpha, use_rslora   give s = lora_alpha / r or lora_alpha / sqrt(r),
  *            computed in double and rounded to fp32 once
- * Asynchronous: copies run on the ctx's side stream.  Before overwriting the
- * slot the side stream waits for every kernel already enqueued by this ctx, so
+ * Asynchronous, on the ctx's side stream: a kernel reads the weights in place
+ * where the device can (16-byte aligned pinned host memory mapped at its host
+ * address, over the link; memory of the ctx's device; managed memory) and
+ * writes the slot; other weights are first copied to a stage buffer.  Before
+ * overwriting the slot the side stream waits for every kernel already enqueued
+ * by this ctx, so
  * an adapter in use by an in-flight batch is never overwritten ("an adapter in
  * use must not be evicted", same page, data-plane section).  Later
  * lora_plan_prepare / lora_shrink / lora_expand / lora_apply calls make their

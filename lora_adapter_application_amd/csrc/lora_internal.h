@@ -151,13 +151,14 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
                          const LaunchTiming &t);
 
 // Slot maintenance, on the side stream: one launch finishes the loads of up to
-// kFinalizeBatch modules (B repack from its staged copy, zero padding rows).
+// kFinalizeBatch modules (A^T copy and B repack, read in place or from a staged
+// copy, and zero padding rows).
 constexpr int kFinalizeBatch = 16;
 struct FinalizeItem {
     void *A_slot;            // the slot's A^T block of the module
     void *Bi_slot;           // the slot's repacked B block
-    const void *A_stage;     // r x d_in, row-major, staged on the device
-    const void *B_stage;     // r x d_out, row-major, staged on the device
+    const void *A_src;       // r x d_in, row-major: the caller's weights or their staged copy
+    const void *B_src;       // r x d_out, row-major: the same
     int32_t d_in, d_out;
 };
 struct FinalizeBatch {

@@ -265,8 +265,8 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
                 t.start = start + j * kTileTokens;
                 t.len = min(kTileTokens, tot - j * kTileTokens);
                 t.rank = 0;
-            t.scale = 0.f;
-            t.pad[0] = t.pad[1] = t.pad[2] = 0;
+                t.scale = 0.f;
+                t.pad[0] = t.pad[1] = t.pad[2] = 0;
                 pb.tiles[tstart + j] = t;
             }
         }
@@ -1560,30 +1560,58 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
 // ----------------------------------------------------------------------------
 // slot maintenance
 
-// Copy A^T (r x d_in) from the stage into the slot, repack B (r x d_out,
-// row-major, staged) into groups of 8 ranks, Bi[j/8][n][j%8], and zero ranks
-// r..R_pad-1 of both; module blockIdx.y of the batch.  Rows are 16-byte
-// multiples (d_in, d_out multiples of 8), so A^T moves in 16-byte pieces.
+// Copy A^T (r x d_in) into the slot, repack B (r x d_out, row-major) into
+// groups of 8 ranks, Bi[j/8][n][j%8], and zero ranks r..R_pad-1 of both;
+// module blockIdx.y of the batch.  The sources are the caller's weights when
+// the device can read them in place (pinned host memory over the link, or
+// device memory), else their staged copies.  Every read is a 16-byte piece of
+// a source row, consecutive lanes taking consecutive pieces, so a wave reads
+// 1 KB of one row per instruction: link reads need such runs.  Rows are
+// 16-byte multiples (d_in, d_out multiples of 8).
 template <typename E>
 __global__ void slot_finalize_kernel(FinalizeBatch fb)
 {
+    constexpr int C = 16 / (int)sizeof(E);          // columns per 16-byte piece
     const FinalizeItem &it = fb.it[blockIdx.y];
     E *A_slot = (E *)it.A_slot, *Bi_slot = (E *)it.Bi_slot;
-    const E *B_stage = (const E *)it.B_stage;
     const int d_in = it.d_in, d_out = it.d_out, r = fb.r, R_pad = fb.R_pad;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nA16 = (int64_t)r * d_in * (int64_t)sizeof(E) / 16;
     for (int64_t o = first; o < nA16; o += stride)
-        ((uint4 *)A_slot)[o] = ((const uint4 *)it.A_stage)[o];
-    const int64_t per_group = (int64_t)d_out * 8;
-    const int64_t nB = (int64_t)R_pad * d_out;
+        ((uint4 *)A_slot)[o] = ((const uint4 *)it.A_src)[o];
+    // B: item o = (rank group G, column piece q); it reads piece q of the group's
+    // rows below r and writes Bi[G][qC .. qC+C-1][0..7], C * 16 contiguous bytes
+    const int pieces = d_out / C;
+    const int64_t nB = (int64_t)(R_pad / 8) * pieces;
+    const E *B_src = (const E *)it.B_src;
     for (int64_t o = first; o < nB; o += stride) {
-        const int G = (int)(o / per_group);
-        const int64_t rem = o - (int64_t)G * per_group;
-        const int n = (int)(rem >> 3), w = (int)(rem & 7);
-        const int j = G * 8 + w;
-        Bi_slot[o] = j < r ? B_stage[(int64_t)j * d_out + n] : E(0);
+        const int G = (int)(o / pieces), q = (int)(o - (int64_t)G * pieces);
+        union Piece {
+            uint4 u;
+            E e[C];
+        } row[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int j = G * 8 + w;
+            row[w].u = j < r ? *(const uint4 *)(B_src + (int64_t)j * d_out + (int64_t)q * C)
+                             : make_uint4(0, 0, 0, 0);
+        }
+        E *out = Bi_slot + ((int64_t)G * d_out + (int64_t)q * C) * 8;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            union Piece lo, hi;         // ranks 0..7 of column qC + c (hi: fp32 ranks 4..7)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                if (w < C)
+                    lo.e[w] = row[w].e[c];
+                else
+                    hi.e[w - C] = row[w].e[c];
+            }
+            *(uint4 *)(out + c * 8) = lo.u;
+            if (C < 8)
+                *(uint4 *)(out + c * 8 + C) = hi.u;
+        }
     }
     const int64_t nZ16 = (int64_t)(R_pad - r) * d_in * (int64_t)sizeof(E) / 16;
     uint4 *A_pad = (uint4 *)(A_slot + (int64_t)r * d_in);
@@ -1595,14 +1623,17 @@ hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t s
 {
     if (b.n <= 0)
         return hipSuccess;
+    // about 256 workgroups in all: reads over the link run fastest with about one
+    // workgroup per CU (more of them measured up to 20% slower)
     int64_t work = 0;
     for (int i = 0; i < b.n; ++i) {
-        const int64_t w = (int64_t)b.R_pad * (b.it[i].d_out > b.it[i].d_in ? b.it[i].d_out : b.it[i].d_in);
+        const int64_t w = (int64_t)b.R_pad * (b.it[i].d_out > b.it[i].d_in ? b.it[i].d_out : b.it[i].d_in) / 8;
         work = w > work ? w : work;
     }
     int blocks = (int)((work + 255) / 256);
-    if (blocks > 1024)
-        blocks = 1024;
+    const int cap = (256 + b.n - 1) / b.n;
+    if (blocks > cap)
+        blocks = cap;
     if (bf16)
         hipLaunchKernelGGL(slot_finalize_kernel<uint16_t>, dim3(blocks, b.n), dim3(256), 0, st, b);
     else

@@ -43,6 +43,7 @@ struct StreamState {
     hipStream_t stream;
     uint64_t waited_gen;    // load generation this stream has waited for
     bool used_since_load;   // launched on since the last load
+    bool since_fence;       // launched on since the side stream last waited for it
     hipEvent_t tail;        // recorded at load time to fence the stream's tail
 };
 
@@ -157,7 +158,7 @@ StreamState *stream_state(lora_ctx *c, hipStream_t s)
     for (auto &st : c->streams)
         if (st.stream == s)
             return &st;
-    StreamState st{s, 0, false, nullptr};
+    StreamState st{s, 0, false, false, nullptr};
     if (hipEventCreateWithFlags(&st.tail, hipEventDisableTiming) != hipSuccess)
         return nullptr;
     c->streams.push_back(st);
@@ -198,6 +199,7 @@ int before_launch(lora_ctx *c, hipStream_t s, bool reads_slots = true)
     // under capture, where no event is recorded
     if (reads_slots && (!c->plan_hinted || stream_capturing(s)))
         st->used_since_load = true;
+    st->since_fence = true;
     return LORA_OK;
 }
 
@@ -226,11 +228,16 @@ int fence_compute_streams(lora_ctx *c)
         HIP_TRY(c, hipEventRecord(st.tail, st.stream));
         HIP_TRY(c, hipStreamWaitEvent(c->side, st.tail, 0));
         st.used_since_load = false;
+        st.since_fence = false;
     }
     return LORA_OK;
 }
 
-int check_source(const void *p)
+// A load source must be pinned host, device or managed memory.  *in_place:
+// the finalize kernel on `device` may read it at its own address (memory of
+// that device, managed memory, or pinned host memory mapped at its host
+// address) and it is 16-byte aligned; otherwise it is staged by a copy.
+int check_source(const void *p, int device, bool *in_place = nullptr)
 {
     hipPointerAttribute_t attr;
     std::memset(&attr, 0, sizeof attr);
@@ -239,10 +246,16 @@ int check_source(const void *p)
         (void)hipGetLastError();
         return LORA_ERR_HOST_NOT_PINNED;
     }
-    if (attr.type == hipMemoryTypeHost || attr.type == hipMemoryTypeDevice ||
-        attr.type == hipMemoryTypeManaged)
-        return LORA_OK;
-    return LORA_ERR_HOST_NOT_PINNED;
+    if (attr.type != hipMemoryTypeHost && attr.type != hipMemoryTypeDevice &&
+        attr.type != hipMemoryTypeManaged)
+        return LORA_ERR_HOST_NOT_PINNED;
+    if (in_place) {
+        const bool mapped = attr.type == hipMemoryTypeManaged ||
+                            (attr.type == hipMemoryTypeDevice && attr.device == device) ||
+                            (attr.type == hipMemoryTypeHost && attr.devicePointer == p);
+        *in_place = mapped && ((uintptr_t)p & 15) == 0;
+    }
+    return LORA_OK;
 }
 
 void free_all(lora_ctx *c)
@@ -719,25 +732,48 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
     if (!std::isfinite(s))
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "scale is not finite (lora_alpha %g)",
                     lora_alpha);
+    std::vector<uint8_t> in_place;
     {
         DeviceGuard guard(ctx->device);
+        in_place.assign(ctx->n_modules, 0);
         for (int m = 0; m < ctx->n_modules; ++m) {
             if ((A_t[m] == nullptr) != (B[m] == nullptr))
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
                             "module %d: A_t and B must both be given or both be NULL", m);
-            if (A_t[m] && (check_source(A_t[m]) || check_source(B[m])))
+            bool ia = false, ib = false;
+            if (A_t[m] && (check_source(A_t[m], ctx->device, &ia) || check_source(B[m], ctx->device, &ib)))
                 return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
                             "module %d: weights must be pinned host or device memory", m);
+            in_place[m] = ia && ib;
             if (A_t[m] && bias && !bias[m])
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: bias entry is NULL", m);
             if (A_t[m] && dora_scale && !dora_scale[m])
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: dora_scale entry is NULL", m);
-            if (A_t[m] && ((bias && check_source(bias[m])) || (dora_scale && check_source(dora_scale[m]))))
+            if (A_t[m] && ((bias && check_source(bias[m], ctx->device)) ||
+                           (dora_scale && check_source(dora_scale[m], ctx->device))))
                 return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
                             "module %d: bias / dora_scale must be pinned host or device memory", m);
         }
     }
     DeviceGuard guard(ctx->device);
+    // A load that may run beside kernels it does not wait for (batches of
+    // declared plans in flight on a stream this ctx launched on) stages its
+    // weights with the copy engine: the in-place finalize streams over the link
+    // on the CUs and would take them from those kernels (measured: a pipelined
+    // churn step 1.32 -> 1.61 ms).  The side stream waits in full for streams
+    // fenced below or at an earlier load with no launch since.
+    bool beside_compute = false;
+    for (auto &st : ctx->streams) {
+        if (st.used_since_load || !st.since_fence)
+            continue;
+        const hipError_t q = hipStreamQuery(st.stream);
+        if (q != hipSuccess)
+            (void)hipGetLastError();   // not-ready is an answer, not an error to keep
+        if (q == hipErrorNotReady)
+            beside_compute = true;
+    }
+    if (beside_compute)
+        std::fill(in_place.begin(), in_place.end(), 0);
     int rc = fence_compute_streams(ctx);
     if (rc)
         return rc;
@@ -747,12 +783,13 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
     }
     int64_t bytes = 0;
     const bool bf16 = ctx->dtype == LORA_BF16;
-    // Every targeted module's A^T and B go to the stage, in module order, A^T
-    // then B; ranges that follow each other both in the source and in the stage
-    // are moved by one copy (an adapter read into one buffer takes one transfer,
-    // where the link is fastest).  One finalize launch per batch of modules (or
-    // when the stage is full) moves A^T into the slot and repacks B, in stream
-    // order after its copies.
+    // One finalize launch per batch of modules moves A^T into the slot and
+    // repacks B.  It reads weights the device can reach in place directly (over
+    // the link for pinned host memory, at about the rate of a copy engine, and
+    // with no copy-to-kernel hand-over per load).  Other weights go to the stage
+    // first, in module order, A^T then B; ranges that follow each other both in
+    // the source and in the stage are moved by one copy, and the finalize runs
+    // in stream order after its copies.
     FinalizeBatch fb;
     std::memset(&fb, 0, sizeof fb);
     fb.r = r;
@@ -784,22 +821,32 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
             continue;
         const auto sh = ctx->shapes[m];
         const int64_t a_elems = (int64_t)r * sh.d_in, b_elems = (int64_t)r * sh.d_out;
+        char *Aslot = (char *)ctx->A[m] + (size_t)slot * ctx->strideA[m] * ctx->elem;
+        char *Bslot = (char *)ctx->Bi[m] + (size_t)slot * ctx->strideB[m] * ctx->elem;
+        const size_t abytes = (size_t)a_elems * ctx->elem, bbytes = (size_t)b_elems * ctx->elem;
+        bytes += (int64_t)abytes + (int64_t)bbytes;
+        if (in_place[m]) {
+            if (fb.n == kFinalizeBatch) {
+                HIP_TRY(ctx, flush_run());
+                HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
+                fb.n = 0;
+                stage_used = 0;
+            }
+            fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, A_t[m], B[m], sh.d_in, sh.d_out};
+            continue;
+        }
         if (fb.n == kFinalizeBatch || stage_used + a_elems + b_elems > ctx->stage_elems) {
             HIP_TRY(ctx, flush_run());
             HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
             fb.n = 0;
             stage_used = 0;
         }
-        char *Aslot = (char *)ctx->A[m] + (size_t)slot * ctx->strideA[m] * ctx->elem;
-        char *Bslot = (char *)ctx->Bi[m] + (size_t)slot * ctx->strideB[m] * ctx->elem;
         char *Ast = (char *)ctx->stage + (size_t)stage_used * ctx->elem;
-        char *Bst = Ast + (size_t)a_elems * ctx->elem;
-        const size_t abytes = (size_t)a_elems * ctx->elem, bbytes = (size_t)b_elems * ctx->elem;
+        char *Bst = Ast + abytes;
         HIP_TRY(ctx, add_range(A_t[m], Ast, abytes));
         HIP_TRY(ctx, add_range(B[m], Bst, bbytes));
         fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, Ast, Bst, sh.d_in, sh.d_out};
         stage_used += a_elems + b_elems;
-        bytes += (int64_t)abytes + (int64_t)bbytes;
     }
     HIP_TRY(ctx, flush_run());
     HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
