@@ -26,6 +26,10 @@ roofline   the kernel with the largest share of the step: its algorithmic bytes 
 cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
            same workload (rank 0, one GPU only): all threads, and one thread on
            a smaller sample; nproc and the CPU model
+
+--workload churn [--prefetch] times adapter uploads with the applies instead
+(see churn and churn_prefetch below); its "h2d" carries the upload rate beside
+copy_GBps, back-to-back pinned copies of one adapter's size on the same link.
 """
 from __future__ import annotations
 
@@ -126,6 +130,26 @@ def measured_copy_gbps(reps=10):
     e1.synchronize()
     gbps = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def measured_h2d_gbps(nbytes=7897088, bufs=16, reps=32):
+    """Rate of back-to-back pinned host to device copies of one adapter's size
+    (torch, current stream): the link's practical ceiling for uploads."""
+    import torch
+    src = [torch.empty(nbytes, dtype=torch.uint8).pin_memory() for _ in range(bufs)]
+    dst = torch.empty(2 * nbytes, dtype=torch.uint8, device="cuda")
+    for i in range(4):
+        dst[(i & 1) * nbytes:((i & 1) + 1) * nbytes].copy_(src[i % bufs], non_blocking=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst[(i & 1) * nbytes:((i & 1) + 1) * nbytes].copy_(src[i % bufs], non_blocking=True)
+    e1.record()
+    e1.synchronize()
+    gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
     torch.cuda.empty_cache()
     return gbps
 
@@ -447,6 +471,8 @@ def churn(args):
         del x, y
     st = lru.stats
     bytes_loaded = slots.stats()["bytes_loaded"]
+    link = measured_h2d_gbps()
+    h2d_rate = bytes_loaded / t_load / 1e9 if t_load else None
     out = {
         "metric": "multi-LoRA tokens/s",
         "value": round(tokens / (t_load + t_apply), 1),
@@ -464,7 +490,9 @@ def churn(args):
                          "apply_only_tokens_per_s": round(tokens_warm / t_apply_warm, 1),
                          "ms_per_step": round((t_load_warm + t_apply_warm) / (args.churn_steps - 1) * 1e3, 4)},
         "h2d": {"bytes": bytes_loaded, "seconds": round(t_load, 6),
-                "GBps": round(bytes_loaded / t_load / 1e9, 2) if t_load else None,
+                "GBps": round(h2d_rate, 2) if h2d_rate else None,
+                "copy_GBps": round(link, 2),
+                "frac_of_copy": round(h2d_rate / link, 3) if h2d_rate else None,
                 "adapter_h2d_seconds_mean": round(float(np.mean(per_miss)), 7) if per_miss else None,
                 "bytes_per_adapter": bytes_loaded // max(st.misses, 1)},
         "lru": {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
@@ -534,6 +562,7 @@ def churn_prefetch(args):
     run(True)                                  # warm-up pass (untimed): allocator, code objects
     t_pre, bytes_loaded = run(True)
     t_ser, _ = run(False)
+    link = measured_h2d_gbps()
     tokens = sum(int(step[0].shape[0]) for step in steps)
     out = {
         "metric": "multi-LoRA tokens/s",
@@ -548,7 +577,8 @@ def churn_prefetch(args):
                    "per_step_cap": 128, "max_rank": 64, "pool_adapters": 200, "zipf": 0.9,
                    "cold_start": True, "parallelism": "none (1 GPU)"},
         "serial": {"value": round(tokens / t_ser, 1), "ms_per_step": round(t_ser / N * 1e3, 4)},
-        "h2d": {"bytes": bytes_loaded, "GBps_over_prefetch_run": round(bytes_loaded / t_pre / 1e9, 2)},
+        "h2d": {"bytes": bytes_loaded, "GBps_over_prefetch_run": round(bytes_loaded / t_pre / 1e9, 2),
+                "copy_GBps": round(link, 2)},
         "lru": {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
                 "reloads_after_eviction": st.reloads_after_eviction,
                 "thrash_ratio": round(st.thrash_ratio, 4)},
