@@ -133,6 +133,8 @@ int lora_slots_destroy(lora_ctx *ctx);
  * use must not be evicted", same page, data-plane section).  Later
  * lora_plan_prepare / lora_shrink / lora_expand / lora_apply calls make their
  * stream wait for the load.  Rows r..R-1 are zeroed, so padding changes nothing.
+ * A load while a stream this ctx has launched on is under graph capture fails
+ * with LORA_ERR_INVALID_ARGUMENT (its fences would join the capture).
  * The bytes moved are sum_m (d_in_m + d_out_m) * r * bytes_per_elem over the
  * targeted modules, the page's adapter size estimate.
  */

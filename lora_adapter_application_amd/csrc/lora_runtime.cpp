@@ -756,6 +756,12 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
         }
     }
     DeviceGuard guard(ctx->device);
+    // The fences below record events on the compute streams; on a stream under
+    // capture that would pull the load into the graph.
+    for (auto &st : ctx->streams)
+        if (stream_capturing(st.stream))
+            return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                        "slot load while a stream this ctx launched on is under graph capture");
     // A load that may run beside kernels it does not wait for (batches of
     // declared plans in flight on a stream this ctx launched on) stages its
     // weights with the copy engine: the in-place finalize streams over the link

@@ -139,3 +139,33 @@ def test_bound_step_matches_direct_calls():
     for mi in range(len(MODS)):
         assert torch.equal(yb[mi], yd[mi])
     S.close()
+
+
+def test_load_during_capture_is_rejected():
+    """A load while a stream the ctx launched on is being captured fails before it
+    enqueues anything (its fences would record into the capture); the capture and
+    later loads are unaffected."""
+    wl = _case(64, 9201)
+    S = make_slots(wl)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in MODS]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in MODS]
+    ad = wl.adapters[0]
+    keep = [to_pinned(ad.At[m.name], wl.dtype) for m in MODS] + \
+           [to_pinned(ad.B[m.name], wl.dtype) for m in MODS]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _steps(S, idx, xs, ys)
+        with pytest.raises(binding.LoraError, match="graph capture"):
+            S.load(0, keep[:3], keep[3:], ad.r, ad.lora_alpha, ad.use_rslora)
+    g.replay()
+    torch.cuda.synchronize()
+    for mi, m in enumerate(MODS):
+        check_close(from_dev(ys[mi], wl.dtype), run_oracle(wl, m.name), wl.dtype, f"replay {m.name}")
+    # after the capture, the same load goes through
+    S.load(0, keep[:3], keep[3:], ad.r, ad.lora_alpha, ad.use_rslora)
+    S.sync_loads()
+    assert S.stats()["loads"] == len([a for a in wl.adapters if a is not None]) + 1
+    S.close()
