@@ -22,7 +22,9 @@ roofline   the kernel with the largest share of the step: its algorithmic bytes 
            its kernel time, from start / stop events the library attaches to each of
            its dispatches (hipExtLaunchKernelGGL) during a second pass of the same K
            steps right after the timed one; also its fraction of a measured 1 GiB
-           device copy (copy_GBps, read plus write) beside the 8 TB/s spec
+           device copy (copy_GBps, read plus write) beside the 8 TB/s spec, and
+           (roofline.mfma) its algorithmic flops per second against the dense
+           bf16 MFMA peak; kernels.lora_* carry both for each kernel
 cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
            same workload (rank 0, one GPU only): all threads, and one thread on
            a smaller sample; nproc and the CPU model
@@ -352,8 +354,12 @@ def main():
                         for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
         group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes}
-        flops = [2 * (m.d_in + m.d_out) * int(sum(wl.adapters[k].r for k in wl.idx[act]))
-                 for m in mods]
+        rsum = int(sum(wl.adapters[k].r for k in wl.idx[act]))    # true ranks of the active tokens
+        flops = [2 * (m.d_in + m.d_out) * rsum for m in mods]
+        # algorithmic flops of each kind per step (true ranks; the expand's MFMAs
+        # also contract h's low half, which is not counted)
+        kind_flops = {"shrink": float(sum(2 * m.d_in * rsum for m in mods)),
+                      "expand": float(sum(2 * m.d_out * rsum for m in mods))}
 
         def avg_us(kind):
             return tot[kind] / n[kind] * 1e3 if n[kind] else None
@@ -367,10 +373,13 @@ def main():
         for kind in ("shrink", "expand"):
             if n[kind]:
                 step_bytes = float(sum(group_bytes[kind]))
+                tfs = kind_flops[kind] * K / (tot[kind] * 1e-3) / 1e12
                 kernels["lora_" + kind] = {
                     "avg_us": avg_us(kind), "per_step_us": tot[kind] / K * 1e3,
                     "alg_bytes_per_step": step_bytes,
-                    "GBps": float(step_bytes * K / (tot[kind] * 1e-3) / 1e9)}
+                    "GBps": float(step_bytes * K / (tot[kind] * 1e-3) / 1e9),
+                    "alg_flops_per_step": kind_flops[kind], "TFLOPs": round(tfs, 2),
+                    "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 5)}
         dom = max(("shrink", "expand"), key=lambda k: tot[k])
         dom_bytes = group_bytes[dom]
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
@@ -383,7 +392,10 @@ def main():
                     "alg_bytes_per_launch": float(np.mean(dom_bytes)),
                     "avg_launch_us": avg_us(dom),
                     "copy_GBps": round(copy_gbps, 1),
-                    "frac_of_copy": round(achieved / copy_gbps, 4)}
+                    "frac_of_copy": round(achieved / copy_gbps, 4),
+                    "mfma": {"achieved": kernels[kname]["TFLOPs"], "peak": BF16_MFMA_PEAK_TFS,
+                             "unit": "TFLOP/s", "frac": kernels[kname]["mfma_frac"],
+                             "flops": "algorithmic, true ranks"}}
         log("kernels:", json.dumps(kernels))
 
     cpu = None
