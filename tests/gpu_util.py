@@ -47,20 +47,41 @@ def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, np.float32).astype(np.float64)
 
 
-def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None) -> binding.Slots:
-    """Create a ctx for the workload's modules and load every slot's adapter."""
+def to_pinned_misaligned(arr: np.ndarray, dtype: str, keep: list) -> torch.Tensor:
+    """A pinned copy one element past a 16-byte boundary (a load stages it)."""
+    t = to_pinned(arr, dtype)
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype).pin_memory()
+    v = buf[1:1 + t.numel()]
+    v.copy_(t.reshape(-1))
+    keep.append(buf)
+    return v.view(t.shape)
+
+
+def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None,
+               source: str = "pinned") -> binding.Slots:
+    """Create a ctx for the workload's modules and load every slot's adapter.
+
+    source: where the adapter weights come from, "pinned" (read in place by the
+    load), "device" (read in place) or "staged" (pinned but misaligned, so the
+    load copies them to its stage first)."""
     S = binding.Slots(wl.max_loras, max_rank or wl.max_rank,
                       [(m.d_in, m.d_out) for m in wl.modules], wl.dtype,
                       max_tokens or max(wl.n_tokens, 1))
     pinned = [] if keep is None else keep
+    if source == "device":
+        weights = lambda arr: to_dev(arr, wl.dtype)
+    elif source == "staged":
+        weights = lambda arr: to_pinned_misaligned(arr, wl.dtype, pinned)
+    else:
+        weights = lambda arr: to_pinned(arr, wl.dtype)
     for k, ad in enumerate(wl.adapters):
         if ad is None:
             continue
         A_t, B, C, G = [], [], [], []
         for m in wl.modules:
             if m.name in ad.At:
-                a = to_pinned(ad.At[m.name], wl.dtype)
-                b = to_pinned(ad.B[m.name], wl.dtype)
+                a = weights(ad.At[m.name])
+                b = weights(ad.B[m.name])
                 pinned += [a, b]
                 A_t.append(a)
                 B.append(b)

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from gpu_util import (as_f64, check_close, from_dev, log, make_slots, rel_l2, run_gpu,
-                      run_oracle, to_dev, to_pinned)
+                      run_oracle, to_dev, to_pinned, to_pinned_misaligned)
 from lora_adapter_application_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
@@ -328,13 +328,9 @@ def test_load_sources_read_in_place_staged_and_from_device_agree(dtype):
     keep = []
 
     def pinned_off(arr):
-        t = to_pinned(arr, dtype)
-        buf = torch.empty(t.numel() + 8, dtype=t.dtype).pin_memory()
-        v = buf[1:1 + t.numel()]
-        v.copy_(t.reshape(-1))
-        keep.append(buf)
+        v = to_pinned_misaligned(arr, dtype, keep)
         assert v.data_ptr() % 16 != 0
-        return v.view(t.shape)
+        return v
 
     makers = [lambda a: to_pinned(a, dtype), pinned_off, lambda a: to_dev(a, dtype)]
     for slot, mk in enumerate(makers):

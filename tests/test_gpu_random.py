@@ -5,7 +5,8 @@ group or two, members sharing one x buffer or not), slot count, padded and
 per-slot ranks, target masks, empty slots, rsLoRA, output bias and DoRA
 factors, a base-only share, and a token count around the boundaries the
 kernels switch at (16 and 64 tokens per tile, 1024 tokens for the inline
-plan).  Every module's output must match the oracle, and tokens the update
+plan).  The adapter weights come from pinned memory, device memory or
+misaligned pinned views in turn, the three ways a load reads them.  Every module's output must match the oracle, and tokens the update
 does not apply to must stay bit-identical.
 """
 import numpy as np
@@ -61,12 +62,16 @@ def _draw(seed):
     return wl, groups, shared
 
 
+SOURCES = ["pinned", "device", "staged"]
+
+
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration_matches_oracle(seed):
     wl, groups, shared = _draw(31000 + seed)
+    source = SOURCES[seed % 3]
     log("case random", seed, "T", wl.n_tokens, "S", wl.max_loras, "R", wl.max_rank,
-        [(m.d_in, m.d_out) for m in wl.modules], "groups", groups, "shared", shared)
-    S = make_slots(wl)
+        [(m.d_in, m.d_out) for m in wl.modules], "groups", groups, "shared", shared, "weights", source)
+    S = make_slots(wl, source=source)
     idx = torch.from_numpy(wl.idx).cuda()
     names = [m.name for m in wl.modules]
     x0 = to_dev(wl.x[names[0]], wl.dtype)
