@@ -28,7 +28,8 @@
  *    lora_apply) share the ctx's plan and intermediate buffers, so they must be
  *    issued on one stream, or ordered by the caller.
  *  - Element type of x, y, A and B is the ctx dtype: bf16 (raw 16-bit
- *    patterns) or fp32.  Accumulation is always fp32; a bf16 y is rounded once,
+ *    patterns) or fp32.  Accumulation is fp32 (for fp32 data, the sums over
+ *    d_in run in fp64, so large scales keep ~1e-5 relative); a bf16 y is rounded once,
  *    to nearest even.
  *  - Graph capture: the launching calls may be captured into a HIP graph
  *    (hipStreamBeginCapture on a non-null stream) and the graph replayed.

@@ -17,7 +17,7 @@
 // intermediate split into a bf16 high and low part stacked along K, so the
 // expand keeps ~16 bits of h); results are rounded to bf16 by
 // v_cvt_pk_bf16_f32 (round to nearest even).  fp32 data runs on plain VALU
-// loops.  One shrink or expand launch covers a group of up to kMaxGroup
+// loops (the shrink's K sums in fp64).  One shrink or expand launch covers a group of up to kMaxGroup
 // modules.
 //
 // Operand layout of a 16x16xK MFMA on a 64-wide wave, as used below: lane l
@@ -1365,10 +1365,14 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
     if (tid < kTileTokens)
         toks[tid] = tid < tile.len ? tok_row[tid] : 0;
     const int npairs = tile.len * rank;   // <= 64 * 128 = 32 per thread
-    float acc[32];
+    // fp64 accumulation over the split's K range (products of two fp32 values
+    // are exact in fp64): with fp32 sums the rounding error of h, multiplied by
+    // a large scale (rsLoRA at high rank, s = alpha / sqrt(r) ~ 20), exceeds
+    // 1e-5 of y in the tails of a batch
+    double acc[32];
 #pragma unroll
     for (int q = 0; q < 32; ++q)
-        acc[q] = 0.f;
+        acc[q] = 0.0;
     __syncthreads();
     for (int kc = k0; kc < k1; kc += 32) {
         for (int e = tid; e < kTileTokens * 32; e += 256) {
@@ -1385,9 +1389,9 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
             const int e = tid + q * 256;
             if (e < npairs) {
                 const int t = e / rank, j = e % rank;
-                float sacc = acc[q];
+                double sacc = acc[q];
                 for (int kk = 0; kk < 32; ++kk)
-                    sacc += xs[t][kk] * as[j][kk];
+                    sacc = fma((double)xs[t][kk], (double)as[j][kk], sacc);
                 acc[q] = sacc;
             }
         }
@@ -1399,7 +1403,7 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(ShrinkArgs a, SlotMeta 
         const int e = tid + q * 256;
         if (e < npairs) {
             const int t = e / rank, j = e % rank;
-            hp[(int64_t)(tile.start + t) * a.R_pad + j] = acc[q];
+            hp[(int64_t)(tile.start + t) * a.R_pad + j] = (float)acc[q];
         }
     }
 }

@@ -190,6 +190,24 @@ def test_consecutive_batches_of_changing_size_on_one_ctx():
     S.close()
 
 
+def test_fp32_large_rslora_scales_keep_the_fp32_bound():
+    """rsLoRA at high rank with lora_alpha = 2r gives s = 2 sqrt(r), up to 22.6, which
+    multiplies the rounding error of h.  A batch of this shape (2047 tokens, K = 2048,
+    28 slots of ranks up to 128) once exceeded 1e-5 (1 + |ref|) in its tail with fp32 sums
+    over K; the fp32 shrink sums in fp64."""
+    mods = [synth.Module("m0", 2048, 1024), synth.Module("m1", 1024, 1536)]
+    ranks = [53, 104, 123, 30, 91, 119, 104, 1, 48, 54, 15, 32, 49, 91, 27, 128, 106, 74, 84,
+             10, 98, 60, 52, 1, 102, 7, 120, 72]
+    wl = synth.random_case(200046, synth.FP32, mods, 2047, 28, 128, ranks, rslora=True,
+                           p_base_only=0.05, zipf_s=0.5)
+    log("case fp32 rslora: T 2047 S 28 R 128")
+    S = make_slots(wl)
+    got = run_gpu(wl, S)
+    for m in mods:
+        check_close(got[m.name], run_oracle(wl, m.name), wl.dtype, f"fp32 rslora {m.name}")
+    S.close()
+
+
 def test_exact_integers_fp32_bit_identical():
     mods = [synth.Module("a", 200, 136), synth.Module("b", 64, 520)]
     wl = synth.random_case(7, synth.FP32, mods, 333, 4, 16, [16, 9, 4, 1], integer=True)
