@@ -20,7 +20,9 @@
  *  - Every call returns an int status (LORA_OK or a negative LORA_ERR_*).  No
  *    call aborts or throws across the ABI.  All argument checks run on the
  *    host before anything is enqueued, so an error has no partial effect.
- *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).  A
+ *    stream the ctx has launched on must stay valid until lora_slots_destroy:
+ *    later loads record events on it and query it.
  *  - x, y and token_slot_idx are device pointers owned by the caller, who
  *    keeps them alive until the stream has passed the call.
  *  - A lora_ctx is used from one host thread at a time.  Calls that launch
