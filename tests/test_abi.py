@@ -56,3 +56,49 @@ def test_status_strings_without_a_device(lib_path):
     assert binding.lora_status_string(0) == "ok"
     assert "rank exceeds maximum" in binding.lora_status_string(binding.LORA_ERR_RANK_EXCEEDS_MAX)
     assert binding.lora_status_string(12345) == "unknown status"
+
+
+def _create(lib, max_loras=4, max_rank=16, shapes=((64, 64),), dtype=0, max_tokens=8, device=0,
+            out=True):
+    arr = (binding._ModuleShape * max(len(shapes), 1))(*[binding._ModuleShape(a, b) for a, b in shapes])
+    ctx = ctypes.c_void_p()
+    st = lib.lora_slots_create(ctypes.byref(ctx) if out else None, max_loras, max_rank,
+                               arr if shapes else None, len(shapes), dtype, max_tokens, device)
+    return st, ctx
+
+
+def test_create_checks_its_arguments_on_the_host(lib_path):
+    """lora_slots_create validates every argument before it touches a device, and says
+    why in lora_last_error(NULL)."""
+    lib = binding.load_library(lib_path)
+    last = lambda: (lib.lora_last_error(None) or b"").decode()
+    cases = [
+        (dict(out=False), binding.LORA_ERR_INVALID_ARGUMENT, "out is NULL"),
+        (dict(max_loras=0), binding.LORA_ERR_INVALID_ARGUMENT, "max_loras"),
+        (dict(max_loras=257), binding.LORA_ERR_INVALID_ARGUMENT, "max_loras"),
+        (dict(max_rank=0), binding.LORA_ERR_INVALID_ARGUMENT, "max_rank"),
+        (dict(max_rank=129), binding.LORA_ERR_RANK_EXCEEDS_MAX, "max_rank"),
+        (dict(shapes=()), binding.LORA_ERR_INVALID_ARGUMENT, "no modules"),
+        (dict(dtype=7), binding.LORA_ERR_INVALID_ARGUMENT, "dtype"),
+        (dict(max_tokens=0), binding.LORA_ERR_INVALID_ARGUMENT, "max_tokens"),
+        (dict(shapes=((64, 60),)), binding.LORA_ERR_INVALID_ARGUMENT, "multiples of 8"),
+        (dict(shapes=((64, 64), (4, 64))), binding.LORA_ERR_INVALID_ARGUMENT, "module 1"),
+        (dict(device=-1), binding.LORA_ERR_INVALID_ARGUMENT, "device -1"),
+    ]
+    for kw, want, text in cases:
+        st, ctx = _create(lib, **kw)
+        assert st == want, (kw, st, last())
+        assert text in last(), (kw, last())
+        assert not ctx.value
+
+
+def test_calls_on_a_null_ctx_fail_cleanly(lib_path):
+    lib = binding.load_library(lib_path)
+    E = binding.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_slots_destroy(None) == binding.LORA_OK
+    assert lib.lora_slot_clear(None, 0) == E
+    assert lib.lora_sync_loads(None) == E
+    assert lib.lora_plan_prepare(None, None, 0, None) == E
+    assert lib.lora_shrink(None, None, 0, None) == E
+    assert lib.lora_expand(None, None, 0, None) == E
+    assert lib.lora_apply(None, None, None, None, 0, 0, None) == E
