@@ -129,7 +129,8 @@ int lora_slots_destroy(lora_ctx *ctx);
  * Asynchronous, on the ctx's side stream: a kernel reads the weights in place
  * where the device can (16-byte aligned pinned host memory mapped at its host
  * address, over the link; memory of the ctx's device; managed memory) and
- * writes the slot; other weights are first copied to a stage buffer.  Before
+ * writes the slot; other weights are first copied to a stage buffer.  The same
+ * holds for the output terms of lora_slot_load_ex.  Before
  * overwriting the slot the side stream waits for every kernel already enqueued
  * by this ctx, so
  * an adapter in use by an in-flight batch is never overwritten ("an adapter in

@@ -159,6 +159,10 @@ struct FinalizeItem {
     void *Bi_slot;           // the slot's repacked B block
     const void *A_src;       // r x d_in, row-major: the caller's weights or their staged copy
     const void *B_src;       // r x d_out, row-major: the same
+    void *bias_dst;          // the slot's bias row (d_out, ctx dtype), or null
+    const void *bias_src;    // the caller's bias, read in place, or null
+    float *dora_dst;         // the slot's DoRA factors (d_out), or null
+    const float *dora_src;   // the caller's factors, read in place, or null
     int32_t d_in, d_out;
 };
 struct FinalizeBatch {

@@ -1565,9 +1565,9 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
 // slot maintenance
 
 // Copy A^T (r x d_in) into the slot, repack B (r x d_out, row-major) into
-// groups of 8 ranks, Bi[j/8][n][j%8], and zero ranks r..R_pad-1 of both;
-// module blockIdx.y of the batch.  The sources are the caller's weights when
-// the device can read them in place (pinned host memory over the link, or
+// groups of 8 ranks, Bi[j/8][n][j%8], zero ranks r..R_pad-1 of both, and copy
+// the output terms given in place; module blockIdx.y of the batch.  The
+// sources are the caller's weights when the device can read them in place (pinned host memory over the link, or
 // device memory), else their staged copies.  Every read is a 16-byte piece of
 // a source row, consecutive lanes taking consecutive pieces, so a wave reads
 // 1 KB of one row per instruction: link reads need such runs.  Rows are
@@ -1621,6 +1621,17 @@ __global__ void slot_finalize_kernel(FinalizeBatch fb)
     uint4 *A_pad = (uint4 *)(A_slot + (int64_t)r * d_in);
     for (int64_t o = first; o < nZ16; o += stride)
         A_pad[o] = make_uint4(0, 0, 0, 0);
+    // output terms read in place: d_out values each, in 16-byte pieces
+    if (it.bias_src) {
+        const int64_t n16 = (int64_t)d_out * (int64_t)sizeof(E) / 16;
+        for (int64_t o = first; o < n16; o += stride)
+            ((uint4 *)it.bias_dst)[o] = ((const uint4 *)it.bias_src)[o];
+    }
+    if (it.dora_src) {
+        const int64_t n16 = (int64_t)d_out * 4 / 16;
+        for (int64_t o = first; o < n16; o += stride)
+            ((uint4 *)it.dora_dst)[o] = ((const uint4 *)it.dora_src)[o];
+    }
 }
 
 hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st)

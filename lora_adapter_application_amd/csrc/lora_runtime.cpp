@@ -732,10 +732,12 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
     if (!std::isfinite(s))
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "scale is not finite (lora_alpha %g)",
                     lora_alpha);
-    std::vector<uint8_t> in_place;
+    std::vector<uint8_t> in_place, bias_in, dora_in;   // per module: read by the finalize in place
     {
         DeviceGuard guard(ctx->device);
         in_place.assign(ctx->n_modules, 0);
+        bias_in.assign(ctx->n_modules, 0);
+        dora_in.assign(ctx->n_modules, 0);
         for (int m = 0; m < ctx->n_modules; ++m) {
             if ((A_t[m] == nullptr) != (B[m] == nullptr))
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
@@ -749,10 +751,13 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: bias entry is NULL", m);
             if (A_t[m] && dora_scale && !dora_scale[m])
                 return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "module %d: dora_scale entry is NULL", m);
-            if (A_t[m] && ((bias && check_source(bias[m], ctx->device)) ||
-                           (dora_scale && check_source(dora_scale[m], ctx->device))))
+            bool ic = false, ig = false;
+            if (A_t[m] && ((bias && check_source(bias[m], ctx->device, &ic)) ||
+                           (dora_scale && check_source(dora_scale[m], ctx->device, &ig))))
                 return fail(ctx, LORA_ERR_HOST_NOT_PINNED,
                             "module %d: bias / dora_scale must be pinned host or device memory", m);
+            bias_in[m] = bias && ic;
+            dora_in[m] = dora_scale && ig;
         }
     }
     DeviceGuard guard(ctx->device);
@@ -778,8 +783,11 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
         if (q == hipErrorNotReady)
             beside_compute = true;
     }
-    if (beside_compute)
+    if (beside_compute) {
         std::fill(in_place.begin(), in_place.end(), 0);
+        std::fill(bias_in.begin(), bias_in.end(), 0);
+        std::fill(dora_in.begin(), dora_in.end(), 0);
+    }
     int rc = fence_compute_streams(ctx);
     if (rc)
         return rc;
@@ -831,6 +839,10 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
         char *Bslot = (char *)ctx->Bi[m] + (size_t)slot * ctx->strideB[m] * ctx->elem;
         const size_t abytes = (size_t)a_elems * ctx->elem, bbytes = (size_t)b_elems * ctx->elem;
         bytes += (int64_t)abytes + (int64_t)bbytes;
+        void *cdst = bias_in[m] ? (char *)ctx->bias[m] + (size_t)slot * sh.d_out * ctx->elem : nullptr;
+        float *gdst = dora_in[m] ? ctx->dora[m] + (size_t)slot * sh.d_out : nullptr;
+        const void *csrc = bias_in[m] ? bias[m] : nullptr;
+        const float *gsrc = dora_in[m] ? dora_scale[m] : nullptr;
         if (in_place[m]) {
             if (fb.n == kFinalizeBatch) {
                 HIP_TRY(ctx, flush_run());
@@ -838,7 +850,8 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
                 fb.n = 0;
                 stage_used = 0;
             }
-            fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, A_t[m], B[m], sh.d_in, sh.d_out};
+            fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, A_t[m], B[m], cdst, csrc, gdst, gsrc,
+                                         sh.d_in, sh.d_out};
             continue;
         }
         if (fb.n == kFinalizeBatch || stage_used + a_elems + b_elems > ctx->stage_elems) {
@@ -851,20 +864,20 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
         char *Bst = Ast + abytes;
         HIP_TRY(ctx, add_range(A_t[m], Ast, abytes));
         HIP_TRY(ctx, add_range(B[m], Bst, bbytes));
-        fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, Ast, Bst, sh.d_in, sh.d_out};
+        fb.it[fb.n++] = FinalizeItem{Aslot, Bslot, Ast, Bst, cdst, csrc, gdst, gsrc, sh.d_in, sh.d_out};
         stage_used += a_elems + b_elems;
     }
     HIP_TRY(ctx, flush_run());
     HIP_TRY(ctx, launch_slot_finalize(bf16, fb, ctx->side));
-    // output terms straight into the slot's rows
+    // output terms the finalize did not read in place, straight into the slot's rows
     for (int m = 0; m < ctx->n_modules && (bias || dora_scale); ++m) {
         if (!A_t[m])
             continue;
         const int d_out = ctx->shapes[m].d_out;
-        if (bias)
+        if (bias && !bias_in[m])
             HIP_TRY(ctx, hipMemcpyAsync((char *)ctx->bias[m] + (size_t)slot * d_out * ctx->elem, bias[m],
                                         (size_t)d_out * ctx->elem, hipMemcpyDefault, ctx->side));
-        if (dora_scale)
+        if (dora_scale && !dora_in[m])
             HIP_TRY(ctx, hipMemcpyAsync(ctx->dora[m] + (size_t)slot * d_out, dora_scale[m],
                                         sizeof(float) * (size_t)d_out, hipMemcpyDefault, ctx->side));
     }

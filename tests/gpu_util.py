@@ -61,9 +61,9 @@ def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None,
                source: str = "pinned") -> binding.Slots:
     """Create a ctx for the workload's modules and load every slot's adapter.
 
-    source: where the adapter weights come from, "pinned" (read in place by the
-    load), "device" (read in place) or "staged" (pinned but misaligned, so the
-    load copies them to its stage first)."""
+    source: where the adapter weights and output terms come from, "pinned"
+    (read in place by the load), "device" (read in place) or "staged" (pinned
+    but misaligned, so the load copies them first)."""
     S = binding.Slots(wl.max_loras, max_rank or wl.max_rank,
                       [(m.d_in, m.d_out) for m in wl.modules], wl.dtype,
                       max_tokens or max(wl.n_tokens, 1))
@@ -86,10 +86,13 @@ def make_slots(wl: synth.Workload, max_tokens=None, max_rank=None, keep=None,
                 A_t.append(a)
                 B.append(b)
                 if ad.bias is not None:
-                    C.append(to_pinned(ad.bias[m.name], wl.dtype))
+                    C.append(weights(ad.bias[m.name]))
                     pinned.append(C[-1])
                 if ad.dora_scale is not None:
-                    G.append(torch.from_numpy(np.ascontiguousarray(ad.dora_scale[m.name], np.float32)).pin_memory())
+                    g = np.ascontiguousarray(ad.dora_scale[m.name], np.float32)
+                    G.append(to_dev(g, synth.FP32) if source == "device" else
+                             to_pinned_misaligned(g, synth.FP32, pinned) if source == "staged" else
+                             to_pinned(g, synth.FP32))
                     pinned.append(G[-1])
             else:
                 A_t.append(None)
