@@ -37,13 +37,18 @@
  *    (hipStreamBeginCapture on a non-null stream) and the graph replayed.
  *    Each launch takes the slot metadata (rank, scale, target modules) by
  *    value when it is enqueued, so a replay uses the metadata as of the
- *    capture and the adapter weights as they are at the replay: reloading a
- *    slot with an adapter of the same rank, lora_alpha and targets is seen by
- *    later replays; any other load or clear needs a new capture.  Loads must be
+ *    capture and the adapter weights as they are at the replay.  Loads must be
  *    complete before the capture starts (lora_sync_loads), else the first
  *    captured launch fails with LORA_ERR_INVALID_ARGUMENT.  Launches under
  *    capture are never timed (lora_profile_begin).  No load or clear may be
  *    issued while a capture is open.
+ *    The library does not see replays, so it cannot order loads against them:
+ *    the caller must (1) make sure no replay that reads a slot is in flight
+ *    when it loads into that slot (e.g. synchronise the replaying stream
+ *    first), and (2) call lora_sync_loads after the load and before a replay
+ *    that must see the new weights.  Under those two rules a slot reloaded
+ *    with an adapter of the same rank, lora_alpha and target modules is seen
+ *    by later replays; any other load or clear needs a new capture.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -96,7 +101,11 @@ typedef struct {
 } lora_stats;
 
 /*
- * Create a slot pool on `device`.
+ * Create a slot pool on `device`.  The two sizes are vLLM's max_loras (the
+ * adapters one batch may use) and max_lora_rank (the largest rank served, to
+ * which every slot is padded) of the parameter table in "Multi-LoRA adapter
+ * cache in production" (oh-bug.com), section "GPU, CPU and disk form the
+ * adapter storage hierarchy".
  *   max_loras   slots, 1..LORA_MAX_SLOTS
  *   max_rank    padded rank of every slot, 1..LORA_MAX_RANK
  *   modules     n_modules shapes; a module index in later calls refers to this array
@@ -104,14 +113,21 @@ typedef struct {
  *   max_tokens  largest n_tokens of a batch, >= 1
  * Allocates and zeroes, per module, A^T storage [max_loras][R][d_in] and B
  * storage for [max_loras][R][d_out] (R = max_rank rounded up to 16), an fp32
- * intermediate, plan buffers, and a side stream for loads.  Every slot starts
- * empty.  On success *out owns all of it until lora_slots_destroy.
+ * intermediate, plan buffers, and a side stream for loads (the memory is
+ * zeroed on that stream, which the call waits for; no device-wide
+ * synchronisation).  Every slot starts empty.  On success *out owns all of it
+ * until lora_slots_destroy.
+ * Errors: sizes out of range or d_in / d_out not a positive multiple of 8 ->
+ * LORA_ERR_INVALID_ARGUMENT (max_rank > LORA_MAX_RANK ->
+ * LORA_ERR_RANK_EXCEEDS_MAX); allocation failure -> LORA_ERR_OUT_OF_MEMORY,
+ * with nothing left allocated; *out is NULL on every error.
  */
 int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
                       const lora_module_shape *modules, int32_t n_modules,
                       lora_dtype dtype, int32_t max_tokens, int32_t device);
 
-/* Wait for all work the ctx enqueued, then free it.  NULL is accepted. */
+/* Wait for the streams the ctx has launched on and for its side stream (not
+ * for the whole device), then free everything it owns.  NULL is accepted. */
 int lora_slots_destroy(lora_ctx *ctx);
 
 /*
@@ -182,7 +198,11 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot);
 int lora_sync_loads(lora_ctx *ctx);
 
 /*
- * Group the batch's tokens by slot on the device (no host synchronisation):
+ * Group the batch's tokens by slot on the device (no host synchronisation).
+ * token_slot_idx is the per-request adapter choice of a mixed batch, each
+ * value a slot of the pool: max_loras bounds how many adapters one batch may
+ * use ("Multi-LoRA adapter cache in production", parameter table and section
+ * "common misconceptions", item 1).  The grouping is
  * a stable counting sort of token_slot_idx (int32[n_tokens], device) into a
  * permutation, per-slot segments and tiles of up to 64 tokens.  Tokens with
  * idx < 0 are not listed; idx >= max_loras are not listed and set
@@ -221,23 +241,40 @@ int lora_plan_prepare_slots(lora_ctx *ctx, const int32_t *token_slot_idx, int32_
 
 /*
  * lora_shrink: h = x . A_k for every planned token (fp32 intermediate of rank
- * R, held in the ctx).  x is [n_tokens][d_in] of the prepared plan.
- * Requires a prepared plan (else LORA_ERR_NO_PLAN).
+ * R, held in the ctx), the first factor of the update with A of shape
+ * d_in x r as the adapter size estimate of "Multi-LoRA adapter cache in
+ * production" (section "adapter capacity cannot be planned by count alone")
+ * implies; r is the "r" of the adapter_config.json in "vLLM LoRA Resolver
+ * plugins explained", section 3.2.  x is [n_tokens][d_in] (row-major, device,
+ * ctx dtype) of the prepared plan.  Requires a prepared plan (else
+ * LORA_ERR_NO_PLAN); a bad module -> LORA_ERR_BAD_MODULE; x NULL with
+ * n_tokens > 0 -> LORA_ERR_INVALID_ARGUMENT.
  */
 int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream);
 
 /*
  * lora_expand: y[t,:] = round(y[t,:] + s_k * h[t,:] . B_k) for every planned
- * token whose slot holds an adapter targeting `module`; every other row of y
- * is left bit-identical.  Must follow lora_shrink of the same module on the
- * same plan, with no lora_slot_load or lora_slot_clear in between (else
- * LORA_ERR_INVALID_ARGUMENT).  y is [n_tokens][d_out].
+ * token whose slot holds an adapter targeting `module` (its "target_modules",
+ * with s_k from "lora_alpha", "r" and "use_rslora" of the adapter_config.json
+ * in "vLLM LoRA Resolver plugins explained", section 3.2; B is r x d_out as
+ * in the size estimate of "Multi-LoRA adapter cache in production"); every
+ * other row of y is left bit-identical.  Must follow lora_shrink of the same
+ * module on the same plan, with no lora_slot_load or lora_slot_clear in
+ * between (else LORA_ERR_INVALID_ARGUMENT).  y is [n_tokens][d_out]
+ * (row-major, device, ctx dtype), read and written in place.
  */
 int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream);
 
 /*
  * One module's update in one call: plan (unless lora_plan_prepare was called
- * for the same token_slot_idx and n_tokens), shrink, expand.  Tokens with
+ * for the same token_slot_idx and n_tokens), shrink, expand.  The update is
+ * the one the adapter fields "r", "lora_alpha", "use_rslora" and
+ * "target_modules" of the example adapter_config.json in "vLLM LoRA Resolver
+ * plugins explained", section 3.2, describe, for slots of the pool sized by
+ * max_loras / max_lora_rank ("Multi-LoRA adapter cache in production",
+ * parameter table).  x: [n_tokens][d_in], y: [n_tokens][d_out] (read and
+ * written in place), token_slot_idx: int32[n_tokens], all device memory owned
+ * by the caller.  Tokens with
  * idx == -1 (base model only), any other negative idx, idx >= max_loras, an
  * empty slot, or a slot whose adapter does not target `module` leave their row
  * of y bit-identical.  n_tokens == 0 is a no-op; n_tokens > max_tokens returns
@@ -264,7 +301,8 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
                      void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
                      void *stream);
 
-/* Synchronise the device, return the sticky LORA_FLAG_* bits and clear them. */
+/* Wait for the streams the ctx has launched on (not for the whole device),
+ * return the sticky LORA_FLAG_* bits in *flags and clear them. */
 int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags);
 
 /* Counters since creation. */

@@ -16,8 +16,8 @@ import os
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# LORA_MI355X_LIB selects another build of the library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(PKG, "liblora_mi355x.so")
+# The in-tree build is the only library the binding loads.
+LIB_PATH = os.path.join(PKG, "liblora_mi355x.so")
 
 LORA_BF16 = 0
 LORA_FP32 = 1

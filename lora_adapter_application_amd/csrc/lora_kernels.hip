@@ -423,11 +423,7 @@ __device__ __forceinline__ void load_kblock(KBlock<NB> &blk, const uint16_t *xro
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-#ifdef LORA_KORDER_PER_LANE
-        const int ke = kb + g * 32 + q * 8;
-#else
         const int ke = kb + q * 32 + g * 8;
-#endif
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             blk.a[b][q] = (b < nb && ke < k1) ? ld16(arow0 + b * 16 * d_in + ke) : make_uint4(0, 0, 0, 0);

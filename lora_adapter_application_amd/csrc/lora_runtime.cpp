@@ -86,7 +86,6 @@ struct lora_ctx {
     int64_t stage_elems = 0;
     float *hpart = nullptr;
     int hbuf_rows = 0;
-    int max_splits = 16;                     // K-split cap of the shrink (tuning)
     PlanBuffers plan{};
     int max_tiles = 0;
     hipStream_t side = nullptr;
@@ -123,6 +122,7 @@ struct lora_ctx {
     int64_t prof_untimed = 0;
     std::string last_error;
     std::vector<void *> allocations;
+    uint32_t flags_host = 0;                 // lora_get_device_flags' copy of the sticky word
 };
 
 namespace {
@@ -285,6 +285,8 @@ void free_all(lora_ctx *c)
     c->side = nullptr;
 }
 
+// Device allocation owned by the ctx, zeroed on the ctx's side stream (the
+// creating call waits for that stream before it returns).
 template <typename T>
 hipError_t dalloc(lora_ctx *c, T **p, size_t bytes)
 {
@@ -293,9 +295,27 @@ hipError_t dalloc(lora_ctx *c, T **p, size_t bytes)
     if (e != hipSuccess)
         return e;
     c->allocations.push_back(q);
-    e = hipMemset(q, 0, bytes ? bytes : 16);
+    e = hipMemsetAsync(q, 0, bytes ? bytes : 16, c->side);
     *p = (T *)q;
     return e;
+}
+
+// Host waits for every stream this ctx has launched on and for its side
+// stream; unrelated streams of the process are not waited for.
+hipError_t sync_ctx_streams(lora_ctx *c)
+{
+    hipError_t first = hipSuccess;
+    for (auto &st : c->streams) {
+        const hipError_t e = hipStreamSynchronize(st.stream);
+        if (e != hipSuccess && first == hipSuccess)
+            first = e;
+    }
+    if (c->side) {
+        const hipError_t e = hipStreamSynchronize(c->side);
+        if (e != hipSuccess && first == hipSuccess)
+            first = e;
+    }
+    return first;
 }
 
 // K-split of the shrink for a batch of T tokens: enough workgroups to cover
@@ -304,7 +324,7 @@ void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
 {
     const int tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
     int want = ceil_div(1024, std::max(tiles, 1));
-    int cap = std::min(c->max_splits, std::max(1, d_in / 256));
+    int cap = std::min(kMaxSplits, std::max(1, d_in / 256));
     cap = std::min(cap, splits_cap(nb_template(c->R_pad)));
     cap = std::min(cap, std::max(1, c->hbuf_rows / std::max(T, 1)));
     int sp = std::max(1, std::min(want, cap));
@@ -619,7 +639,8 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     c->rank_host.assign((size_t)n_modules * max_loras, 0);
     c->scale_host.assign(max_loras, 0.f);
 
-    hipError_t e = hipSuccess;
+    // the side stream first: allocations are zeroed on it
+    hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     int max_out = 0;
     for (int m = 0; m < n_modules && e == hipSuccess; ++m) {
         const auto &sh = modules[m];
@@ -647,11 +668,6 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     c->slot_flags.assign(max_loras, 0);
     c->hint.assign(max_loras, 0);
     c->last_use.assign(max_loras, 0);
-    if (const char *env = std::getenv("LORA_MI355X_MAX_SPLITS")) {
-        const int v = std::atoi(env);
-        if (v >= 1 && v <= kMaxSplits)
-            c->max_splits = v;
-    }
     c->max_tiles = std::max(max_tiles_for(max_tokens, max_loras),
                             max_tiles_for(std::min(max_tokens, (int)kInlinePlanTokens), max_loras,
                                           inline_tile_tokens(c->R_pad)));
@@ -679,9 +695,8 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     if (e == hipSuccess)
         e = dalloc(c, &c->plan.chunk_counts,
                    sizeof(int32_t) * (size_t)ceil_div(max_tokens, 1024) * max_loras);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->load_done, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipStreamSynchronize(c->side);
     if (e != hipSuccess) {
         int status = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
                          ? LORA_ERR_OUT_OF_MEMORY : LORA_ERR_HIP;
@@ -700,7 +715,8 @@ int lora_slots_destroy(lora_ctx *ctx)
     if (!ctx)
         return LORA_OK;
     DeviceGuard guard(ctx->device);
-    (void)hipDeviceSynchronize();
+    (void)sync_ctx_streams(ctx);
+    (void)hipGetLastError();
     free_all(ctx);
     delete ctx;
     return LORA_OK;
@@ -1071,10 +1087,14 @@ int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)
     if (check_ctx(ctx) || !flags)
         return LORA_ERR_INVALID_ARGUMENT;
     DeviceGuard guard(ctx->device);
-    HIP_TRY(ctx, hipDeviceSynchronize());
-    HIP_TRY(ctx, hipMemcpy(flags, ctx->plan.flags, sizeof(uint32_t), hipMemcpyDeviceToHost));
-    HIP_TRY(ctx, hipMemset(ctx->plan.flags, 0, sizeof(uint32_t)));
-    HIP_TRY(ctx, hipDeviceSynchronize());
+    // the kernels that set flags ran on the ctx's streams: wait for those
+    // only, then read and clear the word in order on the side stream
+    HIP_TRY(ctx, sync_ctx_streams(ctx));
+    HIP_TRY(ctx, hipMemcpyAsync(&ctx->flags_host, ctx->plan.flags, sizeof(uint32_t),
+                                hipMemcpyDeviceToHost, ctx->side));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->plan.flags, 0, sizeof(uint32_t), ctx->side));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->side));
+    *flags = ctx->flags_host;
     return LORA_OK;
 }
 
