@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-adapter LoRA apply path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_prefill]
+                    [--extra llama7b_decode,qwen32b_decode]
 
 One step is one pass of the whole hot path over one batch: the device plan
 (lora_plan_prepare) and, for every group of modules of the workload's layer,
@@ -11,23 +12,34 @@ like the layers of a model) so that the bytes the kernels read come from HBM
 rather than from the 256 MB Infinity Cache.  Inputs are resident
 in HBM before timing starts.  Prints one JSON line.
 
-Launch: the K steps are timed twice, as eager library calls from Python (the
-default "value") and as replays of a HIP graph that captured the library calls
-of the L steps of one rotation once (torch.cuda.graph over the library's own
-launches), as a serving engine replays its decode step; the other rate is
-reported beside "value".  --launch graph makes the replay rate "value".
+The headline ("value") is the Llama-7B-shaped prefill (segment-grouped SGMV,
+32 requests of 128..2048 tokens, q/k/v/o 4096->4096, ranks 8..64 padded to 64):
+the largest workload of the metric that fits one GPU.  The two decode (BGMV)
+workloads, Llama-7B q/v at 256 tokens and Qwen3-32B q/k/v/o at 512 tokens, are
+measured after it with their own step counts and reported under their names.
 
-value      tokens of the batch (skipped tokens included) x K / wall time of K steps
+Passes over the same K steps (after W warm-up steps):
+  eager      library calls from Python, one step after the other ("value");
+  graph      the calls of one rotation captured into a HIP graph and replayed,
+             as a serving engine replays its decode step (--launch graph makes
+             this "value");
+  plan_amortized  one lora_plan_prepare, then the K steps' applies only (the
+             layers of a model share one batch and its slot indices);
+  step_spread     an event after each step: p10 / p50 / p90 step times;
+  kernels    per-dispatch start / stop events the library records with each
+             of its dispatches (hipExtLaunchKernelGGL): kernel times.
+
 roofline   the kernel with the largest share of the step: its algorithmic bytes /
-           its kernel time, from start / stop events the library attaches to each of
-           its dispatches (hipExtLaunchKernelGGL) during a second pass of the same K
-           steps right after the timed one; also its fraction of a measured 1 GiB
-           device copy (copy_GBps, read plus write) beside the 8 TB/s spec, and
-           (roofline.mfma) its algorithmic flops per second against the dense
-           bf16 MFMA peak; kernels.lora_* carry both for each kernel
+           its kernel time against the 8 TB/s HBM peak ("frac"), its fraction of
+           a measured 1 GiB device copy (copy_GBps, read plus write), and, flat
+           beside them, its algorithmic flops per second against the 2.5 PFLOP/s
+           dense bf16 MFMA peak ("mfma_frac") with rocprofv3's MfmaUtil reading
+           ("mfma_util_pct", from the committed counter summary when the kernel
+           source is unchanged); "traffic" is the calibrated FETCH_SIZE +
+           WRITE_SIZE of the same kernel, from its committed counter summary
 cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
-           same workload (rank 0, one GPU only): all threads, and one thread on
-           a smaller sample; nproc and the CPU model
+           headline workload (rank 0, one GPU only): all threads, and one thread
+           on a smaller sample; nproc and the CPU model
 
 --workload churn [--prefetch] times adapter uploads with the applies instead
 (see churn and churn_prefetch below); its "h2d" carries the upload rate beside
@@ -61,8 +73,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="llama7b_decode",
+    p.add_argument("--workload", default="llama7b_prefill",
                    choices=["llama7b_decode", "qwen32b_decode", "llama7b_prefill", "churn"])
+    p.add_argument("--extra", default="llama7b_decode,qwen32b_decode",
+                   type=lambda v: [w for w in v.split(",") if w],
+                   help="further workloads measured after the headline one and reported as "
+                        "extra keys (empty: none)")
+    p.add_argument("--extra-steps", type=int, default=2000)
+    p.add_argument("--extra-warmup", type=int, default=200)
     p.add_argument("--churn-steps", type=int, default=50)
     p.add_argument("--prefetch", action="store_true",
                    help="churn: upload the next step's misses while the current step computes "
@@ -161,43 +179,38 @@ def kernel_source_sha():
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
 
 
-def traffic_from_profiles(kernel, wl_name):
-    """HBM bytes per launch from the committed counter summary, if the kernel
-    source is still the one the counters were taken on; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wl_name}.json")
+def profile_figure(kind, kernel, wl_name, key):
+    """A figure from a committed counter summary (profiles/<kind>_<kernel>_<workload>.json),
+    if the kernel source is still the one the counters were taken on; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kind}_{kernel}_{wl_name}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     if d.get("kernel_source_sha256") != kernel_source_sha():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get(key)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
-              "by replicating slot pools per GPU with no exchange, which this benchmark does "
-              "not measure.", file=sys.stderr)
-        sys.exit(2)
+def traffic_from_profiles(kernel, wl_name):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, calibrated) of the kernel."""
+    return profile_figure("traffic", kernel, wl_name, "hbm_bytes_per_launch")
+
+
+def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
+    """Time K steps of one workload (after W warm-up steps) and return its record.
+
+    A step is lora_plan_prepare of the batch and one lora_apply_group per module
+    group, on one of L rotated layer sets.  Passes over the same K steps:
+      eager        the library calls from Python, one step after the other
+      graph        the calls of one rotation captured into a HIP graph, replayed
+      amortized    one lora_plan_prepare before the K steps, then only the applies
+                   (the layers of a model share the batch's slot indices)
+      spread       an event after each step (p10 / p50 / p90)
+      kernels      per-dispatch start / stop events (kernel times, roofline)"""
     import torch
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    if args.calib_copy:
-        calib_copy(args.steps)
-        return
-
-    from lora_adapter_application_amd import binding, synth
-    binding.load_library()
-    if args.workload == "churn":
-        if args.prefetch:
-            churn_prefetch(args)
-        else:
-            churn(args)
-        return
+    from lora_adapter_application_amd import binding
     dev = torch.device("cuda:0")
-    wl = workload(args.workload)
+    wl = workload(wl_name)
     T = wl.n_tokens
     S, R = wl.max_loras, wl.max_rank
     mods = wl.modules
@@ -216,7 +229,7 @@ def main():
                   + (T * m.d_in * b if x_owner[j] == j else 0) for j, m in enumerate(mods))
     L = max(1, math.ceil(args.layer_bytes / per_set))
     log(f"workload {wl.name}: T={T} S={S} R={R} modules={[(m.name, m.d_in, m.d_out) for m in mods]}"
-        f" layer sets={L} ({L * per_set / 1e9:.2f} GB)")
+        f" layer sets={L} ({L * per_set / 1e9:.2f} GB) steps={K} warmup={W}")
 
     def dev_bits(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -259,29 +272,37 @@ def main():
 
     nm = len(mods)
     ng = len(groups)
-    use_timing = not args.no_kernel_timing
 
     # the library calls of one step per layer set, arguments marshalled once
     # (per stream: the eager passes use the current stream, the graph capture its own)
-    def bind_all(stream=None):
+    def bind_all(stream=None, prepare=True):
         return [slots.bind_step([([l * nm + j for j in g], [xs[l * nm + j] for j in g],
-                                  [ys[l * nm + j] for j in g]) for g in groups], idx, stream)
+                                  [ys[l * nm + j] for j in g]) for g in groups], idx, stream,
+                                prepare=prepare)
                 for l in range(L)]
     bound = bind_all()
+    bound_np = bind_all(prepare=False)
 
     def step(i):
         bound[i % L]()
 
-    for i in range(args.warmup):
+    for i in range(W):
         step(i)
     torch.cuda.synchronize()
-    K = args.steps
     # eager: K steps, nothing but the library calls
     t0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i)
+        step(W + i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
+    # plan amortized over the layers: one lora_plan_prepare, then K steps of applies
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    slots.prepare(idx)
+    for i in range(K):
+        bound_np[(W + i) % L]()
+    torch.cuda.synchronize()
+    amort_s = time.perf_counter() - t0
     # graph: the L steps of one rotation (and the K mod L first ones) captured once;
     # K steps = K // L replays of the first graph and one of the second
     slots.sync_loads()
@@ -317,7 +338,7 @@ def main():
     torch.cuda.synchronize()
     evs[0].record()
     for i in range(K):
-        step(args.warmup + i)
+        step(W + i)
         evs[i + 1].record()
     torch.cuda.synchronize()
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K)])
@@ -326,17 +347,15 @@ def main():
                    "p90_us": round(float(np.percentile(per_step, 90)), 3),
                    "pass": "eager, an event after each step"}
     del evs
-    elapsed = graph_s if args.launch == "graph" else eager_s
-    ms_per_step = elapsed / K * 1e3
-    value = T * K / elapsed
-    if use_timing:
+    elapsed = graph_s if launch == "graph" else eager_s
+    if kernel_timing:
         # the same K steps again with per-dispatch kernel events (their host cost
         # would distort the step time above, so they get a pass of their own);
         # the events are created before this pass starts
         slots.profile_begin(K * (2 * ng + 2))
         torch.cuda.synchronize()
         for i in range(K):
-            step(args.warmup + K + i)
+            step(W + K + i)
         torch.cuda.synchronize()
 
     act = (wl.idx >= 0) & (wl.idx < S)
@@ -344,7 +363,7 @@ def main():
     used = np.unique(wl.idx[act])
     sum_r = int(sum(wl.adapters[k].r for k in used))
     roofline, kernels = None, None
-    if use_timing:
+    if kernel_timing:
         prof = slots.profile_end()
         n = prof["launches"]
         tot = prof["total_ms"]
@@ -378,60 +397,125 @@ def main():
                     "avg_us": avg_us(kind), "per_step_us": tot[kind] / K * 1e3,
                     "alg_bytes_per_step": step_bytes,
                     "GBps": float(step_bytes * K / (tot[kind] * 1e-3) / 1e9),
+                    "hbm_frac": round(float(step_bytes * K / (tot[kind] * 1e-3) / 1e9) / HBM_PEAK_GBS, 4),
                     "alg_flops_per_step": kind_flops[kind], "TFLOPs": round(tfs, 2),
-                    "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 5)}
+                    "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 5),
+                    "mfma_util_pct": profile_figure("mfma", "lora_" + kind, wl.name, "mfma_util_pct")}
         dom = max(("shrink", "expand"), key=lambda k: tot[k])
         dom_bytes = group_bytes[dom]
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
         kname = "lora_" + dom
         traffic = traffic_from_profiles(kname, wl.name)
-        copy_gbps = measured_copy_gbps()
+        # flat fields only: the %MFMA half of the metric beside the HBM fraction
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic,
                     "alg_bytes_per_launch": float(np.mean(dom_bytes)),
                     "avg_launch_us": avg_us(dom),
-                    "copy_GBps": round(copy_gbps, 1),
-                    "frac_of_copy": round(achieved / copy_gbps, 4),
-                    "mfma": {"achieved": kernels[kname]["TFLOPs"], "peak": BF16_MFMA_PEAK_TFS,
-                             "unit": "TFLOP/s", "frac": kernels[kname]["mfma_frac"],
-                             "flops": "algorithmic, true ranks"}}
+                    "mfma_frac": kernels[kname]["mfma_frac"],
+                    "mfma_TFLOPs": kernels[kname]["TFLOPs"],
+                    "mfma_peak_TFLOPs": BF16_MFMA_PEAK_TFS,
+                    "mfma_util_pct": kernels[kname]["mfma_util_pct"],
+                    "mfma_flops": "algorithmic, true ranks"}
         log("kernels:", json.dumps(kernels))
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
-
-    out = {
-        "metric": "multi-LoRA tokens/s",
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    rec = {
+        "wl": wl, "T": T, "T_act": T_act, "K": K, "L": L,
+        "value": T * K / elapsed, "ms_per_step": elapsed / K * 1e3,
         "config": {"workload": wl.name, "tokens": T, "active_tokens": T_act,
                    "modules": [f"{m.name} {m.d_in}->{m.d_out}" for m in mods],
                    "max_loras": S, "max_rank": R, "ranks": sorted({a.r for a in wl.adapters if a}),
                    "layer_sets_rotated": L, "groups": [[names[j] for j in g] for g in groups],
                    "shared_x": bool(args.shared_x),
-                   "launch": "hip_graph" if args.launch == "graph" else "eager",
-                   "kernel_timing": "per-dispatch events" if use_timing else "none",
+                   "launch": "hip_graph" if launch == "graph" else "eager",
+                   "kernel_timing": "per-dispatch events" if kernel_timing else "none",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
-        "cpu_baseline": cpu,
         "eager": {"ms_per_step": round(eager_s / K * 1e3, 5), "value": round(T * K / eager_s, 1)},
         "graph": {"ms_per_step": round(graph_s / K * 1e3, 5), "value": round(T * K / graph_s, 1)},
+        "plan_amortized": {"ms_per_step": round(amort_s / K * 1e3, 5),
+                           "value": round(T * K / amort_s, 1),
+                           "pass": "one lora_plan_prepare, then the K steps' applies"},
         "step_spread": step_spread,
         "kernels": kernels,
     }
-    print(json.dumps(out), flush=True)
     slots.close()
+    del xs, ys, bound, bound_np, bound_cap
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
+              "by replicating slot pools per GPU with no exchange, which this benchmark does "
+              "not measure.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calib_copy:
+        calib_copy(args.steps)
+        return
+
+    from lora_adapter_application_amd import binding
+    binding.load_library()
+    if args.workload == "churn":
+        if args.prefetch:
+            churn_prefetch(args)
+        else:
+            churn(args)
+        return
+    rec = measure(args.workload, args, args.steps, args.warmup,
+                  kernel_timing=not args.no_kernel_timing, launch=args.launch)
+    if rec["roofline"] is not None:
+        copy_gbps = measured_copy_gbps()
+        rec["roofline"]["copy_GBps"] = round(copy_gbps, 1)
+        rec["roofline"]["frac_of_copy"] = round(rec["roofline"]["achieved"] / copy_gbps, 4)
+    # the other single-GPU workloads of the metric (decode BGMV), each with its
+    # own step count: their steps take microseconds
+    extras = {}
+    for name in args.extra:
+        if name == args.workload:
+            continue
+        e = measure(name, args, args.extra_steps, args.extra_warmup,
+                    kernel_timing=not args.no_kernel_timing, launch=args.launch)
+        extras[name] = {"value": round(e["value"], 1), "unit": "tokens/s",
+                        "ms_per_step": round(e["ms_per_step"], 5), "steps": e["K"],
+                        "config": e["config"], "roofline": e["roofline"],
+                        "graph": e["graph"], "plan_amortized": e["plan_amortized"],
+                        "step_spread": e["step_spread"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(rec["wl"], args.cpu_seconds)
+
+    out = {
+        "metric": "multi-LoRA tokens/s",
+        "value": round(rec["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "cpu_baseline": cpu,
+        "eager": rec["eager"],
+        "graph": rec["graph"],
+        "plan_amortized": rec["plan_amortized"],
+        "step_spread": rec["step_spread"],
+        "kernels": rec["kernels"],
+    }
+    for name, e in extras.items():
+        out[name] = e
+    print(json.dumps(out), flush=True)
 
 
 def churn(args):

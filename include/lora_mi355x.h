@@ -109,7 +109,9 @@ typedef struct {
  *   max_loras   slots, 1..LORA_MAX_SLOTS
  *   max_rank    padded rank of every slot, 1..LORA_MAX_RANK
  *   modules     n_modules shapes; a module index in later calls refers to this array
- *   dtype       element type of x, y and the adapter weights
+ *   dtype       element type of x, y and the adapter weights: a lora_dtype value
+ *               (LORA_BF16 or LORA_FP32), passed as int32_t so that any other
+ *               value is rejected rather than read as an enum
  *   max_tokens  largest n_tokens of a batch, >= 1
  * Allocates and zeroes, per module, A^T storage [max_loras][R][d_in] and B
  * storage for [max_loras][R][d_out] (R = max_rank rounded up to 16), an fp32
@@ -124,7 +126,7 @@ typedef struct {
  */
 int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
                       const lora_module_shape *modules, int32_t n_modules,
-                      lora_dtype dtype, int32_t max_tokens, int32_t device);
+                      int32_t dtype, int32_t max_tokens, int32_t device);
 
 /* Wait for the streams the ctx has launched on and for its side stream (not
  * for the whole device), then free everything it owns.  NULL is accepted. */

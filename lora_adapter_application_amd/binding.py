@@ -379,12 +379,14 @@ class Slots:
     def apply_group(self, modules, x, y, idx, n_tokens=None, stream=None):
         lora_apply_group(self.ctx, modules, x, y, idx, n_tokens, stream)
 
-    def bind_step(self, groups, idx, stream=None):
-        """One step with its arguments marshalled once: lora_plan_prepare of idx, then
-        lora_apply_group for each (modules, x, y) in `groups`.  Returns a function
-        that makes exactly those library calls.  The tensors are checked here and
-        must stay alive, at the same addresses, while the function is used; the
-        stream is taken now (default: the current one)."""
+    def bind_step(self, groups, idx, stream=None, prepare=True):
+        """One step with its arguments marshalled once: lora_plan_prepare of idx
+        (unless prepare is False: then the step reuses the plan an earlier
+        lora_plan_prepare of the same idx made, as the layers of a model share
+        one batch), then lora_apply_group for each (modules, x, y) in `groups`.
+        Returns a function that makes exactly those library calls.  The tensors
+        are checked here and must stay alive, at the same addresses, while the
+        function is used; the stream is taken now (default: the current one)."""
         import torch
         lib = load_library()
         n_tokens = idx.numel()
@@ -397,14 +399,15 @@ class Slots:
             _, _, yp = _group(modules, y, "y")
             calls.append((n, mods, xp, yp))
         ctx = self.ctx
-        prepare, apply_group = lib.lora_plan_prepare, lib.lora_apply_group
+        plan, apply_group = lib.lora_plan_prepare, lib.lora_apply_group
         refs = (idx, groups)
 
         def step():
             _ = refs
-            rc = prepare(ctx, pidx, n_tokens, st)
-            if rc:
-                _check(rc, ctx)
+            if prepare:
+                rc = plan(ctx, pidx, n_tokens, st)
+                if rc:
+                    _check(rc, ctx)
             for n, mods, xp, yp in calls:
                 rc = apply_group(ctx, n, mods, xp, yp, pidx, n_tokens, st)
                 if rc:

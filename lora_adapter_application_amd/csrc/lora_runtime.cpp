@@ -588,7 +588,7 @@ const char *lora_last_error(lora_ctx *ctx)
 }
 
 int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
-                      const lora_module_shape *modules, int32_t n_modules, lora_dtype dtype,
+                      const lora_module_shape *modules, int32_t n_modules, int32_t dtype_arg,
                       int32_t max_tokens, int32_t device)
 {
     g_create_error.clear();
@@ -605,8 +605,9 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
                     LORA_MAX_RANK);
     if (!modules || n_modules < 1)
         return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "no modules");
-    if (dtype != LORA_BF16 && dtype != LORA_FP32)
-        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (dtype_arg != LORA_BF16 && dtype_arg != LORA_FP32)
+        return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype_arg);
+    const lora_dtype dtype = dtype_arg == LORA_BF16 ? LORA_BF16 : LORA_FP32;
     if (max_tokens < 1)
         return fail(nullptr, LORA_ERR_INVALID_ARGUMENT, "max_tokens %d < 1", max_tokens);
     for (int m = 0; m < n_modules; ++m) {

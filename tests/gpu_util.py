@@ -2,6 +2,7 @@
 the HIP path through the C ABI, run the oracle on the same bits, compare."""
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -151,3 +152,52 @@ def check_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
 def rel_l2(gpu_delta: np.ndarray, ref_delta: np.ndarray) -> float:
     n = np.linalg.norm(ref_delta)
     return float(np.linalg.norm(gpu_delta - ref_delta) / n) if n > 0 else 0.0
+
+
+# Module groups the benchmark launches together (one lora_apply_group each).
+BENCH_GROUPS = {"llama7b_decode": [["q_proj", "v_proj"]],
+                "qwen32b_decode": [["q_proj", "k_proj", "v_proj"], ["o_proj"]],
+                "llama7b_prefill": [["q_proj", "k_proj", "v_proj"], ["o_proj"]],
+                "tiny_fp32": [["linear"]]}
+
+
+def run_gpu_groups(wl: synth.Workload, S: binding.Slots, groups=None):
+    """The benchmark's launch configuration: lora_plan_prepare of the batch, then
+    one lora_apply_group per module group.  Returns {module name: y bits}."""
+    groups = groups or BENCH_GROUPS[wl.name]
+    names = [m.name for m in wl.modules]
+    idx = torch.from_numpy(wl.idx).cuda()
+    S.prepare(idx)
+    out = {}
+    for g in groups:
+        xs = [to_dev(wl.x[n], wl.dtype) for n in g]
+        ys = [to_dev(wl.y[n], wl.dtype) for n in g]
+        S.apply_group([names.index(n) for n in g], xs, ys, idx)
+        for n, y in zip(g, ys):
+            out[n] = y
+        del xs
+    torch.cuda.synchronize()
+    return {k: from_dev(v, wl.dtype) for k, v in out.items()}
+
+
+# Relative L2 error of the update itself (y = 0), by dtype: a diagnostic beside
+# the elementwise bound, which on y ~ N(0, 1) is about as large as the update.
+WEAK_SIGNAL_MAX = {synth.FP32: 1e-5, synth.BF16: 1e-2}
+
+
+# The full-size workloads, drawn once per test session (the prefill workload
+# takes about a minute to draw).  The y = 0 variant is the same draw with base
+# y replaced by zeros: x, slot indices and adapters come from their own seeded
+# streams, so they are identical to synth's own y_zero draw.
+_FULL = {"tiny_fp32": synth.tiny_fp32, "llama7b_decode": synth.llama7b_decode,
+         "llama7b_prefill": synth.llama7b_prefill, "qwen32b_decode": synth.qwen32b_decode}
+_CACHE = {}
+
+
+def full_workload(name: str, y_zero: bool = False) -> synth.Workload:
+    if name not in _CACHE:
+        _CACHE[name] = _FULL[name]()
+    wl = _CACHE[name]
+    if not y_zero:
+        return wl
+    return dataclasses.replace(wl, y={n: np.zeros_like(v) for n, v in wl.y.items()})

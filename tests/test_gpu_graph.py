@@ -169,3 +169,49 @@ def test_load_during_capture_is_rejected():
     S.sync_loads()
     assert S.stats()["loads"] == len([a for a in wl.adapters if a is not None]) + 1
     S.close()
+
+
+def test_reload_between_replays_follows_the_replay_contract():
+    """A slot reloaded between two replays, under the rules the header states
+    (no replay in flight at the load; lora_sync_loads before the next replay),
+    with an adapter of the same rank, lora_alpha and target modules: the first
+    replay gives the old adapter's update, the second the new one's, each
+    checked against the oracle."""
+    wl = _case(300, 9400)
+    log("case reload between replays")
+    S = make_slots(wl)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in MODS]
+    y0 = [to_dev(wl.y[m.name], wl.dtype) for m in MODS]
+    yg = [y.clone() for y in y0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _steps(S, idx, xs, yg)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()                     # rule 1: no replay in flight at the load
+    for mi, m in enumerate(MODS):
+        check_close(from_dev(yg[mi], wl.dtype), run_oracle(wl, m.name), wl.dtype,
+                    f"replay before reload {m.name}")
+    # a new adapter for slot 0: same rank, lora_alpha and targets, other weights
+    old = wl.adapters[0]
+    new = _case(8, 9401).adapters[0]
+    assert new.r == old.r and set(new.At) == set(old.At)
+    keep = [to_pinned(new.At[m.name], wl.dtype) for m in MODS] + \
+           [to_pinned(new.B[m.name], wl.dtype) for m in MODS]
+    S.load(0, keep[:3], keep[3:], new.r, old.lora_alpha, old.use_rslora)
+    S.sync_loads()                               # rule 2: the load is complete before the replay
+    for mi in range(len(MODS)):
+        yg[mi].copy_(y0[mi])
+    g.replay()
+    torch.cuda.synchronize()
+    new.lora_alpha, new.use_rslora = old.lora_alpha, old.use_rslora
+    wl.adapters[0] = new
+    for mi, m in enumerate(MODS):
+        got = from_dev(yg[mi], wl.dtype)
+        check_close(got, run_oracle(wl, m.name), wl.dtype, f"replay after reload {m.name}")
+        on0 = wl.idx == 0
+        assert on0.any()
+    S.close()
