@@ -303,6 +303,26 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
                      void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
                      void *stream);
 
+/*
+ * lora_apply_group for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The batch's plan and its fp32 h partials live in the library's static
+ * scratch array (LORA_NOALLOC_SCRATCH_BYTES on each device, a __device__ array
+ * whose address lora_slots_create looks up once per device) instead of the
+ * ctx's buffers; the ctx's prepared plan is neither used nor changed, and no
+ * device memory is allocated.  Same arguments, results, ordering and errors as
+ * lora_apply_group, except that a batch whose plan and partials do not fit the
+ * array (about 4 * n * n_tokens * R bytes of partials, R = max_rank rounded up
+ * to 16, plus the plan) returns LORA_ERR_TOO_MANY_TOKENS before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that overlap on one GPU (on other streams, from
+ * other ctxs or host threads) race, and the caller must order them.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int lora_apply_group_noalloc(lora_ctx *ctx, int32_t n, const int32_t *modules,
+                             const void *const *x, void *const *y,
+                             const int32_t *token_slot_idx, int32_t n_tokens, void *stream);
+
 /* Wait for the streams the ctx has launched on (not for the whole device),
  * return the sticky LORA_FLAG_* bits in *flags and clear them. */
 int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags);

@@ -41,6 +41,7 @@ EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_sl
            "lora_sync_loads", "lora_plan_prepare", "lora_plan_prepare_slots", "lora_shrink",
            "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
+           "lora_apply_group_noalloc",
            "lora_get_device_flags", "lora_get_stats", "lora_profile_begin", "lora_profile_end",
            "lora_status_string", "lora_last_error")
 
@@ -99,6 +100,8 @@ def load_library(path: str = LIB_PATH):
         "lora_expand_group": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P), P], ctypes.c_int),
         "lora_apply_group": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(P),
                               P, I32, P], ctypes.c_int),
+        "lora_apply_group_noalloc": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P),
+                                      ctypes.POINTER(P), P, I32, P], ctypes.c_int),
         "lora_get_device_flags": ([P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
         "lora_get_stats": ([P, ctypes.POINTER(_Stats)], ctypes.c_int),
         "lora_profile_begin": ([P, I32], ctypes.c_int),
@@ -303,6 +306,21 @@ def lora_apply_group(ctx, modules: Sequence[int], x: Sequence, y: Sequence, toke
                                            int(n_tokens), _stream(stream)), ctx)
 
 
+def lora_apply_group_noalloc(ctx, modules: Sequence[int], x: Sequence, y: Sequence,
+                             token_slot_idx, n_tokens: Optional[int] = None, stream=None) -> None:
+    """lora_apply_group with the batch's plan and partials in the library's static
+    scratch array (no device memory is allocated)."""
+    import torch
+    if n_tokens is None:
+        n_tokens = token_slot_idx.numel() if token_slot_idx is not None else 0
+    if n_tokens:
+        _require_cuda(token_slot_idx, "token_slot_idx", torch.int32, n_tokens)
+    n, mods, xp = _group(modules, x, "x")
+    _, _, yp = _group(modules, y, "y")
+    _check(load_library().lora_apply_group_noalloc(ctx, n, mods, xp, yp, _ptr(token_slot_idx),
+                                                   int(n_tokens), _stream(stream)), ctx)
+
+
 def lora_get_device_flags(ctx) -> int:
     v = ctypes.c_uint32(0)
     _check(load_library().lora_get_device_flags(ctx, ctypes.byref(v)), ctx)
@@ -378,6 +396,9 @@ class Slots:
 
     def apply_group(self, modules, x, y, idx, n_tokens=None, stream=None):
         lora_apply_group(self.ctx, modules, x, y, idx, n_tokens, stream)
+
+    def apply_group_noalloc(self, modules, x, y, idx, n_tokens=None, stream=None):
+        lora_apply_group_noalloc(self.ctx, modules, x, y, idx, n_tokens, stream)
 
     def bind_step(self, groups, idx, stream=None, prepare=True):
         """One step with its arguments marshalled once: lora_plan_prepare of idx

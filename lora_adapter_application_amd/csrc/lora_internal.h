@@ -171,4 +171,14 @@ struct FinalizeBatch {
 };
 hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st);
 
+// Scratch memory of lora_apply_group_noalloc: a static __device__ array of
+// this size in the library's code object, so each device the library runs on
+// holds one copy until the process ends.  It takes one batch's plan buffers and
+// h partials in place of the ctx's own allocation.
+constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
+// Device address of the scratch array on `device`, which must be the current
+// device: looked up with hipGetSymbolAddress at the first call for the device,
+// then kept.
+hipError_t scratch_address(int device, void **ptr);
+
 }  // namespace lora

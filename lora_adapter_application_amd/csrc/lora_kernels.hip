@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lora_internal.h"
 
 namespace lora {
@@ -1628,6 +1630,36 @@ __global__ void slot_finalize_kernel(FinalizeBatch fb)
         for (int64_t o = first; o < n16; o += stride)
             ((uint4 *)it.dora_dst)[o] = ((const uint4 *)it.dora_src)[o];
     }
+}
+
+// ----------------------------------------------------------------------------
+// static scratch of the calls that allocate nothing
+
+// One batch's plan buffers and h partials for lora_apply_group_noalloc.  The
+// host never uses this name as an address: it is a host-side stand-in.  The
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(int device, void **ptr)
+{
+    if (device < 0 || device >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
 }
 
 hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st)

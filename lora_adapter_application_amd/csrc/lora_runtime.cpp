@@ -67,6 +67,27 @@ struct DeviceGuard {
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Where one batch's plan and h partials live: the ctx's own allocation, or the
+// library's static scratch array (lora_apply_group_noalloc).
+struct Workspace {
+    PlanBuffers plan{};
+    float *hpart = nullptr;
+    int hbuf_rows = 0;       // rows of one group member's block of h partials
+};
+
+// The plan of the current batch, and the module list of the last shrink (which
+// the expand must repeat).
+struct BatchState {
+    bool hinted = false;     // the batch declared its slots (lora_plan_prepare_slots)
+    int plan_mode = kPlanTiles;   // PlanMode of the next bf16 launch on this plan
+    int tile_cap = kTileTokens;   // tokens per tile of the plan
+    const int32_t *idx = nullptr;
+    int32_t T = 0;
+    int last_n = 0;
+    int last_modules[kMaxGroup] = {};
+    int last_splits[kMaxGroup] = {};
+};
+
 }  // namespace
 
 struct lora_ctx {
@@ -84,16 +105,14 @@ struct lora_ctx {
     std::vector<float> scale_host;
     void *stage = nullptr;                   // A^T and B staging for the modules of one load
     int64_t stage_elems = 0;
-    float *hpart = nullptr;
-    int hbuf_rows = 0;
-    PlanBuffers plan{};
+    Workspace ws;                            // the ctx's plan buffers and h partials
     int max_tiles = 0;
+    void *scratch = nullptr;                 // this device's static scratch array (no-alloc calls)
     hipStream_t side = nullptr;
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
     uint64_t synced_gen = 0;                 // loads the host has seen complete (lora_sync_loads)
-    // slots the prepared plan reads (lora_plan_prepare_slots); else every slot
-    bool plan_hinted = false;
+    // slots the prepared plan reads (lora_plan_prepare_slots, bs.hinted); else every slot
     std::vector<uint8_t> hint;               // [S]
     // per slot, the number of the last use event recorded after a launch of a
     // declared plan that reads it (0: none since the slot's last load)
@@ -102,17 +121,11 @@ struct lora_ctx {
     hipEvent_t use_ev[kUseEvents] = {};
     uint64_t use_seq = 0;
     std::vector<StreamState> streams;
-    // plan state; an inline plan is computed by every shrink launch itself
+    // plan state of the ctx's workspace; an inline plan is computed by the
+    // first shrink launch itself
     bool plan_valid = false, plan_prepared = false;
-    int plan_mode = kPlanTiles;  // PlanMode of the next bf16 launch on this plan
-    int plan_tile_cap = kTileTokens;  // tokens per tile of the current plan
+    BatchState bs;
     uint64_t slot_epoch = 0, shrink_epoch = 0;   // loads + clears, and their count at the last shrink
-    const int32_t *plan_idx = nullptr;
-    int32_t plan_T = 0;
-    // last shrink group, consumed by expand
-    int last_n = 0;
-    int last_modules[kMaxGroup] = {};
-    int last_splits[kMaxGroup] = {};
     lora_stats stats{};
     // kernel timing (lora_profile_begin / lora_profile_end)
     bool profiling = false;
@@ -182,7 +195,7 @@ bool stream_capturing(hipStream_t s)
 // lora_sync_loads) before a capture starts.
 // reads_slots: the launch reads slot data (shrink, expand); plan kernels read
 // only the slot indices, so a later load need not wait for them.
-int before_launch(lora_ctx *c, hipStream_t s, bool reads_slots = true)
+int before_launch(lora_ctx *c, hipStream_t s, bool reads_slots, bool hinted)
 {
     StreamState *st = stream_state(c, s);
     if (!st)
@@ -197,16 +210,16 @@ int before_launch(lora_ctx *c, hipStream_t s, bool reads_slots = true)
     }
     // a launch of a declared plan is fenced per slot (after its expand), except
     // under capture, where no event is recorded
-    if (reads_slots && (!c->plan_hinted || stream_capturing(s)))
+    if (reads_slots && (!hinted || stream_capturing(s)))
         st->used_since_load = true;
     st->since_fence = true;
     return LORA_OK;
 }
 
 // After an expand of a declared plan: one event, the last use of every declared slot.
-int record_slot_use(lora_ctx *c, hipStream_t s)
+int record_slot_use(lora_ctx *c, hipStream_t s, bool hinted)
 {
-    if (!c->plan_hinted || stream_capturing(s))
+    if (!hinted || stream_capturing(s))
         return LORA_OK;
     const uint64_t seq = ++c->use_seq;
     hipEvent_t &ev = c->use_ev[seq % lora_ctx::kUseEvents];
@@ -320,13 +333,14 @@ hipError_t sync_ctx_streams(lora_ctx *c)
 
 // K-split of the shrink for a batch of T tokens: enough workgroups to cover
 // the chip when the batch is small, none when it is large.
-void choose_splits(const lora_ctx *c, int T, int d_in, int *splits, int *kchunk)
+void choose_splits(const lora_ctx *c, const Workspace &ws, const BatchState &bs, int T, int d_in,
+                   int *splits, int *kchunk)
 {
-    const int tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
+    const int tiles = max_tiles_for(T, c->S, bs.tile_cap);
     int want = ceil_div(1024, std::max(tiles, 1));
     int cap = std::min(kMaxSplits, std::max(1, d_in / 256));
     cap = std::min(cap, splits_cap(nb_template(c->R_pad)));
-    cap = std::min(cap, std::max(1, c->hbuf_rows / std::max(T, 1)));
+    cap = std::min(cap, std::max(1, ws.hbuf_rows / std::max(T, 1)));
     int sp = std::max(1, std::min(want, cap));
     int kc = round_up(ceil_div(d_in, sp), kShrinkKBlock);
     *kchunk = kc;
@@ -351,12 +365,12 @@ LaunchTiming next_timing(lora_ctx *c, int kind, hipStream_t s)
     return c->prof_events[c->prof_used++];
 }
 
-SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
+SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules, bool hinted)
 {
     SlotMeta m;
     std::memset(&m, 0, sizeof m);
     for (int k = 0; k < c->S; ++k) {
-        const bool readable = !c->plan_hinted || c->hint[k];
+        const bool readable = !hinted || c->hint[k];
         m.scale[k] = c->scale_host[k];
         m.rank[k] = readable ? (uint8_t)c->slot_rank[k] : 0;
         m.flags[k] = readable ? c->slot_flags[k] : 0;
@@ -364,42 +378,43 @@ SlotMeta group_meta(const lora_ctx *c, int n, const int32_t *modules)
     for (int i = 0; i < n; ++i) {
         const int32_t *r = c->rank_host.data() + (size_t)modules[i] * c->S;
         for (int k = 0; k < c->S; ++k)
-            if (r[k] > 0 && (!c->plan_hinted || c->hint[k]))
+            if (r[k] > 0 && (!hinted || c->hint[k]))
                 m.target[i][k >> 5] |= 1u << (k & 31);
     }
     return m;
 }
 
-int run_plan(lora_ctx *c, const int32_t *idx, int32_t T, hipStream_t s)
+int run_plan(lora_ctx *c, const Workspace &ws, BatchState &bs, const int32_t *idx, int32_t T,
+             hipStream_t s)
 {
-    c->plan_hinted = false;
-    c->plan_mode = c->dtype == LORA_BF16 && T <= kInlinePlanTokens ? kPlanInline : kPlanTiles;
-    c->plan_tile_cap = c->plan_mode == kPlanInline ? inline_tile_tokens(c->R_pad) : kTileTokens;
-    if (T > 0 && c->plan_mode == kPlanTiles) {
-        int rc = before_launch(c, s, false);
+    bs.hinted = false;
+    bs.plan_mode = c->dtype == LORA_BF16 && T <= kInlinePlanTokens ? kPlanInline : kPlanTiles;
+    bs.tile_cap = bs.plan_mode == kPlanInline ? inline_tile_tokens(c->R_pad) : kTileTokens;
+    if (T > 0 && bs.plan_mode == kPlanTiles) {
+        int rc = before_launch(c, s, false, false);
         if (rc)
             return rc;
         LaunchTiming t[2];
         t[0] = next_timing(c, PROF_PLAN, s);
         if (T > 1024)
             t[1] = next_timing(c, PROF_PLAN, s);
-        HIP_TRY(c, launch_plan(idx, T, c->S, c->plan, s, t));
+        HIP_TRY(c, launch_plan(idx, T, c->S, ws.plan, s, t));
     }
     if (T > 0)
         c->stats.plans += 1;
     c->stats.tokens += T;
-    c->plan_valid = true;
-    c->plan_idx = idx;
-    c->plan_T = T;
-    c->last_n = 0;
+    bs.idx = idx;
+    bs.T = T;
+    bs.last_n = 0;
     return LORA_OK;
 }
 
 // Launch arguments of a shrink of the planned batch for a group of modules
 // (records the K-splits for the expand that follows).
-ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *const *x)
+ShrinkArgs shrink_args(lora_ctx *c, const Workspace &ws, BatchState &bs, int n,
+                       const int32_t *modules, const void *const *x)
 {
-    const int T = c->plan_T;
+    const int T = bs.T;
     ShrinkArgs a;
     std::memset(&a, 0, sizeof a);
     a.n = n;
@@ -408,7 +423,7 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
         const int mod = modules[i];
         const lora_module_shape sh = c->shapes[mod];
         int splits = 1, kchunk = 0;
-        choose_splits(c, T, sh.d_in, &splits, &kchunk);
+        choose_splits(c, ws, bs, T, sh.d_in, &splits, &kchunk);
         a.x[i] = x[i];
         a.A[i] = c->A[mod];
         a.slot_stride_A[i] = c->strideA[mod];
@@ -416,19 +431,19 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
         a.k_chunk[i] = kchunk;
         a.splits[i] = splits;
         a.grid_splits = std::max(a.grid_splits, splits);
-        c->last_splits[i] = splits;
+        bs.last_splits[i] = splits;
     }
-    a.plan = c->plan;
-    a.idx = c->plan_idx;
+    a.plan = ws.plan;
+    a.idx = bs.idx;
     a.T = T;
     a.S = c->S;
-    a.plan_mode = c->plan_mode;
-    a.hpart = c->hpart;
-    a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
+    a.plan_mode = bs.plan_mode;
+    a.hpart = ws.hpart;
+    a.member_stride = (int64_t)ws.hbuf_rows * c->R_pad;
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
-    a.grid_tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
-    a.tile_cap = c->plan_tile_cap;
+    a.grid_tiles = max_tiles_for(T, c->S, bs.tile_cap);
+    a.tile_cap = bs.tile_cap;
     a.mixed = T > 1024;
     // A small batch with a multiple of 8 K-splits runs every tile of one split
     // on one XCD: its workgroups warm that split's x block (all tokens) and,
@@ -449,9 +464,10 @@ ShrinkArgs shrink_args(lora_ctx *c, int n, const int32_t *modules, const void *c
 }
 
 // Launch arguments of the expand matching the last shrink_args.
-ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *y)
+ExpandArgs expand_args(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
+                       const int32_t *modules, void *const *y)
 {
-    const int T = c->plan_T;
+    const int T = bs.T;
     ExpandArgs a;
     std::memset(&a, 0, sizeof a);
     a.n = n;
@@ -465,18 +481,18 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
         a.dora[i] = c->dora[mod];
         a.slot_stride_B[i] = c->strideB[mod];
         a.d_out[i] = sh.d_out;
-        a.splits[i] = c->last_splits[i];
+        a.splits[i] = bs.last_splits[i];
         a.grid_cols = std::max(a.grid_cols, ceil_div(sh.d_out, kExpandCols));
         a.col_start[i + 1] = a.col_start[i] + ceil_div(sh.d_out, kExpandCols);
     }
-    a.tiles = c->plan.tiles;
-    a.tile_tok = c->plan.tile_tok;
-    a.n_tiles = c->plan.n_tiles;
-    a.hpart = c->hpart;
-    a.member_stride = (int64_t)c->hbuf_rows * c->R_pad;
+    a.tiles = ws.plan.tiles;
+    a.tile_tok = ws.plan.tile_tok;
+    a.n_tiles = ws.plan.n_tiles;
+    a.hpart = ws.hpart;
+    a.member_stride = (int64_t)ws.hbuf_rows * c->R_pad;
     a.split_stride = (int64_t)T * c->R_pad;
     a.R_pad = c->R_pad;
-    a.grid_tiles = max_tiles_for(T, c->S, c->plan_tile_cap);
+    a.grid_tiles = max_tiles_for(T, c->S, bs.tile_cap);
     // large batches: one contiguous run of items per XCD.  With long slot
     // segments (prefill) the run is tile-major, every column chunk of a tile on
     // one XCD: the tile's h comes from HBM once and consecutive tiles of a slot
@@ -486,48 +502,50 @@ ExpandArgs expand_args(lora_ctx *c, int n, const int32_t *modules, void *const *
     const int64_t items = (int64_t)a.grid_tiles * a.col_start[n];
     const bool large = T > kInlinePlanTokens;
     a.tile_major = large && T >= 128 * c->S;
-    a.tile_cap = c->plan_tile_cap;
+    a.tile_cap = bs.tile_cap;
     a.xcd_group = large ? (int)((items + 7) / 8) : 1;
     a.terms = 0;
     for (int k = 0; k < c->S; ++k)
-        if (c->slot_flags[k] && (!c->plan_hinted || c->hint[k]))
+        if (c->slot_flags[k] && (!bs.hinted || c->hint[k]))
             a.terms = 1;
     return a;
 }
 
-int run_shrink(lora_ctx *c, int n, const int32_t *modules, const void *const *x, hipStream_t s)
+int run_shrink(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const int32_t *modules,
+               const void *const *x, hipStream_t s)
 {
-    const int T = c->plan_T;
+    const int T = bs.T;
     if (T > 0) {
-        int rc = before_launch(c, s);
+        int rc = before_launch(c, s, true, bs.hinted);
         if (rc)
             return rc;
-        const ShrinkArgs a = shrink_args(c, n, modules, x);
-        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
+        const ShrinkArgs a = shrink_args(c, ws, bs, n, modules, x);
+        HIP_TRY(c, launch_shrink(c->dtype == LORA_BF16, a, group_meta(c, n, modules, bs.hinted), s,
                                  next_timing(c, PROF_SHRINK, s)));
-        if (c->plan_mode == kPlanInline)
-            c->plan_mode = kPlanTiles;   // later launches read the plan this one published
+        if (bs.plan_mode == kPlanInline)
+            bs.plan_mode = kPlanTiles;   // later launches read the plan this one published
         c->stats.shrinks += n;
     }
-    c->last_n = n;
+    bs.last_n = n;
     c->shrink_epoch = c->slot_epoch;
     for (int i = 0; i < n; ++i)
-        c->last_modules[i] = modules[i];
+        bs.last_modules[i] = modules[i];
     return LORA_OK;
 }
 
-int run_expand(lora_ctx *c, int n, const int32_t *modules, void *const *y, hipStream_t s)
+int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
+               const int32_t *modules, void *const *y, hipStream_t s)
 {
-    const int T = c->plan_T;
+    const int T = bs.T;
     if (T > 0) {
-        int rc = before_launch(c, s);
+        int rc = before_launch(c, s, true, bs.hinted);
         if (rc)
             return rc;
-        const ExpandArgs a = expand_args(c, n, modules, y);
-        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules), s,
+        const ExpandArgs a = expand_args(c, ws, bs, n, modules, y);
+        HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules, bs.hinted), s,
                                  next_timing(c, PROF_EXPAND, s)));
         c->stats.expands += n;
-        int rc2 = record_slot_use(c, s);
+        int rc2 = record_slot_use(c, s, bs.hinted);
         if (rc2)
             return rc2;
     }
@@ -559,6 +577,39 @@ int check_ptrs(lora_ctx *c, int32_t n, const void *const *p, const char *what, b
                                 what, j, what, i);
     }
     return LORA_OK;
+}
+
+// One batch's workspace carved out of this device's scratch array: the plan
+// buffers first, the rest for the h partials of n group members.  The flags
+// word stays the ctx's own.  *need is the bytes the batch takes; false when
+// they exceed the array.
+bool scratch_workspace(const lora_ctx *c, int T, int n, Workspace *ws, size_t *need)
+{
+    char *base = (char *)c->scratch;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base + off;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    const int tiles = std::max(max_tiles_for(T, c->S),
+                               max_tiles_for(std::min(T, (int)kInlinePlanTokens), c->S,
+                                             inline_tile_tokens(c->R_pad)));
+    ws->plan.counts = (int32_t *)take(sizeof(int32_t) * (size_t)c->S);
+    ws->plan.seg_start = (int32_t *)take(sizeof(int32_t) * (size_t)c->S);
+    ws->plan.tiles = (Tile *)take(sizeof(Tile) * (size_t)tiles);
+    ws->plan.tile_tok = (int32_t *)take(sizeof(int32_t) * (size_t)tiles * kTileTokens);
+    ws->plan.n_tiles = (int32_t *)take(sizeof(int32_t));
+    ws->plan.n_active = (int32_t *)take(sizeof(int32_t));
+    ws->plan.chunk_counts = (int32_t *)take(sizeof(int32_t) * (size_t)ceil_div(T, 1024) * c->S);
+    ws->plan.flags = c->ws.plan.flags;
+    const size_t row = sizeof(float) * (size_t)c->R_pad * n;    // one token's h, all members
+    *need = off + row * (size_t)T;
+    if (*need > kScratchBytes)
+        return false;
+    ws->hpart = (float *)(base + off);
+    ws->hbuf_rows = (int)((kScratchBytes - off) / row);
+    return true;
 }
 
 }  // namespace
@@ -664,7 +715,7 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
         c->strideB.push_back(sb);
         max_out = std::max(max_out, sh.d_out);
     }
-    c->hbuf_rows = std::max(max_tokens, 16384);
+    c->ws.hbuf_rows = std::max(max_tokens, 16384);
     c->slot_rank.assign(max_loras, 0);
     c->slot_flags.assign(max_loras, 0);
     c->hint.assign(max_loras, 0);
@@ -684,19 +735,22 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
                                                          (64ll << 20) / c->elem));
     if (e == hipSuccess) e = dalloc(c, &c->stage, (size_t)c->stage_elems * c->elem);
     if (e == hipSuccess)
-        e = dalloc(c, &c->hpart, sizeof(float) * (size_t)kMaxGroup * c->hbuf_rows * c->R_pad);
-    if (e == hipSuccess) e = dalloc(c, &c->plan.counts, sizeof(int32_t) * (size_t)max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->plan.seg_start, sizeof(int32_t) * (size_t)max_loras);
-    if (e == hipSuccess) e = dalloc(c, &c->plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
+        e = dalloc(c, &c->ws.hpart, sizeof(float) * (size_t)kMaxGroup * c->ws.hbuf_rows * c->R_pad);
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.counts, sizeof(int32_t) * (size_t)max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.seg_start, sizeof(int32_t) * (size_t)max_loras);
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
     if (e == hipSuccess)
-        e = dalloc(c, &c->plan.tile_tok, sizeof(int32_t) * (size_t)c->max_tiles * kTileTokens);
-    if (e == hipSuccess) e = dalloc(c, &c->plan.n_tiles, sizeof(int32_t));
-    if (e == hipSuccess) e = dalloc(c, &c->plan.n_active, sizeof(int32_t));
-    if (e == hipSuccess) e = dalloc(c, &c->plan.flags, sizeof(uint32_t));
+        e = dalloc(c, &c->ws.plan.tile_tok, sizeof(int32_t) * (size_t)c->max_tiles * kTileTokens);
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_tiles, sizeof(int32_t));
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_active, sizeof(int32_t));
+    if (e == hipSuccess) e = dalloc(c, &c->ws.plan.flags, sizeof(uint32_t));
     if (e == hipSuccess)
-        e = dalloc(c, &c->plan.chunk_counts,
+        e = dalloc(c, &c->ws.plan.chunk_counts,
                    sizeof(int32_t) * (size_t)ceil_div(max_tokens, 1024) * max_loras);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->load_done, hipEventDisableTiming);
+    // this device's static scratch array (lora_apply_group_noalloc), looked up
+    // once per device with the device current
+    if (e == hipSuccess) e = scratch_address(device, &c->scratch);
     if (e == hipSuccess) e = hipStreamSynchronize(c->side);
     if (e != hipSuccess) {
         int status = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
@@ -953,12 +1007,12 @@ int lora_plan_prepare(lora_ctx *ctx, const int32_t *token_slot_idx, int32_t n_to
     if (n_tokens > 0 && !token_slot_idx)
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "token_slot_idx is NULL");
     DeviceGuard guard(ctx->device);
-    int rc = run_plan(ctx, token_slot_idx, n_tokens, (hipStream_t)stream);
+    int rc = run_plan(ctx, ctx->ws, ctx->bs, token_slot_idx, n_tokens, (hipStream_t)stream);
     if (rc) {
         ctx->plan_valid = ctx->plan_prepared = false;
         return rc;
     }
-    ctx->plan_prepared = true;
+    ctx->plan_valid = ctx->plan_prepared = true;
     return LORA_OK;
 }
 
@@ -981,7 +1035,7 @@ int lora_plan_prepare_slots(lora_ctx *ctx, const int32_t *token_slot_idx, int32_
     std::fill(ctx->hint.begin(), ctx->hint.end(), 0);
     for (int i = 0; i < n_used; ++i)
         ctx->hint[used_slots[i]] = 1;
-    ctx->plan_hinted = true;
+    ctx->bs.hinted = true;
     return LORA_OK;
 }
 
@@ -996,10 +1050,10 @@ int lora_shrink_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const vo
         return rc;
     if (!ctx->plan_valid)
         return fail(ctx, LORA_ERR_NO_PLAN, "lora_shrink needs a prepared plan");
-    if (ctx->plan_T > 0 && (rc = check_ptrs(ctx, n, x, "x", false)))
+    if (ctx->bs.T > 0 && (rc = check_ptrs(ctx, n, x, "x", false)))
         return rc;
     DeviceGuard guard(ctx->device);
-    return run_shrink(ctx, n, modules, x, (hipStream_t)stream);
+    return run_shrink(ctx, ctx->ws, ctx->bs, n, modules, x, (hipStream_t)stream);
 }
 
 int lora_expand_group(lora_ctx *ctx, int32_t n, const int32_t *modules, void *const *y,
@@ -1013,19 +1067,19 @@ int lora_expand_group(lora_ctx *ctx, int32_t n, const int32_t *modules, void *co
         return rc;
     if (!ctx->plan_valid)
         return fail(ctx, LORA_ERR_NO_PLAN, "lora_expand needs a prepared plan");
-    bool same = ctx->last_n == n;
+    bool same = ctx->bs.last_n == n;
     for (int i = 0; same && i < n; ++i)
-        same = ctx->last_modules[i] == modules[i];
+        same = ctx->bs.last_modules[i] == modules[i];
     if (!same)
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
                     "lora_expand must follow lora_shrink of the same module list");
     if (ctx->shrink_epoch != ctx->slot_epoch)
         return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
                     "a slot was loaded or cleared between lora_shrink and lora_expand");
-    if (ctx->plan_T > 0 && (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
+    if (ctx->bs.T > 0 && (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
         return rc;
     DeviceGuard guard(ctx->device);
-    return run_expand(ctx, n, modules, y, (hipStream_t)stream);
+    return run_expand(ctx, ctx->ws, ctx->bs, n, modules, y, (hipStream_t)stream);
 }
 
 int lora_shrink(lora_ctx *ctx, const void *x, int32_t module, void *stream)
@@ -1062,25 +1116,68 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
         return rc;
     DeviceGuard guard(ctx->device);
     hipStream_t s = (hipStream_t)stream;
-    if (!(ctx->plan_valid && ctx->plan_prepared && ctx->plan_idx == token_slot_idx &&
-          ctx->plan_T == n_tokens)) {
+    if (!(ctx->plan_valid && ctx->plan_prepared && ctx->bs.idx == token_slot_idx &&
+          ctx->bs.T == n_tokens)) {
         ctx->plan_prepared = false;
-        rc = run_plan(ctx, token_slot_idx, n_tokens, s);
+        rc = run_plan(ctx, ctx->ws, ctx->bs, token_slot_idx, n_tokens, s);
         if (rc) {
             ctx->plan_valid = false;
             return rc;
         }
+        ctx->plan_valid = true;
     }
-    rc = run_shrink(ctx, n, modules, x, s);
+    rc = run_shrink(ctx, ctx->ws, ctx->bs, n, modules, x, s);
     if (rc)
         return rc;
-    return run_expand(ctx, n, modules, y, s);
+    return run_expand(ctx, ctx->ws, ctx->bs, n, modules, y, s);
 }
 
 int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,
                int32_t n_tokens, int32_t module, void *stream)
 {
     return lora_apply_group(ctx, 1, &module, &x, &y, token_slot_idx, n_tokens, stream);
+}
+
+int lora_apply_group_noalloc(lora_ctx *ctx, int32_t n, const int32_t *modules,
+                             const void *const *x, void *const *y,
+                             const int32_t *token_slot_idx, int32_t n_tokens, void *stream)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    int rc = check_group(ctx, n, modules);
+    if (rc)
+        return rc;
+    if (n_tokens < 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "n_tokens %d < 0", n_tokens);
+    if (n_tokens > ctx->max_tokens)
+        return fail(ctx, LORA_ERR_TOO_MANY_TOKENS, "n_tokens %d > max_tokens %d", n_tokens,
+                    ctx->max_tokens);
+    if (n_tokens == 0)
+        return LORA_OK;
+    if (!token_slot_idx)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "token_slot_idx is NULL");
+    if ((rc = check_ptrs(ctx, n, x, "x", false)) ||
+        (rc = check_ptrs(ctx, n, (const void *const *)y, "y", true)))
+        return rc;
+    Workspace ws;
+    size_t need = 0;
+    if (!scratch_workspace(ctx, n_tokens, n, &ws, &need))
+        return fail(ctx, LORA_ERR_TOO_MANY_TOKENS,
+                    "%d tokens x %d modules need %zu bytes of scratch; the static array holds %zu",
+                    n_tokens, n, need, (size_t)kScratchBytes);
+    DeviceGuard guard(ctx->device);
+    hipStream_t s = (hipStream_t)stream;
+    // a plan of its own, in the scratch array; the ctx's plan is left as it is
+    BatchState bs;
+    if ((rc = run_plan(ctx, ws, bs, token_slot_idx, n_tokens, s)))
+        return rc;
+    const uint64_t shrink_epoch = ctx->shrink_epoch;
+    rc = run_shrink(ctx, ws, bs, n, modules, x, s);
+    ctx->shrink_epoch = shrink_epoch;
+    if (rc)
+        return rc;
+    return run_expand(ctx, ws, bs, n, modules, y, s);
 }
 
 int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)
@@ -1091,9 +1188,9 @@ int lora_get_device_flags(lora_ctx *ctx, uint32_t *flags)
     // the kernels that set flags ran on the ctx's streams: wait for those
     // only, then read and clear the word in order on the side stream
     HIP_TRY(ctx, sync_ctx_streams(ctx));
-    HIP_TRY(ctx, hipMemcpyAsync(&ctx->flags_host, ctx->plan.flags, sizeof(uint32_t),
+    HIP_TRY(ctx, hipMemcpyAsync(&ctx->flags_host, ctx->ws.plan.flags, sizeof(uint32_t),
                                 hipMemcpyDeviceToHost, ctx->side));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->plan.flags, 0, sizeof(uint32_t), ctx->side));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->ws.plan.flags, 0, sizeof(uint32_t), ctx->side));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->side));
     *flags = ctx->flags_host;
     return LORA_OK;
