@@ -72,6 +72,9 @@ def _load():
     lib.lora_oracle_apply_ex.restype = ctypes.c_int64
     lib.lora_oracle_apply_ex.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3 + [
         ctypes.c_int32] + [ctypes.c_void_p] * 7 + [ctypes.c_int32]
+    lib.lora_oracle_apply_saved.restype = ctypes.c_int64
+    lib.lora_oracle_apply_saved.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3 + [
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
     lib.lora_oracle_max_threads.restype = ctypes.c_int32
     lib.lora_oracle_max_threads.argtypes = []
     _lib = lib
@@ -172,5 +175,47 @@ def apply(dtype: int, x: np.ndarray, y: np.ndarray, idx: np.ndarray,
                               idx.ctypes.data, n, rank.ctypes.data, alpha.ctypes.data,
                               rs.ctypes.data, ctypes.cast(At_ptrs, ctypes.c_void_p),
                               ctypes.cast(B_ptrs, ctypes.c_void_p), int(n_threads))
+    del keep
+    return out
+
+
+def apply_saved(dtype: int, x: np.ndarray, y: np.ndarray, idx: np.ndarray,
+                saved: Sequence[Optional[dict]], n_threads: int = 0) -> np.ndarray:
+    """Return y after the saved modules ("modules_to_save") replace the base
+    output of their adapters' tokens; y itself is not modified.
+
+    saved  one entry per slot (or adapter id): None when it saves no copy of this
+           module, else a dict with ``W`` (d_out x d_in, the data dtype) and
+           optionally ``bias`` (d_out values): y[t] <- round(x[t] . W^T + bias)
+    """
+    lib = _load()
+    elem = np.uint16 if dtype == BF16 else np.float32
+    x = np.ascontiguousarray(x, dtype=elem)
+    out = np.array(y, dtype=elem, copy=True, order="C")
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, d_in = x.shape
+    d_out = out.shape[1]
+    assert out.shape[0] == T and idx.shape == (T,)
+    n = len(saved)
+    W_ptrs = (ctypes.c_void_p * max(n, 1))()
+    c_ptrs = (ctypes.c_void_p * max(n, 1))()
+    keep = []
+    for k, e in enumerate(saved):
+        if e is None:
+            continue
+        W = np.ascontiguousarray(e["W"], dtype=elem)
+        assert W.shape == (d_out, d_in), W.shape
+        W_ptrs[k] = W.ctypes.data
+        keep.append(W)
+        if e.get("bias") is not None:
+            c = np.ascontiguousarray(e["bias"], dtype=elem)
+            assert c.shape == (d_out,), c.shape
+            c_ptrs[k] = c.ctypes.data
+            keep.append(c)
+    if T == 0:
+        return out
+    lib.lora_oracle_apply_saved(dtype, T, d_in, d_out, x.ctypes.data, out.ctypes.data,
+                                idx.ctypes.data, n, ctypes.cast(W_ptrs, ctypes.c_void_p),
+                                ctypes.cast(c_ptrs, ctypes.c_void_p), int(n_threads))
     del keep
     return out

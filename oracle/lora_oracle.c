@@ -247,6 +247,55 @@ int64_t lora_oracle_apply_ex(int32_t dtype, int32_t n_tokens, int32_t d_in, int3
     return applied;
 }
 
+/*
+ * Whole modules an adapter saves ("modules_to_save" of the example
+ * adapter_config.json in "vLLM LoRA Resolver plugins explained", section 3.2;
+ * null in that example).  Such a module is a complete trained copy of the
+ * linear: for the adapter's tokens it takes the base module's place, so the
+ * output row is the saved module's own product and the base output the caller
+ * put in y is discarded:
+ *
+ *   y[t,n] <- round( sum_{i < d_in} x[t,i] * W_k[n,i]  +  c_k[n] )
+ *
+ *   W    [n_slots] pointers to d_out x d_in row-major weights (the layout of a
+ *        linear layer's weight: row n holds output feature n), NULL when slot k
+ *        saves no copy of this module
+ *   bias [n_slots] pointers to d_out values, or NULL (no bias); NULL array = none
+ * Tokens whose slot is out of range or saves no copy keep their row of y
+ * untouched.  The pages name the field and nothing more; this is the plain
+ * reading of it.  Same precision rules as lora_oracle_apply: double, ascending
+ * index order, no fused multiply-add, one rounding.
+ */
+int64_t lora_oracle_apply_saved(int32_t dtype, int32_t n_tokens, int32_t d_in, int32_t d_out,
+                                const void *x, void *y, const int32_t *idx, int32_t n_slots,
+                                const void *const *W, const void *const *bias, int32_t n_threads)
+{
+    int64_t applied = 0;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : applied)
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        int32_t k = idx[t];
+        if (k < 0 || k >= n_slots || W[k] == NULL)
+            continue;
+        for (int32_t n = 0; n < d_out; ++n) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < d_in; ++i)
+                acc = acc + load_elem(x, dtype, (int64_t)t * d_in + i) *
+                                load_elem(W[k], dtype, (int64_t)n * d_in + i);
+            if (bias && bias[k])
+                acc = acc + load_elem(bias[k], dtype, n);
+            store_elem(y, dtype, (int64_t)t * d_out + n, acc);
+        }
+        applied += 1;
+    }
+    return applied;
+}
+
 int32_t lora_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -491,3 +491,146 @@ def test_bias_matches_dense_merge_plus_bias(dtype):
     else:
         got = oracle.apply(oracle.FP32, x, y, idx, ext).astype(np.float64)
         np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# saved modules ("modules_to_save"): a whole copy of the linear replaces the
+# base output for its adapter's tokens
+
+def _saved(rng, n, d_in, d_out, which, bias=True, integer=False, dtype=oracle.FP32):
+    out = []
+    for k in range(n):
+        if k not in which:
+            out.append(None)
+            continue
+        if integer:
+            W = rng.integers(-2, 3, (d_out, d_in)).astype(np.float32)
+            c = rng.integers(-2, 3, d_out).astype(np.float32)
+        else:
+            W = _f32(rng.standard_normal((d_out, d_in)) * 0.1)
+            c = _f32(rng.standard_normal(d_out) * 0.1)
+        if dtype == oracle.BF16:
+            W, c = synth.to_bf16_bits(W), synth.to_bf16_bits(c)
+        out.append({"W": W, "bias": c if bias else None})
+    return out
+
+
+def _matmul_ref(x, idx, saved, y):
+    """numpy: rows of saved slots become x @ W^T + c (fp64); other rows stay y."""
+    out = np.asarray(y, np.float64).copy()
+    for k, e in enumerate(saved):
+        if e is None:
+            continue
+        rows = np.flatnonzero(idx == k)
+        W = np.asarray(e["W"], np.float64)
+        c = np.zeros(W.shape[0]) if e.get("bias") is None else np.asarray(e["bias"], np.float64)
+        out[rows] = np.asarray(x, np.float64)[rows] @ W.T + c
+    return out
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_saved_module_matches_numpy_matmul_fp32(bias):
+    rng = np.random.default_rng(71)
+    T, d_in, d_out = 40, 48, 24
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = rng.integers(-1, 5, T).astype(np.int32)
+    saved = _saved(rng, 4, d_in, d_out, which={0, 2, 3}, bias=bias)
+    got = oracle.apply_saved(oracle.FP32, x, y, idx, saved).astype(np.float64)
+    ref = _matmul_ref(x, idx, saved, y)
+    # one rounding of the fp64 result into fp32 (the sum orders differ in fp64 only)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-12 * (1 + np.abs(ref)))
+
+
+def test_saved_module_bf16_within_one_rounding_of_numpy():
+    rng = np.random.default_rng(72)
+    T, d_in, d_out = 33, 40, 16
+    x = synth.to_bf16_bits(_f32(rng.standard_normal((T, d_in))))
+    y = synth.to_bf16_bits(_f32(rng.standard_normal((T, d_out))))
+    idx = rng.integers(-1, 3, T).astype(np.int32)
+    saved = _saved(rng, 3, d_in, d_out, which={1, 2}, dtype=oracle.BF16)
+    got = synth.bf16_bits_to_f32(oracle.apply_saved(oracle.BF16, x, y, idx, saved)).astype(np.float64)
+    xf = synth.bf16_bits_to_f32(x)
+    sv = [None if e is None else {"W": synth.bf16_bits_to_f32(e["W"]),
+                                  "bias": synth.bf16_bits_to_f32(e["bias"])} for e in saved]
+    ref = _matmul_ref(xf, idx, sv, synth.bf16_bits_to_f32(y))
+    # half a bf16 ulp: |v| * 2^-8 bounds it from above
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-12)
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP32, oracle.BF16])
+def test_saved_module_exact_integers_bit_identical(dtype):
+    rng = np.random.default_rng(73)
+    T, d_in, d_out = 30, 16, 12            # |x W^T + c| <= 16*4 + 2: exact in bf16
+    x = rng.integers(-2, 3, (T, d_in)).astype(np.float32)
+    y = rng.integers(-2, 3, (T, d_out)).astype(np.float32)
+    idx = rng.integers(-2, 4, T).astype(np.int32)
+    saved = _saved(rng, 3, d_in, d_out, which={0, 2}, integer=True)
+    ref = _matmul_ref(x, idx, saved, y).astype(np.float32)
+    if dtype == oracle.BF16:
+        xb, yb = synth.to_bf16_bits(x), synth.to_bf16_bits(y)
+        sb = [None if e is None else {"W": synth.to_bf16_bits(e["W"]), "bias": synth.to_bf16_bits(e["bias"])}
+              for e in saved]
+        got = oracle.apply_saved(dtype, xb, yb, idx, sb)
+        assert np.array_equal(got, synth.to_bf16_bits(ref))
+    else:
+        got = oracle.apply_saved(dtype, x, y, idx, saved)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_saved_module_replaces_the_base_output():
+    """The saved copy takes the base module's place: the incoming y of its
+    tokens does not matter, and a zero copy gives zero rows."""
+    rng = np.random.default_rng(74)
+    T, d_in, d_out = 20, 8, 8
+    x = _f32(rng.standard_normal((T, d_in)))
+    idx = np.array([0, 1, -1, 0, 1] * 4, np.int32)
+    saved = _saved(rng, 2, d_in, d_out, which={0})
+    y1 = _f32(rng.standard_normal((T, d_out)))
+    y2 = _f32(rng.standard_normal((T, d_out)) * 100)
+    a = oracle.apply_saved(oracle.FP32, x, y1, idx, saved)
+    b = oracle.apply_saved(oracle.FP32, x, y2, idx, saved)
+    on = idx == 0
+    assert np.array_equal(a[on].view(np.uint32), b[on].view(np.uint32))
+    zero = [{"W": np.zeros((d_out, d_in), np.float32), "bias": None}, None]
+    z = oracle.apply_saved(oracle.FP32, x, y1, idx, zero)
+    assert np.all(z[on] == 0.0)
+    assert np.array_equal(z[~on].view(np.uint32), y1[~on].view(np.uint32))
+
+
+def test_saved_module_skips_rows_bit_identical():
+    rng = np.random.default_rng(75)
+    T, d_in, d_out = 24, 16, 8
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = np.array([-1, -7, 0, 1, 2, 3, 9, 1] * 3, np.int32)   # slot 1: no copy; 3, 9: out of range
+    saved = _saved(rng, 3, d_in, d_out, which={0, 2})
+    got = oracle.apply_saved(oracle.FP32, x, y, idx, saved)
+    keep = ~np.isin(idx, [0, 2])
+    assert np.array_equal(got[keep].view(np.uint32), y[keep].view(np.uint32))
+    assert not np.array_equal(got[~keep], y[~keep])
+
+
+def test_saved_identity_module_copies_x_plus_bias():
+    rng = np.random.default_rng(76)
+    T, d = 10, 16
+    x = _f32(rng.standard_normal((T, d)))
+    c = _f32(rng.standard_normal(d))
+    idx = np.zeros(T, np.int32)
+    got = oracle.apply_saved(oracle.FP32, x, np.zeros((T, d), np.float32), idx,
+                             [{"W": np.eye(d, dtype=np.float32), "bias": c}])
+    assert np.array_equal(got.view(np.uint32), (x + c).view(np.uint32))
+
+
+def test_saved_module_permutation_equivariant():
+    rng = np.random.default_rng(77)
+    T, d_in, d_out = 31, 24, 40
+    x = _f32(rng.standard_normal((T, d_in)))
+    y = _f32(rng.standard_normal((T, d_out)))
+    idx = rng.integers(-1, 4, T).astype(np.int32)
+    saved = _saved(rng, 4, d_in, d_out, which={0, 1, 3})
+    p = rng.permutation(T)
+    a = oracle.apply_saved(oracle.FP32, x, y, idx, saved)
+    b = oracle.apply_saved(oracle.FP32, x[p], y[p], idx[p], saved)
+    assert np.array_equal(a[p].view(np.uint32), b.view(np.uint32))
