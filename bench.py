@@ -41,6 +41,10 @@ cpu_baseline  the CPU oracle on the host cores over a bounded sample of the
            headline workload (rank 0, one GPU only): all threads, and one thread
            on a smaller sample; nproc and the CPU model
 
+saved_module  the saved-module product (modules_to_save) on the headline batch,
+           every adapter saving o_proj: the dense segmented GEMM on the matrix
+           cores, its TFLOP/s against the dense bf16 peak
+
 --workload churn [--prefetch] times adapter uploads with the applies instead
 (see churn and churn_prefetch below); its "h2d" carries the upload rate beside
 copy_GBps, back-to-back pinned copies of one adapter's size on the same link.
@@ -81,6 +85,8 @@ def parse():
                         "extra keys (empty: none)")
     p.add_argument("--extra-steps", type=int, default=2000)
     p.add_argument("--extra-warmup", type=int, default=200)
+    p.add_argument("--no-saved", dest="saved", action="store_false",
+                   help="skip the saved-module (modules_to_save) measurement on the headline batch")
     p.add_argument("--churn-steps", type=int, default=50)
     p.add_argument("--prefetch", action="store_true",
                    help="churn: upload the next step's misses while the current step computes "
@@ -445,6 +451,58 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
     return rec
 
 
+def measure_saved(wl, K, W):
+    """Saved modules ("modules_to_save") on the headline batch: every adapter also
+    saves a whole o_proj (4096 x 4096, random bf16 weights drawn on the device), so
+    the o_proj launch writes x . W_k^T for all tokens in place of the base output.
+    Only that module is applied; the saved-module kernel is timed with per-dispatch
+    events over K launches.  Algorithmic flops: 2 d_in d_out per token; bytes: x
+    read, y written, each used slot's W read once."""
+    import torch
+    from lora_adapter_application_amd import binding
+    dev = torch.device("cuda:0")
+    m = next(mm for mm in wl.modules if mm.name == "o_proj")
+    T = wl.n_tokens
+    S = binding.Slots(wl.max_loras, wl.max_rank, [(m.d_in, m.d_out)], "bf16", max_tokens=T)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260202)
+    keep = []
+    for k, ad in enumerate(wl.adapters):
+        S.load(k, [None], [None], ad.r, ad.lora_alpha, ad.use_rslora)   # saves o_proj only
+        Wk = (torch.randn(m.d_out, m.d_in, generator=gen, device=dev) / math.sqrt(m.d_in)).to(torch.bfloat16)
+        keep.append(Wk)
+        S.load_saved(k, 0, Wk)
+    S.sync_loads()
+    idx = torch.from_numpy(wl.idx).to(dev)
+    x = torch.from_numpy(np.ascontiguousarray(wl.x[m.name]).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.zeros(T, m.d_out, dtype=torch.bfloat16, device=dev)
+    S.prepare(idx)
+    for _ in range(W):
+        S.apply_group([0], [x], [y], idx)
+    torch.cuda.synchronize()
+    S.profile_begin(K * 4)
+    for _ in range(K):
+        S.apply_group([0], [x], [y], idx)
+    prof = S.profile_end()
+    S.close()
+    n = prof["launches"]["saved"]
+    us = prof["total_ms"]["saved"] / n * 1e3
+    used = np.unique(wl.idx[(wl.idx >= 0) & (wl.idx < wl.max_loras)])
+    flops = 2.0 * T * m.d_in * m.d_out
+    nbytes = 2.0 * (T * m.d_in + T * m.d_out + len(used) * m.d_in * m.d_out)
+    tfs = flops / (us * 1e-6) / 1e12
+    del keep, x, y
+    torch.cuda.empty_cache()
+    return {"workload": f"{wl.name} batch ({T} tokens), every adapter saving o_proj "
+                        f"{m.d_in}->{m.d_out}",
+            "kernel": "saved_bf16_kernel", "launches": n, "avg_launch_us": round(us, 2),
+            "alg_flops_per_launch": flops, "TFLOPs": round(tfs, 1),
+            "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
+            "alg_bytes_per_launch": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bound": "mfma"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -487,6 +545,10 @@ def main():
                         "config": e["config"], "roofline": e["roofline"],
                         "graph": e["graph"], "plan_amortized": e["plan_amortized"],
                         "step_spread": e["step_spread"]}
+    saved = None
+    if args.saved and rec["wl"].name == "llama7b_prefill" and not args.no_kernel_timing:
+        saved = measure_saved(rec["wl"], args.steps, args.warmup)
+        log("saved_module:", json.dumps(saved))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(rec["wl"], args.cpu_seconds)
@@ -515,6 +577,8 @@ def main():
     }
     for name, e in extras.items():
         out[name] = e
+    if saved is not None:
+        out["saved_module"] = saved
     print(json.dumps(out), flush=True)
 
 

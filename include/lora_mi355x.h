@@ -189,6 +189,35 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
                       const void *const *bias, const float *const *dora_scale, int32_t r,
                       double lora_alpha, int32_t use_rslora);
 
+/*
+ * Give the adapter in `slot` a whole trained copy of one module, the
+ * "modules_to_save" field of the example adapter_config.json in "vLLM LoRA
+ * Resolver plugins explained", section 3.2 (null in that example).  For every
+ * token of the slot, the launches of that module then write
+ *
+ *     y[t,n] = round( sum_i x[t,i] * W[n,i] + bias[n] )
+ *
+ * in place of the base output the caller put in y (the copy takes the base
+ * module's place).  Tokens of other slots are untouched.
+ *   module  the module index; the adapter in the slot must not target it with
+ *           its low-rank update (a module is either targeted or saved), else
+ *           LORA_ERR_INVALID_ARGUMENT
+ *   W       d_out x d_in, row-major (a linear layer's weight: row n is output
+ *           feature n), ctx dtype, pinned host or device memory
+ *   bias    d_out values of the ctx dtype, or NULL for none
+ * The slot must hold an adapter (lora_slot_load first), else
+ * LORA_ERR_INVALID_ARGUMENT; a later lora_slot_load or lora_slot_clear of the
+ * slot drops its saved modules.  Storage: the first saved load of a module
+ * allocates that module's pool for every slot (max_loras x d_out x (d_in + 1)
+ * elements; LORA_ERR_OUT_OF_MEMORY on failure).  The copy runs on the side
+ * stream with the ordering, memory rules and capture rule of lora_slot_load.
+ * lora_expand (and lora_apply) run the product after the low-rank update of
+ * the same call, reading the x given to the matching lora_shrink, which must
+ * therefore stay valid until the stream has passed the lora_expand.
+ */
+int lora_slot_load_saved(lora_ctx *ctx, int32_t slot, int32_t module, const void *W,
+                         const void *bias);
+
 /* Mark `slot` empty for every module.  Batches enqueued after this call skip
  * the slot; batches already enqueued still apply the adapter it held.  Host-only:
  * no device work is enqueued. */
@@ -339,8 +368,9 @@ int lora_get_stats(lora_ctx *ctx, lora_stats *out);
  * are created by lora_profile_begin, outside any timed region.
  */
 typedef struct {
-    int64_t launches[3];   /* [0] plan, [1] shrink, [2] expand dispatches timed */
-    double total_ms[3];    /* their summed kernel time, milliseconds */
+    int64_t launches[4];   /* [0] plan, [1] shrink, [2] expand, [3] saved-module
+                              product dispatches timed */
+    double total_ms[4];    /* their summed kernel time, milliseconds */
     int64_t untimed;       /* dispatches past max_launches (not timed) */
 } lora_profile;
 

@@ -37,7 +37,7 @@ LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_load_ex",
-           "lora_slot_clear",
+           "lora_slot_load_saved", "lora_slot_clear",
            "lora_sync_loads", "lora_plan_prepare", "lora_plan_prepare_slots", "lora_shrink",
            "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
@@ -59,7 +59,7 @@ class _ModuleShape(ctypes.Structure):
 
 
 class _Profile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 3), ("total_ms", ctypes.c_double * 3),
+    _fields_ = [("launches", ctypes.c_int64 * 4), ("total_ms", ctypes.c_double * 4),
                 ("untimed", ctypes.c_int64)]
 
 
@@ -89,6 +89,7 @@ def load_library(path: str = LIB_PATH):
                                ctypes.POINTER(P), I32, D, I32], ctypes.c_int),
         "lora_slot_load": ([P, I32, ctypes.POINTER(P), ctypes.POINTER(P), I32, D, I32],
                            ctypes.c_int),
+        "lora_slot_load_saved": ([P, I32, I32, P, P], ctypes.c_int),
         "lora_slot_clear": ([P, I32], ctypes.c_int),
         "lora_sync_loads": ([P], ctypes.c_int),
         "lora_plan_prepare": ([P, P, I32, P], ctypes.c_int),
@@ -212,6 +213,13 @@ def lora_slot_load_ex(ctx, slot: int, A_t: Sequence, B: Sequence, bias: Optional
     _check(load_library().lora_slot_load_ex(ctx, int(slot), arr(A_t), arr(B), arr(bias),
                                             arr(dora_scale), int(r), float(lora_alpha),
                                             int(bool(use_rslora))), ctx)
+
+
+def lora_slot_load_saved(ctx, slot: int, module: int, W, bias=None) -> None:
+    """A whole saved copy of one module for the adapter in `slot`: W is d_out x d_in
+    (pinned host or device tensor, ctx dtype), bias d_out values or None."""
+    _check(load_library().lora_slot_load_saved(ctx, int(slot), int(module), _ptr(W), _ptr(bias)),
+           ctx)
 
 
 def lora_slot_clear(ctx, slot: int) -> None:
@@ -340,7 +348,7 @@ def lora_profile_begin(ctx, max_launches: int) -> None:
 def lora_profile_end(ctx) -> dict:
     p = _Profile()
     _check(load_library().lora_profile_end(ctx, ctypes.byref(p)), ctx)
-    kinds = ("plan", "shrink", "expand")
+    kinds = ("plan", "shrink", "expand", "saved")
     return {"launches": {k: int(p.launches[i]) for i, k in enumerate(kinds)},
             "total_ms": {k: float(p.total_ms[i]) for i, k in enumerate(kinds)},
             "untimed": int(p.untimed)}
@@ -366,6 +374,9 @@ class Slots:
             lora_slot_load(self.ctx, slot, A_t, B, r, lora_alpha, use_rslora)
         else:
             lora_slot_load_ex(self.ctx, slot, A_t, B, bias, dora_scale, r, lora_alpha, use_rslora)
+
+    def load_saved(self, slot, module, W, bias=None):
+        lora_slot_load_saved(self.ctx, slot, module, W, bias)
 
     def clear(self, slot):
         lora_slot_clear(self.ctx, slot)

@@ -3,7 +3,8 @@
     python -m lora_adapter_application_amd.build
 
 The library is the C ABI of ``include/lora_mi355x.h``: the runtime
-(``csrc/lora_runtime.cpp``) and the kernels (``csrc/lora_kernels.hip``).
+(``csrc/lora_runtime.cpp``), the low-rank kernels (``csrc/lora_kernels.hip``)
+and the saved-module kernels (``csrc/lora_saved.hip``).
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ LIB_NAME = "liblora_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_runtime.cpp")]
+SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_saved.hip"),
+           os.path.join(CSRC, "lora_runtime.cpp")]
 
 # Packed-fp32 instructions stay disabled for device code (the host pass warns
 # that it does not know the feature; that is harmless).

@@ -171,6 +171,31 @@ struct FinalizeBatch {
 };
 hipError_t launch_slot_finalize(bool bf16, const FinalizeBatch &b, hipStream_t st);
 
+// Whole modules an adapter saves (lora_slot_load_saved): for the tokens of a
+// slot that saves member m's module, y = round(x . W^T + c) replaces the base
+// output; a segmented GEMM over the plan's tiles, kSavedCols columns per
+// workgroup (bf16 on MFMA; fp32 on VALU).
+constexpr int kSavedCols = 256;
+struct SavedArgs {
+    int32_t n;                          // group members
+    const void *x[kMaxGroup];           // [T][d_in]
+    void *y[kMaxGroup];                 // [T][d_out]
+    const void *W[kMaxGroup];           // module base: [S][d_out][d_in]
+    const void *bias[kMaxGroup];        // module base: [S][d_out]
+    int64_t slot_stride_W[kMaxGroup];   // elements
+    int32_t d_in[kMaxGroup];
+    int32_t d_out[kMaxGroup];
+    int32_t col_start[kMaxGroup + 1];   // bf16: kSavedCols chunks of the members before member i
+    const Tile *tiles;
+    const int32_t *tile_tok;
+    const int32_t *n_tiles;
+    int32_t grid_tiles;
+    int32_t per_xcd;                    // bf16: work items per XCD (set by launch_saved)
+    uint32_t saved[kMaxGroup][LORA_MAX_SLOTS / 32];     // slot k saves member m's module
+    uint32_t has_bias[kMaxGroup][LORA_MAX_SLOTS / 32];  // ... with a bias
+};
+hipError_t launch_saved(bool bf16, const SavedArgs &a, hipStream_t st, const LaunchTiming &t);
+
 // Scratch memory of lora_apply_group_noalloc: a static __device__ array of
 // this size in the library's code object, so each device the library runs on
 // holds one copy until the process ends.  It takes one batch's plan buffers and

@@ -86,6 +86,7 @@ struct BatchState {
     int last_n = 0;
     int last_modules[kMaxGroup] = {};
     int last_splits[kMaxGroup] = {};
+    const void *last_x[kMaxGroup] = {};   // inputs of the last shrink (saved modules read them)
 };
 
 }  // namespace
@@ -99,6 +100,11 @@ struct lora_ctx {
     std::vector<void *> bias;                // per module: [max_loras][d_out], ctx dtype
     std::vector<float *> dora;               // per module: [max_loras][d_out]
     std::vector<uint8_t> slot_flags;         // [S]: kSlotBias | kSlotDora
+    // saved modules (lora_slot_load_saved): per module a pool [S][d_out][d_in] and
+    // its biases [S][d_out], allocated at the module's first saved load
+    std::vector<void *> saved_W, saved_bias;
+    std::vector<uint8_t> saved_host;         // [n_modules][S]: 1 = the slot saves the module
+    std::vector<uint8_t> saved_bias_host;    // [n_modules][S]: ... with a bias
     std::vector<int64_t> strideA, strideB;   // per-slot element strides
     std::vector<int32_t> rank_host;          // [n_modules][S]: r if the slot's adapter targets m
     std::vector<int32_t> slot_rank;          // [S]: rank of the adapter in the slot (0 = empty)
@@ -349,7 +355,7 @@ void choose_splits(const lora_ctx *c, const Workspace &ws, const BatchState &bs,
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
-enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2 };
+enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2, PROF_SAVED = 3 };
 
 // Events for the next dispatch while profiling (none once the reserve is used
 // up, and none for a dispatch captured into a graph).
@@ -528,9 +534,51 @@ int run_shrink(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const in
     }
     bs.last_n = n;
     c->shrink_epoch = c->slot_epoch;
-    for (int i = 0; i < n; ++i)
+    for (int i = 0; i < n; ++i) {
         bs.last_modules[i] = modules[i];
+        bs.last_x[i] = x[i];
+    }
     return LORA_OK;
+}
+
+// Launch arguments of the saved-module products of a group, or false when no
+// slot the batch may read saves any member's module.
+bool saved_args(const lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
+                const int32_t *modules, void *const *y, SavedArgs *out)
+{
+    SavedArgs &a = *out;
+    std::memset(&a, 0, sizeof a);
+    bool any = false;
+    a.n = n;
+    for (int i = 0; i < n; ++i) {
+        const int mod = modules[i];
+        const lora_module_shape sh = c->shapes[mod];
+        a.x[i] = bs.last_x[i];
+        a.y[i] = y[i];
+        a.W[i] = c->saved_W[mod];
+        a.bias[i] = c->saved_bias[mod];
+        a.slot_stride_W[i] = (int64_t)sh.d_out * sh.d_in;
+        a.d_in[i] = sh.d_in;
+        a.d_out[i] = sh.d_out;
+        a.col_start[i + 1] = a.col_start[i] + ceil_div(sh.d_out, kSavedCols);
+        if (!c->saved_W[mod])
+            continue;
+        const uint8_t *sv = c->saved_host.data() + (size_t)mod * c->S;
+        const uint8_t *sb = c->saved_bias_host.data() + (size_t)mod * c->S;
+        for (int k = 0; k < c->S; ++k) {
+            if (!sv[k] || (bs.hinted && !c->hint[k]))
+                continue;
+            a.saved[i][k >> 5] |= 1u << (k & 31);
+            if (sb[k])
+                a.has_bias[i][k >> 5] |= 1u << (k & 31);
+            any = true;
+        }
+    }
+    a.tiles = ws.plan.tiles;
+    a.tile_tok = ws.plan.tile_tok;
+    a.n_tiles = ws.plan.n_tiles;
+    a.grid_tiles = max_tiles_for(bs.T, c->S, bs.tile_cap);
+    return any;
 }
 
 int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
@@ -545,6 +593,11 @@ int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
         HIP_TRY(c, launch_expand(c->dtype == LORA_BF16, a, group_meta(c, n, modules, bs.hinted), s,
                                  next_timing(c, PROF_EXPAND, s)));
         c->stats.expands += n;
+        // saved modules replace the base output of their slots' tokens (disjoint
+        // from the tokens the low-rank update touches for the same module)
+        SavedArgs sa;
+        if (saved_args(c, ws, bs, n, modules, y, &sa))
+            HIP_TRY(c, launch_saved(c->dtype == LORA_BF16, sa, s, next_timing(c, PROF_SAVED, s)));
         int rc2 = record_slot_use(c, s, bs.hinted);
         if (rc2)
             return rc2;
@@ -718,6 +771,10 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     c->ws.hbuf_rows = std::max(max_tokens, 16384);
     c->slot_rank.assign(max_loras, 0);
     c->slot_flags.assign(max_loras, 0);
+    c->saved_W.assign(n_modules, nullptr);
+    c->saved_bias.assign(n_modules, nullptr);
+    c->saved_host.assign((size_t)n_modules * max_loras, 0);
+    c->saved_bias_host.assign((size_t)n_modules * max_loras, 0);
     c->hint.assign(max_loras, 0);
     c->last_use.assign(max_loras, 0);
     c->max_tiles = std::max(max_tiles_for(max_tokens, max_loras),
@@ -954,8 +1011,11 @@ int lora_slot_load_ex(lora_ctx *ctx, int32_t slot, const void *const *A_t, const
     }
     HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
     ctx->load_gen += 1;
-    for (int m = 0; m < ctx->n_modules; ++m)
+    for (int m = 0; m < ctx->n_modules; ++m) {
         ctx->rank_host[(size_t)m * ctx->S + slot] = A_t[m] ? r : 0;
+        ctx->saved_host[(size_t)m * ctx->S + slot] = 0;      // the new adapter saves nothing yet
+        ctx->saved_bias_host[(size_t)m * ctx->S + slot] = 0;
+    }
     ctx->slot_rank[slot] = r;
     ctx->slot_flags[slot] = (uint8_t)((bias ? kSlotBias : 0) | (dora_scale ? kSlotDora : 0));
     ctx->scale_host[slot] = s;
@@ -974,12 +1034,84 @@ int lora_slot_clear(lora_ctx *ctx, int32_t slot)
         return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "slot %d not in 0..%d", slot, ctx->S - 1);
     // Launches capture the rank table by value, so clearing needs no device work:
     // batches already enqueued keep the adapter, later ones skip the slot.
-    for (int m = 0; m < ctx->n_modules; ++m)
+    for (int m = 0; m < ctx->n_modules; ++m) {
         ctx->rank_host[(size_t)m * ctx->S + slot] = 0;
+        ctx->saved_host[(size_t)m * ctx->S + slot] = 0;
+        ctx->saved_bias_host[(size_t)m * ctx->S + slot] = 0;
+    }
     ctx->slot_rank[slot] = 0;
     ctx->slot_flags[slot] = 0;
     ctx->slot_epoch += 1;
     ctx->stats.clears += 1;
+    return LORA_OK;
+}
+
+int lora_slot_load_saved(lora_ctx *ctx, int32_t slot, int32_t module, const void *W,
+                         const void *bias)
+{
+    if (check_ctx(ctx))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    if (slot < 0 || slot >= ctx->S)
+        return fail(ctx, LORA_ERR_SLOT_OUT_OF_RANGE, "slot %d not in 0..%d", slot, ctx->S - 1);
+    if (module < 0 || module >= ctx->n_modules)
+        return fail(ctx, LORA_ERR_BAD_MODULE, "module %d not in 0..%d", module, ctx->n_modules - 1);
+    if (!W)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT, "W is NULL");
+    if (ctx->slot_rank[slot] == 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                    "slot %d holds no adapter: load the adapter before its saved modules", slot);
+    if (ctx->rank_host[(size_t)module * ctx->S + slot] > 0)
+        return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                    "module %d is a low-rank target of the adapter in slot %d; a module is either "
+                    "targeted or saved", module, slot);
+    DeviceGuard guard(ctx->device);
+    if (check_source(W, ctx->device) || (bias && check_source(bias, ctx->device)))
+        return fail(ctx, LORA_ERR_HOST_NOT_PINNED, "W / bias must be pinned host or device memory");
+    for (auto &st : ctx->streams)
+        if (stream_capturing(st.stream))
+            return fail(ctx, LORA_ERR_INVALID_ARGUMENT,
+                        "slot load while a stream this ctx launched on is under graph capture");
+    const lora_module_shape sh = ctx->shapes[module];
+    const size_t wbytes = (size_t)sh.d_out * sh.d_in * ctx->elem;
+    if (!ctx->saved_W[module]) {
+        // the module's pool, at its first saved load (all slots at once)
+        void *wp = nullptr, *bp = nullptr;
+        hipError_t e = hipMalloc(&wp, wbytes * ctx->S);
+        if (e == hipSuccess)
+            e = hipMalloc(&bp, (size_t)sh.d_out * ctx->elem * ctx->S);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            if (wp)
+                (void)hipFree(wp);
+            return fail(ctx, (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+                                 ? LORA_ERR_OUT_OF_MEMORY : LORA_ERR_HIP,
+                        "saved-module pool of module %d (%zu bytes): %s", module,
+                        wbytes * ctx->S, hipGetErrorString(e));
+        }
+        ctx->allocations.push_back(wp);
+        ctx->allocations.push_back(bp);
+        ctx->saved_W[module] = wp;
+        ctx->saved_bias[module] = bp;
+    }
+    // the same write-after-read fences as a low-rank load of the slot
+    int rc = fence_compute_streams(ctx);
+    if (rc)
+        return rc;
+    if (ctx->last_use[slot]) {
+        HIP_TRY(ctx, hipStreamWaitEvent(ctx->side, ctx->use_ev[ctx->last_use[slot] % lora_ctx::kUseEvents], 0));
+        ctx->last_use[slot] = 0;
+    }
+    HIP_TRY(ctx, hipMemcpyAsync((char *)ctx->saved_W[module] + wbytes * slot, W, wbytes,
+                                hipMemcpyDefault, ctx->side));
+    if (bias)
+        HIP_TRY(ctx, hipMemcpyAsync((char *)ctx->saved_bias[module] + (size_t)sh.d_out * ctx->elem * slot,
+                                    bias, (size_t)sh.d_out * ctx->elem, hipMemcpyDefault, ctx->side));
+    HIP_TRY(ctx, hipEventRecord(ctx->load_done, ctx->side));
+    ctx->load_gen += 1;
+    ctx->saved_host[(size_t)module * ctx->S + slot] = 1;
+    ctx->saved_bias_host[(size_t)module * ctx->S + slot] = bias ? 1 : 0;
+    ctx->slot_epoch += 1;
     return LORA_OK;
 }
 

@@ -1,0 +1,307 @@
+// lora_saved.hip -- gfx950 kernels for modules an adapter saves whole
+// ("modules_to_save" of the example adapter_config.json in "vLLM LoRA Resolver
+// plugins explained", section 3.2).  A saved module is a complete trained copy
+// of a linear; for the tokens of its adapter it takes the base module's place:
+//
+//     y[t, :] = round( x[t, :] . W_k^T + c_k )        (W_k: d_out x d_in)
+//
+// Unlike the low-rank update this is a dense contraction over d_in, so the bf16
+// kernel is a segmented GEMM on the matrix cores over the batch's plan (tiles of
+// at most 64 tokens of one slot, the same tiles the shrink and the expand use).
+//
+// bf16: one workgroup = one tile x kSavedCols output columns x one group
+// member; wave w owns columns 64w .. 64w+63 for all of the tile's 16-token
+// subtiles.  The product is formed transposed, out[n][t] = sum_k W[n][k] x[t][k],
+// with v_mfma_f32_16x16x32_bf16 (lane l gives row l & 15 of the A operand and
+// column l & 15 of the B operand with the K slice 8g .. 8g+7 of lane group
+// g = l >> 4; the result's rows 4g .. 4g+3 of column l & 15 land in lane l).
+// MFMA row i of block b is output column (i / 4) * 16 + b * 4 + i % 4 of the
+// wave's 64, so lane group g owns 16 adjacent columns of one token and y is
+// written 32 bytes per lane.  The tile's x rows (gathered by token id) are
+// staged in LDS one 64-wide K block at a time, double buffered, and shared by
+// the four waves; each wave streams its own W rows straight into registers,
+// also double buffered.  Loads use clamped addresses, never a branch.
+//
+// fp32: VALU, fp64 sums (products of two fp32 values are exact in fp64), the
+// same tiles; it serves fp32 contexts and exactness checks.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_internal.h"
+
+namespace lora {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bool saved_bit(const uint32_t (&bits)[LORA_MAX_SLOTS / 32], int slot)
+{
+    return (bits[slot >> 5] >> (slot & 31)) & 1u;
+}
+
+// Launch, with the dispatch bracketed by t's events when it has them.
+template <typename K, typename... Args>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, const LaunchTiming &t, Args... args)
+{
+    if (t.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, t.start, t.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
+constexpr int kXcds = 8;
+constexpr int kBK = 64;                     // K elements per staged block
+constexpr int kXRow = kBK + 8;              // LDS row of the x stage (bf16 elements, padded)
+
+// Work item of workgroup blockIdx.x: the grid is dealt round-robin to the 8
+// XCDs, and XCD j takes the j-th contiguous eighth of the items, so
+// consecutive tiles of one (member, column chunk) share that chunk's W rows in
+// the XCD's L2.
+__device__ __forceinline__ int saved_item(int per_xcd)
+{
+    return (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+}
+
+// The member, column chunk and tile of work item w (tile fastest).
+__device__ __forceinline__ void saved_decode(const SavedArgs &a, int w, int &m, int &chunk, int &bt)
+{
+    m = 0;
+    while (m + 1 < a.n && w >= a.grid_tiles * a.col_start[m + 1])
+        ++m;
+    const int local = w - a.grid_tiles * a.col_start[m];
+    chunk = local / a.grid_tiles;
+    bt = local - chunk * a.grid_tiles;
+}
+
+__global__ __launch_bounds__(256) void saved_bf16_kernel(SavedArgs a)
+{
+    const int n_items = a.grid_tiles * a.col_start[a.n];
+    const int w = saved_item(a.per_xcd);
+    if (w >= n_items)
+        return;
+    int m, chunk, bt;
+    saved_decode(a, w, m, chunk, bt);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, g = lane >> 4;
+    const int n_tiles = *a.n_tiles;
+    const Tile tile = a.tiles[bt];                     // in bounds: the tile buffer covers the grid
+    const int tokv = a.tile_tok[(int64_t)bt * kTileTokens + lane];
+    if (bt >= n_tiles || !saved_bit(a.saved[m], tile.slot))
+        return;
+    // token of this lane's row in each subtile (shuffled here, where every
+    // lane of the wave is active)
+    int toks[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        toks[st] = __shfl(tokv, st * 16 + row, 64);
+    const int d_in = a.d_in[m], d_out = a.d_out[m];
+    const int cb = chunk * kSavedCols + wave * 64;     // the wave's first column
+    const uint16_t *x = (const uint16_t *)a.x[m];
+    const uint16_t *W = (const uint16_t *)a.W[m] + (int64_t)tile.slot * a.slot_stride_W[m];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTileTokens * kXRow];
+
+    // W rows of this lane: block b, MFMA row `row` -> column cb + (row/4)*16 + b*4 + row%4
+    // (rows past d_out read the last row; those outputs are not stored)
+    const uint16_t *wrow[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int n = min(cb + (row >> 2) * 16 + b * 4 + (row & 3), d_out - 1);
+        wrow[b] = W + (int64_t)n * d_in;
+    }
+    // x stage: thread tid copies 32 bytes of tile row tid / 4 (K offset (tid % 4) * 16);
+    // rows past the tile read token 0, K past d_in is stored as zero
+    const int xr = tid >> 2, xk = (tid & 3) * 16;
+    const int xtok = __shfl(tokv, xr < tile.len ? xr : 0, 64);
+    const uint16_t *xsrc = x + (int64_t)(xr < tile.len ? xtok : 0) * d_in;
+    const int nkb = (d_in + kBK - 1) / kBK;
+    const int kmax = d_in - 8;                          // last 16-byte piece of a row
+
+    uint4 wr[2][2][4];     // [stage][K step of 32][block]
+    uint4 xv[2];
+    auto load_w = [&](uint4 (&dst)[2][4], int kb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                dst[s][b] = *(const uint4 *)(wrow[b] + min(kb + s * 32 + g * 8, kmax));
+    };
+    auto load_x = [&](int kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xv[h] = *(const uint4 *)(xsrc + min(kb + xk + h * 8, kmax));
+    };
+    auto store_x = [&](int buf, int kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *(uint4 *)(&xs[buf][xr * kXRow + xk + h * 8]) =
+                kb + xk + h * 8 < d_in ? xv[h] : make_uint4(0, 0, 0, 0);
+    };
+    f32x4_t acc[4][4];     // [subtile][block]
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            acc[st][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nsub = (tile.len + 15) >> 4;
+    auto mma = [&](const uint4 (&wv)[2][4], int buf) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (st < nsub) {
+                    const bf16x8_t xb = __builtin_bit_cast(
+                        bf16x8_t, *(const uint4 *)(&xs[buf][(st * 16 + row) * kXRow + s * 32 + g * 8]));
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, wv[s][b]), xb, acc[st][b], 0, 0, 0);
+                }
+            }
+        }
+    };
+    // prologue: block 0 into stage 0 and LDS buffer 0
+    load_w(wr[0], 0);
+    load_x(0);
+    store_x(0, 0);
+    __syncthreads();
+    // two blocks per pass, so the register stages are indexed statically; the
+    // loads of block i + 1 are in flight while block i is multiplied (their
+    // addresses are clamped, so the last pass loads in-range data it ignores)
+    for (int i = 0; i < nkb; i += 2) {
+        const int k1 = (i + 1) * kBK, k2 = (i + 2) * kBK;
+        load_w(wr[1], min(k1, (nkb - 1) * kBK));
+        load_x(min(k1, (nkb - 1) * kBK));
+        mma(wr[0], 0);
+        if (i + 1 >= nkb)
+            break;
+        store_x(1, k1);
+        __syncthreads();
+        load_w(wr[0], min(k2, (nkb - 1) * kBK));
+        load_x(min(k2, (nkb - 1) * kBK));
+        mma(wr[1], 1);
+        if (i + 2 >= nkb)
+            break;
+        store_x(0, k2);
+        __syncthreads();
+    }
+    // epilogue: lane group g owns columns cb + 16g .. +15 of token st*16 + row
+    const bool has_bias = saved_bit(a.has_bias[m], tile.slot);
+    const uint16_t *bias = (const uint16_t *)a.bias[m] + (int64_t)tile.slot * d_out;
+    uint16_t *y = (uint16_t *)a.y[m];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int col = cb + g * 16 + p * 8;
+        if (col >= d_out)
+            continue;
+        uint4 cw = make_uint4(0, 0, 0, 0);
+        if (has_bias)
+            cw = *(const uint4 *)(bias + col);
+        const uint32_t c[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int t = st * 16 + row;
+            if (t >= tile.len)
+                continue;
+            const int tok = toks[st];
+            // columns col .. col+7 are rows 4g..4g+3 of blocks 2p and 2p+1
+            const f32x4_t v0 = acc[st][2 * p], v1 = acc[st][2 * p + 1];
+            uint4 o;
+            o.x = pack_bf16x2(v0[0] + bf16_lo(c[0]), v0[1] + bf16_hi(c[0]));
+            o.y = pack_bf16x2(v0[2] + bf16_lo(c[1]), v0[3] + bf16_hi(c[1]));
+            o.z = pack_bf16x2(v1[0] + bf16_lo(c[2]), v1[1] + bf16_hi(c[2]));
+            o.w = pack_bf16x2(v1[2] + bf16_lo(c[3]), v1[3] + bf16_hi(c[3]));
+            *(uint4 *)(y + (int64_t)tok * d_out + col) = o;
+        }
+    }
+}
+
+// fp32: one workgroup = one tile x 64 columns x one member; thread tid takes
+// column tid % 64 for the 16 tokens (tid / 64) * 16 .. +15, with fp64 sums.
+constexpr int kF32Cols = 64;
+
+__global__ __launch_bounds__(256) void saved_f32_kernel(SavedArgs a)
+{
+    const int bt = blockIdx.x, chunk = blockIdx.y, m = blockIdx.z;
+    if (m >= a.n || chunk * kF32Cols >= a.d_out[m])
+        return;
+    const int n_tiles = *a.n_tiles;
+    const Tile tile = a.tiles[bt];
+    if (bt >= n_tiles || !saved_bit(a.saved[m], tile.slot))
+        return;
+    const int d_in = a.d_in[m], d_out = a.d_out[m];
+    const int tid = threadIdx.x;
+    const float *x = (const float *)a.x[m];
+    const float *W = (const float *)a.W[m] + (int64_t)tile.slot * a.slot_stride_W[m];
+    const int32_t *toks = a.tile_tok + (int64_t)bt * kTileTokens;
+    __shared__ float xs[kTileTokens][33];
+    __shared__ float ws[kF32Cols][33];
+    const int c = tid & 63, q = tid >> 6;
+    const int n = chunk * kF32Cols + c;
+    double acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        acc[j] = 0.0;
+    for (int k0 = 0; k0 < d_in; k0 += 32) {
+        for (int e = tid; e < kTileTokens * 32; e += 256) {
+            const int t = e >> 5, kk = e & 31;
+            xs[t][kk] = (t < tile.len && k0 + kk < d_in) ? x[(int64_t)toks[t] * d_in + k0 + kk] : 0.f;
+        }
+        for (int e = tid; e < kF32Cols * 32; e += 256) {
+            const int cc = e >> 5, kk = e & 31, nn = chunk * kF32Cols + cc;
+            ws[cc][kk] = (nn < d_out && k0 + kk < d_in) ? W[(int64_t)nn * d_in + k0 + kk] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            double s = acc[j];
+            for (int kk = 0; kk < 32; ++kk)
+                s = fma((double)xs[q * 16 + j][kk], (double)ws[c][kk], s);
+            acc[j] = s;
+        }
+        __syncthreads();
+    }
+    if (n >= d_out)
+        return;
+    const double cn = saved_bit(a.has_bias[m], tile.slot)
+                          ? (double)((const float *)a.bias[m])[(int64_t)tile.slot * d_out + n] : 0.0;
+    float *y = (float *)a.y[m];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = q * 16 + j;
+        if (t < tile.len)
+            y[(int64_t)toks[t] * d_out + n] = (float)(acc[j] + cn);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_saved(bool bf16, const SavedArgs &a, hipStream_t st, const LaunchTiming &t)
+{
+    if (bf16) {
+        const int64_t items = (int64_t)a.grid_tiles * a.col_start[a.n];
+        SavedArgs b = a;
+        b.per_xcd = (int)((items + kXcds - 1) / kXcds);
+        launch(saved_bf16_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
+    } else {
+        int cols = 1;
+        for (int i = 0; i < a.n; ++i)
+            cols = cols > (a.d_out[i] + kF32Cols - 1) / kF32Cols ? cols : (a.d_out[i] + kF32Cols - 1) / kF32Cols;
+        launch(saved_f32_kernel, dim3(a.grid_tiles, cols, a.n), dim3(256), st, t, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lora

@@ -66,6 +66,8 @@ int main()
     expect(lora_slot_load(nullptr, 0, null_w, null_w, 8, 16.0, 0), LORA_ERR_INVALID_ARGUMENT, "load: ctx NULL");
     expect(lora_slot_load_ex(nullptr, 0, null_w, null_w, nullptr, nullptr, 8, 16.0, 0),
            LORA_ERR_INVALID_ARGUMENT, "load_ex: ctx NULL");
+    expect(lora_slot_load_saved(nullptr, 0, 0, null_w, nullptr), LORA_ERR_INVALID_ARGUMENT,
+           "load_saved: ctx NULL");
     expect(lora_slot_clear(nullptr, 0), LORA_ERR_INVALID_ARGUMENT, "clear: ctx NULL");
     expect(lora_sync_loads(nullptr), LORA_ERR_INVALID_ARGUMENT, "sync_loads: ctx NULL");
     expect(lora_plan_prepare(nullptr, nullptr, 0, nullptr), LORA_ERR_INVALID_ARGUMENT, "plan: ctx NULL");

@@ -70,8 +70,8 @@ def test_runtime_host_checks_under_asan_ubsan():
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     csrc = os.path.join(ROOT, "lora_adapter_application_amd", "csrc")
-    srcs = [os.path.join(csrc, "lora_kernels.hip"), os.path.join(csrc, "lora_runtime.cpp"),
-            os.path.join(SAN, "runtime_check.cpp")]
+    srcs = [os.path.join(csrc, "lora_kernels.hip"), os.path.join(csrc, "lora_saved.hip"),
+            os.path.join(csrc, "lora_runtime.cpp"), os.path.join(SAN, "runtime_check.cpp")]
     out = os.path.join(BUILD, "runtime_check")
     # each -fsanitize= applies to the host pass only
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
