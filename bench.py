@@ -25,6 +25,8 @@ Passes over the same K steps (after W warm-up steps):
              this "value");
   plan_amortized  one lora_plan_prepare, then the K steps' applies only (the
              layers of a model share one batch and its slot indices);
+  fused      (decode batches) lora_apply_group_fused: each group's shrink and
+             expand in one launch;
   step_spread     an event after each step: p10 / p50 / p90 step times;
   kernels    per-dispatch start / stop events the library records with each
              of its dispatches (hipExtLaunchKernelGGL): kernel times.
@@ -281,10 +283,10 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
 
     # the library calls of one step per layer set, arguments marshalled once
     # (per stream: the eager passes use the current stream, the graph capture its own)
-    def bind_all(stream=None, prepare=True):
+    def bind_all(stream=None, prepare=True, fused=False):
         return [slots.bind_step([([l * nm + j for j in g], [xs[l * nm + j] for j in g],
                                   [ys[l * nm + j] for j in g]) for g in groups], idx, stream,
-                                prepare=prepare)
+                                prepare=prepare, fused=fused)
                 for l in range(L)]
     bound = bind_all()
     bound_np = bind_all(prepare=False)
@@ -301,6 +303,20 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         step(W + i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
+    # fused decode: each group's shrink and expand in one launch (bf16 batches of
+    # at most 1024 tokens; lora_apply_group_fused)
+    fused_s = None
+    if T <= 1024:
+        bound_f = bind_all(fused=True)
+        for i in range(W):
+            bound_f[i % L]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            bound_f[(W + i) % L]()
+        torch.cuda.synchronize()
+        fused_s = time.perf_counter() - t0
+        del bound_f
     # plan amortized over the layers: one lora_plan_prepare, then K steps of applies
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -378,13 +394,16 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         shrink_bytes = [sum(b * mods[j].d_in * ((T_act if x_owner[j] == j else 0) + sum_r) for j in g)
                         for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
-        group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes}
+        # a fused decode launch does one group's shrink and expand
+        group_bytes = {"shrink": shrink_bytes, "expand": expand_bytes,
+                       "fused": [a + b for a, b in zip(shrink_bytes, expand_bytes)]}
         rsum = int(sum(wl.adapters[k].r for k in wl.idx[act]))    # true ranks of the active tokens
         flops = [2 * (m.d_in + m.d_out) * rsum for m in mods]
         # algorithmic flops of each kind per step (true ranks; the expand's MFMAs
         # also contract h's low half, which is not counted)
         kind_flops = {"shrink": float(sum(2 * m.d_in * rsum for m in mods)),
                       "expand": float(sum(2 * m.d_out * rsum for m in mods))}
+        kind_flops["fused"] = kind_flops["shrink"] + kind_flops["expand"]
 
         def avg_us(kind):
             return tot[kind] / n[kind] * 1e3 if n[kind] else None
@@ -395,7 +414,7 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
             "step_alg_bytes": float(sum(shrink_bytes) + sum(expand_bytes)),
             "step_alg_flops": float(sum(flops)),
         }
-        for kind in ("shrink", "expand"):
+        for kind in ("shrink", "expand", "fused"):
             if n[kind]:
                 step_bytes = float(sum(group_bytes[kind]))
                 tfs = kind_flops[kind] * K / (tot[kind] * 1e-3) / 1e12
@@ -407,7 +426,7 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
                     "alg_flops_per_step": kind_flops[kind], "TFLOPs": round(tfs, 2),
                     "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 5),
                     "mfma_util_pct": profile_figure("mfma", "lora_" + kind, wl.name, "mfma_util_pct")}
-        dom = max(("shrink", "expand"), key=lambda k: tot[k])
+        dom = max(("shrink", "expand", "fused"), key=lambda k: tot[k])
         dom_bytes = group_bytes[dom]
         achieved = sum(dom_bytes) * K / (tot[dom] * 1e-3) / 1e9      # GB/s
         kname = "lora_" + dom
@@ -438,6 +457,9 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         "roofline": roofline,
         "eager": {"ms_per_step": round(eager_s / K * 1e3, 5), "value": round(T * K / eager_s, 1)},
         "graph": {"ms_per_step": round(graph_s / K * 1e3, 5), "value": round(T * K / graph_s, 1)},
+        "fused": None if fused_s is None else {
+            "ms_per_step": round(fused_s / K * 1e3, 5), "value": round(T * K / fused_s, 1),
+            "pass": "lora_apply_group_fused: each group's shrink and expand in one launch"},
         "plan_amortized": {"ms_per_step": round(amort_s / K * 1e3, 5),
                            "value": round(T * K / amort_s, 1),
                            "pass": "one lora_plan_prepare, then the K steps' applies"},
@@ -544,6 +566,7 @@ def main():
                         "ms_per_step": round(e["ms_per_step"], 5), "steps": e["K"],
                         "config": e["config"], "roofline": e["roofline"],
                         "graph": e["graph"], "plan_amortized": e["plan_amortized"],
+                        "fused": e["fused"],
                         "step_spread": e["step_spread"]}
     saved = None
     if args.saved and rec["wl"].name == "llama7b_prefill" and not args.no_kernel_timing:
@@ -572,6 +595,7 @@ def main():
         "eager": rec["eager"],
         "graph": rec["graph"],
         "plan_amortized": rec["plan_amortized"],
+        "fused": rec["fused"],
         "step_spread": rec["step_spread"],
         "kernels": rec["kernels"],
     }

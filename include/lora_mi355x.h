@@ -89,6 +89,8 @@ enum {
 
 /* Sticky device-side flags, read with lora_get_device_flags. */
 #define LORA_FLAG_SLOT_INDEX_TOO_LARGE 0x1u  /* a token carried idx >= max_loras (skipped) */
+#define LORA_FLAG_FUSED_TIMEOUT 0x2u         /* a fused decode launch gave up waiting for a
+                                                tile's partials (its rows were left untouched) */
 
 typedef struct {
     int64_t loads;          /* lora_slot_load calls that succeeded */
@@ -333,6 +335,22 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
                      void *stream);
 
 /*
+ * lora_apply_group with the shrink and the expand of a decode batch in one
+ * launch (the two kernels of the update fused, h kept between workgroups of
+ * one launch instead of between launches).  Applies to bf16 batches of at most
+ * 1024 tokens; other batches take the two launches of lora_apply_group.  The
+ * expand workgroups wait for their tile's K-split partials through per-(tile,
+ * module) counts that every launch returns to zero, so the call can be
+ * captured into a graph and replayed.  The wait is bounded: if it ever gives
+ * up, the rows it covers are left untouched and LORA_FLAG_FUSED_TIMEOUT is set.
+ * Results equal lora_apply_group bit for bit.  Same arguments, ordering and
+ * errors as lora_apply_group.
+ */
+int lora_apply_group_fused(lora_ctx *ctx, int32_t n, const int32_t *modules,
+                           const void *const *x, void *const *y,
+                           const int32_t *token_slot_idx, int32_t n_tokens, void *stream);
+
+/*
  * lora_apply_group for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * The batch's plan and its fp32 h partials live in the library's static
@@ -368,9 +386,9 @@ int lora_get_stats(lora_ctx *ctx, lora_stats *out);
  * are created by lora_profile_begin, outside any timed region.
  */
 typedef struct {
-    int64_t launches[4];   /* [0] plan, [1] shrink, [2] expand, [3] saved-module
-                              product dispatches timed */
-    double total_ms[4];    /* their summed kernel time, milliseconds */
+    int64_t launches[5];   /* [0] plan, [1] shrink, [2] expand, [3] saved-module
+                              product, [4] fused decode dispatches timed */
+    double total_ms[5];    /* their summed kernel time, milliseconds */
     int64_t untimed;       /* dispatches past max_launches (not timed) */
 } lora_profile;
 

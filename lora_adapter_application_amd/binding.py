@@ -34,6 +34,7 @@ LORA_ERR_HIP = -8
 LORA_ERR_NO_PLAN = -9
 
 LORA_FLAG_SLOT_INDEX_TOO_LARGE = 0x1
+LORA_FLAG_FUSED_TIMEOUT = 0x2
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_slot_load_ex",
@@ -41,7 +42,7 @@ EXPORTS = ("lora_slots_create", "lora_slots_destroy", "lora_slot_load", "lora_sl
            "lora_sync_loads", "lora_plan_prepare", "lora_plan_prepare_slots", "lora_shrink",
            "lora_expand", "lora_apply",
            "lora_shrink_group", "lora_expand_group", "lora_apply_group",
-           "lora_apply_group_noalloc",
+           "lora_apply_group_noalloc", "lora_apply_group_fused",
            "lora_get_device_flags", "lora_get_stats", "lora_profile_begin", "lora_profile_end",
            "lora_status_string", "lora_last_error")
 
@@ -59,7 +60,7 @@ class _ModuleShape(ctypes.Structure):
 
 
 class _Profile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 4), ("total_ms", ctypes.c_double * 4),
+    _fields_ = [("launches", ctypes.c_int64 * 5), ("total_ms", ctypes.c_double * 5),
                 ("untimed", ctypes.c_int64)]
 
 
@@ -103,6 +104,8 @@ def load_library(path: str = LIB_PATH):
                               P, I32, P], ctypes.c_int),
         "lora_apply_group_noalloc": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P),
                                       ctypes.POINTER(P), P, I32, P], ctypes.c_int),
+        "lora_apply_group_fused": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(P),
+                                    ctypes.POINTER(P), P, I32, P], ctypes.c_int),
         "lora_get_device_flags": ([P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
         "lora_get_stats": ([P, ctypes.POINTER(_Stats)], ctypes.c_int),
         "lora_profile_begin": ([P, I32], ctypes.c_int),
@@ -329,6 +332,20 @@ def lora_apply_group_noalloc(ctx, modules: Sequence[int], x: Sequence, y: Sequen
                                                    int(n_tokens), _stream(stream)), ctx)
 
 
+def lora_apply_group_fused(ctx, modules: Sequence[int], x: Sequence, y: Sequence,
+                           token_slot_idx, n_tokens: Optional[int] = None, stream=None) -> None:
+    """lora_apply_group with the shrink and the expand of a decode batch in one launch."""
+    import torch
+    if n_tokens is None:
+        n_tokens = token_slot_idx.numel() if token_slot_idx is not None else 0
+    if n_tokens:
+        _require_cuda(token_slot_idx, "token_slot_idx", torch.int32, n_tokens)
+    n, mods, xp = _group(modules, x, "x")
+    _, _, yp = _group(modules, y, "y")
+    _check(load_library().lora_apply_group_fused(ctx, n, mods, xp, yp, _ptr(token_slot_idx),
+                                                 int(n_tokens), _stream(stream)), ctx)
+
+
 def lora_get_device_flags(ctx) -> int:
     v = ctypes.c_uint32(0)
     _check(load_library().lora_get_device_flags(ctx, ctypes.byref(v)), ctx)
@@ -348,7 +365,7 @@ def lora_profile_begin(ctx, max_launches: int) -> None:
 def lora_profile_end(ctx) -> dict:
     p = _Profile()
     _check(load_library().lora_profile_end(ctx, ctypes.byref(p)), ctx)
-    kinds = ("plan", "shrink", "expand", "saved")
+    kinds = ("plan", "shrink", "expand", "saved", "fused")
     return {"launches": {k: int(p.launches[i]) for i, k in enumerate(kinds)},
             "total_ms": {k: float(p.total_ms[i]) for i, k in enumerate(kinds)},
             "untimed": int(p.untimed)}
@@ -408,10 +425,13 @@ class Slots:
     def apply_group(self, modules, x, y, idx, n_tokens=None, stream=None):
         lora_apply_group(self.ctx, modules, x, y, idx, n_tokens, stream)
 
+    def apply_group_fused(self, modules, x, y, idx, n_tokens=None, stream=None):
+        lora_apply_group_fused(self.ctx, modules, x, y, idx, n_tokens, stream)
+
     def apply_group_noalloc(self, modules, x, y, idx, n_tokens=None, stream=None):
         lora_apply_group_noalloc(self.ctx, modules, x, y, idx, n_tokens, stream)
 
-    def bind_step(self, groups, idx, stream=None, prepare=True):
+    def bind_step(self, groups, idx, stream=None, prepare=True, fused=False):
         """One step with its arguments marshalled once: lora_plan_prepare of idx
         (unless prepare is False: then the step reuses the plan an earlier
         lora_plan_prepare of the same idx made, as the layers of a model share
@@ -431,7 +451,8 @@ class Slots:
             _, _, yp = _group(modules, y, "y")
             calls.append((n, mods, xp, yp))
         ctx = self.ctx
-        plan, apply_group = lib.lora_plan_prepare, lib.lora_apply_group
+        plan = lib.lora_plan_prepare
+        apply_group = lib.lora_apply_group_fused if fused else lib.lora_apply_group
         refs = (idx, groups)
 
         def step():

@@ -147,6 +147,19 @@ struct ExpandArgs {
 
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);
+
+// Fused decode (bf16, batches of at most kInlinePlanTokens): the shrink and the
+// expand of one group in one launch; expand workgroups wait for the K-split
+// partials of their tile through per-(tile, member) counts in `sync`, which
+// every launch leaves at zero.
+struct FusedArgs {
+    ShrinkArgs s;
+    ExpandArgs e;
+    uint32_t *sync;              // [max_tiles][kMaxGroup][2]: partials stored, consumers past the wait
+    int32_t shrink_blocks;       // workgroups of the shrink phase (set by launch_fused)
+    int32_t spin_limit;          // polls of a waiting workgroup before it gives up
+};
+hipError_t launch_fused(const FusedArgs &f, const SlotMeta &m, hipStream_t st, const LaunchTiming &t);
 hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);
 

@@ -73,7 +73,13 @@ struct Workspace {
     PlanBuffers plan{};
     float *hpart = nullptr;
     int hbuf_rows = 0;       // rows of one group member's block of h partials
+    uint32_t *sync = nullptr;   // fused decode counts [max_tiles][kMaxGroup][2], kept at zero
+                                // between launches (null: no fused launches on this workspace)
 };
+
+// Polls of a fused decode workgroup waiting for its tile's partials before it
+// gives up (about 20 ms; a launch normally waits a few microseconds).
+constexpr int kFusedSpinLimit = 20000;
 
 // The plan of the current batch, and the module list of the last shrink (which
 // the expand must repeat).
@@ -355,7 +361,7 @@ void choose_splits(const lora_ctx *c, const Workspace &ws, const BatchState &bs,
 
 int check_ctx(lora_ctx *c) { return c ? LORA_OK : LORA_ERR_INVALID_ARGUMENT; }
 
-enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2, PROF_SAVED = 3 };
+enum { PROF_PLAN = 0, PROF_SHRINK = 1, PROF_EXPAND = 2, PROF_SAVED = 3, PROF_FUSED = 4 };
 
 // Events for the next dispatch while profiling (none once the reserve is used
 // up, and none for a dispatch captured into a graph).
@@ -605,6 +611,46 @@ int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
     return LORA_OK;
 }
 
+// Shrink and expand of one group in one launch (bf16 batches of at most
+// kInlinePlanTokens on a workspace with fused counts), then the saved-module
+// products of the group.
+int run_fused(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const int32_t *modules,
+              const void *const *x, void *const *y, hipStream_t s)
+{
+    const int T = bs.T;
+    for (int i = 0; i < n; ++i) {
+        bs.last_modules[i] = modules[i];
+        bs.last_x[i] = x[i];
+    }
+    bs.last_n = n;
+    c->shrink_epoch = c->slot_epoch;
+    if (T == 0)
+        return LORA_OK;
+    int rc = before_launch(c, s, true, bs.hinted);
+    if (rc)
+        return rc;
+    FusedArgs f;
+    std::memset(&f, 0, sizeof f);
+    f.s = shrink_args(c, ws, bs, n, modules, x);     // records the K-splits for the expand
+    f.e = expand_args(c, ws, bs, n, modules, y);
+    f.sync = ws.sync;
+    f.spin_limit = kFusedSpinLimit;
+    HIP_TRY(c, launch_fused(f, group_meta(c, n, modules, bs.hinted), s, next_timing(c, PROF_FUSED, s)));
+    if (bs.plan_mode == kPlanInline)
+        bs.plan_mode = kPlanTiles;   // later launches read the plan this one published
+    c->stats.shrinks += n;
+    c->stats.expands += n;
+    SavedArgs sa;
+    if (saved_args(c, ws, bs, n, modules, y, &sa))
+        HIP_TRY(c, launch_saved(c->dtype == LORA_BF16, sa, s, next_timing(c, PROF_SAVED, s)));
+    return record_slot_use(c, s, bs.hinted);
+}
+
+bool fused_applies(const lora_ctx *c, const Workspace &ws, const BatchState &bs)
+{
+    return c->dtype == LORA_BF16 && ws.sync && bs.T <= kInlinePlanTokens;
+}
+
 int check_group(lora_ctx *c, int32_t n, const int32_t *modules)
 {
     if (n < 1 || n > LORA_MAX_GROUP || !modules)
@@ -798,6 +844,8 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.tiles, sizeof(Tile) * (size_t)c->max_tiles);
     if (e == hipSuccess)
         e = dalloc(c, &c->ws.plan.tile_tok, sizeof(int32_t) * (size_t)c->max_tiles * kTileTokens);
+    if (e == hipSuccess)
+        e = dalloc(c, &c->ws.sync, sizeof(uint32_t) * 2 * kMaxGroup * (size_t)c->max_tiles);
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_tiles, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_active, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.flags, sizeof(uint32_t));
@@ -1224,9 +1272,13 @@ int lora_expand(lora_ctx *ctx, void *y, int32_t module, void *stream)
     return lora_expand_group(ctx, 1, &module, &y, stream);
 }
 
-int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
-                     void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
-                     void *stream)
+namespace {
+
+// lora_apply_group and lora_apply_group_fused: plan unless prepared, then the
+// group's update as two launches, or as one fused launch where it applies.
+int apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                void *const *y, const int32_t *token_slot_idx, int32_t n_tokens, void *stream,
+                bool fused)
 {
     if (check_ctx(ctx))
         return LORA_ERR_INVALID_ARGUMENT;
@@ -1258,10 +1310,28 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
         }
         ctx->plan_valid = true;
     }
+    if (fused && fused_applies(ctx, ctx->ws, ctx->bs))
+        return run_fused(ctx, ctx->ws, ctx->bs, n, modules, x, y, s);
     rc = run_shrink(ctx, ctx->ws, ctx->bs, n, modules, x, s);
     if (rc)
         return rc;
     return run_expand(ctx, ctx->ws, ctx->bs, n, modules, y, s);
+}
+
+}  // namespace
+
+int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                     void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
+                     void *stream)
+{
+    return apply_group(ctx, n, modules, x, y, token_slot_idx, n_tokens, stream, false);
+}
+
+int lora_apply_group_fused(lora_ctx *ctx, int32_t n, const int32_t *modules, const void *const *x,
+                           void *const *y, const int32_t *token_slot_idx, int32_t n_tokens,
+                           void *stream)
+{
+    return apply_group(ctx, n, modules, x, y, token_slot_idx, n_tokens, stream, true);
 }
 
 int lora_apply(lora_ctx *ctx, const void *x, void *y, const int32_t *token_slot_idx,

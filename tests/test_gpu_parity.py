@@ -543,4 +543,18 @@ def test_profile_times_every_dispatch():
     S.apply(xs[0], ys[0], idx, 0)
     p = S.profile_end()
     assert p["launches"]["shrink"] == 1 and p["untimed"] == 3
+    S.profile_begin(4)
+    S.apply_group_fused([0], [xs[0]], [ys[0]], idx)      # one fused dispatch
+    p = S.profile_end()
+    assert p["launches"]["fused"] == 1 and p["untimed"] == 0
+    # a batch above 1024 tokens: plan kernels, then two launches even when fused is asked for
+    big = synth.random_case(19, synth.BF16, [synth.Module("a", 512, 512)], 1500, 4, 16, [16, 8, 4, 16])
+    Sb = make_slots(big)
+    Sb.profile_begin(8)
+    Sb.apply_group_fused([0], [to_dev(big.x["a"], big.dtype)], [to_dev(big.y["a"], big.dtype)],
+                         torch.from_numpy(big.idx).cuda())
+    pb = Sb.profile_end()
+    assert pb["launches"]["plan"] == 2 and pb["launches"]["shrink"] == 1 and pb["launches"]["expand"] == 1
+    assert pb["launches"]["fused"] == 0
+    Sb.close()
     S.close()
