@@ -89,6 +89,8 @@ def parse():
     p.add_argument("--extra-warmup", type=int, default=200)
     p.add_argument("--no-saved", dest="saved", action="store_false",
                    help="skip the saved-module (modules_to_save) measurement on the headline batch")
+    p.add_argument("--saved-only", action="store_true",
+                   help="measure only the saved-module product on the prefill batch")
     p.add_argument("--churn-steps", type=int, default=50)
     p.add_argument("--prefetch", action="store_true",
                    help="churn: upload the next step's misses while the current step computes "
@@ -547,6 +549,13 @@ def main():
             churn_prefetch(args)
         else:
             churn(args)
+        return
+    if args.saved_only:
+        saved = measure_saved(workload("llama7b_prefill"), args.steps, args.warmup)
+        print(json.dumps({"metric": "saved-module product TFLOP/s", "value": saved["TFLOPs"],
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "saved_module": saved}), flush=True)
         return
     rec = measure(args.workload, args, args.steps, args.warmup,
                   kernel_timing=not args.no_kernel_timing, launch=args.launch)
