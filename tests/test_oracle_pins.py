@@ -387,6 +387,30 @@ def test_bf16_output_rounding_through_apply():
     assert np.array_equal(got, ref)
 
 
+def test_bf16_output_of_apply_is_rounded_once_from_the_exact_sum():
+    """The stored output, not only the rounding routine, rounds the exact sum once.
+
+    x = [2^-8, 2^-15], A^T = [1, 2^-15], B = [1], r = 1, s = 1 and y = +-1 give
+    y + s x A B = +-(1 + 2^-8 + 2^-30): just past the tie between 1 and 1 + 2^-7,
+    so it rounds away from 1.  Rounding to fp32 first (whose spacing at 1 is
+    2^-23) would land exactly on the tie and round to even, back to 1.
+    """
+    x = synth.to_bf16_bits(np.array([[2.0 ** -8, 2.0 ** -15]] * 2, np.float32))
+    At = synth.to_bf16_bits(np.array([[1.0, 2.0 ** -15]], np.float32))
+    B = synth.to_bf16_bits(np.array([[1.0]], np.float32))
+    y = synth.to_bf16_bits(np.array([[1.0], [-1.0]], np.float32))
+    ad = {"r": 1, "lora_alpha": 1.0, "use_rslora": False, "At": At, "B": B}
+    got = oracle.apply(oracle.BF16, x, y, np.zeros(2, np.int32), [ad])
+    # 1 + 2^-8 + 2^-30 -> 1 + 2^-7 (0x3F81).  Row 1 is -1 + 2^-8 + 2^-30, no tie
+    # (bf16 spacing below 1 is 2^-8): its nearest value is -(1 - 2^-8), 0xBF7F.
+    assert got[0, 0] == 0x3F81
+    assert got[1, 0] == oracle.round_bf16(-1.0 + 2.0 ** -8 + 2.0 ** -30) == 0xBF7F
+    yneg = synth.to_bf16_bits(np.array([[-1.0]], np.float32))
+    xneg = synth.to_bf16_bits(np.array([[-(2.0 ** -8), -(2.0 ** -15)]], np.float32))
+    got = oracle.apply(oracle.BF16, xneg, yneg, np.zeros(1, np.int32), [ad])
+    assert got[0, 0] == 0xBF81          # -(1 + 2^-8 + 2^-30) -> -(1 + 2^-7)
+
+
 # ---------------------------------------------------------------------------
 # the adapter size estimate on the pages
 
