@@ -9,7 +9,9 @@
  * use_rslora of the example adapter_config.json ("vLLM LoRA Resolver plugins
  * explained", section 3.2) describe.  The cases cover the edges: no tokens,
  * rank 1, empty slots, negative and too-large slot indices, ragged sizes, fp32
- * and bf16, output bias and DoRA factors.  The exit status is the number of
+ * and bf16, output bias and DoRA factors; and the saved-module product
+ * ("modules_to_save" of the same example config), checked against a plain
+ * x . W^T + bias written here.  The exit status is the number of
  * failed checks; the sanitizers abort on the first memory or UB error.
  */
 #include <math.h>
@@ -31,6 +33,9 @@ int64_t lora_oracle_apply_ex(int32_t dtype, int32_t n_tokens, int32_t d_in, int3
                              const int32_t *use_rslora, const void *const *At,
                              const void *const *B, const void *const *bias,
                              const double *const *dora, int32_t n_threads);
+int64_t lora_oracle_apply_saved(int32_t dtype, int32_t n_tokens, int32_t d_in, int32_t d_out,
+                                const void *x, void *y, const int32_t *idx, int32_t n_slots,
+                                const void *const *W, const void *const *bias, int32_t n_threads);
 double lora_oracle_scale(double lora_alpha, int32_t r, int32_t use_rslora);
 int64_t lora_oracle_adapter_bytes(const int32_t *d_in, const int32_t *d_out,
                                   const int32_t *targeted, int32_t n_modules, int32_t r,
@@ -177,6 +182,86 @@ static void run_case(int dtype, int T, int d_in, int d_out, int n_slots, const i
     free(rk); free(rs); free(alpha); free(x); free(y); free(y0); free(xv); free(yv);
 }
 
+/* Saved modules: slots with has_W[k] save a d_out x d_in W (and, for odd k, a
+ * bias); the other tokens keep y bit for bit. */
+static void run_saved_case(int dtype, int T, int d_in, int d_out, int n_slots, const int *has_W,
+                           const int *idx)
+{
+    const size_t es = dtype == BF16 ? 2 : 4;
+    void *x = malloc((size_t)T * d_in * es + 1), *y = malloc((size_t)T * d_out * es + 1);
+    void *y0 = malloc((size_t)T * d_out * es + 1);
+    double *xv = malloc(sizeof(double) * ((size_t)T * d_in + 1));
+    const void **W = calloc((size_t)n_slots, sizeof(void *));
+    const void **bias = calloc((size_t)n_slots, sizeof(void *));
+    double **Wv = calloc((size_t)n_slots, sizeof(double *)), **cv = calloc((size_t)n_slots, sizeof(double *));
+#define PUTS(buf, i, v, dst) do { double v_ = (v); \
+        if (dtype == BF16) { float f_ = (float)v_; uint32_t u_; memcpy(&u_, &f_, 4); \
+            ((uint16_t *)(buf))[i] = (uint16_t)(u_ >> 16); (dst) = bf16_value(((uint16_t *)(buf))[i]); } \
+        else { ((float *)(buf))[i] = (float)v_; (dst) = ((float *)(buf))[i]; } } while (0)
+    double scratch;
+    for (int64_t i = 0; i < (int64_t)T * d_in; ++i)
+        PUTS(x, i, urand(), xv[i]);
+    for (int64_t i = 0; i < (int64_t)T * d_out; ++i)
+        PUTS(y, i, urand(), scratch);
+    memcpy(y0, y, (size_t)T * d_out * es);
+    for (int k = 0; k < n_slots; ++k) {
+        if (!has_W[k])
+            continue;
+        void *w = malloc((size_t)d_out * d_in * es);
+        Wv[k] = malloc(sizeof(double) * (size_t)d_out * d_in);
+        for (int64_t i = 0; i < (int64_t)d_out * d_in; ++i)
+            PUTS(w, i, urand(), Wv[k][i]);
+        W[k] = w;
+        if (k & 1) {
+            void *c = malloc((size_t)d_out * es);
+            cv[k] = malloc(sizeof(double) * (size_t)d_out);
+            for (int n = 0; n < d_out; ++n)
+                PUTS(c, n, urand(), cv[k][n]);
+            bias[k] = c;
+        }
+    }
+#undef PUTS
+    int64_t applied = lora_oracle_apply_saved(dtype, T, d_in, d_out, x, y, idx, n_slots, W, bias, 2);
+    int64_t want = 0;
+    double worst = 0.0;
+    for (int t = 0; t < T; ++t) {
+        const int k = idx[t];
+        const int on = k >= 0 && k < n_slots && has_W[k];
+        want += on;
+        for (int n = 0; n < d_out; ++n) {
+            const int64_t o = (int64_t)t * d_out + n;
+            if (!on) {
+                if (memcmp((char *)y + o * es, (char *)y0 + o * es, es) != 0)
+                    ++failures;
+                continue;
+            }
+            double ref = cv[k] ? cv[k][n] : 0.0, mag = fabs(ref);
+            for (int i = 0; i < d_in; ++i) {
+                ref += xv[(int64_t)t * d_in + i] * Wv[k][(int64_t)n * d_in + i];
+                mag += fabs(xv[(int64_t)t * d_in + i] * Wv[k][(int64_t)n * d_in + i]);
+            }
+            double got = dtype == BF16 ? bf16_value(((uint16_t *)y)[o]) : ((float *)y)[o];
+            const double bound = (dtype == BF16 ? ldexp(fabs(ref), -8) : ldexp(fabs(ref), -23)) +
+                                 1e-12 * mag + 1e-300;
+            const double err = fabs(got - ref) / bound;
+            if (err > worst)
+                worst = err;
+        }
+    }
+    if (applied != want || worst > 1.0)
+        ++failures;
+    printf("saved case dtype=%s T=%d d_in=%d d_out=%d slots=%d: applied %lld of %lld, "
+           "worst err/bound %.3f\n", dtype == BF16 ? "bf16" : "fp32", T, d_in, d_out, n_slots,
+           (long long)applied, (long long)want, worst);
+    for (int k = 0; k < n_slots; ++k) {
+        free((void *)W[k]);
+        free((void *)bias[k]);
+        free(Wv[k]);
+        free(cv[k]);
+    }
+    free(W); free(bias); free(Wv); free(cv); free(x); free(y); free(y0); free(xv);
+}
+
 int main(void)
 {
     const int ranks4[4] = {4, 1, 0, 8};
@@ -190,6 +275,11 @@ int main(void)
         const int r1[1] = {1};
         const int one[3] = {0, 0, -1};
         run_case(dtype, 3, 16, 8, 1, r1, one, 0);             /* rank 1, one slot */
+    }
+    const int saved4[4] = {1, 1, 0, 1};
+    for (int dtype = 0; dtype < 2; ++dtype) {
+        run_saved_case(dtype, 0, 16, 8, 4, saved4, idx);      /* no tokens */
+        run_saved_case(dtype, 37, 24, 40, 4, saved4, idx);    /* bias on slots 1 and 3 */
     }
     const int32_t din[3] = {5120, 5120, 8192}, dout[3] = {8192, 1024, 5120}, tg[3] = {1, 0, 1};
     if (lora_oracle_adapter_bytes(din, dout, tg, 3, 32, 2) != (int64_t)(13312 + 13312) * 32 * 2)

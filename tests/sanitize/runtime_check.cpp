@@ -44,7 +44,7 @@ int main()
            LORA_ERR_INVALID_ARGUMENT, "create: modules NULL");
     expect(lora_slots_create(&ctx, 8, 16, ok_shape, 0, LORA_BF16, 256, 0),
            LORA_ERR_INVALID_ARGUMENT, "create: no modules");
-    expect(lora_slots_create(&ctx, 8, 16, ok_shape, 2, (lora_dtype)7, 256, 0),
+    expect(lora_slots_create(&ctx, 8, 16, ok_shape, 2, 7, 256, 0),
            LORA_ERR_INVALID_ARGUMENT, "create: unknown dtype");
     expect(lora_slots_create(&ctx, 8, 16, ok_shape, 2, LORA_BF16, 0, 0),
            LORA_ERR_INVALID_ARGUMENT, "create: max_tokens 0");
@@ -81,6 +81,10 @@ int main()
     expect(lora_expand_group(nullptr, 1, mods, ys, nullptr), LORA_ERR_INVALID_ARGUMENT, "expand_group: ctx NULL");
     expect(lora_apply_group(nullptr, 1, mods, xs, ys, nullptr, 0, nullptr), LORA_ERR_INVALID_ARGUMENT,
            "apply_group: ctx NULL");
+    expect(lora_apply_group_fused(nullptr, 1, mods, xs, ys, nullptr, 0, nullptr), LORA_ERR_INVALID_ARGUMENT,
+           "apply_group_fused: ctx NULL");
+    expect(lora_apply_group_noalloc(nullptr, 1, mods, xs, ys, nullptr, 0, nullptr),
+           LORA_ERR_INVALID_ARGUMENT, "apply_group_noalloc: ctx NULL");
     expect(lora_get_device_flags(nullptr, &flags), LORA_ERR_INVALID_ARGUMENT, "flags: ctx NULL");
     expect(lora_get_stats(nullptr, &st), LORA_ERR_INVALID_ARGUMENT, "stats: ctx NULL");
     expect(lora_profile_begin(nullptr, 4), LORA_ERR_INVALID_ARGUMENT, "profile_begin: ctx NULL");
