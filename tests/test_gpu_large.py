@@ -1,0 +1,100 @@
+"""Large bf16 batches of long slot runs (prefill-shaped), every row.
+
+Batches above 1024 tokens take the plan kernels and the segment-grouped
+(SGMV) shrink; these cases cover slot runs of every length: one slot, two
+equal runs, steep popularity (runs of a few tokens, which take the gather
+path), empty slots, modules an adapter does not target, skipped tokens, rank
+128, and a ctx sized for more tokens than the batch (where the shrink may
+split K).  Every row of every module is compared with the oracle; rows the
+update does not touch must stay bit-identical.  The no-alloc call runs one
+case too.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_close, from_dev, log, make_slots, run_oracle, to_dev
+from lora_adapter_application_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+# (name, T, slots, max rank, module shapes, zipf, base-only share, extras)
+CASES = [
+    ("one slot", 1025, 1, 16, [(512, 256)], 0.0, 0.0, {}),
+    ("two equal runs, rank 8", 5000, 2, 8, [(256, 512)], 0.0, 0.0, {}),
+    ("group of three", 3000, 8, 64, [(512, 1024), (1024, 256), (256, 256)], 1.1, 0.1,
+     {"empty": [5], "untargeted": [(2, 1), (6, 0)]}),
+    ("steep popularity, rank 128", 8192, 16, 128, [(1024, 512)], 3.0, 0.05, {}),
+    ("skipped tokens, rsLoRA", 20000, 4, 32, [(1024, 1024)], 0.5, 0.2,
+     {"rslora": True, "bad_idx": True}),
+    ("ctx for more tokens", 4096, 8, 64, [(512, 512), (512, 512)], 1.1, 0.0, {"max_tokens": 16384}),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def _case(i):
+    name, T, S, R, shapes, zipf, base, ex = CASES[i]
+    assert T > 1024 and T >= 128 * S        # long runs, plan kernels
+    rng = np.random.default_rng(71000 + i)
+    mods = [synth.Module(f"m{j}", d_in, d_out) for j, (d_in, d_out) in enumerate(shapes)]
+    ranks = [int(r) for r in rng.integers(1, R + 1, S)]
+    targeted = None
+    if ex.get("untargeted"):
+        targeted = [[True] * len(mods) for _ in range(S)]
+        for k, j in ex["untargeted"]:
+            targeted[k][j] = False
+    wl = synth.random_case(int(rng.integers(1 << 30)), synth.BF16, mods, T, S, R, ranks,
+                           targeted=targeted, p_base_only=base, zipf_s=zipf,
+                           empty_slots=ex.get("empty", []), rslora=ex.get("rslora", False))
+    if ex.get("bad_idx"):
+        wl.idx[rng.integers(0, T, 40)] = S + 3
+        wl.idx[rng.integers(0, T, 40)] = -7
+    return wl, ex
+
+
+def _check(wl, ys, what):
+    S = wl.max_loras
+    for i, m in enumerate(wl.modules):
+        got = from_dev(ys[i], wl.dtype)
+        check_close(got, run_oracle(wl, m.name), wl.dtype, f"{what} {m.name}")
+        applied = np.array([0 <= k < S and wl.adapters[k] is not None and m.name in wl.adapters[k].At
+                            for k in wl.idx])
+        assert np.array_equal(got[~applied], wl.y[m.name][~applied]), f"{what} {m.name}: untouched rows"
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_large_batch_matches_oracle(i):
+    wl, ex = _case(i)
+    counts = np.bincount(wl.idx[(wl.idx >= 0) & (wl.idx < wl.max_loras)], minlength=wl.max_loras)
+    log("case large batch", CASES[i][0], "T", wl.n_tokens, "S", wl.max_loras, "R", wl.max_rank,
+        "runs", counts.tolist())
+    Sl = make_slots(wl, max_tokens=ex.get("max_tokens"))
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in wl.modules]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in wl.modules]
+    Sl.prepare(idx)
+    Sl.apply_group(list(range(len(wl.modules))), xs, ys, idx)
+    torch.cuda.synchronize()
+    flags = Sl.flags()
+    Sl.close()
+    _check(wl, ys, CASES[i][0])
+    assert bool(flags & binding.LORA_FLAG_SLOT_INDEX_TOO_LARGE) == bool(ex.get("bad_idx"))
+
+
+def test_large_batch_through_the_no_alloc_call():
+    wl, _ = _case(2)
+    log("case large batch no-alloc", CASES[2][0])
+    Sl = make_slots(wl)
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in wl.modules]
+    ys = [to_dev(wl.y[m.name], wl.dtype) for m in wl.modules]
+    Sl.apply_group_noalloc(list(range(len(wl.modules))), xs, ys, idx)
+    torch.cuda.synchronize()
+    Sl.close()
+    _check(wl, ys, "no-alloc")
