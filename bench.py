@@ -391,8 +391,9 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         prof = slots.profile_end()
         n = prof["launches"]
         tot = prof["total_ms"]
-        # algorithmic bytes of one launch of each group
-        # x once per buffer read (once per group with --shared-x) plus each used slot's A^T
+        # algorithmic bytes of one launch of each group: the shrink reads x once per
+        # buffer (once per group with --shared-x) plus each used slot's A^T; the
+        # expand reads and writes y and reads each used slot's B
         shrink_bytes = [sum(b * mods[j].d_in * ((T_act if x_owner[j] == j else 0) + sum_r) for j in g)
                         for g in groups]
         expand_bytes = [sum(b * mods[j].d_out * (2 * T_act + sum_r) for j in g) for g in groups]
