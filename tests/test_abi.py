@@ -102,3 +102,14 @@ def test_calls_on_a_null_ctx_fail_cleanly(lib_path):
     assert lib.lora_shrink(None, None, 0, None) == E
     assert lib.lora_expand(None, None, 0, None) == E
     assert lib.lora_apply(None, None, None, None, 0, 0, None) == E
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message, before any GPU use."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
