@@ -4,8 +4,9 @@ Batches above 1024 tokens take the plan kernels and the segment-grouped
 (SGMV) shrink; these cases cover slot runs of every length: one slot, two
 equal runs, steep popularity (runs of a few tokens, which take the gather
 path), empty slots, modules an adapter does not target, skipped tokens, rank
-128, and a ctx sized for more tokens than the batch (where the shrink may
-split K).  Every row of every module is compared with the oracle; rows the
+128, a ctx sized for more tokens than the batch (where the shrink may split
+K), the largest pool the library allows (256 slots of rank 128) with 65536
+tokens, and fp32 data above 1024 tokens.  Every row of every module is compared with the oracle; rows the
 update does not touch must stay bit-identical.  The no-alloc call runs one
 case too.
 """
@@ -28,6 +29,9 @@ CASES = [
     ("skipped tokens, rsLoRA", 20000, 4, 32, [(1024, 1024)], 0.5, 0.2,
      {"rslora": True, "bad_idx": True}),
     ("ctx for more tokens", 4096, 8, 64, [(512, 512), (512, 512)], 1.1, 0.0, {"max_tokens": 16384}),
+    ("largest pool: 256 slots, rank 128, 65536 tokens", 65536, 256, 128, [(256, 256), (256, 264)],
+     0.5, 0.05, {}),
+    ("fp32 above 1024 tokens", 3000, 4, 32, [(264, 136)], 1.1, 0.1, {"dtype": "fp32"}),
 ]
 
 
@@ -49,7 +53,8 @@ def _case(i):
         targeted = [[True] * len(mods) for _ in range(S)]
         for k, j in ex["untargeted"]:
             targeted[k][j] = False
-    wl = synth.random_case(int(rng.integers(1 << 30)), synth.BF16, mods, T, S, R, ranks,
+    dtype = synth.FP32 if ex.get("dtype") == "fp32" else synth.BF16
+    wl = synth.random_case(int(rng.integers(1 << 30)), dtype, mods, T, S, R, ranks,
                            targeted=targeted, p_base_only=base, zipf_s=zipf,
                            empty_slots=ex.get("empty", []), rslora=ex.get("rslora", False))
     if ex.get("bad_idx"):
