@@ -85,6 +85,8 @@ def parse():
                    type=lambda v: [w for w in v.split(",") if w],
                    help="further workloads measured after the headline one and reported as "
                         "extra keys (empty: none)")
+    p.add_argument("--max-tokens", type=int, default=0,
+                   help="token capacity of the slot ctx (default: the batch's own size)")
     p.add_argument("--extra-steps", type=int, default=2000)
     p.add_argument("--extra-warmup", type=int, default=200)
     p.add_argument("--no-saved", dest="saved", action="store_false",
@@ -245,7 +247,7 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     shapes = [(m.d_in, m.d_out) for _ in range(L) for m in mods]
-    slots = binding.Slots(S, R, shapes, "bf16", max_tokens=T)
+    slots = binding.Slots(S, R, shapes, "bf16", max_tokens=max(T, args.max_tokens))
     gen = torch.Generator(device=dev)
     gen.manual_seed(20260101)
     for k, ad in enumerate(wl.adapters):

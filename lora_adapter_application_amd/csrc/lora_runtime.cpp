@@ -343,13 +343,19 @@ hipError_t sync_ctx_streams(lora_ctx *c)
     return first;
 }
 
-// K-split of the shrink for a batch of T tokens: enough workgroups to cover
-// the chip when the batch is small, none when it is large.
+// K-split of the shrink for a batch of T tokens in a group of n modules:
+// enough workgroups to cover the chip when the batch is small, none when it is
+// large.  A batch whose tiles times members already fill the chip's resident
+// workgroups (512) is not split even when the ctx has room for more partials:
+// a split saves the prefill shrink a few us and costs the expand, which sums
+// the partials, more (0.759 against 0.744 ms per Llama-7B prefill step).
 void choose_splits(const lora_ctx *c, const Workspace &ws, const BatchState &bs, int T, int d_in,
-                   int *splits, int *kchunk)
+                   int n, int *splits, int *kchunk)
 {
     const int tiles = max_tiles_for(T, c->S, bs.tile_cap);
     int want = ceil_div(1024, std::max(tiles, 1));
+    if (T > kInlinePlanTokens && tiles * n >= 512)
+        want = 1;
     int cap = std::min(kMaxSplits, std::max(1, d_in / 256));
     cap = std::min(cap, splits_cap(nb_template(c->R_pad)));
     cap = std::min(cap, std::max(1, ws.hbuf_rows / std::max(T, 1)));
@@ -435,7 +441,7 @@ ShrinkArgs shrink_args(lora_ctx *c, const Workspace &ws, BatchState &bs, int n,
         const int mod = modules[i];
         const lora_module_shape sh = c->shapes[mod];
         int splits = 1, kchunk = 0;
-        choose_splits(c, ws, bs, T, sh.d_in, &splits, &kchunk);
+        choose_splits(c, ws, bs, T, sh.d_in, n, &splits, &kchunk);
         a.x[i] = x[i];
         a.A[i] = c->A[mod];
         a.slot_stride_A[i] = c->strideA[mod];

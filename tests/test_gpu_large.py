@@ -6,7 +6,8 @@ equal runs, steep popularity (runs of a few tokens, which take the gather
 path), empty slots, modules an adapter does not target, skipped tokens, rank
 128, a ctx sized for more tokens than the batch (where the shrink may split
 K), the largest pool the library allows (256 slots of rank 128) with 65536
-tokens, and fp32 data above 1024 tokens.  Every row of every module is compared with the oracle; rows the
+tokens, fp32 data above 1024 tokens, and a batch that fills the chip in a ctx
+with room for three times its tokens (not split in K).  Every row of every module is compared with the oracle; rows the
 update does not touch must stay bit-identical.  The no-alloc call runs one
 case too.
 """
@@ -32,6 +33,8 @@ CASES = [
     ("largest pool: 256 slots, rank 128, 65536 tokens", 65536, 256, 128, [(256, 256), (256, 264)],
      0.5, 0.05, {}),
     ("fp32 above 1024 tokens", 3000, 4, 32, [(264, 136)], 1.1, 0.1, {"dtype": "fp32"}),
+    ("ctx for three times the batch, unsplit", 40000, 8, 64, [(512, 512)], 1.1, 0.0,
+     {"max_tokens": 131072}),
 ]
 
 
