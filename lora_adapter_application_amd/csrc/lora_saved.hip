@@ -20,7 +20,10 @@
 // written 32 bytes per lane.  The tile's x rows (gathered by token id) are
 // staged in LDS one 64-wide K block at a time, double buffered, and shared by
 // the four waves; each wave streams its own W rows straight into registers,
-// also double buffered.  Loads use clamped addresses, never a branch.
+// also double buffered.  Loads use clamped addresses, never a branch.  A launch
+// whose modules all have d_in a multiple of 64 takes saved_bf16_dma_kernel
+// instead: the same items, with x and W both staged in LDS by direct-to-LDS
+// loads three blocks deep.
 //
 // fp32: VALU, fp64 sums (products of two fp32 values are exact in fp64), the
 // same tiles; it serves fp32 contexts and exactness checks.
@@ -279,6 +282,237 @@ __global__ __launch_bounds__(256, 2) void saved_bf16_kernel(SavedArgs a)
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 with both operands staged in LDS by direct-to-LDS loads (modules whose
+// d_in is a multiple of 64).  Same work items and output as saved_bf16_kernel;
+// the four waves tile the run's 128 tokens x 256 columns 2 x 2 (wave w: tokens
+// 64 (w & 1) .., columns 128 (w >> 1) ..), and each 64-wide K block of x (128
+// rows) and of W (256 rows) goes global -> LDS with global_load_lds_dwordx4:
+// lane l of an instruction writes the 16 bytes at LDS offset 16 l of the
+// instruction's 1 KB, so no registers stage them.  A row of a stage is 128 bytes
+// (8 pieces of 16); piece c of row r sits in slot c ^ (r & 7), so that the 16
+// rows an MFMA operand read touches fall on distinct banks.  Three stages
+// rotate: the loads of blocks k + 1 and k + 2 run while block k is multiplied.
+constexpr int kDmaRowsX = 128, kDmaRowsW = kSavedCols;
+constexpr int kDmaStage = (kDmaRowsX + kDmaRowsW) * kBK;      // bf16 elements per stage
+
+// a wave issues 12 load instructions per block (4 for x, 8 for W): the
+// vmcnt(12) wait below leaves the next block's in flight
+static_assert(kDmaRowsX / 32 + kDmaRowsW / 32 == 12, "load instructions per block");
+
+// one global_load_lds_dwordx4, written as asm so that the compiler does not
+// track it: its own tracking cannot tell the stages apart and would wait for
+// every load in flight before each LDS read.  The waits for these loads are
+// explicit (s_waitcnt vmcnt in the kernel); lds is the wave-uniform LDS byte
+// address of the instruction's 1 KB.  m0 is not named as clobbered: the
+// compiler reserves it and sets it before each of its own uses.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint16_t *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
+}
+
+template <int R>
+__device__ __forceinline__ void dma_rows(uint32_t stage, const uint16_t *const (&src)[R / 32], int kb,
+                                         int wave, int lane)
+{
+    // instruction q of wave w fills LDS pieces (q * 4 + w) * 64 + lane: row
+    // (q * 4 + w) * 8 + lane / 8, slot lane % 8, which holds piece
+    // slot ^ (row & 7) of the row (rows are 8-aligned per instruction, so
+    // row & 7 = lane / 8)
+    const int piece = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int q = 0; q < R / 32; ++q)
+        dma16(src[q] + kb + piece * 8, stage + (uint32_t)((q * 4 + wave) * 64) * 16);
+}
+
+__device__ __forceinline__ uint4 lds_piece(const uint16_t *stage, int row, int piece)
+{
+    return *(const uint4 *)(stage + row * kBK + ((piece ^ (row & 7)) << 3));
+}
+
+__global__ __launch_bounds__(256, 1) void saved_bf16_dma_kernel(SavedArgs a)
+{
+    const int pairs = (a.grid_tiles + 1) / 2;
+    const int n_items = pairs * a.col_start[a.n];
+    const int w = saved_item(a.per_xcd);
+    if (w >= n_items)
+        return;
+    int m, chunk, pair;
+    saved_decode(a, w, m, chunk, pair);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, g = lane >> 4;
+    const int n_tiles = *a.n_tiles;
+    const int bt0 = 2 * pair, bt1 = min(2 * pair + 1, a.grid_tiles - 1);   // in bounds of the tile buffer
+    const Tile t0 = a.tiles[bt0], t1 = a.tiles[bt1];
+    const int tok0 = a.tile_tok[(int64_t)bt0 * kTileTokens + lane];
+    const int tok1 = a.tile_tok[(int64_t)bt1 * kTileTokens + lane];
+    if (bt0 >= n_tiles)
+        return;
+    const bool has1 = 2 * pair + 1 < n_tiles;
+    // three stages as three objects, so that the compiler can tell a stage
+    // being read from the ones the loads are filling and need not wait for
+    // those loads
+    __shared__ __attribute__((aligned(16))) uint16_t stage0[kDmaStage];
+    __shared__ __attribute__((aligned(16))) uint16_t stage1[kDmaStage];
+    __shared__ __attribute__((aligned(16))) uint16_t stage2[kDmaStage];
+    // the runs of the pair: one of up to 128 tokens when both tiles are the
+    // slot's, else each tile on its own
+    const bool joint = has1 && t1.slot == t0.slot;
+    const int n_runs = joint ? 1 : (has1 ? 2 : 1);
+    const int d_in = a.d_in[m], d_out = a.d_out[m];
+    const int nkb = d_in / kBK;
+    for (int run = 0; run < n_runs; ++run) {
+        const int slot = run == 0 ? t0.slot : t1.slot;
+        if (!saved_bit(a.saved[m], slot))
+            continue;
+        const int len = joint ? t0.len + t1.len : (run == 0 ? t0.len : t1.len);
+        const int lenA = joint ? t0.len : len;
+        const int tA = run == 0 ? tok0 : tok1;
+        // token of run row t (shuffles where every lane is active)
+        auto run_tok = [&](int t) {
+            const int ta = __shfl(tA, min(t, 63), 64);
+            const int tb = __shfl(tok1, max(t - lenA, 0) & 63, 64);
+            return t < lenA ? ta : tb;
+        };
+        // source rows of this thread's DMA instructions: x rows (q * 4 + wave) * 8
+        // + lane / 8 of the run (token 0's row past its end), W rows of the chunk
+        // (the last row past d_out)
+        const uint16_t *xsrc[kDmaRowsX / 32], *wsrc[kDmaRowsW / 32];
+        const uint16_t *x = (const uint16_t *)a.x[m];
+        const uint16_t *W = (const uint16_t *)a.W[m] + (int64_t)slot * a.slot_stride_W[m];
+#pragma unroll
+        for (int q = 0; q < kDmaRowsX / 32; ++q) {
+            const int r = (q * 4 + wave) * 8 + (lane >> 3);
+            const int tok = run_tok(r);
+            xsrc[q] = x + (int64_t)(r < len ? tok : 0) * d_in;
+        }
+#pragma unroll
+        for (int q = 0; q < kDmaRowsW / 32; ++q) {
+            const int r = (q * 4 + wave) * 8 + (lane >> 3);
+            wsrc[q] = W + (int64_t)min(chunk * kSavedCols + r, d_out - 1) * d_in;
+        }
+        f32x4_t acc[4][8];     // [subtile][column block]
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                acc[st][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int th = wave & 1, ch = wave >> 1;
+        const bool any_rows = th * 64 < len;
+        // one block: every operand fragment of the stage is read from LDS
+        // first, then the loads of the next block are issued into the other
+        // stage, then the MFMAs run while those loads are in flight (issued
+        // after the reads, the loads cannot make them wait)
+        uint4 xf[2][4], wf[2][8];
+        auto read_stage = [&](const uint16_t *cur) __attribute__((always_inline)) {
+            const uint16_t *xs = cur, *ws = cur + kDmaRowsX * kBK;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    xf[s][st] = lds_piece(xs, th * 64 + st * 16 + row, s * 4 + g);
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    // MFMA row i of block b -> column (i / 4) * 16 + (b % 4) * 4 + i % 4
+                    // of 64-column group b / 4
+                    const int n = ch * 128 + (b >> 2) * 64 + (row >> 2) * 16 + (b & 3) * 4 + (row & 3);
+                    wf[s][b] = lds_piece(ws, n, s * 4 + g);
+                }
+            }
+        };
+        auto mma_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st)
+                        acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, wf[s][b]), __builtin_bit_cast(bf16x8_t, xf[s][st]),
+                            acc[st][b], 0, 0, 0);
+        };
+        const int uwave = __builtin_amdgcn_readfirstlane(wave);
+        auto dma_stage = [&](const uint16_t *dst, int kb) __attribute__((always_inline)) {
+            const uint32_t base = lds_address(dst);
+            dma_rows<kDmaRowsX>(base, xsrc, kb, uwave, lane);
+            dma_rows<kDmaRowsW>(base + kDmaRowsX * kBK * 2, wsrc, kb, uwave, lane);
+        };
+        // block k: wait for this wave's loads of block k (those of block k + 1
+        // may still run: the 12 most recent), meet the other waves (their
+        // loads of block k are in too, and every read of block k - 1 is
+        // done), read block k, issue the loads of block k + 2 into the stage
+        // block k - 1 used, multiply
+        auto step = [&](const uint16_t *cur, const uint16_t *next2, int k) __attribute__((always_inline)) {
+            if (k + 1 < nkb)
+                asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            read_stage(cur);
+            if (k + 2 < nkb)
+                dma_stage(next2, (k + 2) * kBK);
+            if (any_rows)
+                mma_block();
+        };
+        if (run > 0)
+            __syncthreads();     // the first run's last LDS reads are done
+        dma_stage(stage0, 0);
+        if (nkb > 1)
+            dma_stage(stage1, kBK);
+        for (int k = 0; k < nkb; k += 3) {
+            step(stage0, stage2, k);
+            if (k + 1 >= nkb)
+                break;
+            step(stage1, stage0, k + 1);
+            if (k + 2 >= nkb)
+                break;
+            step(stage2, stage1, k + 2);
+        }
+        // epilogue: lane group g owns columns 16g .. 16g+15 of each 64-column
+        // group of the wave, for token th * 64 + st * 16 + row
+        int toks[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            toks[st] = run_tok(th * 64 + st * 16 + row);
+        const bool has_bias = saved_bit(a.has_bias[m], slot);
+        const uint16_t *bias = (const uint16_t *)a.bias[m] + (int64_t)slot * d_out;
+        uint16_t *y = (uint16_t *)a.y[m];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int col = chunk * kSavedCols + ch * 128 + grp * 64 + g * 16 + p * 8;
+                if (col >= d_out)
+                    continue;
+                uint4 cw = make_uint4(0, 0, 0, 0);
+                if (has_bias)
+                    cw = *(const uint4 *)(bias + col);
+                const uint32_t c[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int t = th * 64 + st * 16 + row;
+                    const int tok = toks[st];
+                    if (t >= len)
+                        continue;
+                    // columns col .. col+7 are rows 4g..4g+3 of blocks grp*4 + 2p and + 1
+                    const f32x4_t v0 = acc[st][grp * 4 + 2 * p], v1 = acc[st][grp * 4 + 2 * p + 1];
+                    uint4 o;
+                    o.x = pack_bf16x2(v0[0] + bf16_lo(c[0]), v0[1] + bf16_hi(c[0]));
+                    o.y = pack_bf16x2(v0[2] + bf16_lo(c[1]), v0[3] + bf16_hi(c[1]));
+                    o.z = pack_bf16x2(v1[0] + bf16_lo(c[2]), v1[1] + bf16_hi(c[2]));
+                    o.w = pack_bf16x2(v1[2] + bf16_lo(c[3]), v1[3] + bf16_hi(c[3]));
+                    *(uint4 *)(y + (int64_t)tok * d_out + col) = o;
+                }
+            }
+        }
+    }
+}
+
 // fp32: one workgroup = one tile x 64 columns x one member; thread tid takes
 // column tid % 64 for the 16 tokens (tid / 64) * 16 .. +15, with fp64 sums.
 constexpr int kF32Cols = 64;
@@ -345,7 +579,13 @@ hipError_t launch_saved(bool bf16, const SavedArgs &a, hipStream_t st, const Lau
         const int64_t items = (int64_t)((a.grid_tiles + 1) / 2) * a.col_start[a.n];
         SavedArgs b = a;
         b.per_xcd = (int)((items + kXcds - 1) / kXcds);
-        launch(saved_bf16_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
+        bool dma = true;
+        for (int i = 0; i < a.n; ++i)
+            dma = dma && a.d_in[i] % kBK == 0;
+        if (dma)
+            launch(saved_bf16_dma_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
+        else
+            launch(saved_bf16_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
     } else {
         int cols = 1;
         for (int i = 0; i < a.n; ++i)

@@ -206,3 +206,53 @@ def test_saved_module_full_size_prefill_sampled():
     log(f"saved o_proj full size: {len(rows)} rows, worst err/bound {w:.3f}")
     for n in ("q_proj", "k_proj", "v_proj"):
         check_close(got[n], run_oracle(wl, n), wl.dtype, f"prefill with saved o_proj {n}")
+
+
+# Modules whose d_in is a multiple of 64 take the kernel that stages x and W
+# through LDS with direct-to-LDS loads; these cases run it alone (groups of such
+# modules only): one K block (d_in 64), several, joint runs of two tiles and
+# pairs that straddle two slots, a bias on some slots.
+MODS64 = [synth.Module("q", 64, 72), synth.Module("o", 1024, 520), synth.Module("v", 512, 4104)]
+
+
+@pytest.mark.parametrize("T,path", [(700, "group"), (2500, "group"), (1500, "apply"), (37, "group")])
+def test_saved_modules_lds_staged_kernel_match_oracle(T, path):
+    targeted = [[(k, m.name) not in WHICH for m in MODS64] for k in range(6)]
+    wl = synth.random_case(8400 + T, synth.BF16, MODS64, T, 6, 32, [32, 16, 8, 1, 24, 32],
+                           targeted=targeted, p_base_only=0.1)
+    saved = _saved_weights(8500 + T, wl, WHICH)
+    keep = []
+    S = make_slots(wl, keep=keep)
+    _load_saved(S, wl, saved, keep)
+    log(f"case saved lds-staged T={T} {path}")
+    if path == "group":
+        got = run_gpu_groups(wl, S, groups=[["q", "o", "v"]])
+    else:
+        got = run_gpu(wl, S, path=path)
+    assert S.flags() == 0
+    S.close()
+    for m in MODS64:
+        ref = _reference(wl, saved, m.name)
+        w = check_close(got[m.name], ref, synth.BF16, f"saved lds-staged {m.name}")
+        touched = (wl.idx >= 0) & (wl.idx < 6)
+        assert np.array_equal(got[m.name][~touched], wl.y[m.name][~touched])
+        log(f"saved lds-staged T={T} {m.name}: worst err/bound {w:.3f}")
+
+
+def test_saved_lds_staged_kernel_exact_integers_bit_identical():
+    mods = [synth.Module("q", 64, 24), synth.Module("o", 128, 8)]
+    which = {(0, "q"), (1, "o"), (2, "q")}
+    targeted = [[(k, m.name) not in which for m in mods] for k in range(3)]
+    wl = synth.random_case(8600, synth.BF16, mods, 1333, 3, 16, [2, 1, 2], targeted=targeted,
+                           p_base_only=0.1, integer=True)
+    saved = _saved_weights(8601, wl, which, integer=True, bias_every=1)
+    keep = []
+    S = make_slots(wl, keep=keep)
+    _load_saved(S, wl, saved, keep)
+    got = run_gpu_groups(wl, S, groups=[["q", "o"]])
+    S.close()
+    for m in mods:
+        savers = [k for k in range(3) if (k, m.name) in which]
+        on = np.isin(wl.idx, savers)
+        ref = _reference(wl, saved, m.name)
+        assert np.array_equal(got[m.name][on], ref[on]), m.name
