@@ -203,6 +203,7 @@ struct SavedArgs {
     const int32_t *tile_tok;
     const int32_t *n_tiles;
     int32_t grid_tiles;
+    int32_t T;                          // tokens of the batch
     int32_t per_xcd;                    // bf16: work items per XCD (set by launch_saved)
     uint32_t saved[kMaxGroup][LORA_MAX_SLOTS / 32];     // slot k saves member m's module
     uint32_t has_bias[kMaxGroup][LORA_MAX_SLOTS / 32];  // ... with a bias

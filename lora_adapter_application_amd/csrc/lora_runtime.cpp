@@ -590,6 +590,7 @@ bool saved_args(const lora_ctx *c, const Workspace &ws, const BatchState &bs, in
     a.tile_tok = ws.plan.tile_tok;
     a.n_tiles = ws.plan.n_tiles;
     a.grid_tiles = max_tiles_for(bs.T, c->S, bs.tile_cap);
+    a.T = bs.T;
     return any;
 }
 

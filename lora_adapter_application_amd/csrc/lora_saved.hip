@@ -312,6 +312,13 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds)
                  : "memory");
 }
 
+// the same with a wave-uniform 64-bit base and a 32-bit byte offset per lane
+__device__ __forceinline__ void dma16_off(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const uint16_t *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
@@ -513,6 +520,250 @@ __global__ __launch_bounds__(256, 1) void saved_bf16_dma_kernel(SavedArgs a)
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 on 256 x 256 tiles, both operands staged in LDS by direct-to-LDS loads
+// (modules whose d_in is a multiple of 32).
+//
+// Work item = (member, column chunk of 256, quad of four consecutive plan
+// tiles).  The quad's consecutive tiles of one slot form a run, and run row r is
+// row r % 64 of the run's tile r / 64 (rows past a tile's length are computed
+// and not stored).  Eight waves (two per SIMD, so that one wave's LDS reads run
+// under the other's MFMAs) tile 256 run rows x 256 columns 2 x 4: wave w takes
+// rows 128 (w & 1) .. + 127 and columns 64 (w >> 1) .. + 63, 32 accumulators of
+// four.  Against the 128 x 256 tile above, a CU pulls half the L2 bytes per
+// flop: 32 KB per 32-deep block for 256 x 256 x 32 multiply-adds.
+//
+// Stage: 512 rows of 64 bytes (K = 32).  Rows 0 .. 255 are the run's x rows;
+// rows 256 .. 511 the chunk's W rows in MFMA order: stage row 256 + c*64 + b*16
+// + i holds column c*64 + (i/4)*16 + b*4 + i%4 of the chunk, so that each MFMA
+// operand is 16 consecutive stage rows and lane group g of a result owns 16
+// adjacent output columns.  16-byte piece p of stage row r sits in slot
+// p ^ qswz(r), qswz(r) = {0, 2, 1, 3}[(r >> 2) & 3]: the 16 rows of an operand
+// read fall on distinct banks whether the LDS serves 16 consecutive lanes of a
+// 16-byte read together, or lanes 0-7 with lanes 16-23.  Four 32 KB stages
+// rotate: at block k the loads of block k + 4 go into the stage block k came
+// from, the fragments of block k + 1 are read, and block k is multiplied from
+// registers.
+constexpr int kQRows = 256;                                  // run rows of a work item
+constexpr int kQBK = 32;                                     // K elements per stage row
+constexpr int kQStageBytes = (kQRows + kSavedCols) * kQBK * 2;   // 32 KB
+constexpr int kQThreads = 512;
+constexpr int kQBlockQuads = 4, kQBlockCols = 8;             // an L2 block of work items
+constexpr int kQBlockItems = kQBlockQuads * kQBlockCols;
+// direct-to-LDS loads per wave per block (1 KB each: 16 stage rows)
+constexpr int kQLoads = (kQRows + kSavedCols) * kQBK * 2 / 1024 / (kQThreads / 64);
+static_assert(kQLoads == 4, "loads per wave per block");
+
+__device__ __forceinline__ int qswz(int r)
+{
+    const int s = (r >> 2) & 3;
+    return ((s & 1) << 1) | (s >> 1);
+}
+
+// Work item w -> (member, column chunk, quad).  Per member, the (quad, chunk)
+// grid is padded to whole blocks of kQBlockQuads x kQBlockCols and laid out
+// block after block, chunk fastest inside a block: the items an XCD runs at one
+// time (one per CU) then share four quads of x rows and eight chunks of W rows
+// in its L2.  Returns false for padding.
+__device__ __forceinline__ bool quad_decode(const SavedArgs &a, int w, int &m, int &chunk, int &quad)
+{
+    const int quads = (a.grid_tiles + 3) >> 2;
+    const int qb = (quads + kQBlockQuads - 1) / kQBlockQuads;
+    int base = 0;
+    for (m = 0; m < a.n; ++m) {
+        const int cols = a.col_start[m + 1] - a.col_start[m];
+        const int cb = (cols + kQBlockCols - 1) / kQBlockCols;
+        const int items = qb * cb * kQBlockItems;
+        if (w < base + items) {
+            const int local = w - base;
+            const int blk = local / kQBlockItems, in = local % kQBlockItems;
+            quad = (blk / cb) * kQBlockQuads + in / kQBlockCols;
+            chunk = (blk % cb) * kQBlockCols + in % kQBlockCols;
+            return quad < quads && chunk < cols;
+        }
+        base += items;
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs a)
+{
+    int m, chunk, quad;
+    if (!quad_decode(a, saved_item(a.per_xcd), m, chunk, quad))
+        return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = lane & 15, g = lane >> 4;
+    const int n_tiles = *a.n_tiles;
+    const int bt0 = 4 * quad;
+    if (bt0 >= n_tiles)
+        return;
+    __shared__ __attribute__((aligned(16))) unsigned char stages[4 * kQStageBytes];
+    __shared__ int32_t qtok[4][kTileTokens];
+    __shared__ int32_t qslot[4], qlen[4];
+    if (tid < 4 * kTileTokens) {
+        // tile q of the quad (clamped into the tile buffer): tokens, slot, length
+        const int q = tid >> 6, bt = min(bt0 + q, a.grid_tiles - 1);
+        qtok[q][lane] = a.tile_tok[(int64_t)bt * kTileTokens + lane];
+        if (lane == 0) {
+            const Tile t = a.tiles[bt];
+            qslot[q] = t.slot;
+            qlen[q] = t.len;
+        }
+    }
+    __syncthreads();
+    const int nq = min(4, n_tiles - bt0);
+    const int d_in = a.d_in[m], d_out = a.d_out[m];
+    const int nkb = d_in / kQBK;
+    const int th = wave & 1, cq = wave >> 1;
+    const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)stages;
+    const uint16_t *x = (const uint16_t *)a.x[m];
+    int q0 = 0;
+    while (q0 < nq) {
+        const int slot = qslot[q0];
+        int q1 = q0 + 1;
+        while (q1 < nq && qslot[q1] == slot)
+            ++q1;
+        if (!saved_bit(a.saved[m], slot)) {
+            q0 = q1;
+            continue;
+        }
+        // run row r -> token, or -1 past the run or its tile
+        auto run_tok = [&](int r) {
+            const int q = q0 + (r >> 6), p = r & 63;
+            return (q < q1 && p < qlen[q]) ? qtok[q][p] : -1;
+        };
+        // this lane's rows of the wave's direct-to-LDS loads of a block:
+        // load i fills stage rows 16 j .. 16 j + 15, j = wave + 8 i, lane l
+        // row 16 j + l / 4 and slot l % 4 (piece (l % 4) ^ qswz(row))
+        // (byte offsets from the x or the slot's W base, kept in 32 bits: the
+        // launch takes this kernel only when both fit)
+        uint32_t src[kQLoads];
+        const uint16_t *W = (const uint16_t *)a.W[m] + (int64_t)slot * a.slot_stride_W[m];
+#pragma unroll
+        for (int i = 0; i < kQLoads; ++i) {
+            const int srow = 16 * (wave + 8 * i) + (lane >> 2);
+            const int piece = (lane & 3) ^ qswz(srow);
+            if (srow < kQRows) {
+                const int tok = run_tok(srow);
+                src[i] = ((uint32_t)(tok < 0 ? 0 : tok) * (uint32_t)d_in + piece * 8) * 2u;
+            } else {
+                const int rho = srow - kQRows, c = rho >> 6, b = (rho >> 4) & 3, ii = rho & 15;
+                const int n = min(chunk * kSavedCols + c * 64 + (ii >> 2) * 16 + b * 4 + (ii & 3), d_out - 1);
+                src[i] = ((uint32_t)n * (uint32_t)d_in + piece * 8) * 2u;
+            }
+        }
+        auto dma_block = [&](int stage, int kb) __attribute__((always_inline)) {
+            const uint32_t base = sbase + (uint32_t)stage * kQStageBytes + (uint32_t)wave * 1024u;
+#pragma unroll
+            for (int i = 0; i < kQLoads; ++i)
+                dma16_off(16 * (wave + 8 * i) < kQRows ? (const void *)x : (const void *)W,
+                          src[i] + (uint32_t)kb * 2u, base + (uint32_t)i * 8192u);
+        };
+        // fragments: x subtile st of a block (run rows th*128 + st*16 ..) and
+        // W block b (stage rows 256 + cq*64 + b*16 ..)
+        auto x_frag = [&](int stage, int st) __attribute__((always_inline)) {
+            const int r = th * 128 + st * 16 + row;
+            return *(const uint4 *)(stages + stage * kQStageBytes + r * 64 + ((g ^ qswz(r)) << 4));
+        };
+        auto w_frag = [&](int stage, int b) __attribute__((always_inline)) {
+            const int r = kQRows + cq * 64 + b * 16 + row;
+            return *(const uint4 *)(stages + stage * kQStageBytes + r * 64 + ((g ^ qswz(r)) << 4));
+        };
+        f32x4_t acc[8][4];     // [x subtile][W block]
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[st][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uint4 X[8], Wf[4];
+        // Block k (its fragments in X and Wf): wait for this wave's loads of
+        // block k + 1 (those of k + 2 and k + 3 may still run) and for its
+        // fragment reads of block k; meet the other waves (their loads of block
+        // k + 1 are in, their reads of block k are done); load block k + 4 into
+        // block k's stage; multiply block k subtile by subtile, reading block
+        // k + 1's x fragment of each subtile once the subtile is done with
+        // block k's, then block k + 1's W fragments.  The waits and loads
+        // depend on how many blocks remain; the reads and MFMAs do not (after
+        // the last block the reads fetch a stale stage that nothing uses, and a
+        // wave whose rows are all past the run multiplies what is never
+        // stored), so the multiply code has no branches.
+        if (q0 > 0)
+            __syncthreads();     // the previous run's last fragment reads are done
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < nkb)
+                dma_block(j, j * kQBK);
+        // block 0's loads are the oldest: the rest (up to 12) may still run
+        if (nkb >= 4)
+            asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            X[st] = x_frag(0, st);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            Wf[b] = w_frag(0, b);
+        for (int k = 0; k < nkb; ++k) {
+            const int ahead = nkb - 2 - k;
+            if (ahead >= 2)
+                asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else if (ahead == 1)
+                asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (k + 4 < nkb)
+                dma_block(k & 3, (k + 4) * kQBK);
+            const int nx = (k + 1) & 3;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, Wf[b]), __builtin_bit_cast(bf16x8_t, X[st]), acc[st][b],
+                        0, 0, 0);
+                X[st] = x_frag(nx, st);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                Wf[b] = w_frag(nx, b);
+        }
+        // epilogue: lane group g owns columns cq*64 + g*16 .. +15 of the chunk
+        // for run rows th*128 + st*16 + row
+        if (q0 + 2 * th < q1) {
+            uint16_t *y = (uint16_t *)a.y[m];
+            const bool has_bias = saved_bit(a.has_bias[m], slot);
+            const uint16_t *bias = (const uint16_t *)a.bias[m] + (int64_t)slot * d_out;
+            const int col = chunk * kSavedCols + cq * 64 + g * 16;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                if (col + p * 8 >= d_out)
+                    continue;
+                uint4 cw = make_uint4(0, 0, 0, 0);
+                if (has_bias)
+                    cw = *(const uint4 *)(bias + col + p * 8);
+                const uint32_t c[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    const int tok = run_tok(th * 128 + st * 16 + row);
+                    if (tok < 0)
+                        continue;
+                    // columns col + 8p .. +7: rows 4g..4g+3 of blocks 2p and 2p + 1
+                    const f32x4_t v0 = acc[st][2 * p], v1 = acc[st][2 * p + 1];
+                    uint4 o;
+                    o.x = pack_bf16x2(v0[0] + bf16_lo(c[0]), v0[1] + bf16_hi(c[0]));
+                    o.y = pack_bf16x2(v0[2] + bf16_lo(c[1]), v0[3] + bf16_hi(c[1]));
+                    o.z = pack_bf16x2(v1[0] + bf16_lo(c[2]), v1[1] + bf16_hi(c[2]));
+                    o.w = pack_bf16x2(v1[2] + bf16_lo(c[3]), v1[3] + bf16_hi(c[3]));
+                    *(uint4 *)(y + (int64_t)tok * d_out + col + p * 8) = o;
+                }
+            }
+        }
+        q0 = q1;
+    }
+}
+
 // fp32: one workgroup = one tile x 64 columns x one member; thread tid takes
 // column tid % 64 for the 16 tokens (tid / 64) * 16 .. +15, with fp64 sums.
 constexpr int kF32Cols = 64;
@@ -573,11 +824,37 @@ __global__ __launch_bounds__(256) void saved_f32_kernel(SavedArgs a)
 
 }  // namespace
 
+// The 256 x 256 kernel takes a launch whose modules all have d_in a multiple
+// of 32 and whose x and per-slot W are under 4 GB (its loads address them by
+// 32-bit byte offsets); any other bf16 launch takes saved_bf16_kernel.
+static bool quad_fits(const SavedArgs &a)
+{
+    for (int i = 0; i < a.n; ++i) {
+        const uint64_t d_in = (uint64_t)a.d_in[i];
+        if (d_in % kQBK || (uint64_t)a.T * d_in * 2 > UINT32_MAX || (uint64_t)a.d_out[i] * d_in * 2 > UINT32_MAX)
+            return false;
+    }
+    return true;
+}
+
 hipError_t launch_saved(bool bf16, const SavedArgs &a, hipStream_t st, const LaunchTiming &t)
 {
     if (bf16) {
-        const int64_t items = (int64_t)((a.grid_tiles + 1) / 2) * a.col_start[a.n];
         SavedArgs b = a;
+        if (quad_fits(a)) {
+            // work items as quad_decode lays them out (whole blocks per member)
+            const int64_t quads = (a.grid_tiles + 3) / 4;
+            const int64_t qb = (quads + kQBlockQuads - 1) / kQBlockQuads;
+            int64_t items = 0;
+            for (int i = 0; i < a.n; ++i) {
+                const int64_t cols = a.col_start[i + 1] - a.col_start[i];
+                items += qb * ((cols + kQBlockCols - 1) / kQBlockCols) * kQBlockItems;
+            }
+            b.per_xcd = (int)((items + kXcds - 1) / kXcds);
+            launch(saved_bf16_quad_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(kQThreads), st, t, b);
+            return hipGetLastError();
+        }
+        const int64_t items = (int64_t)((a.grid_tiles + 1) / 2) * a.col_start[a.n];
         b.per_xcd = (int)((items + kXcds - 1) / kXcds);
         bool dma = true;
         for (int i = 0; i < a.n; ++i)
