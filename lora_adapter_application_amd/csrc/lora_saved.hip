@@ -9,21 +9,21 @@
 // kernel is a segmented GEMM on the matrix cores over the batch's plan (tiles of
 // at most 64 tokens of one slot, the same tiles the shrink and the expand use).
 //
-// bf16: one workgroup = a pair of consecutive plan tiles x kSavedCols output
-// columns x one group member; wave w owns columns 64w .. 64w+63 for all of the
-// run's 16-token subtiles.  The product is formed transposed, out[n][t] = sum_k W[n][k] x[t][k],
-// with v_mfma_f32_16x16x32_bf16 (lane l gives row l & 15 of the A operand and
-// column l & 15 of the B operand with the K slice 8g .. 8g+7 of lane group
-// g = l >> 4; the result's rows 4g .. 4g+3 of column l & 15 land in lane l).
-// MFMA row i of block b is output column (i / 4) * 16 + b * 4 + i % 4 of the
-// wave's 64, so lane group g owns 16 adjacent columns of one token and y is
-// written 32 bytes per lane.  The tile's x rows (gathered by token id) are
-// staged in LDS one 64-wide K block at a time, double buffered, and shared by
-// the four waves; each wave streams its own W rows straight into registers,
-// also double buffered.  Loads use clamped addresses, never a branch.  A launch
-// whose modules all have d_in a multiple of 64 takes saved_bf16_dma_kernel
-// instead: the same items, with x and W both staged in LDS by direct-to-LDS
-// loads three blocks deep.
+// bf16, any d_in (saved_bf16_kernel): one workgroup = a pair of consecutive
+// plan tiles x kSavedCols output columns x one group member; wave w owns
+// columns 64w .. 64w+63 for all of the run's 16-token subtiles.  The product is
+// formed transposed, out[n][t] = sum_k W[n][k] x[t][k], with
+// v_mfma_f32_16x16x32_bf16 (lane l gives row l & 15 of the A operand and column
+// l & 15 of the B operand with the K slice 8g .. 8g+7 of lane group g = l >> 4;
+// the result's rows 4g .. 4g+3 of column l & 15 land in lane l).  MFMA row i of
+// block b is output column (i / 4) * 16 + b * 4 + i % 4 of the wave's 64, so
+// lane group g owns 16 adjacent columns of one token and y is written 32 bytes
+// per lane.  The tile's x rows (gathered by token id) are staged in LDS one
+// 64-wide K block at a time, double buffered, and shared by the four waves;
+// each wave streams its own W rows straight into registers, also double
+// buffered.  Loads use clamped addresses, never a branch.  A launch whose
+// modules all have d_in a multiple of 64 takes saved_bf16_quad_kernel instead:
+// 256 x 256 tiles with x and W both staged in LDS by direct-to-LDS loads.
 //
 // fp32: VALU, fp64 sums (products of two fp32 values are exact in fp64), the
 // same tiles; it serves fp32 contexts and exactness checks.
@@ -282,247 +282,23 @@ __global__ __launch_bounds__(256, 2) void saved_bf16_kernel(SavedArgs a)
     }
 }
 
-// ----------------------------------------------------------------------------
-// bf16 with both operands staged in LDS by direct-to-LDS loads (modules whose
-// d_in is a multiple of 64).  Same work items and output as saved_bf16_kernel;
-// the four waves tile the run's 128 tokens x 256 columns 2 x 2 (wave w: tokens
-// 64 (w & 1) .., columns 128 (w >> 1) ..), and each 64-wide K block of x (128
-// rows) and of W (256 rows) goes global -> LDS with global_load_lds_dwordx4:
-// lane l of an instruction writes the 16 bytes at LDS offset 16 l of the
-// instruction's 1 KB, so no registers stage them.  A row of a stage is 128 bytes
-// (8 pieces of 16); piece c of row r sits in slot c ^ (r & 7), so that the 16
-// rows an MFMA operand read touches fall on distinct banks.  Three stages
-// rotate: the loads of blocks k + 1 and k + 2 run while block k is multiplied.
-constexpr int kDmaRowsX = 128, kDmaRowsW = kSavedCols;
-constexpr int kDmaStage = (kDmaRowsX + kDmaRowsW) * kBK;      // bf16 elements per stage
-
-// a wave issues 12 load instructions per block (4 for x, 8 for W): the
-// vmcnt(12) wait below leaves the next block's in flight
-static_assert(kDmaRowsX / 32 + kDmaRowsW / 32 == 12, "load instructions per block");
-
-// one global_load_lds_dwordx4, written as asm so that the compiler does not
-// track it: its own tracking cannot tell the stages apart and would wait for
-// every load in flight before each LDS read.  The waits for these loads are
-// explicit (s_waitcnt vmcnt in the kernel); lds is the wave-uniform LDS byte
-// address of the instruction's 1 KB.  m0 is not named as clobbered: the
-// compiler reserves it and sets it before each of its own uses.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-                 : "memory");
-}
-
-// the same with a wave-uniform 64-bit base and a 32-bit byte offset per lane
+// One global_load_lds_dwordx4 with a wave-uniform 64-bit base and a 32-bit
+// byte offset per lane, written as asm so that the compiler does not track it:
+// its own tracking cannot tell the stages apart and would wait for every load
+// in flight before each LDS read.  The waits for these loads are explicit
+// (s_waitcnt vmcnt in the kernel); lane l writes the 16 bytes at LDS offset
+// 16 l of the instruction's 1 KB, whose wave-uniform address is lds.  m0 is
+// not named as clobbered: the compiler reserves it and sets it before each of
+// its own uses.
 __device__ __forceinline__ void dma16_off(const void *base, uint32_t off, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                  : "memory");
 }
 
-__device__ __forceinline__ uint32_t lds_address(const uint16_t *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
-}
-
-template <int R>
-__device__ __forceinline__ void dma_rows(uint32_t stage, const uint16_t *const (&src)[R / 32], int kb,
-                                         int wave, int lane)
-{
-    // instruction q of wave w fills LDS pieces (q * 4 + w) * 64 + lane: row
-    // (q * 4 + w) * 8 + lane / 8, slot lane % 8, which holds piece
-    // slot ^ (row & 7) of the row (rows are 8-aligned per instruction, so
-    // row & 7 = lane / 8)
-    const int piece = (lane & 7) ^ (lane >> 3);
-#pragma unroll
-    for (int q = 0; q < R / 32; ++q)
-        dma16(src[q] + kb + piece * 8, stage + (uint32_t)((q * 4 + wave) * 64) * 16);
-}
-
-__device__ __forceinline__ uint4 lds_piece(const uint16_t *stage, int row, int piece)
-{
-    return *(const uint4 *)(stage + row * kBK + ((piece ^ (row & 7)) << 3));
-}
-
-__global__ __launch_bounds__(256, 1) void saved_bf16_dma_kernel(SavedArgs a)
-{
-    const int pairs = (a.grid_tiles + 1) / 2;
-    const int n_items = pairs * a.col_start[a.n];
-    const int w = saved_item(a.per_xcd);
-    if (w >= n_items)
-        return;
-    int m, chunk, pair;
-    saved_decode(a, w, m, chunk, pair);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = lane & 15, g = lane >> 4;
-    const int n_tiles = *a.n_tiles;
-    const int bt0 = 2 * pair, bt1 = min(2 * pair + 1, a.grid_tiles - 1);   // in bounds of the tile buffer
-    const Tile t0 = a.tiles[bt0], t1 = a.tiles[bt1];
-    const int tok0 = a.tile_tok[(int64_t)bt0 * kTileTokens + lane];
-    const int tok1 = a.tile_tok[(int64_t)bt1 * kTileTokens + lane];
-    if (bt0 >= n_tiles)
-        return;
-    const bool has1 = 2 * pair + 1 < n_tiles;
-    // three stages as three objects, so that the compiler can tell a stage
-    // being read from the ones the loads are filling and need not wait for
-    // those loads
-    __shared__ __attribute__((aligned(16))) uint16_t stage0[kDmaStage];
-    __shared__ __attribute__((aligned(16))) uint16_t stage1[kDmaStage];
-    __shared__ __attribute__((aligned(16))) uint16_t stage2[kDmaStage];
-    // the runs of the pair: one of up to 128 tokens when both tiles are the
-    // slot's, else each tile on its own
-    const bool joint = has1 && t1.slot == t0.slot;
-    const int n_runs = joint ? 1 : (has1 ? 2 : 1);
-    const int d_in = a.d_in[m], d_out = a.d_out[m];
-    const int nkb = d_in / kBK;
-    for (int run = 0; run < n_runs; ++run) {
-        const int slot = run == 0 ? t0.slot : t1.slot;
-        if (!saved_bit(a.saved[m], slot))
-            continue;
-        const int len = joint ? t0.len + t1.len : (run == 0 ? t0.len : t1.len);
-        const int lenA = joint ? t0.len : len;
-        const int tA = run == 0 ? tok0 : tok1;
-        // token of run row t (shuffles where every lane is active)
-        auto run_tok = [&](int t) {
-            const int ta = __shfl(tA, min(t, 63), 64);
-            const int tb = __shfl(tok1, max(t - lenA, 0) & 63, 64);
-            return t < lenA ? ta : tb;
-        };
-        // source rows of this thread's DMA instructions: x rows (q * 4 + wave) * 8
-        // + lane / 8 of the run (token 0's row past its end), W rows of the chunk
-        // (the last row past d_out)
-        const uint16_t *xsrc[kDmaRowsX / 32], *wsrc[kDmaRowsW / 32];
-        const uint16_t *x = (const uint16_t *)a.x[m];
-        const uint16_t *W = (const uint16_t *)a.W[m] + (int64_t)slot * a.slot_stride_W[m];
-#pragma unroll
-        for (int q = 0; q < kDmaRowsX / 32; ++q) {
-            const int r = (q * 4 + wave) * 8 + (lane >> 3);
-            const int tok = run_tok(r);
-            xsrc[q] = x + (int64_t)(r < len ? tok : 0) * d_in;
-        }
-#pragma unroll
-        for (int q = 0; q < kDmaRowsW / 32; ++q) {
-            const int r = (q * 4 + wave) * 8 + (lane >> 3);
-            wsrc[q] = W + (int64_t)min(chunk * kSavedCols + r, d_out - 1) * d_in;
-        }
-        f32x4_t acc[4][8];     // [subtile][column block]
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                acc[st][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int th = wave & 1, ch = wave >> 1;
-        const bool any_rows = th * 64 < len;
-        // one block: every operand fragment of the stage is read from LDS
-        // first, then the loads of the next block are issued into the other
-        // stage, then the MFMAs run while those loads are in flight (issued
-        // after the reads, the loads cannot make them wait)
-        uint4 xf[2][4], wf[2][8];
-        auto read_stage = [&](const uint16_t *cur) __attribute__((always_inline)) {
-            const uint16_t *xs = cur, *ws = cur + kDmaRowsX * kBK;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    xf[s][st] = lds_piece(xs, th * 64 + st * 16 + row, s * 4 + g);
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    // MFMA row i of block b -> column (i / 4) * 16 + (b % 4) * 4 + i % 4
-                    // of 64-column group b / 4
-                    const int n = ch * 128 + (b >> 2) * 64 + (row >> 2) * 16 + (b & 3) * 4 + (row & 3);
-                    wf[s][b] = lds_piece(ws, n, s * 4 + g);
-                }
-            }
-        };
-        auto mma_block = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-#pragma unroll
-                    for (int st = 0; st < 4; ++st)
-                        acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, wf[s][b]), __builtin_bit_cast(bf16x8_t, xf[s][st]),
-                            acc[st][b], 0, 0, 0);
-        };
-        const int uwave = __builtin_amdgcn_readfirstlane(wave);
-        auto dma_stage = [&](const uint16_t *dst, int kb) __attribute__((always_inline)) {
-            const uint32_t base = lds_address(dst);
-            dma_rows<kDmaRowsX>(base, xsrc, kb, uwave, lane);
-            dma_rows<kDmaRowsW>(base + kDmaRowsX * kBK * 2, wsrc, kb, uwave, lane);
-        };
-        // block k: wait for this wave's loads of block k (those of block k + 1
-        // may still run: the 12 most recent), meet the other waves (their
-        // loads of block k are in too, and every read of block k - 1 is
-        // done), read block k, issue the loads of block k + 2 into the stage
-        // block k - 1 used, multiply
-        auto step = [&](const uint16_t *cur, const uint16_t *next2, int k) __attribute__((always_inline)) {
-            if (k + 1 < nkb)
-                asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            read_stage(cur);
-            if (k + 2 < nkb)
-                dma_stage(next2, (k + 2) * kBK);
-            if (any_rows)
-                mma_block();
-        };
-        if (run > 0)
-            __syncthreads();     // the first run's last LDS reads are done
-        dma_stage(stage0, 0);
-        if (nkb > 1)
-            dma_stage(stage1, kBK);
-        for (int k = 0; k < nkb; k += 3) {
-            step(stage0, stage2, k);
-            if (k + 1 >= nkb)
-                break;
-            step(stage1, stage0, k + 1);
-            if (k + 2 >= nkb)
-                break;
-            step(stage2, stage1, k + 2);
-        }
-        // epilogue: lane group g owns columns 16g .. 16g+15 of each 64-column
-        // group of the wave, for token th * 64 + st * 16 + row
-        int toks[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-            toks[st] = run_tok(th * 64 + st * 16 + row);
-        const bool has_bias = saved_bit(a.has_bias[m], slot);
-        const uint16_t *bias = (const uint16_t *)a.bias[m] + (int64_t)slot * d_out;
-        uint16_t *y = (uint16_t *)a.y[m];
-#pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int col = chunk * kSavedCols + ch * 128 + grp * 64 + g * 16 + p * 8;
-                if (col >= d_out)
-                    continue;
-                uint4 cw = make_uint4(0, 0, 0, 0);
-                if (has_bias)
-                    cw = *(const uint4 *)(bias + col);
-                const uint32_t c[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int t = th * 64 + st * 16 + row;
-                    const int tok = toks[st];
-                    if (t >= len)
-                        continue;
-                    // columns col .. col+7 are rows 4g..4g+3 of blocks grp*4 + 2p and + 1
-                    const f32x4_t v0 = acc[st][grp * 4 + 2 * p], v1 = acc[st][grp * 4 + 2 * p + 1];
-                    uint4 o;
-                    o.x = pack_bf16x2(v0[0] + bf16_lo(c[0]), v0[1] + bf16_hi(c[0]));
-                    o.y = pack_bf16x2(v0[2] + bf16_lo(c[1]), v0[3] + bf16_hi(c[1]));
-                    o.z = pack_bf16x2(v1[0] + bf16_lo(c[2]), v1[1] + bf16_hi(c[2]));
-                    o.w = pack_bf16x2(v1[2] + bf16_lo(c[3]), v1[3] + bf16_hi(c[3]));
-                    *(uint4 *)(y + (int64_t)tok * d_out + col) = o;
-                }
-            }
-        }
-    }
-}
-
 // ----------------------------------------------------------------------------
 // bf16 on 256 x 256 tiles, both operands staged in LDS by direct-to-LDS loads
-// (modules whose d_in is a multiple of 32).
+// (modules whose d_in is a multiple of 64).
 //
 // Work item = (member, column chunk of 256, quad of four consecutive plan
 // tiles).  The quad's consecutive tiles of one slot form a run, and run row r is
@@ -530,35 +306,32 @@ __global__ __launch_bounds__(256, 1) void saved_bf16_dma_kernel(SavedArgs a)
 // and not stored).  Eight waves (two per SIMD, so that one wave's LDS reads run
 // under the other's MFMAs) tile 256 run rows x 256 columns 2 x 4: wave w takes
 // rows 128 (w & 1) .. + 127 and columns 64 (w >> 1) .. + 63, 32 accumulators of
-// four.  Against the 128 x 256 tile above, a CU pulls half the L2 bytes per
-// flop: 32 KB per 32-deep block for 256 x 256 x 32 multiply-adds.
+// four.  Against the 128 x 256 tile above, a CU pulls two thirds of the L2
+// bytes per flop.
 //
-// Stage: 512 rows of 64 bytes (K = 32).  Rows 0 .. 255 are the run's x rows;
-// rows 256 .. 511 the chunk's W rows in MFMA order: stage row 256 + c*64 + b*16
-// + i holds column c*64 + (i/4)*16 + b*4 + i%4 of the chunk, so that each MFMA
-// operand is 16 consecutive stage rows and lane group g of a result owns 16
-// adjacent output columns.  16-byte piece p of stage row r sits in slot
-// p ^ qswz(r), qswz(r) = {0, 2, 1, 3}[(r >> 2) & 3]: the 16 rows of an operand
-// read fall on distinct banks whether the LDS serves 16 consecutive lanes of a
-// 16-byte read together, or lanes 0-7 with lanes 16-23.  Four 32 KB stages
-// rotate: at block k the loads of block k + 4 go into the stage block k came
-// from, the fragments of block k + 1 are read, and block k is multiplied from
-// registers.
+// Stage: 512 rows of 128 bytes (K = 64), so that every load request covers a
+// whole 128-byte line (64-byte rows, with twice the stages, ran 10% slower).
+// Rows 0 .. 255 are the run's x rows; rows 256 .. 511 the chunk's W rows in
+// MFMA order: stage row 256 + c*64 + b*16 + i holds column c*64 + (i/4)*16 +
+// b*4 + i%4 of the chunk, so that each MFMA operand is 16 consecutive stage rows
+// and lane group g of a result owns 16 adjacent output columns.  16-byte piece p
+// of stage row r sits in slot p ^ qswz(r), qswz(r) = (r & 7) ^ ((r >> 3) & 1):
+// the 16 rows of an operand read fall on distinct banks whether the LDS serves
+// 16 consecutive lanes of a 16-byte read together, or lanes 0-7 with lanes
+// 16-23.  Two 64 KB stages alternate: halfway through block k (its second
+// 32-deep half is in registers by then) the loads of block k + 2 go into block
+// k's stage.
 constexpr int kQRows = 256;                                  // run rows of a work item
-constexpr int kQBK = 32;                                     // K elements per stage row
-constexpr int kQStageBytes = (kQRows + kSavedCols) * kQBK * 2;   // 32 KB
+constexpr int kQBK = 64;                                     // K elements per stage row
+constexpr int kQStageBytes = (kQRows + kSavedCols) * kQBK * 2;   // 64 KB
 constexpr int kQThreads = 512;
 constexpr int kQBlockQuads = 4, kQBlockCols = 8;             // an L2 block of work items
 constexpr int kQBlockItems = kQBlockQuads * kQBlockCols;
 // direct-to-LDS loads per wave per block (1 KB each: 16 stage rows)
 constexpr int kQLoads = (kQRows + kSavedCols) * kQBK * 2 / 1024 / (kQThreads / 64);
-static_assert(kQLoads == 4, "loads per wave per block");
+static_assert(kQLoads == 8, "loads per wave per block");
 
-__device__ __forceinline__ int qswz(int r)
-{
-    const int s = (r >> 2) & 3;
-    return ((s & 1) << 1) | (s >> 1);
-}
+__device__ __forceinline__ int qswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Work item w -> (member, column chunk, quad).  Per member, the (quad, chunk)
 // grid is padded to whole blocks of kQBlockQuads x kQBlockCols and laid out
@@ -598,7 +371,7 @@ __global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs
     const int bt0 = 4 * quad;
     if (bt0 >= n_tiles)
         return;
-    __shared__ __attribute__((aligned(16))) unsigned char stages[4 * kQStageBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char stages[2 * kQStageBytes];
     __shared__ int32_t qtok[4][kTileTokens];
     __shared__ int32_t qslot[4], qlen[4];
     if (tid < 4 * kTileTokens) {
@@ -634,16 +407,16 @@ __global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs
             return (q < q1 && p < qlen[q]) ? qtok[q][p] : -1;
         };
         // this lane's rows of the wave's direct-to-LDS loads of a block:
-        // load i fills stage rows 16 j .. 16 j + 15, j = wave + 8 i, lane l
-        // row 16 j + l / 4 and slot l % 4 (piece (l % 4) ^ qswz(row))
+        // load i fills stage rows 8 j .. 8 j + 7, j = wave + 8 i, lane l row
+        // 8 j + l / 8 and slot l % 8 (piece (l % 8) ^ qswz(row))
         // (byte offsets from the x or the slot's W base, kept in 32 bits: the
         // launch takes this kernel only when both fit)
         uint32_t src[kQLoads];
         const uint16_t *W = (const uint16_t *)a.W[m] + (int64_t)slot * a.slot_stride_W[m];
 #pragma unroll
         for (int i = 0; i < kQLoads; ++i) {
-            const int srow = 16 * (wave + 8 * i) + (lane >> 2);
-            const int piece = (lane & 3) ^ qswz(srow);
+            const int srow = 8 * (wave + 8 * i) + (lane >> 3);
+            const int piece = (lane & 7) ^ qswz(srow);
             if (srow < kQRows) {
                 const int tok = run_tok(srow);
                 src[i] = ((uint32_t)(tok < 0 ? 0 : tok) * (uint32_t)d_in + piece * 8) * 2u;
@@ -657,18 +430,18 @@ __global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs
             const uint32_t base = sbase + (uint32_t)stage * kQStageBytes + (uint32_t)wave * 1024u;
 #pragma unroll
             for (int i = 0; i < kQLoads; ++i)
-                dma16_off(16 * (wave + 8 * i) < kQRows ? (const void *)x : (const void *)W,
+                dma16_off(8 * (wave + 8 * i) < kQRows ? (const void *)x : (const void *)W,
                           src[i] + (uint32_t)kb * 2u, base + (uint32_t)i * 8192u);
         };
         // fragments: x subtile st of a block (run rows th*128 + st*16 ..) and
         // W block b (stage rows 256 + cq*64 + b*16 ..)
-        auto x_frag = [&](int stage, int st) __attribute__((always_inline)) {
+        auto x_frag = [&](int stage, int st, int s) __attribute__((always_inline)) {
             const int r = th * 128 + st * 16 + row;
-            return *(const uint4 *)(stages + stage * kQStageBytes + r * 64 + ((g ^ qswz(r)) << 4));
+            return *(const uint4 *)(stages + stage * kQStageBytes + r * 128 + (((s * 4 + g) ^ qswz(r)) << 4));
         };
-        auto w_frag = [&](int stage, int b) __attribute__((always_inline)) {
+        auto w_frag = [&](int stage, int b, int s) __attribute__((always_inline)) {
             const int r = kQRows + cq * 64 + b * 16 + row;
-            return *(const uint4 *)(stages + stage * kQStageBytes + r * 64 + ((g ^ qswz(r)) << 4));
+            return *(const uint4 *)(stages + stage * kQStageBytes + r * 128 + (((s * 4 + g) ^ qswz(r)) << 4));
         };
         f32x4_t acc[8][4];     // [x subtile][W block]
 #pragma unroll
@@ -677,45 +450,39 @@ __global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs
             for (int b = 0; b < 4; ++b)
                 acc[st][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         uint4 X[8], Wf[4];
-        // Block k (its fragments in X and Wf): wait for this wave's loads of
-        // block k + 1 (those of k + 2 and k + 3 may still run) and for its
-        // fragment reads of block k; meet the other waves (their loads of block
-        // k + 1 are in, their reads of block k are done); load block k + 4 into
-        // block k's stage; multiply block k subtile by subtile, reading block
-        // k + 1's x fragment of each subtile once the subtile is done with
-        // block k's, then block k + 1's W fragments.  The waits and loads
-        // depend on how many blocks remain; the reads and MFMAs do not (after
-        // the last block the reads fetch a stale stage that nothing uses, and a
-        // wave whose rows are all past the run multiplies what is never
-        // stored), so the multiply code has no branches.
+        // Block k, with the fragments of its first 32-deep half in X and Wf:
+        // multiply that half subtile by subtile, reading the second half's x
+        // fragment of each subtile once the subtile is done with the first's
+        // (its W fragments before); then wait for this wave's loads of block
+        // k + 1 and its reads of block k, meet the other waves (their loads of
+        // block k + 1 are in, their reads of block k are done), load block
+        // k + 2 into block k's stage, and multiply the second half while
+        // reading block k + 1's first.  After the last block those reads fetch
+        // a stale stage that nothing uses, and a wave whose rows are all past
+        // the run multiplies what is never stored, so the multiply code has no
+        // branches.
         if (q0 > 0)
             __syncthreads();     // the previous run's last fragment reads are done
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (j < nkb)
-                dma_block(j, j * kQBK);
-        // block 0's loads are the oldest: the rest (up to 12) may still run
-        if (nkb >= 4)
-            asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+        dma_block(0, 0);
+        if (nkb > 1)
+            dma_block(1, kQBK);
+        if (nkb > 1)
+            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
         for (int st = 0; st < 8; ++st)
-            X[st] = x_frag(0, st);
+            X[st] = x_frag(0, st, 0);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            Wf[b] = w_frag(0, b);
+            Wf[b] = w_frag(0, b, 0);
         for (int k = 0; k < nkb; ++k) {
-            const int ahead = nkb - 2 - k;
-            if (ahead >= 2)
-                asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else if (ahead == 1)
-                asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (k + 4 < nkb)
-                dma_block(k & 3, (k + 4) * kQBK);
-            const int nx = (k + 1) & 3;
+            const int cs = k & 1, ns = cs ^ 1;
+            uint4 Wn[4];
+            // sub-step 0 of block k; read sub-step 1's fragments
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                Wn[b] = w_frag(cs, b, 1);
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
 #pragma unroll
@@ -723,11 +490,30 @@ __global__ __launch_bounds__(kQThreads, 1) void saved_bf16_quad_kernel(SavedArgs
                     acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, Wf[b]), __builtin_bit_cast(bf16x8_t, X[st]), acc[st][b],
                         0, 0, 0);
-                X[st] = x_frag(nx, st);
+                X[st] = x_frag(cs, st, 1);
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                Wf[b] = w_frag(nx, b);
+                Wf[b] = Wn[b];
+            // block k + 1 landed everywhere, block k read everywhere
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (k + 2 < nkb)
+                dma_block(cs, (k + 2) * kQBK);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                Wn[b] = w_frag(ns, b, 0);
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[st][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, Wf[b]), __builtin_bit_cast(bf16x8_t, X[st]), acc[st][b],
+                        0, 0, 0);
+                X[st] = x_frag(ns, st, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                Wf[b] = Wn[b];
         }
         // epilogue: lane group g owns columns cq*64 + g*16 .. +15 of the chunk
         // for run rows th*128 + st*16 + row
@@ -825,7 +611,7 @@ __global__ __launch_bounds__(256) void saved_f32_kernel(SavedArgs a)
 }  // namespace
 
 // The 256 x 256 kernel takes a launch whose modules all have d_in a multiple
-// of 32 and whose x and per-slot W are under 4 GB (its loads address them by
+// of 64 and whose x and per-slot W are under 4 GB (its loads address them by
 // 32-bit byte offsets); any other bf16 launch takes saved_bf16_kernel.
 static bool quad_fits(const SavedArgs &a)
 {
@@ -856,13 +642,7 @@ hipError_t launch_saved(bool bf16, const SavedArgs &a, hipStream_t st, const Lau
         }
         const int64_t items = (int64_t)((a.grid_tiles + 1) / 2) * a.col_start[a.n];
         b.per_xcd = (int)((items + kXcds - 1) / kXcds);
-        bool dma = true;
-        for (int i = 0; i < a.n; ++i)
-            dma = dma && a.d_in[i] % kBK == 0;
-        if (dma)
-            launch(saved_bf16_dma_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
-        else
-            launch(saved_bf16_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
+        launch(saved_bf16_kernel, dim3((unsigned)(b.per_xcd * kXcds)), dim3(256), st, t, b);
     } else {
         int cols = 1;
         for (int i = 0; i < a.n; ++i)
