@@ -519,7 +519,7 @@ def measure_saved(wl, K, W):
     nbytes = 2.0 * (T * m.d_in + T * m.d_out + len(used) * m.d_in * m.d_out)
     tfs = flops / (us * 1e-6) / 1e12
     # the launch stages x and W through LDS when every member's d_in is a multiple of 64
-    kernel = "saved_bf16_quad_kernel" if m.d_in % 32 == 0 else "saved_bf16_kernel"
+    kernel = "saved_bf16_quad_kernel" if m.d_in % 64 == 0 else "saved_bf16_kernel"
     del keep, x, y
     torch.cuda.empty_cache()
     return {"workload": f"{wl.name} batch ({T} tokens), every adapter saving o_proj "

@@ -611,13 +611,16 @@ __global__ __launch_bounds__(256) void saved_f32_kernel(SavedArgs a)
 }  // namespace
 
 // The 256 x 256 kernel takes a launch whose modules all have d_in a multiple
-// of 64 and whose x and per-slot W are under 4 GB (its loads address them by
-// 32-bit byte offsets); any other bf16 launch takes saved_bf16_kernel.
+// of 64, whose x buffers are 16-byte aligned (its direct-to-LDS loads move
+// aligned 16-byte pieces) and whose x and per-slot W are under 4 GB (they are
+// addressed by 32-bit byte offsets); any other bf16 launch takes
+// saved_bf16_kernel.
 static bool quad_fits(const SavedArgs &a)
 {
     for (int i = 0; i < a.n; ++i) {
         const uint64_t d_in = (uint64_t)a.d_in[i];
-        if (d_in % kQBK || (uint64_t)a.T * d_in * 2 > UINT32_MAX || (uint64_t)a.d_out[i] * d_in * 2 > UINT32_MAX)
+        if (d_in % kQBK || ((uintptr_t)a.x[i] & 15) || (uint64_t)a.T * d_in * 2 > UINT32_MAX ||
+            (uint64_t)a.d_out[i] * d_in * 2 > UINT32_MAX)
             return false;
     }
     return true;

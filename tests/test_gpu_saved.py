@@ -208,10 +208,12 @@ def test_saved_module_full_size_prefill_sampled():
         check_close(got[n], run_oracle(wl, n), wl.dtype, f"prefill with saved o_proj {n}")
 
 
-# Modules whose d_in is a multiple of 64 take the kernel that stages x and W
-# through LDS with direct-to-LDS loads; these cases run it alone (groups of such
-# modules only): one K block (d_in 64), several, joint runs of two tiles and
-# pairs that straddle two slots, a bias on some slots.
+# Modules whose d_in is a multiple of 64 take the 256 x 256 kernel that stages x
+# and W through LDS with direct-to-LDS loads; these cases run it alone (groups of
+# such modules only): one K block (d_in 64), several, runs of one to four tiles
+# and quads of tiles that straddle two or more slots, tiles of 32 or 48 tokens
+# (batches of at most 1024 tokens) and of 64, d_out not a multiple of 16, a bias
+# on some slots.
 MODS64 = [synth.Module("q", 64, 72), synth.Module("o", 1024, 520), synth.Module("v", 512, 4104)]
 
 
