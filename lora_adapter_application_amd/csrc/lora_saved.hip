@@ -327,7 +327,7 @@ constexpr int kQStageBytes = (kQRows + kSavedCols) * kQBK * 2;   // 64 KB
 constexpr int kQThreads = 512;
 constexpr int kQBlockQuads = 4, kQBlockCols = 8;             // an L2 block of work items
 constexpr int kQBlockItems = kQBlockQuads * kQBlockCols;
-// direct-to-LDS loads per wave per block (1 KB each: 16 stage rows)
+// direct-to-LDS loads per wave per block (1 KB each: 8 stage rows)
 constexpr int kQLoads = (kQRows + kSavedCols) * kQBK * 2 / 1024 / (kQThreads / 64);
 static_assert(kQLoads == 8, "loads per wave per block");
 
