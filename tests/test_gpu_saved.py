@@ -258,3 +258,56 @@ def test_saved_lds_staged_kernel_exact_integers_bit_identical():
         on = np.isin(wl.idx, savers)
         ref = _reference(wl, saved, m.name)
         assert np.array_equal(got[m.name][on], ref[on]), m.name
+
+
+@pytest.mark.parametrize("T", [700, 2500])
+def test_saved_modules_graph_replay_matches_eager(T):
+    """A step with saved modules (both bf16 kernels: q's d_in is not a multiple
+    of 64, o's and v's are) captured into a HIP graph and replayed three times,
+    with eager work on the same ctx between the replays: every replay equals
+    the eager result bit for bit, and the eager result matches the oracle."""
+    mods = [synth.Module("q", 264, 392), synth.Module("o", 1024, 520), synth.Module("v", 512, 4104)]
+    targeted = [[(k, m.name) not in WHICH for m in mods] for k in range(6)]
+    wl = synth.random_case(8700 + T, synth.BF16, mods, T, 6, 32, [32, 16, 8, 1, 24, 32], targeted=targeted,
+                           p_base_only=0.1)
+    saved = _saved_weights(8800 + T, wl, WHICH)
+    keep = []
+    S = make_slots(wl, keep=keep)
+    _load_saved(S, wl, saved, keep)
+    log(f"case saved graph T={T}")
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+    y0 = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+    groups = [[0], [1, 2]]
+
+    def step(ys):
+        S.prepare(idx)
+        for g in groups:
+            S.apply_group(g, [xs[i] for i in g], [ys[i] for i in g], idx)
+
+    ye = [y.clone() for y in y0]
+    step(ye)
+    torch.cuda.synchronize()
+    ref = [from_dev(y, wl.dtype) for y in ye]
+    for mi, m in enumerate(mods):
+        check_close(ref[mi], _reference(wl, saved, m.name), wl.dtype, f"eager {m.name}")
+    yg = [y.clone() for y in y0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(yg)
+    torch.cuda.synchronize()
+    yo = [y.clone() for y in y0]
+    for rep in range(3):
+        for mi in range(len(mods)):
+            yg[mi].copy_(y0[mi])
+            yo[mi].copy_(y0[mi])
+        step(yo)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for mi, m in enumerate(mods):
+            assert np.array_equal(from_dev(yg[mi], wl.dtype), ref[mi]), f"replay {rep} {m.name}"
+            assert np.array_equal(from_dev(yo[mi], wl.dtype), ref[mi]), f"eager {rep} {m.name}"
+    S.close()
