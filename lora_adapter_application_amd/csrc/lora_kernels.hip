@@ -222,7 +222,9 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
     int32_t *wcnt = sm;              // [16][S]
     int32_t *seg = sm + 16 * S;      // [S] first position of slot s
     int32_t *tbase = sm + 17 * S;    // [S] first tile of slot s
+    int32_t *scnt = sm + 18 * S;     // [S] tokens of slot s
     __shared__ int2 wsum[17];
+    __shared__ int32_t n_tiles_sh;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int chunk = blockIdx.x;
     const int i = chunk * 1024 + tid;
@@ -248,11 +250,11 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
     __syncthreads();
     const int my_rank = wave_stable_rank(v, valid, wcnt, S);
     int start = tot, tstart = (tot + kTileTokens - 1) / kTileTokens, n_active, n_tiles;
-    const int nt = tstart;
     block_excl_scan2_1024(start, tstart, wsum, n_active, n_tiles);
     if (tid < S) {
         seg[tid] = start;
         tbase[tid] = tstart;
+        scnt[tid] = tot;
         int run = start + pre;
 #pragma unroll
         for (int w = 0; w < 16; ++w) {
@@ -263,23 +265,40 @@ __global__ __launch_bounds__(1024) void plan_scatter_kernel(const int32_t *__res
         if (chunk == 0) {
             pb.counts[tid] = tot;
             pb.seg_start[tid] = start;
-            for (int j = 0; j < nt; ++j) {
-                Tile t;
-                t.slot = tid;
-                t.start = start + j * kTileTokens;
-                t.len = min(kTileTokens, tot - j * kTileTokens);
-                t.rank = 0;
-                t.scale = 0.f;
-                t.pad[0] = t.pad[1] = t.pad[2] = 0;
-                pb.tiles[tstart + j] = t;
-            }
         }
     }
-    if (chunk == 0 && tid == 0) {
-        *pb.n_tiles = n_tiles;
-        *pb.n_active = n_active;
+    if (tid == 0) {
+        n_tiles_sh = n_tiles;
+        if (chunk == 0) {
+            *pb.n_tiles = n_tiles;
+            *pb.n_active = n_active;
+        }
     }
     __syncthreads();
+    if (chunk == 0) {
+        // the tile list, one tile per thread: tile j belongs to the last slot
+        // whose first tile is at most j (an empty slot shares its first tile
+        // index with the next slot, so that slot is never empty)
+        for (int j = tid; j < n_tiles_sh; j += 1024) {
+            int lo = 0, hi = S - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tbase[mid] <= j)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int q = j - tbase[lo];
+            Tile t;
+            t.slot = lo;
+            t.start = seg[lo] + q * kTileTokens;
+            t.len = min(kTileTokens, scnt[lo] - q * kTileTokens);
+            t.rank = 0;
+            t.scale = 0.f;
+            t.pad[0] = t.pad[1] = t.pad[2] = 0;
+            pb.tiles[j] = t;
+        }
+    }
     if (valid) {
         const int rel = wcnt[wave * S + v] + my_rank - seg[v];
         pb.tile_tok[(int64_t)(tbase[v] + rel / kTileTokens) * kTileTokens + rel % kTileTokens] = i;
@@ -297,7 +316,7 @@ hipError_t launch_plan(const int32_t *idx, int32_t T, int32_t S, const PlanBuffe
         const int n_chunks = (T + 1023) / 1024;
         launch(plan_count_kernel, dim3(n_chunks), dim3(1024), sizeof(int32_t) * (size_t)S * 16, st,
                t ? t[0] : none, idx, T, S, pb);
-        launch(plan_scatter_kernel, dim3(n_chunks), dim3(1024), sizeof(int32_t) * (size_t)S * 18,
+        launch(plan_scatter_kernel, dim3(n_chunks), dim3(1024), sizeof(int32_t) * (size_t)S * 19,
                st, t ? t[1] : none, idx, T, S, n_chunks, pb);
     }
     return hipGetLastError();
