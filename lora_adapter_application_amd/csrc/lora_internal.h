@@ -148,15 +148,19 @@ struct ExpandArgs {
 hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipStream_t st,
                          const LaunchTiming &t);
 
-// Fused decode (bf16, batches of at most kInlinePlanTokens): the shrink and the
-// expand of one group in one launch; expand workgroups wait for the K-split
-// partials of their tile through per-(tile, member) counts in `sync`, which
-// every launch leaves at zero.
+// Fused decode (bf16, batches of at most kInlinePlanTokens, on a device that
+// places workgroup i of a launch on XCD i % 8): the shrink and the expand of
+// one group in one launch; expand workgroups wait for the K-split partials of
+// their tile through per-(tile, member) counts in `sync`, which every launch
+// leaves at zero.  The counts of a tile fill a 128-byte line of their own
+// (kSyncWordsPerTile words: partials stored and consumers past the wait, per
+// member), so no line is shared by tiles of two XCDs.
+constexpr int kSyncWordsPerTile = 32;
+static_assert(2 * kMaxGroup <= kSyncWordsPerTile, "a tile's counts fit its line");
 struct FusedArgs {
     ShrinkArgs s;
     ExpandArgs e;
-    uint32_t *sync;              // [max_tiles][kMaxGroup][2]: partials stored, consumers past the wait
-    int32_t shrink_blocks;       // workgroups of the shrink phase (set by launch_fused)
+    uint32_t *sync;              // [max_tiles][kSyncWordsPerTile]
     int32_t spin_limit;          // polls of a waiting workgroup before it gives up
 };
 hipError_t launch_fused(const FusedArgs &f, const SlotMeta &m, hipStream_t st, const LaunchTiming &t);
@@ -219,5 +223,8 @@ constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
 // device: looked up with hipGetSymbolAddress at the first call for the device,
 // then kept.
 hipError_t scratch_address(int device, void **ptr);
+// Whether workgroup i of a launch runs on XCD i % 8 on `device` (the current
+// device); probed once per device with two launches on `st`, then kept.
+hipError_t xcd_dispatch_check(int device, hipStream_t st, bool *ok);
 
 }  // namespace lora

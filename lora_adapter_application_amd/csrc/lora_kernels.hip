@@ -338,40 +338,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
-// h partials handed from one workgroup to another inside one launch (the fused
-// decode kernel): agent-scope relaxed atomic stores and loads, which gfx950
-// issues as plain global stores / loads with the sc1 bit.  Such a store is
-// written through to memory; such a load is not served from a stale line of
-// the reading XCD's L2.  So partials written on one XCD are read correctly on
-// another without the whole-L2 write-back and invalidation of an agent-scope
-// fence.  Each 16 bytes move as two 8-byte atomics.
-template <bool COH>
-__device__ __forceinline__ void store_h(float *p, const f32x4_t v)
-{
-    if constexpr (COH) {
-        uint64_t *q = (uint64_t *)p;
-        __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2_t{v[0], v[1]}), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, f32x2_t{v[2], v[3]}), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        *(f32x4_t *)p = v;
-    }
-}
-
-template <bool COH>
-__device__ __forceinline__ f32x4_t load_h(const float *p)
-{
-    if constexpr (COH) {
-        uint64_t *q = (uint64_t *)p;
-        const f32x2_t a = __builtin_bit_cast(f32x2_t, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        const f32x2_t b = __builtin_bit_cast(f32x2_t, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        return f32x4_t{a[0], a[1], b[0], b[1]};
-    } else {
-        return *(const f32x4_t *)p;
-    }
-}
-
 __device__ __forceinline__ int member_rank(const SlotMeta &meta, int m, int slot)
 {
     return ((meta.target[m][slot >> 5] >> (slot & 31)) & 1u) ? (int)meta.rank[slot] : 0;
@@ -500,7 +466,7 @@ __device__ __forceinline__ void mfma_kblock(f32x4_t (&acc)[NB], const KBlock<NB>
     }
 }
 
-template <int NB, bool DOUBLE_BUFFER, bool COH = false>
+template <int NB, bool DOUBLE_BUFFER>
 __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
                                             unsigned char *smem)
 {
@@ -567,7 +533,7 @@ __device__ __forceinline__ void shrink_bgmv(const ShrinkView &v, const Tile &til
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if (b < nb)
-                store_h<COH>(hrow + b * 16 + g * 4, acc[b]);
+                *(f32x4_t *)(hrow + b * 16 + g * 4) = acc[b];
     }
 }
 
@@ -589,7 +555,7 @@ constexpr int kLdsRow = kShrinkKBlock + 8;   // bf16 elements per staged A row (
 // register sets are small.
 constexpr int sgmv_depth(int NB) { return NB <= 2 ? 4 : NB == 4 ? 3 : 2; }
 
-template <int NB, bool COH = false>
+template <int NB>
 __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &tile, int tokv, int nb,
                                             uint16_t *lds)
 {
@@ -719,7 +685,7 @@ __device__ __forceinline__ void shrink_sgmv(const ShrinkView &v, const Tile &til
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if (b < nb)
-                store_h<COH>(hrow + b * 16 + g * 4, acc[b]);
+                *(f32x4_t *)(hrow + b * 16 + g * 4) = acc[b];
     }
 }
 
@@ -950,7 +916,7 @@ constexpr int shrink_smem_bytes(int NB)
 
 // The shrink of one tile for K split `split` of member m: writes the member's h
 // partial of that split for the tile's rows.  Requires 0 < tile.rank.
-template <int NB, bool MIXED, bool COH = false>
+template <int NB, bool MIXED>
 __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int split, const Tile &tile,
                                             int tokv, unsigned char *smem)
 {
@@ -967,15 +933,15 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs &a, int m, int spli
         // the segment loop sized to the tile's own rank blocks: a wider one
         // would load (clamped) A^T rows past them on every K block
         if (NB >= 2 && nb <= 1)
-            shrink_sgmv<1, COH>(v, tile, tokv, nb, (uint16_t *)smem);
+            shrink_sgmv<1>(v, tile, tokv, nb, (uint16_t *)smem);
         else if (NB >= 4 && nb <= 2)
-            shrink_sgmv<(NB >= 4 ? 2 : NB), COH>(v, tile, tokv, nb, (uint16_t *)smem);
+            shrink_sgmv<(NB >= 4 ? 2 : NB)>(v, tile, tokv, nb, (uint16_t *)smem);
         else if (NB >= 8 && nb <= 4)
-            shrink_sgmv<(NB >= 8 ? 4 : NB), COH>(v, tile, tokv, nb, (uint16_t *)smem);
+            shrink_sgmv<(NB >= 8 ? 4 : NB)>(v, tile, tokv, nb, (uint16_t *)smem);
         else
-            shrink_sgmv<NB, COH>(v, tile, tokv, nb, (uint16_t *)smem);
+            shrink_sgmv<NB>(v, tile, tokv, nb, (uint16_t *)smem);
     } else
-        shrink_bgmv<NB, !MIXED && NB <= 4, COH>(v, tile, tokv, nb, smem);
+        shrink_bgmv<NB, !MIXED && NB <= 4>(v, tile, tokv, nb, smem);
 }
 
 // L2 warm-up of one (K split, member) block while the inline plan is formed.
@@ -1237,7 +1203,7 @@ __device__ __forceinline__ void expand_store(const uint16_t *hs_hi, const uint16
 
 // h partials of a tile for the expand, summed over the K splits in split
 // order: thread tid owns quads e = tid + 256 i (i < NB) of the len x nb*16 block.
-template <int NB, bool COH = false>
+template <int NB>
 __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArgs &a, int m,
                                             const Tile &tile, int nb)
 {
@@ -1251,7 +1217,7 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
         for (int i = 0; i < NB; ++i) {
             const int e = tid + 256 * i;
             const int t = e / quads, q = e - t * quads;
-            hsum[i] = e < n_el ? load_h<COH>(hbase + (int64_t)(tile.start + t) * a.R_pad + q * 4)
+            hsum[i] = e < n_el ? *(const f32x4_t *)(hbase + (int64_t)(tile.start + t) * a.R_pad + q * 4)
                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     } else {
@@ -1265,7 +1231,7 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
             const float *hp = hbase + (int64_t)(tile.start + t) * a.R_pad + q * 4;
 #pragma unroll
             for (int u = 0; u < MS; ++u)
-                pv[u] = (e < n_el && u < splits) ? load_h<COH>(hp + (int64_t)u * a.split_stride)
+                pv[u] = (e < n_el && u < splits) ? *(const f32x4_t *)(hp + (int64_t)u * a.split_stride)
                                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
             f32x4_t sum = pv[0];
 #pragma unroll
@@ -1276,15 +1242,15 @@ __device__ __forceinline__ void load_h_sums(f32x4_t (&hsum)[NB], const ExpandArg
     }
 }
 
-// Hand-over of a tile's h partials inside one fused launch.  A shrink
-// workgroup, once its partial is stored (agent scope) and every one of its
-// stores has completed, adds one to the (tile, member) count.  An expand
-// workgroup waits until the count reaches the member's K-split count, with a
-// bounded number of polls; past the bound it sets LORA_FLAG_FUSED_TIMEOUT and
-// leaves its rows of y untouched.  Every expand workgroup of the (tile,
-// member) then adds one to the consumer count, and the last one returns both
-// counts to zero, so the next launch (or the next replay of a captured graph)
-// starts from zero.
+// Hand-over of a tile's h partials inside one fused launch (fused_xcd_kernel).
+// A shrink workgroup, once its partial is stored and every one of its stores
+// has completed, adds one to the (tile, member) count.  An expand workgroup
+// waits until the count reaches the member's K-split count, with a bounded
+// number of polls; past the bound it sets LORA_FLAG_FUSED_TIMEOUT and leaves
+// its rows of y untouched.  Every expand workgroup of the (tile, member) then
+// adds one to the consumer count, and the last one returns both counts to
+// zero, so the next launch (or the next replay of a captured graph) starts
+// from zero.
 struct FusedWait {
     uint32_t *cnt;          // K-split partials stored so far
     uint32_t *consumed;     // expand workgroups past the wait
@@ -1294,24 +1260,38 @@ struct FusedWait {
     uint32_t *flags;        // sticky device flags
 };
 
-__device__ __forceinline__ void fused_signal(uint32_t *cnt)
+// Hand-over inside one XCD (fused_xcd_kernel, where every workgroup of a tile
+// runs on the tile's XCD).  The L2 is shared by the CUs of an XCD, global
+// stores pass the write-through L1 into it, and atomics execute in it, so a
+// count kept with workgroup-scope atomics (no cache bypass) and partials
+// written with plain stores are seen by the other workgroups of the XCD at L2
+// latency.  The shrink side waits until its own stores are acknowledged (they
+// are in L2) before the count moves.
+__device__ __forceinline__ void xcd_signal(uint32_t *cnt)
 {
-    // each thread's stores of the partial have completed (written through)
-    // before the count moves
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ bool fused_wait(const FusedWait &fw)
+// The expand side polls the count with an atomic compare-and-swap that never
+// succeeds (the count never reaches ~0u): an atomic executes in L2 and returns
+// its value there, where a load could be served by a stale line of the CU's
+// L1.  The partials it reads afterwards were not read on this CU earlier in
+// the launch (every line of a tile's rows is read only once its count is
+// complete, and tiles of adjacent rows run on other XCDs), and the L1 starts
+// the launch empty of them, so plain loads return the L2 copy.
+__device__ __forceinline__ bool xcd_wait(const FusedWait &fw)
 {
     __shared__ int ok;
     if (threadIdx.x == 0) {
         bool done = false;
         for (int n = 0; n <= fw.limit; ++n) {
-            if ((int)__hip_atomic_load(fw.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= fw.expected) {
+            uint32_t seen = ~0u;
+            __hip_atomic_compare_exchange_strong(fw.cnt, &seen, ~0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            if ((int)seen >= fw.expected) {
                 done = true;
                 break;
             }
@@ -1319,16 +1299,14 @@ __device__ __forceinline__ bool fused_wait(const FusedWait &fw)
         }
         if (!done)
             atomicOr(fw.flags, LORA_FLAG_FUSED_TIMEOUT);
-        const uint32_t prev = __hip_atomic_fetch_add(fw.consumed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(fw.consumed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if ((int)prev + 1 == fw.consumers) {
-            __hip_atomic_store(fw.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(fw.consumed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(fw.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(fw.consumed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         ok = done ? 1 : 0;
     }
     __syncthreads();
-    // the partials are read after the count was seen (program order and the
-    // barrier; the compiler must not hoist them)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return ok != 0;
 }
@@ -1337,8 +1315,8 @@ __device__ __forceinline__ bool fused_wait(const FusedWait &fw)
 // Requires 0 < tile.rank and an adapter that targets the member.  Every global
 // load (h partials, B, y) is issued before any arithmetic.  FUSED (the fused
 // decode kernel): B, y and the output terms are loaded first, then the
-// workgroup waits for the tile's partials (fw) and reads them with agent-scope
-// loads.
+// workgroup waits for the tile's partials (fw) and reads them from the L2 of
+// its XCD.
 template <int NB, bool TERMS, int SUB, bool FUSED = false>
 __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chunk, const Tile &tile,
                                             int tokv, int flags, uint16_t *hs_hi, uint16_t *hs_lo,
@@ -1394,9 +1372,9 @@ __device__ __forceinline__ void expand_tile(const ExpandArgs &a, int m, int chun
             ot.c[piece] = *(const uint4 *)((const uint16_t *)a.bias[m] + o);
     }
     if constexpr (FUSED) {
-        if (!fused_wait(*fw))
+        if (!xcd_wait(*fw))
             return;
-        load_h_sums<NB, true>(hsum, a, m, tile, nb);
+        load_h_sums<NB>(hsum, a, m, tile, nb);
     }
     // h -> bf16 high and low halves in LDS
     constexpr int HS = NB * 16 + 8;             // row stride (bf16 elements, 16-byte multiple)
@@ -1461,44 +1439,36 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 }
 
 // ----------------------------------------------------------------------------
-// fused decode: shrink and expand of one module group in one launch
-//
-// The first f.shrink_blocks workgroups are the shrink of shrink_bf16_kernel
-// (inline plan or published tiles), storing their partials with agent scope
-// and counting them per (tile, member); the rest are the expand of
-// expand_bf16_kernel, which find their tile the same way (inline plan or
-// published record), load B, y and the output terms, wait for the tile's
-// count and then read its partials.  Each XCD dispatches its workgroups in
-// order, and every shrink workgroup precedes every expand workgroup, so no
-// expand workgroup can hold a CU that a shrink workgroup it waits for needs.
-template <int NB, bool TERMS, int SUB, int PLAN, bool WARM>
-__global__ __launch_bounds__(256) void fused_bf16_kernel(FusedArgs f, SlotMeta meta)
+// fused decode with the hand-over inside each XCD.  The chip dispatches
+// workgroup i to XCD i % 8 (checked once per device at ctx creation); tile t
+// belongs to XCD t % 8, and on each XCD the workgroups come in the order: the
+// shrink of its tiles ((K split, member) pairs, tile after tile), then their
+// expand ((member, column chunk) pairs, tile after tile).  So every workgroup
+// of a tile shares one L2, and the partials and counts move at L2 latency
+// (xcd_signal / xcd_wait); an expand workgroup waits only for shrink
+// workgroups dispatched before it on its own XCD.
+template <int NB, bool TERMS, int SUB, int PLAN>
+__global__ __launch_bounds__(256) void fused_xcd_kernel(FusedArgs f, SlotMeta meta)
 {
     constexpr int kExpandLds = 2 * expand_hs_elems(NB, SUB) * 2;
     __shared__ __attribute__((aligned(16))) unsigned char lds[cmax(shrink_smem_bytes(NB), kExpandLds)];
     __shared__ TilePlanLds P;
     const int lane = threadIdx.x & 63;
     const MetaRegs mr = load_meta_regs(meta);
+    const int x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+    const int n_x = (f.s.grid_tiles - x + kXcds - 1) / kXcds;      // tiles x, x + 8, ...
+    const int s_per = f.s.grid_splits * f.s.n, e_per = f.e.col_start[f.e.n];
     Tile tile;
     int tokv;
-    if ((int)blockIdx.x < f.shrink_blocks) {
+    if (j < n_x * s_per) {
         const ShrinkArgs &a = f.s;
-        const int w = xcd_item(a.n, (int)blockIdx.x);
-        if (w >= a.grid_tiles * a.grid_splits * a.n)
-            return;
-        const int m = w % a.n, split = (w / a.n) % a.grid_splits, bt = w / (a.n * a.grid_splits);
+        const int r = j % s_per;
+        const int m = r % a.n, split = r / a.n, bt = (j / s_per) * kXcds + x;
         const bool lead = split == 0 && m == 0;     // publishes the tile
         if constexpr (PLAN == kPlanInline) {
             int v[kPlanPerThread];
             plan_load_idx(a.idx, a.T, v);
-            uint32_t wv[kWarmLoads];
-            if constexpr (WARM)
-                warm_split(a, m, split, bt, wv);
-            const bool has_tile = plan_tile(v, a.T, a.S, a.tile_cap, mr, a.plan, P, bt, lead,
-                                            lead && bt == 0, tile, tokv);
-            if constexpr (WARM)
-                keep_warm(wv);
-            if (!has_tile)
+            if (!plan_tile(v, a.T, a.S, a.tile_cap, mr, a.plan, P, bt, lead, lead && bt == 0, tile, tokv))
                 return;
         } else {
             const int n_tiles = *a.plan.n_tiles;
@@ -1511,20 +1481,17 @@ __global__ __launch_bounds__(256) void fused_bf16_kernel(FusedArgs f, SlotMeta m
         }
         if (split >= a.splits[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
             return;
-        shrink_tile<NB, false, true>(a, m, split, tile, tokv, lds);
-        fused_signal(f.sync + ((int64_t)bt * kMaxGroup + m) * 2);
-    } else {
+        shrink_tile<NB, false>(a, m, split, tile, tokv, lds);
+        xcd_signal(f.sync + (int64_t)bt * kSyncWordsPerTile + 2 * m);
+    } else if (j < n_x * (s_per + e_per)) {
         const ExpandArgs &a = f.e;
-        const int n_items = a.grid_tiles * a.col_start[a.n];
-        const int w = xcd_item(a.xcd_group, (int)blockIdx.x - f.shrink_blocks);
-        if (w >= n_items)
-            return;
+        const int jj = j - n_x * s_per;
+        const int c = jj % e_per, bt = (jj / e_per) * kXcds + x;
         int m = 0;
-        while (m + 1 < a.n && w >= a.grid_tiles * a.col_start[m + 1])
+        while (m + 1 < a.n && c >= a.col_start[m + 1])
             ++m;
-        const int local = w - a.grid_tiles * a.col_start[m];
+        const int chunk = c - a.col_start[m];
         const int chunks = a.col_start[m + 1] - a.col_start[m];
-        const int bt = local % a.grid_tiles, chunk = local / a.grid_tiles;
         if constexpr (PLAN == kPlanInline) {
             int v[kPlanPerThread];
             plan_load_idx(f.s.idx, f.s.T, v);
@@ -1542,7 +1509,7 @@ __global__ __launch_bounds__(256) void fused_bf16_kernel(FusedArgs f, SlotMeta m
         const int flags = meta_flags(mr, tile.slot);
         if (chunk * kExpandCols >= a.d_out[m] || tile.rank == 0 || !meta_targets(mr, m, tile.slot))
             return;
-        uint32_t *cnt = f.sync + ((int64_t)bt * kMaxGroup + m) * 2;
+        uint32_t *cnt = f.sync + (int64_t)bt * kSyncWordsPerTile + 2 * m;
         const FusedWait fw{cnt, cnt + 1, a.splits[m], chunks, f.spin_limit, f.s.plan.flags};
         uint16_t *hs_hi = (uint16_t *)lds, *hs_lo = hs_hi + expand_hs_elems(NB, SUB);
         expand_tile<NB, TERMS, SUB, true>(a, m, chunk, tile, tokv, flags, hs_hi, hs_lo, &fw);
@@ -1771,59 +1738,50 @@ hipError_t launch_expand(bool bf16, const ExpandArgs &a, const SlotMeta &m, hipS
     return hipGetLastError();
 }
 
-template <bool TERMS, int PLAN, bool WARM>
-static void launch_fused_bf16(const FusedArgs &f, const SlotMeta &m, dim3 grid, hipStream_t st,
-                              const LaunchTiming &t)
+template <bool TERMS, int PLAN>
+static void launch_fused_xcd(const FusedArgs &f, const SlotMeta &m, dim3 grid, hipStream_t st,
+                             const LaunchTiming &t)
 {
     const int nbmax = f.s.R_pad / 16;
     const int sub = (f.e.tile_cap + 15) / 16;
     const dim3 block(256);
     if (nbmax <= 1) {
         if (sub <= 2)
-            launch(fused_bf16_kernel<1, TERMS, 2, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<1, TERMS, 2, PLAN>, grid, block, 0, st, t, f, m);
         else
-            launch(fused_bf16_kernel<1, TERMS, 4, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<1, TERMS, 4, PLAN>, grid, block, 0, st, t, f, m);
     } else if (nbmax <= 2) {
         if (sub <= 3)
-            launch(fused_bf16_kernel<2, TERMS, 3, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<2, TERMS, 3, PLAN>, grid, block, 0, st, t, f, m);
         else
-            launch(fused_bf16_kernel<2, TERMS, 4, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<2, TERMS, 4, PLAN>, grid, block, 0, st, t, f, m);
     } else if (nbmax <= 4) {
         if (sub <= 3)
-            launch(fused_bf16_kernel<4, TERMS, 3, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<4, TERMS, 3, PLAN>, grid, block, 0, st, t, f, m);
         else
-            launch(fused_bf16_kernel<4, TERMS, 4, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<4, TERMS, 4, PLAN>, grid, block, 0, st, t, f, m);
     } else {
         if (sub <= 3)
-            launch(fused_bf16_kernel<8, TERMS, 3, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<8, TERMS, 3, PLAN>, grid, block, 0, st, t, f, m);
         else
-            launch(fused_bf16_kernel<8, TERMS, 4, PLAN, WARM>, grid, block, 0, st, t, f, m);
+            launch(fused_xcd_kernel<8, TERMS, 4, PLAN>, grid, block, 0, st, t, f, m);
     }
 }
 
-hipError_t launch_fused(const FusedArgs &f_in, const SlotMeta &m, hipStream_t st, const LaunchTiming &t)
+hipError_t launch_fused(const FusedArgs &f, const SlotMeta &m, hipStream_t st, const LaunchTiming &t)
 {
-    FusedArgs f = f_in;
-    const dim3 gs = xcd_grid((int64_t)f.s.grid_tiles * f.s.grid_splits * f.s.n, f.s.n);
-    const dim3 ge = xcd_grid((int64_t)f.e.grid_tiles * f.e.col_start[f.e.n], f.e.xcd_group);
-    f.shrink_blocks = (int)gs.x;
-    const dim3 grid(gs.x + ge.x);
+    // every XCD runs the shrink and expand items of ceil(grid_tiles / 8) tiles
+    // (XCDs with fewer tiles leave their last items idle)
+    const int64_t per_xcd = (int64_t)((f.s.grid_tiles + kXcds - 1) / kXcds) *
+                            (f.s.grid_splits * f.s.n + f.e.col_start[f.e.n]);
+    const dim3 grid((unsigned)(per_xcd * kXcds));
     const bool inl = f.s.plan_mode == kPlanInline;
-    if (f.e.terms) {
-        if (inl)
-            f.s.warm ? launch_fused_bf16<true, kPlanInline, true>(f, m, grid, st, t)
-                     : launch_fused_bf16<true, kPlanInline, false>(f, m, grid, st, t);
-        else
-            f.s.warm ? launch_fused_bf16<true, kPlanTiles, true>(f, m, grid, st, t)
-                     : launch_fused_bf16<true, kPlanTiles, false>(f, m, grid, st, t);
-    } else {
-        if (inl)
-            f.s.warm ? launch_fused_bf16<false, kPlanInline, true>(f, m, grid, st, t)
-                     : launch_fused_bf16<false, kPlanInline, false>(f, m, grid, st, t);
-        else
-            f.s.warm ? launch_fused_bf16<false, kPlanTiles, true>(f, m, grid, st, t)
-                     : launch_fused_bf16<false, kPlanTiles, false>(f, m, grid, st, t);
-    }
+    if (f.e.terms)
+        inl ? launch_fused_xcd<true, kPlanInline>(f, m, grid, st, t)
+            : launch_fused_xcd<true, kPlanTiles>(f, m, grid, st, t);
+    else
+        inl ? launch_fused_xcd<false, kPlanInline>(f, m, grid, st, t)
+            : launch_fused_xcd<false, kPlanTiles>(f, m, grid, st, t);
     return hipGetLastError();
 }
 
@@ -1913,6 +1871,49 @@ constexpr int kScratchDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kScratchDevices] = {};
 }  // namespace
+
+// XCD of the executing wave: HW_REG_XCC_ID (hardware register 20), bits 3:0.
+__global__ void xcd_check_kernel(uint32_t *mismatch)
+{
+    const int id = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 0xfu);
+    if (threadIdx.x == 0 && id != (int)blockIdx.x % kXcds)
+        atomicAdd(mismatch, 1u);
+}
+
+namespace {
+std::mutex g_xcd_mu;
+int g_xcd_state[kScratchDevices] = {};     // 0 unknown, 1 matches, 2 does not
+}  // namespace
+
+hipError_t xcd_dispatch_check(int device, hipStream_t st, bool *ok)
+{
+    if (device < 0 || device >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_xcd_mu);
+    if (g_xcd_state[device] == 0) {
+        uint32_t *d = nullptr, h = 1;
+        hipError_t e = hipMalloc(&d, sizeof(uint32_t));
+        if (e == hipSuccess)
+            e = hipMemsetAsync(d, 0, sizeof(uint32_t), st);
+        // a grid of several workgroups per CU, with workgroups of 256 and 1024 threads
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(xcd_check_kernel, dim3(4096), dim3(256), 0, st, d);
+            hipLaunchKernelGGL(xcd_check_kernel, dim3(1024), dim3(1024), 0, st, d);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(&h, d, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(st);
+        if (d)
+            (void)hipFree(d);
+        if (e != hipSuccess)
+            return e;
+        g_xcd_state[device] = h == 0 ? 1 : 2;
+    }
+    *ok = g_xcd_state[device] == 1;
+    return hipSuccess;
+}
 
 hipError_t scratch_address(int device, void **ptr)
 {

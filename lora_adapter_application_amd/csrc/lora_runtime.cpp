@@ -73,7 +73,7 @@ struct Workspace {
     PlanBuffers plan{};
     float *hpart = nullptr;
     int hbuf_rows = 0;       // rows of one group member's block of h partials
-    uint32_t *sync = nullptr;   // fused decode counts [max_tiles][kMaxGroup][2], kept at zero
+    uint32_t *sync = nullptr;   // fused decode counts [max_tiles][kSyncWordsPerTile], kept at zero
                                 // between launches (null: no fused launches on this workspace)
 };
 
@@ -120,6 +120,7 @@ struct lora_ctx {
     Workspace ws;                            // the ctx's plan buffers and h partials
     int max_tiles = 0;
     void *scratch = nullptr;                 // this device's static scratch array (no-alloc calls)
+    bool xcd_local = false;                  // workgroup i runs on XCD i % 8 (fused decode hand-over in L2)
     hipStream_t side = nullptr;
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
@@ -619,8 +620,8 @@ int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
 }
 
 // Shrink and expand of one group in one launch (bf16 batches of at most
-// kInlinePlanTokens on a workspace with fused counts), then the saved-module
-// products of the group.
+// kInlinePlanTokens on a workspace with fused counts, on a device that places
+// workgroup i on XCD i % 8), then the saved-module products of the group.
 int run_fused(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const int32_t *modules,
               const void *const *x, void *const *y, hipStream_t s)
 {
@@ -655,7 +656,7 @@ int run_fused(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const int
 
 bool fused_applies(const lora_ctx *c, const Workspace &ws, const BatchState &bs)
 {
-    return c->dtype == LORA_BF16 && ws.sync && bs.T <= kInlinePlanTokens;
+    return c->dtype == LORA_BF16 && c->xcd_local && ws.sync && bs.T <= kInlinePlanTokens;
 }
 
 int check_group(lora_ctx *c, int32_t n, const int32_t *modules)
@@ -852,7 +853,7 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     if (e == hipSuccess)
         e = dalloc(c, &c->ws.plan.tile_tok, sizeof(int32_t) * (size_t)c->max_tiles * kTileTokens);
     if (e == hipSuccess)
-        e = dalloc(c, &c->ws.sync, sizeof(uint32_t) * 2 * kMaxGroup * (size_t)c->max_tiles);
+        e = dalloc(c, &c->ws.sync, sizeof(uint32_t) * kSyncWordsPerTile * (size_t)c->max_tiles);
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_tiles, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.n_active, sizeof(int32_t));
     if (e == hipSuccess) e = dalloc(c, &c->ws.plan.flags, sizeof(uint32_t));
@@ -863,6 +864,7 @@ int lora_slots_create(lora_ctx **out, int32_t max_loras, int32_t max_rank,
     // this device's static scratch array (lora_apply_group_noalloc), looked up
     // once per device with the device current
     if (e == hipSuccess) e = scratch_address(device, &c->scratch);
+    if (e == hipSuccess) e = xcd_dispatch_check(device, c->side, &c->xcd_local);
     if (e == hipSuccess) e = hipStreamSynchronize(c->side);
     if (e != hipSuccess) {
         int status = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)

@@ -1,6 +1,7 @@
 """The fused decode launch (lora_apply_group_fused on bf16 batches of at most
-1024 tokens: shrink and expand in one launch, the expand workgroups waiting for
-their tile's K-split partials through per-(tile, member) counts).
+1024 tokens: shrink and expand in one launch, every workgroup of a tile on the
+tile's XCD, the expand workgroups waiting for their tile's K-split partials
+through per-(tile, member) counts).
 
 Its results must equal the two-launch path of the separate lora_shrink /
 lora_expand entry points bit for bit, launch after launch (the counts return to
@@ -47,12 +48,18 @@ def test_fused_equals_two_launches_repeatedly(case):
     xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
     mi = list(range(len(mods)))
     S.prepare(idx)
+    S.profile_begin(64)
     for rep in range(12):                           # inline plan first, published tiles after
         ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
         S.apply_group_fused(mi, xs, ys, idx)
         torch.cuda.synchronize()
         for i, m in enumerate(mods):
             assert np.array_equal(from_dev(ys[i], wl.dtype), split[m.name]), (rep, m.name)
+    launches = S.profile_end()["launches"]
+    log(f"fused case {case}: launches {launches}")
+    # one fused launch per call (this device places workgroup i on XCD i % 8,
+    # else the calls would have taken the two launches)
+    assert launches["fused"] == 12 and launches["shrink"] == 0 and launches["expand"] == 0, launches
     assert S.flags() == 0
     for m in mods:
         check_close(split[m.name], run_oracle(wl, m.name), wl.dtype, f"fused case {case} {m.name}")
