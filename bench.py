@@ -26,7 +26,8 @@ Passes over the same K steps (after W warm-up steps):
   plan_amortized  one lora_plan_prepare, then the K steps' applies only (the
              layers of a model share one batch and its slot indices);
   fused      (decode batches) lora_apply_group_fused: each group's shrink and
-             expand in one launch;
+             expand in one launch; and its plan_amortized form, one
+             lora_plan_prepare, then the K steps' fused applies;
   step_spread     an event after each step: p10 / p50 / p90 step times;
   kernels    per-dispatch start / stop events the library records with each
              of its dispatches (hipExtLaunchKernelGGL): kernel times.
@@ -309,7 +310,7 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
     eager_s = time.perf_counter() - t0
     # fused decode: each group's shrink and expand in one launch (bf16 batches of
     # at most 1024 tokens; lora_apply_group_fused)
-    fused_s = None
+    fused_s = fused_amort_s = None
     if T <= 1024:
         bound_f = bind_all(fused=True)
         for i in range(W):
@@ -321,6 +322,18 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         torch.cuda.synchronize()
         fused_s = time.perf_counter() - t0
         del bound_f
+        # the same with the plan amortized over the layers: one lora_plan_prepare,
+        # then K steps of fused applies (the first forms the plan inline and
+        # publishes it, the others read it)
+        bound_fa = bind_all(prepare=False, fused=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        slots.prepare(idx)
+        for i in range(K):
+            bound_fa[(W + i) % L]()
+        torch.cuda.synchronize()
+        fused_amort_s = time.perf_counter() - t0
+        del bound_fa
     # plan amortized over the layers: one lora_plan_prepare, then K steps of applies
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -464,7 +477,10 @@ def measure(wl_name, args, K, W, kernel_timing=True, launch="eager"):
         "graph": {"ms_per_step": round(graph_s / K * 1e3, 5), "value": round(T * K / graph_s, 1)},
         "fused": None if fused_s is None else {
             "ms_per_step": round(fused_s / K * 1e3, 5), "value": round(T * K / fused_s, 1),
-            "pass": "lora_apply_group_fused: each group's shrink and expand in one launch"},
+            "pass": "lora_apply_group_fused: each group's shrink and expand in one launch",
+            "plan_amortized": {"ms_per_step": round(fused_amort_s / K * 1e3, 5),
+                               "value": round(T * K / fused_amort_s, 1),
+                               "pass": "one lora_plan_prepare, then the K steps' fused applies"}},
         "plan_amortized": {"ms_per_step": round(amort_s / K * 1e3, 5),
                            "value": round(T * K / amort_s, 1),
                            "pass": "one lora_plan_prepare, then the K steps' applies"},

@@ -1448,7 +1448,7 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 // (xcd_signal / xcd_wait); an expand workgroup waits only for shrink
 // workgroups dispatched before it on its own XCD.
 template <int NB, bool TERMS, int SUB, int PLAN>
-__global__ __launch_bounds__(256) void fused_xcd_kernel(FusedArgs f, SlotMeta meta)
+__device__ __forceinline__ void fused_xcd_body(const FusedArgs &f, const SlotMeta &meta)
 {
     constexpr int kExpandLds = 2 * expand_hs_elems(NB, SUB) * 2;
     __shared__ __attribute__((aligned(16))) unsigned char lds[cmax(shrink_smem_bytes(NB), kExpandLds)];
@@ -1514,6 +1514,25 @@ __global__ __launch_bounds__(256) void fused_xcd_kernel(FusedArgs f, SlotMeta me
         uint16_t *hs_hi = (uint16_t *)lds, *hs_lo = hs_hi + expand_hs_elems(NB, SUB);
         expand_tile<NB, TERMS, SUB, true>(a, m, chunk, tile, tokv, flags, hs_hi, hs_lo, &fw);
     }
+}
+
+template <int NB, bool TERMS, int SUB, int PLAN>
+__global__ __launch_bounds__(256) void fused_xcd_kernel(FusedArgs f, SlotMeta meta)
+{
+    fused_xcd_body<NB, TERMS, SUB, PLAN>(f, meta);
+}
+
+// The same for rank blocks of 16, tiles of 32 tokens and no output terms, held
+// to 128 registers a lane so that four waves fit each SIMD: four workgroups a
+// CU, so the whole grid of a Llama-7B-shaped decode group is resident at once
+// (at three, a quarter of its expand workgroups started only as shrink
+// workgroups retired).  This instance fits without spilling; the wider ones
+// do not.
+template <int PLAN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void fused_xcd_r16_kernel(
+    FusedArgs f, SlotMeta meta)
+{
+    fused_xcd_body<1, false, 2, PLAN>(f, meta);
 }
 
 // ----------------------------------------------------------------------------
@@ -1746,7 +1765,9 @@ static void launch_fused_xcd(const FusedArgs &f, const SlotMeta &m, dim3 grid, h
     const int sub = (f.e.tile_cap + 15) / 16;
     const dim3 block(256);
     if (nbmax <= 1) {
-        if (sub <= 2)
+        if (sub <= 2 && !TERMS)
+            launch(fused_xcd_r16_kernel<PLAN>, grid, block, 0, st, t, f, m);
+        else if (sub <= 2)
             launch(fused_xcd_kernel<1, TERMS, 2, PLAN>, grid, block, 0, st, t, f, m);
         else
             launch(fused_xcd_kernel<1, TERMS, 4, PLAN>, grid, block, 0, st, t, f, m);
