@@ -66,6 +66,42 @@ def test_fused_equals_two_launches_repeatedly(case):
     S.close()
 
 
+TERMS_CASES = [
+    # modules, max_loras, R, ranks, T, bias slots, DoRA slots
+    ([(4096, 4096), (4096, 1024)], 8, 16, [16, 9, 16, 16, 4, 16, 16, 1], 256, {1, 3, 4}, {2, 3, 6}),
+    ([(5120, 1032), (1000, 520)], 6, 32, [32, 17, 32, 5, 32, 32], 600, {0, 2, 5}, {1, 2}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TERMS_CASES)))
+def test_fused_with_output_terms_equals_two_launches(case):
+    # slots with an output bias and / or a DoRA factor take the fused kernel's
+    # output-terms instances
+    shapes, S_, R, ranks, T, bias, dora = TERMS_CASES[case]
+    mods = [synth.Module(f"m{i}", a, b) for i, (a, b) in enumerate(shapes)]
+    wl = synth.random_case(9800 + case, synth.BF16, mods, T, S_, R, ranks, p_base_only=0.1, zipf_s=1.0)
+    synth.add_output_terms(wl, 9800 + case, bias_slots=bias, dora_slots=dora)
+    log(f"case fused terms {case}: {shapes} S={S_} R={R} T={T} bias {sorted(bias)} dora {sorted(dora)}")
+    S = make_slots(wl)
+    split = run_gpu(wl, S, path="split")
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+    S.prepare(idx)
+    S.profile_begin(16)
+    for rep in range(3):
+        ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+        S.apply_group_fused(list(range(len(mods))), xs, ys, idx)
+        torch.cuda.synchronize()
+        for i, m in enumerate(mods):
+            assert np.array_equal(from_dev(ys[i], wl.dtype), split[m.name]), (rep, m.name)
+    launches = S.profile_end()["launches"]
+    assert launches["fused"] == 3 and launches["shrink"] == 0 and launches["expand"] == 0, launches
+    assert S.flags() == 0
+    for m in mods:
+        check_close(split[m.name], run_oracle(wl, m.name), wl.dtype, f"fused terms case {case} {m.name}")
+    S.close()
+
+
 def test_fused_graph_replays():
     mods = [synth.Module("q", 4096, 4096), synth.Module("v", 4096, 4096)]
     wl = synth.random_case(9700, synth.BF16, mods, 256, 8, 16, [16] * 8, p_base_only=0.1)
