@@ -102,6 +102,69 @@ def test_fused_with_output_terms_equals_two_launches(case):
     S.close()
 
 
+def test_fused_launches_on_two_streams_at_once():
+    # two ctxs launching fused decodes on two streams with no synchronisation
+    # between them, so their kernels run side by side: each launch's
+    # workgroups must still meet on their tiles' XCDs
+    mods = [synth.Module("q", 4096, 4096), synth.Module("v", 4096, 1024)]
+    cases = []
+    for c, (S_, R) in enumerate([(8, 16), (12, 32)]):
+        wl = synth.random_case(9900 + c, synth.BF16, mods, 384, S_, R, [R] * S_, p_base_only=0.1)
+        S = make_slots(wl)
+        split = run_gpu(wl, S, path="split")
+        idx = torch.from_numpy(wl.idx).cuda()
+        xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+        cases.append((wl, S, split, idx, xs))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = [[], []]
+    for rep in range(16):
+        for c, (wl, S, split, idx, xs) in enumerate(cases):
+            with torch.cuda.stream(streams[c]):
+                ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+                S.apply_group_fused([0, 1], xs, ys, idx, stream=streams[c])
+                outs[c].append(ys)
+    torch.cuda.synchronize()
+    for c, (wl, S, split, idx, xs) in enumerate(cases):
+        for rep, ys in enumerate(outs[c]):
+            for i, m in enumerate(mods):
+                assert np.array_equal(from_dev(ys[i], wl.dtype), split[m.name]), (c, rep, m.name)
+        assert S.flags() == 0
+        S.close()
+
+
+def test_fused_launches_beside_a_long_kernel():
+    # fused decodes on one stream while another stream runs large matrix
+    # products that hold most of the chip: the fused workgroups start as CUs
+    # free up, in whatever order, and must still meet on their tiles' XCDs
+    mods = [synth.Module("q", 4096, 4096), synth.Module("v", 4096, 4096)]
+    wl = synth.random_case(9950, synth.BF16, mods, 256, 8, 16, [16] * 8, p_base_only=0.1)
+    S = make_slots(wl)
+    split = run_gpu(wl, S, path="split")
+    idx = torch.from_numpy(wl.idx).cuda()
+    xs = [to_dev(wl.x[m.name], wl.dtype) for m in mods]
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.randn(4096, 4096, device="cuda")
+    busy, work = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    with torch.cuda.stream(busy):
+        for _ in range(6):
+            c = torch.mm(a, b)
+    for rep in range(24):
+        with torch.cuda.stream(work):
+            ys = [to_dev(wl.y[m.name], wl.dtype) for m in mods]
+            S.apply_group_fused([0, 1], xs, ys, idx, stream=work)
+            outs.append(ys)
+    torch.cuda.synchronize()
+    del c
+    for rep, ys in enumerate(outs):
+        for i, m in enumerate(mods):
+            assert np.array_equal(from_dev(ys[i], wl.dtype), split[m.name]), (rep, m.name)
+    assert S.flags() == 0
+    S.close()
+
+
 def test_fused_graph_replays():
     mods = [synth.Module("q", 4096, 4096), synth.Module("v", 4096, 4096)]
     wl = synth.random_case(9700, synth.BF16, mods, 256, 8, 16, [16] * 8, p_base_only=0.1)
