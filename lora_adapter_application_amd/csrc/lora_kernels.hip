@@ -1439,9 +1439,14 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(ExpandArgs a, SlotMeta
 }
 
 // ----------------------------------------------------------------------------
-// fused decode with the hand-over inside each XCD.  The chip dispatches
-// workgroup i to XCD i % 8 (checked once per device at ctx creation); tile t
-// belongs to XCD t % 8, and on each XCD the workgroups come in the order: the
+// fused decode with the hand-over inside each XCD.  The chip deals the
+// workgroups of a launch to its XCDs in turn: workgroup i to XCD i % 8 on an
+// idle chip (checked once per device at ctx creation), and to XCD (i + c) % 8
+// for some c when other kernels run beside the launch.  Either way workgroups
+// whose indices agree mod 8 share an XCD, which is all the hand-over needs (a
+// placement that broke it would show as waits that give up, flagged, never as
+// partials read before they are in).  Tile t belongs to residue t % 8, and on
+// each XCD the workgroups come in the order: the
 // shrink of its tiles ((K split, member) pairs, tile after tile), then their
 // expand ((member, column chunk) pairs, tile after tile).  So every workgroup
 // of a tile shares one L2, and the partials and counts move at L2 latency
