@@ -338,8 +338,9 @@ int lora_apply_group(lora_ctx *ctx, int32_t n, const int32_t *modules, const voi
  * lora_apply_group with the shrink and the expand of a decode batch in one
  * launch (the two kernels of the update fused, h kept between workgroups of
  * one launch instead of between launches).  Applies to bf16 batches of at most
- * 1024 tokens on a device that places workgroup i of a launch on XCD i % 8
- * (MI355X; lora_slots_create checks this once per device); other batches, and
+ * 1024 tokens on a device that deals the workgroups of a launch to its XCDs
+ * in turn, so that workgroups whose indices agree mod 8 share an XCD (MI355X;
+ * lora_slots_create checks this once per device); other batches, and
  * every batch elsewhere, take the two launches of lora_apply_group.  All
  * workgroups of a tile run on one XCD, and the expand workgroups wait for
  * their tile's K-split partials through per-(tile, module) counts in that

@@ -149,7 +149,7 @@ hipError_t launch_shrink(bool bf16, const ShrinkArgs &a, const SlotMeta &m, hipS
                          const LaunchTiming &t);
 
 // Fused decode (bf16, batches of at most kInlinePlanTokens, on a device that
-// places workgroup i of a launch on XCD i % 8): the shrink and the expand of
+// deals the workgroups of a launch to its XCDs in turn): the shrink and the expand of
 // one group in one launch; expand workgroups wait for the K-split partials of
 // their tile through per-(tile, member) counts in `sync`, which every launch
 // leaves at zero.  The counts of a tile fill a 128-byte line of their own
@@ -223,8 +223,9 @@ constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
 // device: looked up with hipGetSymbolAddress at the first call for the device,
 // then kept.
 hipError_t scratch_address(int device, void **ptr);
-// Whether workgroup i of a launch runs on XCD i % 8 on `device` (the current
-// device); probed once per device with two launches on `st`, then kept.
+// Whether the workgroups of a launch whose indices agree mod 8 run on one XCD
+// on `device` (the current device); probed once per device with two launches
+// on `st`, then kept.
 hipError_t xcd_dispatch_check(int device, hipStream_t st, bool *ok);
 
 }  // namespace lora

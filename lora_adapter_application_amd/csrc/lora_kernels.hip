@@ -1898,44 +1898,54 @@ std::mutex g_scratch_mu;
 void *g_scratch_ptr[kScratchDevices] = {};
 }  // namespace
 
-// XCD of the executing wave: HW_REG_XCC_ID (hardware register 20), bits 3:0.
-__global__ void xcd_check_kernel(uint32_t *mismatch)
+// Placement probe.  state[r] (r < 8) records 1 + the XCD of the first
+// workgroup of residue r mod 8 to get there; state[8] counts workgroups that
+// find their residue on another XCD.  The XCD of the executing wave is
+// HW_REG_XCC_ID (hardware register 20), bits 3:0.
+__global__ void xcd_check_kernel(uint32_t *state)
 {
-    const int id = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 0xfu);
-    if (threadIdx.x == 0 && id != (int)blockIdx.x % kXcds)
-        atomicAdd(mismatch, 1u);
+    if (threadIdx.x == 0) {
+        const uint32_t id = 1u + (__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 0xfu);
+        const uint32_t seen = atomicCAS(&state[blockIdx.x % kXcds], 0u, id);
+        if (seen != 0u && seen != id)
+            atomicAdd(&state[kXcds], 1u);
+    }
 }
 
 namespace {
 std::mutex g_xcd_mu;
-int g_xcd_state[kScratchDevices] = {};     // 0 unknown, 1 matches, 2 does not
+int g_xcd_state[kScratchDevices] = {};     // 0 unknown, 1 holds, 2 does not
 }  // namespace
 
+// Whether the workgroups of a launch whose indices agree mod 8 share an XCD
+// (the deal may start at any XCD when other kernels run, so the probe checks
+// that, not i % 8 itself): two launches of several workgroups per CU, with
+// workgroups of 256 and of 1024 threads, each against cleared state.
 hipError_t xcd_dispatch_check(int device, hipStream_t st, bool *ok)
 {
     if (device < 0 || device >= kScratchDevices)
         return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(g_xcd_mu);
     if (g_xcd_state[device] == 0) {
-        uint32_t *d = nullptr, h = 1;
-        hipError_t e = hipMalloc(&d, sizeof(uint32_t));
+        constexpr size_t kWords = kXcds + 1;
+        uint32_t *d = nullptr, h[2][kWords] = {};
+        hipError_t e = hipMalloc(&d, 2 * kWords * sizeof(uint32_t));
         if (e == hipSuccess)
-            e = hipMemsetAsync(d, 0, sizeof(uint32_t), st);
-        // a grid of several workgroups per CU, with workgroups of 256 and 1024 threads
+            e = hipMemsetAsync(d, 0, 2 * kWords * sizeof(uint32_t), st);
         if (e == hipSuccess) {
             hipLaunchKernelGGL(xcd_check_kernel, dim3(4096), dim3(256), 0, st, d);
-            hipLaunchKernelGGL(xcd_check_kernel, dim3(1024), dim3(1024), 0, st, d);
+            hipLaunchKernelGGL(xcd_check_kernel, dim3(1024), dim3(1024), 0, st, d + kWords);
             e = hipGetLastError();
         }
         if (e == hipSuccess)
-            e = hipMemcpyAsync(&h, d, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+            e = hipMemcpyAsync(h, d, sizeof h, hipMemcpyDeviceToHost, st);
         if (e == hipSuccess)
             e = hipStreamSynchronize(st);
         if (d)
             (void)hipFree(d);
         if (e != hipSuccess)
             return e;
-        g_xcd_state[device] = h == 0 ? 1 : 2;
+        g_xcd_state[device] = h[0][kXcds] == 0 && h[1][kXcds] == 0 ? 1 : 2;
     }
     *ok = g_xcd_state[device] == 1;
     return hipSuccess;

@@ -120,7 +120,7 @@ struct lora_ctx {
     Workspace ws;                            // the ctx's plan buffers and h partials
     int max_tiles = 0;
     void *scratch = nullptr;                 // this device's static scratch array (no-alloc calls)
-    bool xcd_local = false;                  // workgroup i runs on XCD i % 8 (fused decode hand-over in L2)
+    bool xcd_local = false;                  // workgroups equal mod 8 share an XCD (fused decode hand-over in L2)
     hipStream_t side = nullptr;
     hipEvent_t load_done = nullptr;
     uint64_t load_gen = 0;
@@ -621,7 +621,8 @@ int run_expand(lora_ctx *c, const Workspace &ws, const BatchState &bs, int n,
 
 // Shrink and expand of one group in one launch (bf16 batches of at most
 // kInlinePlanTokens on a workspace with fused counts, on a device that places
-// workgroup i on XCD i % 8), then the saved-module products of the group.
+// workgroups whose indices agree mod 8 on one XCD), then the saved-module
+// products of the group.
 int run_fused(lora_ctx *c, const Workspace &ws, BatchState &bs, int n, const int32_t *modules,
               const void *const *x, void *const *y, hipStream_t s)
 {
