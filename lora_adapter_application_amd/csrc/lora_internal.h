@@ -137,7 +137,7 @@ struct ExpandArgs {
     int32_t grid_tiles;
     int32_t grid_cols;                  // max column chunks over the members
     int32_t col_start[kMaxGroup + 1];   // bf16 kernel: chunks of the members before member i
-    int32_t xcd_group;                  // work items per XCD group (bf16 kernel)
+    int32_t xcd_group;                  // work items per XCD group (bf16 kernel); < 0: tile t on residue t % 8
     int32_t tile_major;                 // bf16 kernel: chunks of a tile are consecutive items
     const void *bias[kMaxGroup];        // module base: [S][d_out], ctx dtype
     const float *dora[kMaxGroup];       // module base: [S][d_out]

@@ -522,7 +522,7 @@ ExpandArgs expand_args(lora_ctx *c, const Workspace &ws, const BatchState &bs, i
     const bool large = T > kInlinePlanTokens;
     a.tile_major = large && T >= 128 * c->S;
     a.tile_cap = bs.tile_cap;
-    a.xcd_group = large ? (int)((items + 7) / 8) : 1;
+    a.xcd_group = large ? (int)((items + 7) / 8) : -1;
     a.terms = 0;
     for (int k = 0; k < c->S; ++k)
         if (c->slot_flags[k] && (!bs.hinted || c->hint[k]))
